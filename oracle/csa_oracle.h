@@ -1,0 +1,32 @@
+/* csa_oracle.h -- CPU reference of the CSA decode step.  TEST INFRASTRUCTURE
+ * ONLY (tests, smoke check, benchmark CPU baseline); never part of the
+ * product path.  Shares nothing with the HIP library. */
+#ifndef CSA_ORACLE_H
+#define CSA_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+double csa_oracle_e2m1(int code);  /* 0..15 */
+double csa_oracle_e4m3(int code);  /* 0..255 */
+double csa_oracle_ue8m0(int byte); /* 0..255 */
+double csa_oracle_f16(int bits);   /* 0..65535 */
+
+void csa_oracle_decode_idx_rows(const uint8_t *rows, int64_t n, float *out /* [n][128] */);
+void csa_oracle_decode_kv_rows(const uint8_t *rows, int64_t n, float *out /* [n][512] */);
+void csa_oracle_score(const uint8_t *idx_rows, int64_t n, const float *q_idx, const float *w_idx,
+                      int n_idx_heads, float *scores);
+int64_t csa_oracle_topk(const float *scores, int64_t n, int k, int32_t *sel, float *sel_score);
+int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel, int n_sel,
+                         const float *q_attn, int n_heads, double softmax_scale, float *out,
+                         float *lse);
+int csa_oracle_decode_step(const uint8_t *idx_rows, const uint8_t *kv_rows, int64_t n_rows,
+                           const float *q_idx, const float *w_idx, int n_idx_heads,
+                           const float *q_attn, int n_heads, double softmax_scale, int k,
+                           int32_t *sel, float *sel_score, float *out, float *lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,288 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``check_*`` function takes an ``oracle.Oracle`` and raises
+``AssertionError`` on a mismatch.  They are used twice: on the real oracle
+(test_oracle_pins.py) and on deliberately broken copies of its source
+(test_oracle_mutants.py), which every plausible mistake must fail.
+
+Independent references used here:
+  * element decoding by library routines: ``torch.float8_e4m3fn``,
+    ``torch.float8_e8m0fnu`` and ``numpy.float16`` (little-endian '<f2');
+  * the E2M1 value table of the OCP MX v1.0 specification (golden file);
+  * numbers printed on the DS4X page, "Packed cache ABI" (golden file);
+  * numpy float64 ``einsum`` for the score, Python ``sorted`` for the top-k,
+    ``torch.nn.functional.scaled_dot_product_attention`` in float64 on the CPU
+    for attention, plus closed-form special cases.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- golden files
+
+def load_kv_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            k, v = (s.strip() for s in line.split("=", 1))
+            out[k] = float(v) if "." in v else int(v)
+    return out
+
+
+def e2m1_golden() -> np.ndarray:
+    vals = {}
+    with open(os.path.join(GOLDEN, "ocp_mx_e2m1_values.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                c, v = line.split()
+                vals[int(c)] = float(v)
+    mags = np.array([vals[c] for c in range(8)], dtype=np.float64)
+    return np.concatenate([mags, -mags])  # codes 8..15 carry the sign bit
+
+
+# ------------------------------------------------ library-based element decode
+
+def lib_e4m3(codes) -> np.ndarray:
+    t = torch.as_tensor(np.asarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def lib_ue8m0(b) -> np.ndarray:
+    t = torch.as_tensor(np.asarray(b, dtype=np.uint8)).view(torch.float8_e8m0fnu)
+    return t.to(torch.float64).numpy()
+
+
+def lib_f16(bits) -> np.ndarray:
+    return np.asarray(bits, dtype="<u2").view("<f2").astype(np.float64)
+
+
+def ref_decode_idx(rows: np.ndarray) -> np.ndarray:
+    """Decode 68-byte indexer rows with the library references above."""
+    rows = np.asarray(rows, dtype=np.uint8).reshape(-1, 68)
+    codes = np.empty((rows.shape[0], 128), dtype=np.int64)
+    codes[:, 0::2] = rows[:, :64] & 15
+    codes[:, 1::2] = rows[:, :64] >> 4
+    vals = e2m1_golden()[codes]
+    scale = np.repeat(lib_ue8m0(rows[:, 64:68]), 32, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return (vals * scale).astype(np.float32)
+
+
+def ref_decode_kv(rows: np.ndarray) -> np.ndarray:
+    rows = np.asarray(rows, dtype=np.uint8).reshape(-1, 583)
+    out = np.empty((rows.shape[0], 512), dtype=np.float32)
+    scale = np.repeat(lib_ue8m0(rows[:, 576:583]), 64, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        out[:, :448] = (lib_e4m3(rows[:, :448]) * scale).astype(np.float32)
+    out[:, 448:] = np.ascontiguousarray(rows[:, 448:576]).view("<f2").astype(np.float32)
+    return out
+
+
+def same_bits_or_nan(a: np.ndarray, b: np.ndarray) -> bool:
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    an, bn = np.isnan(a), np.isnan(b)
+    if not np.array_equal(an, bn):
+        return False
+    return np.array_equal(a[~an].view(np.uint32), b[~bn].view(np.uint32))
+
+
+# ------------------------------------------------------------ row builders
+
+def idx_rows_all_pairs() -> np.ndarray:
+    """Rows that put every (E2M1 code, UE8M0 byte) pair through the decoder:
+    row r uses scale byte r for all four blocks and codes cycling 0..15."""
+    rows = np.zeros((256, 68), dtype=np.uint8)
+    el = np.arange(128) % 16
+    packed = (el[0::2] | (el[1::2] << 4)).astype(np.uint8)
+    rows[:, :64] = packed
+    rows[:, 64:68] = np.arange(256, dtype=np.uint8)[:, None]
+    return rows
+
+
+def kv_rows_all_pairs() -> np.ndarray:
+    """Every (E4M3 byte, UE8M0 byte) pair: row r has scale byte r in all seven
+    blocks and non-RoPE bytes cycling through 0..255; RoPE slots hold
+    assorted FP16 codes (normal, subnormal, inf, NaN)."""
+    rows = np.zeros((256, 583), dtype=np.uint8)
+    rows[:, :448] = (np.arange(448) % 256).astype(np.uint8)[None, :]
+    rows[:, 576:583] = np.arange(256, dtype=np.uint8)[:, None]
+    rng = np.random.default_rng(7)
+    f16 = rng.integers(0, 65536, size=(256, 64), dtype=np.uint32).astype("<u2")
+    f16[:, :8] = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x7C00], dtype="<u2")
+    f16[:, 8] = 0xFC00
+    f16[:, 9] = 0x7E01
+    rows[:, 448:576] = f16.view(np.uint8).reshape(256, 128)
+    return rows
+
+
+def random_idx_rows(n: int, seed: int) -> np.ndarray:
+    """Random codes with mixed, moderate scales (bytes 120..134)."""
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, 256, size=(n, 68), dtype=np.uint8)
+    rows[:, 64:68] = rng.integers(120, 135, size=(n, 4), dtype=np.uint8)
+    return rows
+
+
+def random_kv_rows(n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, 256, size=(n, 583), dtype=np.uint8)
+    codes = rows[:, :448]
+    codes[(codes & 0x7F) == 0x7F] = 0x3F  # no NaN codes
+    rows[:, 576:583] = rng.integers(120, 132, size=(n, 7), dtype=np.uint8)
+    f16 = rng.standard_normal((n, 64)).astype("<f2")
+    rows[:, 448:576] = f16.view(np.uint8).reshape(n, 128)
+    return rows
+
+
+# ------------------------------------------------------------------ checks
+
+def check_tables(o) -> None:
+    e2 = e2m1_golden()
+    got = np.array([o.e2m1(c) for c in range(16)])
+    assert np.array_equal(got, e2) and math.copysign(1, o.e2m1(8)) < 0, "E2M1 table"
+    got = np.array([o.e4m3(c) for c in range(256)])
+    ref = lib_e4m3(np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "E4M3 NaN codes"
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)]), "E4M3 table"
+    got = np.array([o.ue8m0(b) for b in range(256)])
+    ref = lib_ue8m0(np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "UE8M0 NaN"
+    assert np.array_equal(got[:255], ref[:255]), "UE8M0 table"
+    bits = np.arange(65536)
+    got = np.array([o.f16(int(b)) for b in bits])
+    ref = lib_f16(bits)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "FP16 NaN"
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m]), "FP16 table"
+    # spot values of the formats' definitions
+    assert o.e4m3(0x7E) == 448.0 and o.e4m3(0x38) == 1.0 and o.e4m3(0x08) == 2.0**-6
+    assert o.e4m3(0x01) == 2.0**-9
+    assert o.ue8m0(127) == 1.0 and o.ue8m0(0) == 2.0**-127 and o.ue8m0(254) == 2.0**127
+    assert o.f16(0x3C00) == 1.0 and o.f16(0x0001) == 2.0**-24 and o.f16(0x7BFF) == 65504.0
+
+
+def check_decode(o) -> None:
+    rows = idx_rows_all_pairs()
+    assert same_bits_or_nan(o.decode_idx(rows), ref_decode_idx(rows)), "indexer row decode (code x scale grid)"
+    rows = kv_rows_all_pairs()
+    assert same_bits_or_nan(o.decode_kv(rows), ref_decode_kv(rows)), "KV row decode (code x scale grid)"
+    # row stride and field positions: distinct random rows decode independently
+    rows = random_idx_rows(5, 1)
+    assert same_bits_or_nan(o.decode_idx(rows), ref_decode_idx(rows)), "indexer row stride"
+    rows = random_kv_rows(5, 2)
+    assert same_bits_or_nan(o.decode_kv(rows), ref_decode_kv(rows)), "KV row stride"
+
+
+def ref_score(idx_rows, q_idx, w_idx) -> np.ndarray:
+    k = ref_decode_idx(idx_rows).astype(np.float64)
+    d = np.einsum("hi,ji->jh", np.asarray(q_idx, np.float64), k)
+    s = (np.asarray(w_idx, np.float64)[None, :] * np.maximum(d, 0.0)).sum(axis=1)
+    return s.astype(np.float32)
+
+
+def check_score(o) -> None:
+    rng = np.random.default_rng(11)
+    for n, h in ((1, 1), (7, 2), (64, 3), (33, 8)):
+        rows = random_idx_rows(n, 100 + n)
+        q = rng.standard_normal((h, 128)).astype(np.float32)
+        w = rng.uniform(0, 1, h).astype(np.float32)
+        got = o.score(rows, q, w)
+        ref = ref_score(rows, q, w)
+        assert np.all(np.abs(got - ref) <= 2.0**-23 * np.abs(ref)), f"score n={n} H={h}"
+    # H = 1, w = 1 with a positive dot product: the score is the plain dot
+    rows = random_idx_rows(16, 5)
+    k = ref_decode_idx(rows).astype(np.float64)
+    q = np.sign(k[0]).astype(np.float32)[None, :]
+    got = o.score(rows[:1], q, np.ones(1, np.float32))
+    assert got[0] == np.float32(np.dot(q[0].astype(np.float64), k[0])), "H=1 plain dot"
+    # w = 0 -> 0; the zero cache -> every score exactly +0
+    assert np.all(o.score(rows, rng.standard_normal((4, 128)).astype(np.float32), np.zeros(4, np.float32)) == 0)
+    zero = np.zeros((9, 68), dtype=np.uint8)
+    zero[:, 64:] = 127
+    s = o.score(zero, rng.standard_normal((4, 128)).astype(np.float32), np.ones(4, np.float32))
+    assert np.all(s.view(np.uint32) == 0), "zero cache scores are +0"
+    # a head whose dot is negative contributes nothing (ReLU), weights scale heads
+    q2 = np.stack([q[0], -q[0]])
+    got = o.score(rows[:1], q2, np.array([0.25, 1.0], np.float32))
+    assert got[0] == np.float32(0.25 * np.dot(q[0].astype(np.float64), k[0])), "ReLU / weights"
+
+
+def ref_topk(scores: np.ndarray, k: int):
+    order = sorted(range(len(scores)), key=lambda j: (1 if math.isnan(scores[j]) else 0,
+                                                       0.0 if math.isnan(scores[j]) else -float(scores[j]), j))
+    return order[:k]
+
+
+def check_topk(o) -> None:
+    rng = np.random.default_rng(3)
+    for n in (0, 1, 5, 511, 512, 513, 1500):
+        s = rng.integers(0, 40, n).astype(np.float32) * 0.5  # many ties
+        sel, ss, k_eff = o.topk(s, 512)
+        ref = ref_topk(list(s), 512)
+        assert k_eff == min(512, n)
+        assert list(sel[:k_eff]) == ref, f"top-k n={n}"
+        assert np.all(sel[k_eff:] == -1)
+        assert np.array_equal(ss[:k_eff], s[ref]) if k_eff else True
+    # zero cache: every score ties, rows 0..511 in order
+    sel, _, _ = o.topk(np.zeros(4096, np.float32), 512)
+    assert list(sel) == list(range(512)), "zero-cache tie break"
+    # -0 ties with +0; NaN sorts after every number
+    s = np.array([np.nan, -0.0, 0.0, -1.0, np.inf, np.nan], np.float32)
+    sel, _, _ = o.topk(s, 6)
+    assert list(sel) == [4, 1, 2, 3, 0, 5], "signed zero / NaN order"
+    s = rng.standard_normal(3000).astype(np.float32)
+    sel, _, _ = o.topk(s, 512)
+    assert list(sel) == ref_topk(list(s), 512), "distinct scores"
+
+
+def ref_attention(kv_rows, sel, q_attn, scale):
+    kv = torch.from_numpy(ref_decode_kv(np.asarray(kv_rows)[np.asarray(sel)]).astype(np.float64))
+    q = torch.from_numpy(np.asarray(q_attn, np.float64))
+    h, n = q.shape[0], kv.shape[0]
+    kvb = kv[None, None].expand(1, h, n, 512)
+    o = torch.nn.functional.scaled_dot_product_attention(q[None, :, None, :], kvb, kvb,
+                                                         scale=float(scale))[0, :, 0, :]
+    logits = (q @ kv.T) * float(scale)
+    lse = torch.logsumexp(logits, dim=1)
+    return o.numpy(), lse.numpy()
+
+
+def check_attention(o) -> None:
+    rng = np.random.default_rng(9)
+    rows = random_kv_rows(40, 4)
+    scale = float(np.float32(1 / math.sqrt(512)))
+    for nsel, h in ((1, 1), (3, 2), (17, 4), (40, 3)):
+        sel = rng.permutation(40)[:nsel].astype(np.int32)
+        q = rng.standard_normal((h, 512)).astype(np.float32)
+        out, lse = o.attention(rows, sel, q, scale)
+        ref_o, ref_l = ref_attention(rows, sel, q, scale)
+        assert np.max(np.abs(out - ref_o)) <= 1e-6 * max(1e-30, np.max(np.abs(ref_o))), f"attention n_sel={nsel}"
+        assert np.allclose(lse, ref_l, rtol=1e-6, atol=1e-6), "lse"
+    kv = ref_decode_kv(rows)
+    # one selected row: the output is that row exactly
+    out, _ = o.attention(rows, np.array([7], np.int32), rng.standard_normal((2, 512)).astype(np.float32), scale)
+    assert np.array_equal(out[0], kv[7]) and np.array_equal(out[1], kv[7]), "k=1"
+    # q = 0: the output is the mean of the selected rows and lse = log(n)
+    sel = np.array([1, 5, 9, 30], np.int32)
+    out, lse = o.attention(rows, sel, np.zeros((1, 512), np.float32), scale)
+    mean = kv[sel].astype(np.float64).mean(axis=0)
+    assert np.max(np.abs(out[0] - mean)) <= 1e-6 * np.max(np.abs(mean)), "q=0 mean"
+    assert abs(lse[0] - math.log(4)) < 1e-6, "q=0 lse"
+    # no row selected: zero output and lse = -inf
+    out, lse = o.attention(rows, np.zeros(0, np.int32), np.ones((2, 512), np.float32), scale)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention)

@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in copies of the oracle's C source (on the CPU)
+and require that the pins catch every one of them."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+# (name, exact text in csa_oracle.c, replacement)
+MUTANTS = [
+    ("e2m1_bias", "ldexp(1.0 + m / 2.0, e - 1)", "ldexp(1.0 + m / 2.0, e)"),
+    ("e2m1_subnormal", "ldexp((double)m, -1)", "ldexp((double)m, 0)"),
+    ("nibble_order", "(i % 2 == 0) ? (byte & 15) : (byte >> 4)", "(i % 2 == 0) ? (byte >> 4) : (byte & 15)"),
+    ("idx_scale_block", "r[64 + i / 32]", "r[64 + (i / 32 + 1) % 4]"),
+    ("idx_stride", "rows + j * IDX_ROW;\n    for (int i = 0; i < 128", "rows + j * 64;\n    for (int i = 0; i < 128"),
+    ("e4m3_subnormal", "ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    ("e4m3_bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("e4m3_nan", "if (e == 15 && m == 7) return NAN;", ""),
+    ("ue8m0_bias", "ldexp(1.0, byte - 127)", "ldexp(1.0, byte - 128)"),
+    ("ue8m0_nan", "if (byte == 255) return NAN;", ""),
+    ("kv_scale_block", "r[576 + i / 64]", "r[576 + (i / 64 + 1) % 7]"),
+    ("f16_endian", "r[448 + 2 * t] | (r[448 + 2 * t + 1] << 8)", "(r[448 + 2 * t] << 8) | r[448 + 2 * t + 1]"),
+    ("f16_bias", "ldexp(1.0 + m / 1024.0, e - 15)", "ldexp(1.0 + m / 1024.0, e - 14)"),
+    ("f16_subnormal", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("rope_dropped", "out[j * 512 + 448 + t] = (float)csa_oracle_f16(bits);", "out[j * 512 + 448 + t] = 0.0f * bits;"),
+    ("score_no_relu", "double relu = (d > 0.0) ? d : 0.0;", "double relu = d;"),
+    ("score_no_weight", "s += (double)w_idx[h] * relu;", "s += relu;"),
+    ("score_q_transposed", "(double)q_idx[h * 128 + i]", "(double)q_idx[i * n_idx_heads + h]"),
+    ("score_float_accum", "double d = 0.0;\n      for (int i = 0; i < 128; ++i) d +=",
+     "float d = 0.0f;\n      for (int i = 0; i < 128; ++i) d +="),
+    ("topk_ascending", "if (a->s > b->s) return -1;", "if (a->s > b->s) return 1;"),
+    ("topk_tie_high_index", "return (a->j < b->j) ? -1 : (a->j > b->j) ? 1 : 0;",
+     "return (a->j > b->j) ? -1 : (a->j < b->j) ? 1 : 0;"),
+    ("topk_nan_first", "if (an != bn) return an ? 1 : -1;", "if (an != bn) return an ? -1 : 1;"),
+    ("attn_no_scale", "logit[t] = softmax_scale * d;", "logit[t] = d;"),
+    ("attn_lse_no_max", "lse[h] = (float)(m + log(z));", "lse[h] = (float)log(z);"),
+    ("attn_no_normalise", "(float)(acc[e] / z)", "(float)(acc[e])"),
+    ("attn_q_row", "const float *q = q_attn + (size_t)h * 512;", "const float *q = q_attn;"),
+]
+
+
+def _caught(o) -> list:
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(o)
+        except AssertionError:
+            failed.append(check.__name__)
+        except (ValueError, FloatingPointError, MemoryError):
+            failed.append(check.__name__)
+    return failed
+
+
+def test_mutant_list_applies():
+    src = open(oracle.SRC).read()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) == 1, f"mutant {name}: pattern must occur exactly once"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mut.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        so = oracle.build(src=path, out=os.path.join(d, "libmut.so"))
+        failed = _caught(oracle.Oracle(so))
+    assert failed, f"planted mistake '{name}' passed every pin"
