@@ -1,0 +1,192 @@
+"""Benchmark of the CSA decode step on one MI355X.
+
+One step = score every packed indexer row, select the exact top-512, attend
+over the selected packed KV rows, for every session of the workload (all of
+it inside libcsa.so).  Inputs are seeded synthetic data already resident in
+HBM.  Before every timed step the 256 MB Infinity Cache (MALL) and the L2s
+are flushed by reading a 1 GiB buffer outside the step's events, so each
+step streams its history from HBM ("cold"); back-to-back ("warm") timing is
+reported as a secondary figure.
+
+Prints one JSON line (rank 0).  Usage:
+    python bench.py [--gpus 1] [--steps 50] [--warmup 3] [--workload frontier-1m-rows]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "CSA decode-step latency (ms) + achieved HBM GB/s vs peak at 128K–1M rows"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="frontier-1m-rows")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=0,
+                   help="rows of session 0 the oracle runs on (0: the whole session)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(n_rows: int, n_idx_heads: int, n_heads: int) -> dict:
+    """Bytes a decode step must move at least once (one session)."""
+    k = min(512, n_rows)
+    score = 68 * n_rows + 4 * 128 * n_idx_heads + 4 * n_idx_heads
+    attn = 583 * k + 4 * 512 * n_heads + 4 * 512 * n_heads + 4 * n_heads + 4 * 512 + 4 * 512
+    return {"score": score, "attention": attn, "step": score + attn}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
+              "(the row-sharded multi-GPU plan is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import long_context_sparse_score_amd as csa
+
+    wl = {w.name: w for w in gen.WORKLOADS}[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    sess_np = [gen.session(wl.cid, s=i) for i in range(wl.n_sessions)]
+    sess = []
+    for s in sess_np:
+        sess.append({k: torch.from_numpy(s[k]).to(dev) for k in ("idx_rows", "kv_rows", "q_idx", "w_idx", "q_attn")})
+    scale = sess_np[0]["softmax_scale"]
+    print(f"[bench] workload {wl.name}: {wl.n_sessions} x {wl.n_rows} rows, generated in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+
+    step = csa.DecodeStep(sess, scale)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)  # 1 GiB
+    stream = torch.cuda.current_stream()
+
+    def do_flush():
+        flush.sum()
+
+    for _ in range(a.warmup):
+        do_flush()
+        step()
+    torch.cuda.synchronize()
+
+    # cold steps: events bracket the decode step only
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for e0, e1 in ev:
+        do_flush()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    cold = [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    # warm steps: back to back
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(a.steps):
+        step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm = w0.elapsed_time(w1) / a.steps
+
+    # dominant kernel: the indexer score pass, timed cold on the same stream
+    sc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    scores = [torch.empty(wl.n_rows, dtype=torch.float32, device=dev) for _ in sess]
+    for e0, e1 in sc_ev:
+        do_flush()
+        e0.record(stream)
+        for s, o in zip(sess, scores):
+            csa.score(s["idx_rows"], s["q_idx"], s["w_idx"], o)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    score_ms = statistics.mean(e0.elapsed_time(e1) for e0, e1 in sc_ev) / wl.n_sessions
+
+    ab = algorithmic_bytes(wl.n_rows, wl.n_idx_heads, wl.n_heads)
+    ms = statistics.mean(cold)
+    med = statistics.median(cold)
+    step_bytes = ab["step"] * wl.n_sessions
+    score_gbs = ab["score"] / (score_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(ms, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) rows packed to MXFP4 / E4M3+FP16+UE8M0)",
+        "config": {
+            "workload": wl.name,
+            "rows_per_session": wl.n_rows,
+            "sessions": wl.n_sessions,
+            "indexer_heads": wl.n_idx_heads,
+            "attention_heads": wl.n_heads,
+            "topk": 512,
+            "cache": "cold: MALL and L2 flushed before each step, outside its events",
+        },
+        "median_ms": round(med, 5),
+        "p10_ms": round(float(np.percentile(cold, 10)), 5),
+        "p90_ms": round(float(np.percentile(cold, 90)), 5),
+        "warm_ms_per_step": round(warm, 5),
+        "wall_ms_per_step_incl_flush": round(wall * 1e3 / a.steps, 5),
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+        "roofline": {
+            "kernel": "csa score pass (score_rows_kernel)",
+            "bound": "hbm",
+            "achieved": round(score_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(score_gbs / HBM_PEAK_GBS, 5),
+            "traffic": None,
+            "launch_ms": round(score_ms, 5),
+            "algorithmic_bytes_per_launch": ab["score"],
+        },
+    }
+
+    if not a.no_cpu_baseline:
+        import oracle
+
+        s0 = sess_np[0]
+        n = a.cpu_sample_rows or wl.n_rows
+        o = oracle.get()
+        t = time.perf_counter()
+        o.decode_step(s0["idx_rows"][:n], s0["kv_rows"][:n], s0["q_idx"], s0["w_idx"], s0["q_attn"], scale)
+        dt = time.perf_counter() - t
+        per_session_ms = dt * 1e3 * (wl.n_rows / n)
+        line["cpu_baseline"] = {
+            "value": round(per_session_ms * wl.n_sessions, 3),
+            "unit": "ms",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"one decode step of session 0 over its first {n} rows "
+                      f"({dt:.2f} s measured), scaled by rows x sessions to the whole workload",
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

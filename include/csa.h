@@ -1,0 +1,147 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) CSA decode-step library, libcsa.so.
+ *
+ * The operation: one decode step of DeepSeek-V4-Flash compressed sparse
+ * attention (CSA) over a packed, compressed KV history, as described on the
+ * DS4X page: the batch-one indexer scores the query against every packed
+ * 68-byte indexer row ("Optimization details"), the exact top-512 rows are
+ * selected with float score order and lower-index tie break ("CSA
+ * score/top-512 fusion"), and attention runs over only those packed 583-byte
+ * KV rows ("Packed cache ABI"; kernel group "indexed attention" in the 1M
+ * Nsight table).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named *_rows, q_*, w_*, scores, sel_*, out, lse and ws are
+ *    DEVICE pointers owned by the caller.  The library allocates no device
+ *    memory; scratch space comes from the caller's workspace `ws`, which must
+ *    be 256-byte aligned and at least csa_workspace_bytes(...) long.  Only
+ *    the csa_session array passed to csa_decode_step lives in HOST memory and
+ *    is read before the call returns.
+ *  - `hip_stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on it and returns; results are valid once
+ *    the stream reaches that point.  Calls on one workspace must not overlap.
+ *  - Return value: CSA_OK, or a negative csa_status.  Arguments are checked
+ *    on the host before anything is launched; on an error nothing is
+ *    enqueued and outputs are untouched.  CSA_EDEVICE reports a HIP error at
+ *    launch time; CSA_EUNSUPPORTED a device that is not gfx950.
+ *  - Data validity is not checked on the device: NaN scale bytes (0xFF) or
+ *    NaN E4M3 codes give deterministic results outside the accuracy contract.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1u
+
+/* Indexer row (DS4X page, "Packed cache ABI"): 128 E2M1 codes, two per byte,
+ * element 2i in the low nibble (64 B), then 4 UE8M0 scales, scale b covering
+ * elements [32b, 32b+32).  68 bytes, rows densely packed. */
+#define CSA_IDX_ROW_BYTES 68
+#define CSA_IDX_DIM 128
+/* KV row (same section): 448 E4M3 (OCP "FN") non-RoPE bytes, 64 little-endian
+ * FP16 RoPE values (128 B), 7 UE8M0 scales, scale b covering non-RoPE
+ * elements [64b, 64b+64); the RoPE tail is unscaled.  583 bytes, 512
+ * elements, rows densely packed (no alignment). */
+#define CSA_KV_ROW_BYTES 583
+#define CSA_KV_DIM 512
+#define CSA_KV_NOPE 448
+/* Rows kept by the selection. */
+#define CSA_TOPK 512
+/* Limits checked by every entry point. */
+#define CSA_MAX_HEADS 64
+#define CSA_MAX_SESSIONS 64
+#define CSA_MAX_ROWS (((int64_t)1) << 30)
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_EINVAL = -1,       /* a null pointer, a size out of range */
+  CSA_EWORKSPACE = -2,   /* workspace too small or not 256-byte aligned */
+  CSA_EDEVICE = -3,      /* a HIP runtime error while enqueueing */
+  CSA_EUNSUPPORTED = -4  /* the current device is not gfx950 */
+} csa_status;
+
+/* One decode session: its own history and its own query token. */
+typedef struct csa_session {
+  const uint8_t *idx_rows; /* [n_rows][68] indexer rows */
+  const uint8_t *kv_rows;  /* [n_rows][583] KV rows */
+  int64_t n_rows;          /* 0 <= n_rows <= CSA_MAX_ROWS */
+  const float *q_idx;      /* [n_idx_heads][128] indexer query */
+  const float *w_idx;      /* [n_idx_heads] per-head indexer weights */
+  const float *q_attn;     /* [n_heads][512] attention query */
+  int32_t *sel_idx;        /* out [512]: selected rows, best first, -1 padded */
+  float *sel_score;        /* out [512] or NULL: their scores, -inf padded */
+  float *out;              /* out [n_heads][512] attention output */
+  float *lse;              /* out [n_heads] or NULL: natural-log sum-exp */
+} csa_session;
+
+/* CSA_ABI_VERSION of the loaded library. */
+uint32_t csa_abi_version(void);
+
+/* Static text for a csa_status value. */
+const char *csa_strerror(int status);
+
+/* Workspace bytes every entry point needs for sessions of up to
+ * `max_rows_per_session` rows (0 if the arguments are out of range).  The
+ * same workspace serves csa_score, csa_topk, csa_sparse_attn and
+ * csa_decode_step; its contents need no initialisation and are scratch
+ * between calls. */
+size_t csa_workspace_bytes(int64_t max_rows_per_session, int n_sessions);
+
+/* Indexer score of every row (the legacy first stage; DS4X page, "What DS4X
+ * changes": full F32 score array, then a separate exact top-512 pass):
+ *   scores[j] = sum_h w_idx[h] * max(0, sum_i q_idx[h][i] * k_j[i]),
+ * k_j the decoded row j.  fp32 arithmetic with a fixed operation order, so a
+ * row's score does not depend on its position; -0 is stored as +0.  The
+ * fused csa_decode_step computes bit-identical scores.
+ * n_idx_heads in [1, 64]; n_rows in [0, CSA_MAX_ROWS]. */
+int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
+              int n_idx_heads, float *scores, void *hip_stream);
+
+/* Exact top-k of a score array (DS4X page, "CSA score/top-512 fusion"):
+ * the min(k, n_rows) largest scores, larger score first, equal scores by
+ * lower row index, NaN after every number.  sel_idx[k] receives the rows
+ * (-1 after the first min(k, n_rows)), sel_score[k] (may be NULL) their
+ * scores (-inf padding).  k in [1, 512]. */
+int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float *sel_score,
+             void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Softmax attention over selected KV rows (DS4X page, kernel group "indexed
+ * attention"; packed row layout from "Packed cache ABI").  Each selected row
+ * is decoded to 512 fp32 values and serves as both key and value:
+ *   l[h][t] = softmax_scale * q_attn[h] . kv[sel_idx[t]],
+ *   out[h]  = sum_t softmax(l[h])[t] * kv[sel_idx[t]],
+ *   lse[h]  = log(sum_t exp(l[h][t])).
+ * n_sel in [0, 512] (n_sel = 0 gives out = 0 and lse = -inf); n_heads in
+ * [1, 64]; lse may be NULL.  Entries of sel_idx outside [0, n_rows) are
+ * skipped (they contribute nothing).  fp32 arithmetic, split over the
+ * selected rows and recombined through their log-sum-exp. */
+int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_idx, int n_sel,
+                    const float *q_attn, int n_heads, float softmax_scale, float *out, float *lse,
+                    void *ws, size_t ws_bytes, void *hip_stream);
+
+/* One CSA decode step for each of n_sessions independent sessions: score
+ * every indexer row, select the exact top-512 (csa_topk order) and attend
+ * over the selected KV rows (csa_sparse_attn).  Selections and outputs are
+ * bit-identical to csa_score -> csa_topk(k = 512) -> csa_sparse_attn on the
+ * same inputs.  `sessions` is a HOST array; n_sessions in [1, 64];
+ * n_idx_heads, n_heads in [1, 64]; ws sized by csa_workspace_bytes for the
+ * largest session. */
+int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                    float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Test entry points: decode packed rows to fp32, [n][128] and [n][512]
+ * (exact products; overflow gives +-inf; a 0xFF scale or an E4M3 NaN code
+ * gives NaN).  Used to check the kernels' decode bit for bit. */
+int csa_dequant_idx(const uint8_t *idx_rows, int64_t n_rows, float *out, void *hip_stream);
+int csa_dequant_kv(const uint8_t *kv_rows, int64_t n_rows, float *out, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

@@ -1,0 +1,221 @@
+"""MI355X (gfx950) CSA decode step: Python binding of libcsa.so.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libcsa.so`` (C ABI in ``include/csa.h``).  PyTorch supplies device
+memory and the current HIP stream.  There is no fallback: if the library is
+missing or fails to load, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+IDX_ROW_BYTES = 68
+KV_ROW_BYTES = 583
+IDX_DIM = 128
+KV_DIM = 512
+TOPK = 512
+MAX_HEADS = 64
+MAX_SESSIONS = 64
+ABI_VERSION = 1
+
+OK, EINVAL, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} ({status})")
+        self.status = status
+
+
+class Session(ctypes.Structure):
+    """Mirror of ``csa_session`` in include/csa.h."""
+
+    _fields_ = [
+        ("idx_rows", ctypes.c_void_p),
+        ("kv_rows", ctypes.c_void_p),
+        ("n_rows", ctypes.c_int64),
+        ("q_idx", ctypes.c_void_p),
+        ("w_idx", ctypes.c_void_p),
+        ("q_attn", ctypes.c_void_p),
+        ("sel_idx", ctypes.c_void_p),
+        ("sel_score", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.csa_abi_version.restype = ctypes.c_uint32
+    L.csa_abi_version.argtypes = []
+    L.csa_strerror.restype = ctypes.c_char_p
+    L.csa_strerror.argtypes = [i32]
+    L.csa_workspace_bytes.restype = sz
+    L.csa_workspace_bytes.argtypes = [i64, i32]
+    L.csa_score.restype = i32
+    L.csa_score.argtypes = [vp, i64, vp, vp, i32, vp, vp]
+    L.csa_topk.restype = i32
+    L.csa_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
+    L.csa_sparse_attn.restype = i32
+    L.csa_sparse_attn.argtypes = [vp, i64, vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.csa_decode_step.restype = i32
+    L.csa_decode_step.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, vp, sz, vp]
+    L.csa_dequant_idx.restype = i32
+    L.csa_dequant_idx.argtypes = [vp, i64, vp, vp]
+    L.csa_dequant_kv.restype = i32
+    L.csa_dequant_kv.argtypes = [vp, i64, vp, vp]
+    if L.csa_abi_version() != ABI_VERSION:
+        raise ImportError(f"libcsa.so ABI {L.csa_abi_version()} != {ABI_VERSION}")
+    return L
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.csa_strerror(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise CsaError(status, where)
+
+
+def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "") -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def workspace_bytes(max_rows_per_session: int, n_sessions: int = 1) -> int:
+    return int(lib.csa_workspace_bytes(max_rows_per_session, n_sessions))
+
+
+def alloc_workspace(max_rows_per_session: int, n_sessions: int = 1, device="cuda") -> torch.Tensor:
+    nb = workspace_bytes(max_rows_per_session, n_sessions)
+    if nb == 0:
+        raise ValueError("workspace size out of range")
+    return torch.empty(nb, dtype=torch.uint8, device=device)  # caching allocator: 256-B aligned
+
+
+def score(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, scores: torch.Tensor | None = None,
+          stream=None) -> torch.Tensor:
+    n = idx_rows.shape[0]
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=idx_rows.device)
+    _check(lib.csa_score(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(q_idx, torch.float32, "q_idx"),
+                         _ptr(w_idx, torch.float32, "w_idx"), w_idx.shape[0], _ptr(scores, torch.float32, "scores"),
+                         _stream(stream)), "csa_score")
+    return scores
+
+
+def topk(scores: torch.Tensor, k: int = TOPK, ws: torch.Tensor | None = None, stream=None):
+    n = scores.shape[0]
+    if ws is None:
+        ws = alloc_workspace(n, 1, scores.device)
+    sel = torch.empty(k, dtype=torch.int32, device=scores.device)
+    sel_score = torch.empty(k, dtype=torch.float32, device=scores.device)
+    _check(lib.csa_topk(_ptr(scores, torch.float32, "scores"), n, k, _ptr(sel, torch.int32), _ptr(sel_score),
+                        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_topk")
+    return sel, sel_score
+
+
+def sparse_attn(kv_rows: torch.Tensor, sel_idx: torch.Tensor, n_sel: int, q_attn: torch.Tensor, softmax_scale: float,
+                ws: torch.Tensor | None = None, stream=None):
+    h = q_attn.shape[0]
+    dev = q_attn.device
+    if ws is None:
+        ws = alloc_workspace(0, 1, dev)
+    out = torch.empty((h, KV_DIM), dtype=torch.float32, device=dev)
+    lse = torch.empty(h, dtype=torch.float32, device=dev)
+    _check(lib.csa_sparse_attn(_ptr(kv_rows, torch.uint8, "kv_rows"), kv_rows.shape[0], _ptr(sel_idx, torch.int32, "sel"),
+                               n_sel, _ptr(q_attn, torch.float32, "q_attn"), h, softmax_scale, _ptr(out), _ptr(lse),
+                               _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_sparse_attn")
+    return out, lse
+
+
+class DecodeStep:
+    """Pre-marshalled csa_decode_step over fixed device buffers.
+
+    ``sessions`` is a sequence of dicts with device tensors ``idx_rows``,
+    ``kv_rows``, ``q_idx``, ``w_idx``, ``q_attn``; outputs ``sel``,
+    ``sel_score``, ``out``, ``lse`` are allocated here.  ``__call__`` enqueues
+    one decode step of every session on the current stream.
+    """
+
+    def __init__(self, sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None):
+        if not 1 <= len(sessions) <= MAX_SESSIONS:
+            raise ValueError("1..64 sessions")
+        self.sessions = list(sessions)
+        self.n_idx_heads = int(sessions[0]["w_idx"].shape[0])
+        self.n_heads = int(sessions[0]["q_attn"].shape[0])
+        self.softmax_scale = float(softmax_scale)
+        dev = sessions[0]["q_attn"].device
+        max_rows = max(int(s["idx_rows"].shape[0]) for s in sessions)
+        self.ws = alloc_workspace(max_rows, len(sessions), dev) if ws is None else ws
+        arr = (Session * len(sessions))()
+        for i, s in enumerate(self.sessions):
+            n = int(s["idx_rows"].shape[0])
+            if s["kv_rows"].shape[0] != n:
+                raise ValueError("idx_rows and kv_rows disagree on n_rows")
+            if s["w_idx"].shape[0] != self.n_idx_heads or s["q_attn"].shape[0] != self.n_heads:
+                raise ValueError("all sessions need the same head counts")
+            s.setdefault("sel", torch.empty(TOPK, dtype=torch.int32, device=dev))
+            s.setdefault("sel_score", torch.empty(TOPK, dtype=torch.float32, device=dev))
+            s.setdefault("out", torch.empty((self.n_heads, KV_DIM), dtype=torch.float32, device=dev))
+            s.setdefault("lse", torch.empty(self.n_heads, dtype=torch.float32, device=dev))
+            arr[i] = Session(_ptr(s["idx_rows"], torch.uint8, "idx_rows"), _ptr(s["kv_rows"], torch.uint8, "kv_rows"), n,
+                             _ptr(s["q_idx"], torch.float32, "q_idx"), _ptr(s["w_idx"], torch.float32, "w_idx"),
+                             _ptr(s["q_attn"], torch.float32, "q_attn"), _ptr(s["sel"], torch.int32, "sel"),
+                             _ptr(s["sel_score"], torch.float32), _ptr(s["out"], torch.float32),
+                             _ptr(s["lse"], torch.float32))
+        self._arr = arr
+
+    def __call__(self, stream=None) -> None:
+        _check(lib.csa_decode_step(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads, self.softmax_scale,
+                                   _ptr(self.ws, torch.uint8, "ws"), self.ws.numel(), _stream(stream)),
+               "csa_decode_step")
+
+
+def decode_step(sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None, stream=None):
+    """One decode step over ``sessions`` (see DecodeStep); returns the session dicts with outputs."""
+    step = DecodeStep(sessions, softmax_scale, ws)
+    step(stream)
+    return step.sessions
+
+
+def dequant_idx(idx_rows: torch.Tensor, stream=None) -> torch.Tensor:
+    n = idx_rows.shape[0]
+    out = torch.empty((n, IDX_DIM), dtype=torch.float32, device=idx_rows.device)
+    _check(lib.csa_dequant_idx(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(out), _stream(stream)), "csa_dequant_idx")
+    return out
+
+
+def dequant_kv(kv_rows: torch.Tensor, stream=None) -> torch.Tensor:
+    n = kv_rows.shape[0]
+    out = torch.empty((n, KV_DIM), dtype=torch.float32, device=kv_rows.device)
+    _check(lib.csa_dequant_kv(_ptr(kv_rows, torch.uint8, "kv_rows"), n, _ptr(out), _stream(stream)), "csa_dequant_kv")
+    return out

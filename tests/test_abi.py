@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host (no compute call: these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+@pytest.fixture(scope="module")
+def csa():
+    from long_context_sparse_score_amd import _build
+
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    import long_context_sparse_score_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("csa_score", "csa_topk", "csa_sparse_attn", "csa_decode_step", "csa_workspace_bytes",
+              "csa_abi_version", "csa_strerror"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(csa):
+    lib = ctypes.CDLL(csa.LIB_PATH)
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_constants_match_header(csa):
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (CSA_[A-Z_]+) (\d+)u?\b", text))
+    assert int(consts["CSA_IDX_ROW_BYTES"]) == csa.IDX_ROW_BYTES == 68
+    assert int(consts["CSA_KV_ROW_BYTES"]) == csa.KV_ROW_BYTES == 583
+    assert int(consts["CSA_TOPK"]) == csa.TOPK == 512
+    assert int(consts["CSA_ABI_VERSION"]) == csa.lib.csa_abi_version() == csa.ABI_VERSION
+
+
+def test_strerror_and_workspace(csa):
+    for st in (0, -1, -2, -3, -4):
+        assert csa.strerror(st) and csa.strerror(st) != "unknown status"
+    assert csa.strerror(-99) == "unknown status"
+    assert csa.workspace_bytes(0, 1) > 0
+    assert csa.workspace_bytes(1 << 20, 1) >= (1 << 20) * 4
+    assert csa.workspace_bytes(1 << 20, 16) > csa.workspace_bytes(1 << 20, 1)
+    assert csa.workspace_bytes(1 << 20, 1) % 256 == 0
+    assert csa.workspace_bytes(-1, 1) == 0
+    assert csa.workspace_bytes(10, 0) == 0 and csa.workspace_bytes(10, 65) == 0
+    assert csa.workspace_bytes((1 << 30) + 1, 1) == 0
+
+
+def test_invalid_arguments_rejected_on_host(csa):
+    L = csa.lib
+    fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    assert L.csa_score(fake, 10, fake, fake, 0, fake, None) == csa.EINVAL  # 0 heads
+    assert L.csa_score(fake, 10, fake, fake, 65, fake, None) == csa.EINVAL
+    assert L.csa_score(None, 10, fake, fake, 8, fake, None) == csa.EINVAL
+    assert L.csa_score(fake, -1, fake, fake, 8, fake, None) == csa.EINVAL
+    assert L.csa_topk(fake, 10, 0, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_topk(fake, 10, 513, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_topk(fake, 10, 8, None, None, fake, 1 << 30, None) == csa.EINVAL
+    # workspace: too small, misaligned, missing
+    assert L.csa_topk(fake, 10, 8, fake, None, fake, 16, None) == csa.EWORKSPACE
+    assert L.csa_topk(fake, 10, 8, fake, None, ctypes.c_void_p(4096 + 8), 1 << 30, None) == csa.EWORKSPACE
+    assert L.csa_topk(fake, 10, 8, fake, None, None, 1 << 30, None) == csa.EWORKSPACE
+    assert L.csa_sparse_attn(fake, 10, fake, 513, fake, 8, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_sparse_attn(fake, 10, fake, 4, fake, 0, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_sparse_attn(fake, 10, None, 4, fake, 8, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    sess = (csa.Session * 2)()
+    assert L.csa_decode_step(sess, 0, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_decode_step(sess, 65, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL  # null members
+    assert L.csa_decode_step(None, 1, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
+    for i in range(2):
+        sess[i] = csa.Session(fake, fake, 100, fake, fake, fake, fake, None, fake, None)
+    assert L.csa_decode_step(sess, 2, 8, 0, 0.1, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 64, None) == csa.EWORKSPACE
