@@ -60,7 +60,7 @@ extern "C" {
 
 typedef enum csa_status {
   CSA_OK = 0,
-  CSA_EINVAL = -1,       /* a null pointer, a size out of range */
+  CSA_EINVAL = -1,       /* a null pointer, a size out of range, a misaligned row buffer */
   CSA_EWORKSPACE = -2,   /* workspace too small or not 256-byte aligned */
   CSA_EDEVICE = -3,      /* a HIP runtime error while enqueueing */
   CSA_EUNSUPPORTED = -4  /* the current device is not gfx950 */
@@ -68,7 +68,7 @@ typedef enum csa_status {
 
 /* One decode session: its own history and its own query token. */
 typedef struct csa_session {
-  const uint8_t *idx_rows; /* [n_rows][68] indexer rows */
+  const uint8_t *idx_rows; /* [n_rows][68] indexer rows, 16-byte aligned */
   const uint8_t *kv_rows;  /* [n_rows][583] KV rows */
   int64_t n_rows;          /* 0 <= n_rows <= CSA_MAX_ROWS */
   const float *q_idx;      /* [n_idx_heads][128] indexer query */
@@ -96,12 +96,17 @@ size_t csa_workspace_bytes(int64_t max_rows_per_session, int n_sessions);
 /* Indexer score of every row (the legacy first stage; DS4X page, "What DS4X
  * changes": full F32 score array, then a separate exact top-512 pass):
  *   scores[j] = sum_h w_idx[h] * max(0, sum_i q_idx[h][i] * k_j[i]),
- * k_j the decoded row j.  fp32 arithmetic with a fixed operation order, so a
- * row's score does not depend on its position; -0 is stored as +0.  The
- * fused csa_decode_step computes bit-identical scores.
- * n_idx_heads in [1, 64]; n_rows in [0, CSA_MAX_ROWS]. */
+ * k_j the decoded row j.  Computed on the matrix cores from the packed row
+ * itself (E2M1 codes and UE8M0 scales as a block-scaled fp4 operand); the
+ * fp32 query enters as a sum of five fp6 terms (relative residual below
+ * 2^-19 of each 32-value block's maximum), products are exact and sums are
+ * fp32.  The operation order is fixed, so a row's score does not depend on
+ * its position; -0 is stored as +0.  The fused csa_decode_step computes
+ * bit-identical scores.  n_idx_heads in [1, 64]; n_rows in [0, CSA_MAX_ROWS];
+ * idx_rows must be 16-byte aligned (rows are streamed in 16-byte pieces;
+ * CSA_EINVAL otherwise); ws sized by csa_workspace_bytes(n_rows, 1). */
 int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
-              int n_idx_heads, float *scores, void *hip_stream);
+              int n_idx_heads, float *scores, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Exact top-k of a score array (DS4X page, "CSA score/top-512 fusion"):
  * the min(k, n_rows) largest scores, larger score first, equal scores by
@@ -134,6 +139,18 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
  * largest session. */
 int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Stages of csa_decode_step, in launch order. */
+#define CSA_STAGES 4 /* 0 query split, 1 score + tile top-512, 2 merge, 3 attention */
+
+/* csa_decode_step that also records events[2*s] right before and
+ * events[2*s+1] right after the launches of stage s on hip_stream, so a
+ * caller can time each stage with hipEventElapsedTime.  `events` is a HOST
+ * array of 2*CSA_STAGES hipEvent_t (as void*) created by the caller; the
+ * work done is exactly that of csa_decode_step. */
+int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                          float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
+                          void *const *events);
 
 /* Test entry points: decode packed rows to fp32, [n][128] and [n][512]
  * (exact products; overflow gives +-inf; a 0xFF scale or an E4M3 NaN code

@@ -24,6 +24,7 @@ TOPK = 512
 MAX_HEADS = 64
 MAX_SESSIONS = 64
 ABI_VERSION = 1
+STAGES = ("query split", "score + tile top-512", "merge", "attention")
 
 OK, EINVAL, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4
 
@@ -64,13 +65,16 @@ def _load() -> ctypes.CDLL:
     L.csa_workspace_bytes.restype = sz
     L.csa_workspace_bytes.argtypes = [i64, i32]
     L.csa_score.restype = i32
-    L.csa_score.argtypes = [vp, i64, vp, vp, i32, vp, vp]
+    L.csa_score.argtypes = [vp, i64, vp, vp, i32, vp, vp, sz, vp]
     L.csa_topk.restype = i32
     L.csa_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
     L.csa_sparse_attn.restype = i32
     L.csa_sparse_attn.argtypes = [vp, i64, vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
     L.csa_decode_step.restype = i32
     L.csa_decode_step.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, vp, sz, vp]
+    L.csa_decode_step_timed.restype = i32
+    L.csa_decode_step_timed.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, vp, sz, vp,
+                                        ctypes.POINTER(ctypes.c_void_p)]
     L.csa_dequant_idx.restype = i32
     L.csa_dequant_idx.argtypes = [vp, i64, vp, vp]
     L.csa_dequant_kv.restype = i32
@@ -122,13 +126,15 @@ def alloc_workspace(max_rows_per_session: int, n_sessions: int = 1, device="cuda
 
 
 def score(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, scores: torch.Tensor | None = None,
-          stream=None) -> torch.Tensor:
+          ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     n = idx_rows.shape[0]
     if scores is None:
         scores = torch.empty(n, dtype=torch.float32, device=idx_rows.device)
+    if ws is None:
+        ws = alloc_workspace(n, 1, idx_rows.device)
     _check(lib.csa_score(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(q_idx, torch.float32, "q_idx"),
                          _ptr(w_idx, torch.float32, "w_idx"), w_idx.shape[0], _ptr(scores, torch.float32, "scores"),
-                         _stream(stream)), "csa_score")
+                         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_score")
     return scores
 
 
@@ -198,6 +204,19 @@ class DecodeStep:
         _check(lib.csa_decode_step(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads, self.softmax_scale,
                                    _ptr(self.ws, torch.uint8, "ws"), self.ws.numel(), _stream(stream)),
                "csa_decode_step")
+
+    def timed(self, events: Sequence["torch.cuda.Event"], stream=None) -> None:
+        """Same work as ``__call__``; records ``events[2s]`` / ``events[2s+1]``
+        around stage s (STAGES) on the stream."""
+        if len(events) != 2 * len(STAGES):
+            raise ValueError(f"need {2 * len(STAGES)} events")
+        for e in events:
+            if not e.cuda_event:  # torch creates the HIP event on its first record
+                e.record()
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        _check(lib.csa_decode_step_timed(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads,
+                                         self.softmax_scale, _ptr(self.ws, torch.uint8, "ws"), self.ws.numel(),
+                                         _stream(stream), handles), "csa_decode_step_timed")
 
 
 def decode_step(sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None, stream=None):

@@ -6,6 +6,7 @@
 
 #include "../../include/csa.h"
 #include "csa_internal.hpp"
+#include "csa_score.hpp"
 
 namespace {
 
@@ -16,20 +17,32 @@ constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
-// Workspace layout for (max rows per session, sessions):
-//   [scores: sessions x rows_cap fp32][attention partials: sessions x kAttnPartFloats]
+// Workspace layout for (max rows per session, sessions); sized for the
+// smallest tile so that it grows monotonically with max_rows:
+//   [query split][tile heads][tile candidates][attention partials]
 struct Layout {
-  size_t rows_cap;  // floats per session in the score area
-  size_t part_off;
-  size_t total;
+  int64_t tiles_cap;  // tiles per session at the smallest tile size
+  size_t qsplit_off, heads_off, cand_off, part_off, total;
 };
 
 Layout make_layout(int64_t max_rows, int n_sessions) {
   Layout L;
-  L.rows_cap = align_up((size_t)max_rows * sizeof(float)) / sizeof(float);
-  L.part_off = align_up((size_t)n_sessions * L.rows_cap * sizeof(float));
-  L.total = L.part_off + align_up((size_t)n_sessions * kAttnPartFloats * sizeof(float));
+  L.tiles_cap = (max_rows + kMinTileRows - 1) / kMinTileRows;
+  const size_t ns = (size_t)n_sessions;
+  L.qsplit_off = 0;
+  L.heads_off = align_up(ns * kQSplitBytes);
+  L.cand_off = L.heads_off + align_up(ns * (size_t)L.tiles_cap * 16 * sizeof(uint64_t));
+  L.part_off = L.cand_off + align_up(ns * (size_t)L.tiles_cap * CSA_TOPK * sizeof(uint64_t));
+  L.total = L.part_off + align_up(ns * kAttnPartFloats * sizeof(float));
   return L;
+}
+
+// Tile rows: as large as possible (fewer candidate lists) while the launch
+// keeps at least ~512 workgroups (two per compute unit).
+int choose_tile_rows(int64_t total_rows) {
+  int T = kMinTileRows;
+  while (T < kMaxTileRows && total_rows / (2 * (int64_t)T) >= 512) T *= 2;
+  return T;
 }
 
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
@@ -52,11 +65,30 @@ int status_of(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EDEVICE; }
 
 bool rows_ok(int64_t n) { return n >= 0 && n <= CSA_MAX_ROWS; }
 bool heads_ok(int h) { return h >= 1 && h <= CSA_MAX_HEADS; }
+// The scorer streams indexer rows with 16-byte loads.
+bool idx_aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_ws(const void *ws, size_t ws_bytes, int64_t max_rows, int n_sessions, Layout *L) {
   *L = make_layout(max_rows, n_sessions);
   if (ws == nullptr || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < L->total) return CSA_EWORKSPACE;
   return CSA_OK;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+void fill_job(TileJob &job, const Layout &L, void *ws, int n_sessions) {
+  job.n_sessions = n_sessions;
+  job.qsplit = at<uint32_t>(ws, L.qsplit_off);
+  job.heads = at<uint64_t>(ws, L.heads_off);
+  job.cand = at<uint64_t>(ws, L.cand_off);
+  job.heads_stride = L.tiles_cap * 16;
+  job.cand_stride = L.tiles_cap * CSA_TOPK;
+  int64_t total = 0;
+  for (int i = 0; i < n_sessions; ++i) total += job.n_rows[i];
+  job.tile_rows = choose_tile_rows(total);
 }
 
 }  // namespace
@@ -96,13 +128,26 @@ int csa_dequant_kv(const uint8_t *kv_rows, int64_t n_rows, float *out, void *hip
 }
 
 int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
-              int n_idx_heads, float *scores, void *hip_stream) {
+              int n_idx_heads, float *scores, void *ws, size_t ws_bytes, void *hip_stream) {
   if (!rows_ok(n_rows) || !heads_ok(n_idx_heads) || !q_idx || !w_idx) return CSA_EINVAL;
-  if (n_rows > 0 && (!idx_rows || !scores)) return CSA_EINVAL;
-  int rc = check_device();
+  if (n_rows > 0 && (!idx_rows || !scores || !idx_aligned(idx_rows))) return CSA_EINVAL;
+  Layout L;
+  int rc = check_ws(ws, ws_bytes, n_rows, 1, &L);
   if (rc != CSA_OK) return rc;
-  ScoreSession s{idx_rows, q_idx, w_idx, scores, n_rows};
-  return status_of(launch_score(&s, 1, n_idx_heads, n_rows, (hipStream_t)hip_stream));
+  rc = check_device();
+  if (rc != CSA_OK) return rc;
+  hipStream_t st = (hipStream_t)hip_stream;
+  TileJob job;
+  job.mode = TileJob::kScore;
+  job.n_idx_heads = n_idx_heads;
+  job.idx_rows[0] = idx_rows;
+  job.scores_in[0] = nullptr;
+  job.scores_out[0] = scores;
+  job.n_rows[0] = n_rows;
+  fill_job(job, L, ws, 1);
+  hipError_t e = launch_q_split(&q_idx, &w_idx, 1, n_idx_heads, const_cast<uint32_t *>(job.qsplit), st);
+  if (e == hipSuccess) e = launch_tiles(job, st);
+  return status_of(e);
 }
 
 int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float *sel_score,
@@ -114,8 +159,18 @@ int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float
   if (rc != CSA_OK) return rc;
   rc = check_device();
   if (rc != CSA_OK) return rc;
-  SelectSession s{scores, sel_idx, sel_score, n_rows};
-  return status_of(launch_select(&s, 1, k, (hipStream_t)hip_stream));
+  hipStream_t st = (hipStream_t)hip_stream;
+  TileJob job;
+  job.mode = TileJob::kArraySelect;
+  job.n_idx_heads = 1;
+  job.idx_rows[0] = nullptr;
+  job.scores_in[0] = scores;
+  job.scores_out[0] = nullptr;
+  job.n_rows[0] = n_rows;
+  fill_job(job, L, ws, 1);
+  hipError_t e = launch_tiles(job, st);
+  if (e == hipSuccess) e = launch_merge(job, &sel_idx, &sel_score, k, st);
+  return status_of(e);
 }
 
 int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_idx, int n_sel,
@@ -130,12 +185,13 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   rc = check_device();
   if (rc != CSA_OK) return rc;
   AttnSession s{kv_rows, sel_idx, q_attn, out, lse, n_rows, n_sel};
-  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part_off);
-  return status_of(launch_attention(&s, 1, n_heads, softmax_scale, part, (hipStream_t)hip_stream));
+  return status_of(launch_attention(&s, 1, n_heads, softmax_scale, at<float>(ws, L.part_off),
+                                    (hipStream_t)hip_stream));
 }
 
-int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
-                    float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream) {
+static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                            float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
+                            void *const *events) {
   if (!sessions || n_sessions < 1 || n_sessions > CSA_MAX_SESSIONS || !heads_ok(n_idx_heads) ||
       !heads_ok(n_heads))
     return CSA_EINVAL;
@@ -143,7 +199,7 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
   for (int i = 0; i < n_sessions; ++i) {
     const csa_session &s = sessions[i];
     if (!rows_ok(s.n_rows) || !s.q_idx || !s.w_idx || !s.q_attn || !s.sel_idx || !s.out) return CSA_EINVAL;
-    if (s.n_rows > 0 && (!s.idx_rows || !s.kv_rows)) return CSA_EINVAL;
+    if (s.n_rows > 0 && (!s.idx_rows || !s.kv_rows || !idx_aligned(s.idx_rows))) return CSA_EINVAL;
     if (s.n_rows > max_rows) max_rows = s.n_rows;
   }
   Layout L;
@@ -152,24 +208,60 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
   rc = check_device();
   if (rc != CSA_OK) return rc;
   hipStream_t st = (hipStream_t)hip_stream;
-  float *score_base = reinterpret_cast<float *>(ws);
-  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part_off);
 
-  ScoreSession sc[CSA_MAX_SESSIONS];
-  SelectSession se[CSA_MAX_SESSIONS];
-  AttnSession at[CSA_MAX_SESSIONS];
+  TileJob job;
+  job.mode = TileJob::kScoreSelect;
+  job.n_idx_heads = n_idx_heads;
+  const float *q[CSA_MAX_SESSIONS], *w[CSA_MAX_SESSIONS];
+  int32_t *sel[CSA_MAX_SESSIONS];
+  float *sel_score[CSA_MAX_SESSIONS];
+  AttnSession at_s[CSA_MAX_SESSIONS];
   for (int i = 0; i < n_sessions; ++i) {
     const csa_session &s = sessions[i];
-    float *scores = score_base + (size_t)i * L.rows_cap;
+    job.idx_rows[i] = s.idx_rows;
+    job.scores_in[i] = nullptr;
+    job.scores_out[i] = nullptr;
+    job.n_rows[i] = s.n_rows;
+    q[i] = s.q_idx;
+    w[i] = s.w_idx;
+    sel[i] = s.sel_idx;
+    sel_score[i] = s.sel_score;
     const int32_t n_sel = (int32_t)(s.n_rows < CSA_TOPK ? s.n_rows : CSA_TOPK);
-    sc[i] = ScoreSession{s.idx_rows, s.q_idx, s.w_idx, scores, s.n_rows};
-    se[i] = SelectSession{scores, s.sel_idx, s.sel_score, s.n_rows};
-    at[i] = AttnSession{s.kv_rows, s.sel_idx, s.q_attn, s.out, s.lse, s.n_rows, n_sel};
+    at_s[i] = AttnSession{s.kv_rows, s.sel_idx, s.q_attn, s.out, s.lse, s.n_rows, n_sel};
   }
-  hipError_t e = launch_score(sc, n_sessions, n_idx_heads, max_rows, st);
-  if (e == hipSuccess) e = launch_select(se, n_sessions, CSA_TOPK, st);
-  if (e == hipSuccess) e = launch_attention(at, n_sessions, n_heads, softmax_scale, part, st);
+  fill_job(job, L, ws, n_sessions);
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_q_split(q, w, n_sessions, n_idx_heads, const_cast<uint32_t *>(job.qsplit), st);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess) e = launch_tiles(job, st);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = launch_merge(job, sel, sel_score, CSA_TOPK, st);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(6);
+  if (e == hipSuccess) e = launch_attention(at_s, n_sessions, n_heads, softmax_scale, at<float>(ws, L.part_off), st);
+  if (e == hipSuccess) e = mark(7);
   return status_of(e);
+}
+
+int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                    float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream) {
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, ws_bytes, hip_stream,
+                          nullptr);
+}
+
+int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                          float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
+                          void *const *events) {
+  if (!events) return CSA_EINVAL;
+  for (int i = 0; i < 2 * CSA_STAGES; ++i)
+    if (!events[i]) return CSA_EINVAL;
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, ws_bytes, hip_stream,
+                          events);
 }
 
 }  // extern "C"

@@ -73,10 +73,44 @@ __global__ void __launch_bounds__(256) attn_partial_kernel(const AttnPartArgs a)
     rowid[tid] = idx;
   }
   __syncthreads();
-  for (int e = tid; e < kR * CSA_KV_DIM; e += 256) {
-    const int r = e / CSA_KV_DIM, i = e % CSA_KV_DIM;
-    const int64_t idx = rowid[r];
-    kv[r][i] = (idx >= 0) ? decode_kv_elem(S.kv_rows + idx * kKvRowBytes, i) : 0.0f;
+  // thread -> elements tid and tid + 256 of all 16 rows; every byte load is
+  // issued before any is used.  Invalid rows load nothing (the history may
+  // be empty, with no row to read) and decode to zero.
+  {
+    uint32_t lo[kR][2], hi[kR][2], sc[kR][2];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int64_t idx = rowid[r];  // workgroup-uniform
+      if (idx < 0) {
+        lo[r][0] = lo[r][1] = hi[r][0] = hi[r][1] = sc[r][0] = sc[r][1] = 0;
+        continue;
+      }
+      const uint8_t *row = S.kv_rows + idx * kKvRowBytes;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int i = tid + 256 * hh;
+        if (i < kKvNope) {
+          lo[r][hh] = row[i];
+          sc[r][hh] = row[576 + (i >> 6)];
+          hi[r][hh] = 0;
+        } else {
+          const int o = kKvNope + 2 * (i - kKvNope);
+          lo[r][hh] = row[o];
+          hi[r][hh] = row[o + 1];
+          sc[r][hh] = 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int i = tid + 256 * hh;
+        const float v = (i < kKvNope) ? e4m3_value(lo[r][hh]) * ue8m0_scale(sc[r][hh])
+                                      : f16_value(lo[r][hh] | (hi[r][hh] << 8));
+        kv[r][i] = rowid[r] >= 0 ? v : 0.0f;
+      }
+    }
   }
   __syncthreads();
 
@@ -134,8 +168,19 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnCombArgs a)
   const int nsplit = (S.n_sel + kR - 1) / kR;
   const float *base = a.part + (size_t)sess * kAttnSplits * CSA_MAX_HEADS * kPartStride + (size_t)h * kPartStride;
   const size_t sstride = (size_t)CSA_MAX_HEADS * kPartStride;
+  // every partial load is issued up front (fixed trip counts, clamped)
+  float ms[kAttnSplits], ls[kAttnSplits], a0[kAttnSplits], a1[kAttnSplits];
+#pragma unroll
+  for (int s = 0; s < kAttnSplits; ++s) {
+    const float *ps = base + (s < nsplit ? s : 0) * sstride;
+    ms[s] = ps[CSA_KV_DIM];
+    ls[s] = ps[CSA_KV_DIM + 1];
+    a0[s] = ps[tid];
+    a1[s] = ps[tid + 256];
+  }
   float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * sstride + CSA_KV_DIM]);
+#pragma unroll
+  for (int s = 0; s < kAttnSplits; ++s) M = (s < nsplit) ? fmaxf(M, ms[s]) : M;
   float *out = S.out + (size_t)h * CSA_KV_DIM;
   if (M == -__builtin_inff()) {
     out[tid] = 0.0f;
@@ -144,14 +189,14 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnCombArgs a)
     return;
   }
   float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float *ps = base + s * sstride;
-    const float ms = ps[CSA_KV_DIM];
-    if (ms == -__builtin_inff()) continue;
-    const float wgt = __expf(ms - M);
-    L = __builtin_fmaf(wgt, ps[CSA_KV_DIM + 1], L);
-    o0 = __builtin_fmaf(wgt, ps[tid], o0);
-    o1 = __builtin_fmaf(wgt, ps[tid + 256], o1);
+#pragma unroll
+  for (int s = 0; s < kAttnSplits; ++s) {
+    if (s < nsplit && ms[s] != -__builtin_inff()) {
+      const float wgt = __expf(ms[s] - M);
+      L = __builtin_fmaf(wgt, ls[s], L);
+      o0 = __builtin_fmaf(wgt, a0[s], o0);
+      o1 = __builtin_fmaf(wgt, a1[s], o1);
+    }
   }
   const float inv = 1.0f / L;
   out[tid] = o0 * inv;

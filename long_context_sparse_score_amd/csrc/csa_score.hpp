@@ -1,35 +1,176 @@
-// csa_score.hpp -- the per-row indexer score, the one definition used by the
-// unfused score kernel and the fused score/select kernel, so both produce
-// bit-identical scores.
+// csa_score.hpp -- the indexer score on gfx950 matrix cores, the single
+// definition shared by every kernel that scores rows (so unfused and fused
+// paths produce bit-identical scores).
+//
+// Score (lightning-indexer form adopted for the library; the DS4X page
+// describes the batch-one scorer only as a block-scaled MXFP4 matrix product
+// over the 68-byte rows, "Optimization details"):
+//     s_j = sum_h w_h * max(0, q_h . k_j)
+//
+// The packed rows are consumed as they are stored: the 64 E2M1 code bytes of
+// a row are the fp4 B operand of V_MFMA_SCALE_F32_16X16X128_F8F6F4 and its
+// four UE8M0 bytes are the B block scales (one per 32 values, exactly the
+// row's block structure).  The fp32 query cannot be an MX operand, so it is
+// split into kTerms fp6 (E2M3) terms with their own E8M0 block scales,
+//     q = sum_t qt + r,   |r| <= 2^-19.6 * blockmax|q| per element,
+// and the dot product is the fp32 accumulation of the kTerms exact-product
+// MFMAs (q_split_kernel builds the terms once per call).  Every product is
+// exact; accumulation is fp32 inside the matrix core.
+//
+// Lane layout of the 16x16x128 instruction (verified on MI355X): lane l holds
+// A row l%16 and B column l%16, for K elements [32*(l/16), 32*(l/16)+32),
+// value i of the slice at bit 6i (fp6) or 4i (fp4); its scale byte is byte 0
+// of the scale operand; the 16x16 result gives lane l rows 4*(l/16)+v, v<4,
+// of column l%16.  With A = 16 query heads and B = 16 history rows, lane l
+// therefore loads the 16 code bytes [16*(l/16), +16) and scale byte 64+l/16
+// of row l%16.
 #pragma once
+
+#include <utility>
 
 #include "csa_device.hpp"
 
 namespace csa {
 
-// words[0..15]: the row's 64 E2M1 code bytes, little-endian (element 8d+t in
-// bits 4t..4t+3 of word d); words[16]: the four UE8M0 scale bytes.
-// q: [H][128] fp32 (wave-uniform address), wt: [H].
-__device__ __forceinline__ float score_row(const uint32_t (&words)[17], const float *__restrict__ q,
-                                           const float *__restrict__ wt, int H) {
-  float k[128];
-  const uint32_t sc = words[16];
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kTerms = 5;        // fp6 terms of the query split
+constexpr int kMaxGroups = 4;    // 16-head groups (64 indexer heads)
+constexpr int kFmtFp6 = 2;       // MFMA operand format codes: E2M3
+constexpr int kFmtFp4 = 4;       // E2M1
+
+// Per-session query split in the workspace: [group][term][lane][8 dwords],
+// dwords 0..5 = 32 fp6 codes, dword 6 = E8M0 scale byte; then 64 weights.
+constexpr int kQSplitDwords = kMaxGroups * kTerms * 64 * 8;
+constexpr int kQSplitBytes = kQSplitDwords * 4 + 64 * 4;
+
+constexpr int kScaleWords = (kTerms + 3) / 4;  // A scale bytes packed four per register
+
+template <int G>
+struct QFrag {
+  v8i a[G][kTerms];
+  int scw[G][kScaleWords];  // byte t%4 of word t/4: E8M0 scale of term t
+  float w[G][4];
+};
+
+// Load this lane's query fragments of groups [g0, g0 + G) (written by
+// q_split_kernel).
+template <int G>
+__device__ __forceinline__ void load_qfrag(QFrag<G> &q, const uint32_t *__restrict__ qs, int lane, int g0) {
+  const float *wp = reinterpret_cast<const float *>(qs + kQSplitDwords) + 16 * g0;
+  qs += g0 * kTerms * 64 * 8;
 #pragma unroll
-  for (int d = 0; d < 16; ++d) {
-    const float scale = ue8m0_scale((sc >> (8 * (d >> 2))) & 255u);
+  for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) k[8 * d + t] = e2m1_value((words[d] >> (4 * t)) & 15u) * scale;
+    for (int w = 0; w < kScaleWords; ++w) q.scw[g][w] = 0;
+#pragma unroll
+    for (int t = 0; t < kTerms; ++t) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(qs + ((g * kTerms + t) * 64 + lane) * 8);
+      const uint4 lo = p[0], hi = p[1];
+      q.a[g][t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
+      q.scw[g][t / 4] |= (int)((hi.z & 255u) << (8 * (t % 4)));
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) q.w[g][v] = wp[16 * g + 4 * (lane >> 4) + v];
   }
-  float s = 0.0f;
-  for (int h = 0; h < H; ++h) {
-    const float *qh = q + h * 128;
-    float dot = 0.0f;
+}
+
+struct RowOperand {
+  uint4 codes;
+  int sb;
+};
+
+__device__ __forceinline__ v8i as_b(const RowOperand &o) {
+  return v8i{(int)o.codes.x, (int)o.codes.y, (int)o.codes.z, (int)o.codes.w, 0, 0, 0, 0};
+}
+
+// Term t of every group for NS row operands: c[s][g] += (query term t of
+// group g) x (row operand s).  Issued term-major so that NS*G independent
+// accumulation chains are in flight; the op_sel immediate picks term t's
+// scale byte out of its packed register.
+template <int G, int NS, int T>
+__device__ __forceinline__ void mfma_term(const QFrag<G> &q, const v8i (&b)[NS], const int (&sb)[NS],
+                                          v4f (&c)[NS][G]) {
 #pragma unroll
-    for (int i = 0; i < 128; ++i) dot = __builtin_fmaf(qh[i], k[i], dot);
-    const float relu = dot > 0.0f ? dot : 0.0f;
-    s = __builtin_fmaf(wt[h], relu, s);
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r)
+      c[r][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[g][T], b[r], c[r][g], kFmtFp6, kFmtFp4, T % 4,
+                                                                  q.scw[g][T / 4], 0, sb[r]);
   }
+}
+
+template <int G, int NS, int... Ts>
+__device__ __forceinline__ void mfma_terms(const QFrag<G> &q, const v8i (&b)[NS], const int (&sb)[NS],
+                                           v4f (&c)[NS][G], std::integer_sequence<int, Ts...>) {
+  (mfma_term<G, NS, Ts>(q, b, sb, c), ...);
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 as (p0 + p1) + (p2 + p3), p_r
+// the value of lane row r, the same association in every lane
+// (v_permlane16_swap / v_permlane32_swap exchange 16-lane rows).
+__device__ __forceinline__ float row_butterfly(float p) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Partial score of one half of the head groups for NS 16-row tiles: for each
+// operand r (this lane's 16 code bytes of row l%16 and its scale byte),
+//   part_r = butterfly( fma-chain over groups g, then the lane's heads v, of
+//                       w_gv * max(0, d_gv) ),
+// d the matrix-core dot product of the query terms (in order) with the row.
+// Every lane returns its row's value.  The full score of a row is
+// part(first half) + part(second half), -0 stored as +0 (score_finish).
+template <int G, int NS>
+__device__ __forceinline__ void score_part(const QFrag<G> &q, const RowOperand (&ops)[NS], float (&out)[NS]) {
+  v8i b[NS];
+  int sb[NS];
+  v4f c[NS][G];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    b[r] = as_b(ops[r]);
+    sb[r] = ops[r].sb;
+#pragma unroll
+    for (int g = 0; g < G; ++g) c[r][g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  mfma_terms<G, NS>(q, b, sb, c, std::make_integer_sequence<int, kTerms>{});
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    float p = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float d = c[r][g][v];
+        p = __builtin_fmaf(q.w[g][v], d > 0.0f ? d : 0.0f, p);
+      }
+    }
+    out[r] = row_butterfly(p);
+  }
+}
+
+// The score of a row from its two half partials (first + second).
+__device__ __forceinline__ float score_finish(float first, float second) {
+  const float s = first + second;
   return s == 0.0f ? 0.0f : s;
+}
+
+// This lane's operand data for the 16-row tile starting at `row` (rows past
+// `n` are clamped to the last row; callers drop their scores).
+
+__device__ __forceinline__ RowOperand load_row_operand(const uint8_t *__restrict__ idx_rows, int64_t row,
+                                                       int64_t n, int lane) {
+  int64_t r = row + (lane & 15);
+  r = r < n ? r : n - 1;
+  const uint32_t *p = reinterpret_cast<const uint32_t *>(idx_rows + r * kIdxRowBytes);
+  const int g = lane >> 4;
+  RowOperand o;
+  o.codes = uint4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+  o.sb = (int)((p[16] >> (8 * g)) & 255u);
+  return o;
 }
 
 }  // namespace csa

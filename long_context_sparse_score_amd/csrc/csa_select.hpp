@@ -1,0 +1,276 @@
+// csa_select.hpp -- workgroup-level exact selection on 64-bit keys.
+//
+// Keys are (ord(score) << 32) | (2^32 - 1 - row): distinct, larger = better
+// (larger score, then lower row index), and every real key is >= 2^31, so 0
+// means "no key".  block_kth_largest() is an MSB-first radix select that
+// starts at the highest bit in which the candidate keys differ, uses 8-bit
+// digits with one LDS histogram per wave, and stops as soon as the keys
+// sharing the current prefix are exactly the ones still needed.
+#pragma once
+
+#include "csa_device.hpp"
+
+namespace csa {
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NW>  // waves per workgroup
+struct SelScratch {
+  uint32_t hist[NW][256];
+  uint64_t wmax[NW], wmin[NW];
+  uint32_t wcnt[NW];
+  uint64_t r_max, r_min;
+  uint32_t r_cnt;
+  int digit;
+  uint32_t above, bin;
+};
+
+// Wave 0 only: digit d with sum(h[d+1..]) < need <= sum(h[d..]); returns d,
+// writes the count above it.
+__device__ __forceinline__ int find_digit_wave(const uint32_t *h, uint32_t need, uint32_t *above) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t c0 = h[4 * lane], c1 = h[4 * lane + 1], c2 = h[4 * lane + 2], c3 = h[4 * lane + 3];
+  const uint32_t mine = c0 + c1 + c2 + c3;
+  uint32_t suf = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = (uint32_t)__shfl_down((int)suf, off, 64);
+    if (lane + off < 64) suf += v;
+  }
+  const uint32_t after = suf - mine;
+  int digit = -1;
+  uint32_t ab = 0;
+  if (after < need && need <= suf) {
+    uint32_t acc = after;
+    if (acc + c3 >= need) {
+      digit = 4 * lane + 3; ab = acc;
+    } else {
+      acc += c3;
+      if (acc + c2 >= need) {
+        digit = 4 * lane + 2; ab = acc;
+      } else {
+        acc += c2;
+        if (acc + c1 >= need) { digit = 4 * lane + 1; ab = acc; }
+        else { acc += c1; digit = 4 * lane; ab = acc; }
+      }
+    }
+  }
+  const unsigned long long ball = __ballot(digit >= 0);
+  const int src = ball ? (int)__ffsll((long long)ball) - 1 : 0;
+  *above = (uint32_t)__shfl((int)ab, src, 64);
+  return __shfl(digit, src, 64);
+}
+
+// Threshold of the k largest keys among {key(i) : i < count, key(i) >= lb}:
+// returns thr such that exactly min(k, #valid) valid keys are >= thr (thr >=
+// lb).  All NW*64 threads of the workgroup must call it; k >= 1.
+template <int NW, class KeyFn>
+__device__ uint64_t block_kth_largest(KeyFn key, int count, int k, uint64_t lb, SelScratch<NW> &sc) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NT = NW * 64;
+  uint64_t kmax = 0, kmin = ~0ull;
+  uint32_t cnt = 0;
+  for (int i = tid; i < count; i += NT) {
+    const uint64_t x = key(i);
+    if (x >= lb) {
+      kmax = x > kmax ? x : kmax;
+      kmin = x < kmin ? x : kmin;
+      ++cnt;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t a = shfl_xor_u64(kmax, m), b = shfl_xor_u64(kmin, m);
+    kmax = a > kmax ? a : kmax;
+    kmin = b < kmin ? b : kmin;
+    cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
+  }
+  if (lane == 0) { sc.wmax[wave] = kmax; sc.wmin[wave] = kmin; sc.wcnt[wave] = cnt; }
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t M = 0, m = ~0ull;
+    uint32_t c = 0;
+    for (int w = 0; w < NW; ++w) {
+      M = sc.wmax[w] > M ? sc.wmax[w] : M;
+      m = sc.wmin[w] < m ? sc.wmin[w] : m;
+      c += sc.wcnt[w];
+    }
+    sc.r_max = M; sc.r_min = m; sc.r_cnt = c;
+  }
+  __syncthreads();
+  const uint32_t total = sc.r_cnt;
+  const uint64_t gmax = sc.r_max, gmin = sc.r_min;
+  __syncthreads();
+  if (total <= (uint32_t)k) return lb;
+  int hi = 63 - __clzll((long long)(gmax ^ gmin));  // keys are distinct: gmax != gmin
+  uint64_t prefix = (hi == 63) ? 0ull : (gmax & ~((2ull << hi) - 1));
+  uint32_t need = (uint32_t)k;
+  for (;;) {
+    const int width = hi + 1 < 8 ? hi + 1 : 8;
+    const int shift = hi - width + 1;
+    const uint64_t pmask = (hi == 63) ? 0ull : ~((2ull << hi) - 1);
+    for (int i = tid; i < NW * 256; i += NT) (&sc.hist[0][0])[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < count; i += NT) {
+      const uint64_t x = key(i);
+      if (x >= lb && (x & pmask) == prefix) atomicAdd(&sc.hist[wave][(uint32_t)(x >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < 256; b += NT) {
+      uint32_t s = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += sc.hist[w][b];
+      sc.hist[0][b] = s;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t above;
+      const int d = find_digit_wave(sc.hist[0], need, &above);
+      if (lane == 0) { sc.digit = d; sc.above = above; sc.bin = sc.hist[0][d]; }
+    }
+    __syncthreads();
+    const int d = sc.digit;
+    need -= sc.above;
+    prefix |= (uint64_t)d << shift;
+    const bool done = (sc.bin == need);
+    __syncthreads();
+    if (done) return prefix > lb ? prefix : lb;
+    hi = shift - 1;
+  }
+}
+
+// Same contract as block_kth_largest, for keys held in registers: each
+// thread passes KPT slots of which the first nj (the same in every thread)
+// are live; 0 or keys below lb are ignored.  Every pass reads registers
+// only; LDS holds just the per-wave histograms.
+template <int NW, int KPT>
+__device__ uint64_t block_kth_largest_reg(const uint64_t (&x)[KPT], int nj, int k, uint64_t lb,
+                                          SelScratch<NW> &sc) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NT = NW * 64;
+  uint64_t kmax = 0, kmin = ~0ull;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool v = j < nj && x[j] >= lb && x[j] != 0;
+    kmax = (v && x[j] > kmax) ? x[j] : kmax;
+    kmin = (v && x[j] < kmin) ? x[j] : kmin;
+    cnt += v ? 1u : 0u;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t a = shfl_xor_u64(kmax, m), b = shfl_xor_u64(kmin, m);
+    kmax = a > kmax ? a : kmax;
+    kmin = b < kmin ? b : kmin;
+    cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
+  }
+  if (lane == 0) { sc.wmax[wave] = kmax; sc.wmin[wave] = kmin; sc.wcnt[wave] = cnt; }
+  __syncthreads();
+  uint64_t gmax = 0, gmin = ~0ull;
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    gmax = sc.wmax[w] > gmax ? sc.wmax[w] : gmax;
+    gmin = sc.wmin[w] < gmin ? sc.wmin[w] : gmin;
+    total += sc.wcnt[w];
+  }
+  if (total <= (uint32_t)k) {
+    __syncthreads();
+    return lb;
+  }
+  int hi = 63 - __clzll((long long)(gmax ^ gmin));
+  uint64_t prefix = (hi == 63) ? 0ull : (gmax & ~((2ull << hi) - 1));
+  uint32_t need = (uint32_t)k;
+  for (;;) {
+    const int width = hi + 1 < 8 ? hi + 1 : 8;
+    const int shift = hi - width + 1;
+    const uint64_t pmask = (hi == 63) ? 0ull : ~((2ull << hi) - 1);
+    for (int i = tid; i < NW * 256; i += NT) (&sc.hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (j < nj && x[j] >= lb && x[j] != 0 && (x[j] & pmask) == prefix)
+        atomicAdd(&sc.hist[wave][(uint32_t)(x[j] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < 256; b += NT) {
+      uint32_t s = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += sc.hist[w][b];
+      sc.hist[0][b] = s;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t above;
+      const int d = find_digit_wave(sc.hist[0], need, &above);
+      if (lane == 0) { sc.digit = d; sc.above = above; sc.bin = sc.hist[0][d]; }
+    }
+    __syncthreads();
+    const int d = sc.digit;
+    need -= sc.above;
+    prefix |= (uint64_t)d << shift;
+    const bool done = (sc.bin == need);
+    __syncthreads();
+    if (done) return prefix > lb ? prefix : lb;
+    hi = shift - 1;
+  }
+}
+
+// Descending order of up to NT*ranks distinct keys in LDS by counting: the
+// rank of a key is the number of larger keys.  keys[0..n) -> out[0..n).
+// No barrier inside the counting; n <= 1024.
+template <int NT>
+__device__ void block_rank_sort_desc(const uint64_t *keys, int n, uint64_t *out) {
+  constexpr int PER = NT >= 1024 ? 1 : 1024 / NT;
+  for (int base = 0; base < PER; ++base) {
+    const int i = threadIdx.x + base * NT;
+    if (i < n) {
+      const uint64_t x = keys[i];
+      int r = 0;
+      for (int j = 0; j < n; ++j) r += keys[j] > x ? 1 : 0;
+      out[r] = x;
+    }
+  }
+  __syncthreads();
+}
+
+// Bitonic sort of n2 (a power of two) keys in LDS, descending.
+template <int NT>
+__device__ void block_sort_desc(uint64_t *keys, int n2) {
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < (n2 >> 1); t += NT) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = ((lo & size) == 0);
+        const uint64_t a = keys[lo], b = keys[hi];
+        if ((a < b) == desc) { keys[lo] = b; keys[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// One wave sorts the 16 keys held by lanes 0..15 (descending); other lanes'
+// values are ignored.  Returns this lane's sorted key (lanes 0..15).
+__device__ __forceinline__ uint64_t wave_sort16_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, stride);
+      const bool desc = ((lane & size) == 0) || size == 16;
+      const bool lower = (lane & stride) == 0;
+      const bool take_max = (lower == desc);
+      v = take_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  }
+  return v;
+}
+
+}  // namespace csa

@@ -70,6 +70,27 @@ def test_topk_matches_oracle_exactly(csa, orc, n):
         assert pins.same_bits_or_nan(_np(sel_score)[:k_eff], ref_score[:k_eff])
 
 
+@pytest.mark.parametrize("pattern", ["ascending", "descending", "one_tile", "two_values", "clustered"])
+@pytest.mark.parametrize("n", [40000, 1 << 20])
+def test_topk_adversarial_layouts(csa, orc, pattern, n):
+    rng = np.random.default_rng(n % 1000 + len(pattern))
+    if pattern == "ascending":  # every winner in the last tiles
+        s = np.arange(n, dtype=np.float32)
+    elif pattern == "descending":
+        s = np.arange(n, 0, -1).astype(np.float32)
+    elif pattern == "one_tile":  # all winners packed in one tile, ties inside it
+        s = rng.standard_normal(n).astype(np.float32)
+        s[n // 3:n // 3 + 700] = 100.0 + (np.arange(700) % 7).astype(np.float32)
+    elif pattern == "two_values":
+        s = np.where(rng.random(n) < 0.001, 2.0, 1.0).astype(np.float32)
+    else:  # many near-equal values around the threshold
+        s = (1000.0 + rng.integers(0, 3, n) * np.float32(2.0**-13)).astype(np.float32)
+    sel, sel_score = csa.topk(torch.from_numpy(s).cuda(), 512)
+    ref_sel, ref_score, _ = orc.topk(s, 512)
+    assert np.array_equal(_np(sel), ref_sel)
+    assert pins.same_bits_or_nan(_np(sel_score), ref_score)
+
+
 def test_topk_all_ties_and_distinct(csa, orc):
     z = np.zeros(300000, np.float32)
     sel, _ = csa.topk(torch.from_numpy(z).cuda())
@@ -93,7 +114,7 @@ def _score_tolerance_ok(gpu, ref, rows, q, w, orc):
     return float(np.max(err[nz] / np.abs(ref[nz]))) if nz.any() else 0.0
 
 
-@pytest.mark.parametrize("cid,n", [(0, 2048), (1, 32768)])
+@pytest.mark.parametrize("cid,n", [(0, 2048), (1, 32768), (0, 2049), (1, 6001), (0, 70001)])
 def test_score_matches_oracle(csa, orc, cid, n):
     s = gen.session(cid, n_rows=n)
     d = gu.to_dev(s)
