@@ -37,7 +37,63 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=0,
                    help="rows of session 0 the oracle runs on (0: the whole session)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="repeat the oracle step until this much CPU time has been measured")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB three times (scale for the HBM byte counters)")
     return p.parse_args()
+
+
+# Kernel sources whose HBM counters profiles/ records; the recorded figures
+# are used only while these files are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_kernel_frontier-1m-rows_hbm_counters.txt")
+TRAFFIC_SOURCES = ["csa_topk_tile.hip", "csa_score.hpp", "csa_select.hpp", "csa_stream.hpp", "csa_device.hpp",
+                   "csa_internal.hpp"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "long_context_sparse_score_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused tile kernel from the recorded
+    FETCH_SIZE / WRITE_SIZE counters, each scaled by what the same counter
+    read for a copy of known size; None if not recorded for this workload or
+    the kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("workload") != workload or kv.get("source_sha256_16") != kernel_source_hash():
+            return None
+        return int(round(float(kv["scaled_fetch_bytes_per_launch"]) + float(kv["scaled_write_bytes_per_launch"])))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}),
+          flush=True)
 
 
 def algorithmic_bytes(n_rows: int, n_idx_heads: int, n_heads: int) -> dict:
@@ -54,6 +110,10 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
               "(the row-sharded multi-GPU plan is described, not built)", file=sys.stderr)
         sys.exit(2)
+
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -160,7 +220,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(score_gbs / HBM_PEAK_GBS, 5),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "launch_ms": round(score_ms, 5),
             "algorithmic_bytes_per_launch": ab["score"] * wl.n_sessions,
         },
@@ -172,17 +232,20 @@ def main():
         s0 = sess_np[0]
         n = a.cpu_sample_rows or wl.n_rows
         o = oracle.get()
-        t = time.perf_counter()
-        o.decode_step(s0["idx_rows"][:n], s0["kv_rows"][:n], s0["q_idx"], s0["w_idx"], s0["q_attn"], scale)
-        dt = time.perf_counter() - t
-        per_session_ms = dt * 1e3 * (wl.n_rows / n)
+        reps, dt = 0, 0.0
+        while dt < a.cpu_seconds and reps < 20:
+            t = time.perf_counter()
+            o.decode_step(s0["idx_rows"][:n], s0["kv_rows"][:n], s0["q_idx"], s0["w_idx"], s0["q_attn"], scale)
+            dt += time.perf_counter() - t
+            reps += 1
+        per_session_ms = dt / reps * 1e3 * (wl.n_rows / n)
         line["cpu_baseline"] = {
             "value": round(per_session_ms * wl.n_sessions, 3),
             "unit": "ms",
             "cores": 1,
             "kind": "oracle",
-            "sample": f"one decode step of session 0 over its first {n} rows "
-                      f"({dt:.2f} s measured), scaled by rows x sessions to the whole workload",
+            "sample": f"{reps} decode steps of session 0 over its first {n} rows "
+                      f"({dt:.2f} s measured), mean scaled by rows x sessions to the whole workload",
         }
     print(json.dumps(line), flush=True)
 
