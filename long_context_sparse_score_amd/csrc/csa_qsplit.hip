@@ -6,8 +6,10 @@
 //   q_t = RNE_E2M3(r / 2^E) * 2^E,   r <- r - q_t   (exact in fp32),
 // repeated kTerms times.  The block maximum of r shrinks by at least 2^-3.9
 // per term, so after 5 terms every element is within 2^-19.6 of the block
-// maximum of q.  The fragment of head h, block b becomes MFMA lane
-// 16b + h%16 of group h/16.
+// maximum of q; elements below the maximum keep E2M3's relative precision in
+// every term.  The fragment of head h, block b becomes MFMA lane 16b + h%16
+// of group h/16.  Eight threads share a fragment, four values each: a term
+// costs one three-step maximum and three byte stores per thread.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "csa_score.hpp"
@@ -37,56 +39,53 @@ struct QSplitArgs {
 };
 
 constexpr int kSplitThreads = 256;
-constexpr int kFragsPerBlock = kSplitThreads / 32;                       // 8
-constexpr int kSplitBlocks = kMaxGroups * 16 * 4 / kFragsPerBlock;       // 32 per session
+constexpr int kSplitSub = 8;                                                   // threads per fragment
+constexpr int kSplitBlocks = kMaxGroups * 16 * 4 * kSplitSub / kSplitThreads;  // 8 per session
 
-// One thread per query element; the 32 lanes of a half-wave hold one
-// (head, 32-value block) fragment and reduce its maximum with shuffles.
 __global__ void __launch_bounds__(kSplitThreads) q_split_kernel(const QSplitArgs a) {
   const int sess = blockIdx.y;
-  const int frag = blockIdx.x * kFragsPerBlock + (threadIdx.x >> 5);
-  const int i = threadIdx.x & 31;
+  const int gt = blockIdx.x * kSplitThreads + threadIdx.x;
+  const int frag = gt / kSplitSub, sub = gt % kSplitSub;
   const int h = frag >> 2, blk = frag & 3;
   const int g = h >> 4, lane = (blk << 4) | (h & 15);  // MFMA lane holding this fragment
   uint32_t *out = a.out + (size_t)sess * (kQSplitBytes / 4);
-  float r = (h < a.n_heads) ? a.q[sess][h * 128 + 32 * blk + i] : 0.0f;
-  for (int t = 0; t < kTerms; ++t) {
-    float amax = fabsf(r);
+  float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (h < a.n_heads) {
+    const float *src = a.q[sess] + h * 128 + 32 * blk + 4 * sub;
 #pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    for (int i = 0; i < 4; ++i) r[i] = src[i];
+  }
+  uint8_t *bytes = reinterpret_cast<uint8_t *>(out);
+#pragma unroll
+  for (int t = 0; t < kTerms; ++t) {
+    float amax = fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3])));
+#pragma unroll
+    for (int k = 1; k < kSplitSub; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k, kSplitSub));
     int sbyte = 127;
-    uint32_t code = 0;
+    uint32_t word = 0;
     if (amax > 0.0f) {
       int E = ilogbf(amax) - 2;  // amax / 2^E in [4, 8)
       if (ldexpf(amax, -E) > 7.5f) E += 1;
       E = E < -127 ? -127 : (E > 127 ? 127 : E);
       sbyte = E + 127;
-      const float y = ldexpf(r, -E);
-      float mag;
-      code = e2m3_mag(fminf(fabsf(y), 7.5f), &mag) | (y < 0.0f ? 32u : 0u);
-      r -= copysignf(ldexpf(mag, E), y);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = ldexpf(r[i], -E);
+        float mag;
+        const uint32_t code = e2m3_mag(fminf(fabsf(y), 7.5f), &mag) | (y < 0.0f ? 32u : 0u);
+        r[i] -= copysignf(ldexpf(mag, E), y);
+        word |= code << (6 * i);
+      }
     }
-    // dword d of the fragment ORs the codes whose 6 bits overlap bits
-    // [32d, 32d+32): butterfly OR over the 32 lanes, one word per dword
-    uint32_t word[6];
-#pragma unroll
-    for (int d = 0; d < 6; ++d) {
-      const int bit = 6 * i - 32 * d;
-      uint32_t v = (bit >= 0 && bit < 32) ? (code << bit) : ((bit < 0 && bit > -6) ? (code >> (-bit)) : 0u);
-#pragma unroll
-      for (int m = 1; m < 32; m <<= 1) v |= (uint32_t)__shfl_xor((int)v, m, 32);
-      word[d] = v;
-    }
-    uint32_t *dst = out + ((g * kTerms + t) * 64 + lane) * 8;
-    if (i < 6) {
-      uint32_t wv = word[0];
-#pragma unroll
-      for (int d = 1; d < 6; ++d) wv = (i == d) ? word[d] : wv;
-      dst[i] = wv;
-    } else if (i == 6) {
-      dst[6] = (uint32_t)sbyte;
-    } else if (i == 7) {
-      dst[7] = 0u;
+    // this thread's 4 codes are bits [24 sub, 24 sub + 24) of the fragment
+    const size_t rec = (size_t)((g * kTerms + t) * 64 + lane) * 8;  // dword index of the record
+    uint8_t *dst = bytes + rec * 4 + 3 * sub;
+    dst[0] = (uint8_t)word;
+    dst[1] = (uint8_t)(word >> 8);
+    dst[2] = (uint8_t)(word >> 16);
+    if (sub == 0) {
+      out[rec + 6] = (uint32_t)sbyte;
+      out[rec + 7] = 0u;
     }
   }
   if (blockIdx.x == 0 && threadIdx.x < 64) {
