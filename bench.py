@@ -214,7 +214,7 @@ def main():
         "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2),
         "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, stage_ms)},
         "roofline": {
-            "kernel": "tile_kernel: fused score + tile top-512 (all sessions, one launch)",
+            "kernel": "tile_kernel: fused score + tile heads (all sessions, one launch)",
             "bound": "hbm",
             "achieved": round(score_gbs, 2),
             "peak": HBM_PEAK_GBS,

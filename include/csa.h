@@ -124,8 +124,10 @@ int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float
  *   lse[h]  = log(sum_t exp(l[h][t])).
  * n_sel in [0, 512] (n_sel = 0 gives out = 0 and lse = -inf); n_heads in
  * [1, 64]; lse may be NULL.  Entries of sel_idx outside [0, n_rows) are
- * skipped (they contribute nothing).  fp32 arithmetic, split over the
- * selected rows and recombined through their log-sum-exp. */
+ * skipped (they contribute nothing; with none valid, out = 0 and lse = -inf).
+ * The logits and the value sum run on the bf16 matrix cores with exact
+ * operand splits (query: three bf16 terms; weights: two; values exact, FP16
+ * RoPE values as two terms), so products are exact and sums fp32. */
 int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_idx, int n_sel,
                     const float *q_attn, int n_heads, float softmax_scale, float *out, float *lse,
                     void *ws, size_t ws_bytes, void *hip_stream);
@@ -141,7 +143,7 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Stages of csa_decode_step, in launch order. */
-#define CSA_STAGES 4 /* 0 query split, 1 score + tile top-512, 2 merge, 3 attention */
+#define CSA_STAGES 4 /* 0 query split, 1 score + tile heads, 2 select + logits, 3 softmax + PV */
 
 /* csa_decode_step that also records events[2*s] right before and
  * events[2*s+1] right after the launches of stage s on hip_stream, so a

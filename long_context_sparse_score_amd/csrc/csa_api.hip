@@ -19,30 +19,39 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout for (max rows per session, sessions); sized for the
 // smallest tile so that it grows monotonically with max_rows:
-//   [query split][tile heads][tile candidates][attention partials]
+//   [query split][tile heads][scores][attention logits]
 struct Layout {
   int64_t tiles_cap;  // tiles per session at the smallest tile size
-  size_t qsplit_off, heads_off, cand_off, part_off, total;
+  int64_t rows_cap;   // score slots per session
+  size_t qsplit_off, heads_off, scores_off, logits_off, total;
 };
 
 Layout make_layout(int64_t max_rows, int n_sessions) {
   Layout L;
   L.tiles_cap = (max_rows + kMinTileRows - 1) / kMinTileRows;
+  L.rows_cap = (max_rows + 63) & ~(int64_t)63;
   const size_t ns = (size_t)n_sessions;
   L.qsplit_off = 0;
   L.heads_off = align_up(ns * kQSplitBytes);
-  L.cand_off = L.heads_off + align_up(ns * (size_t)L.tiles_cap * 16 * sizeof(uint64_t));
-  L.part_off = L.cand_off + align_up(ns * (size_t)L.tiles_cap * CSA_TOPK * sizeof(uint64_t));
-  L.total = L.part_off + align_up(ns * kAttnPartFloats * sizeof(float));
+  L.scores_off = L.heads_off + align_up(ns * (size_t)L.tiles_cap * kMaxTileHeads * sizeof(uint64_t));
+  L.logits_off = L.scores_off + align_up(ns * (size_t)L.rows_cap * sizeof(float));
+  L.total = L.logits_off + align_up(ns * kLogitFloats * sizeof(float));
   return L;
 }
 
-// Tile rows: as large as possible (fewer candidate lists) while the launch
+// Tile rows: as large as possible (fewer heads to merge) while the launch
 // keeps at least ~512 workgroups (two per compute unit).
 int choose_tile_rows(int64_t total_rows) {
   int T = kMinTileRows;
   while (T < kMaxTileRows && total_rows / (2 * (int64_t)T) >= 512) T *= 2;
   return T;
+}
+
+// Workgroups per session of the selection kernel: about one per compute
+// unit in total.
+int choose_slices(int n_sessions) {
+  int s = 256 / n_sessions;
+  return s < 4 ? 4 : (s > 32 ? 32 : s);
 }
 
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
@@ -83,12 +92,33 @@ void fill_job(TileJob &job, const Layout &L, void *ws, int n_sessions) {
   job.n_sessions = n_sessions;
   job.qsplit = at<uint32_t>(ws, L.qsplit_off);
   job.heads = at<uint64_t>(ws, L.heads_off);
-  job.cand = at<uint64_t>(ws, L.cand_off);
-  job.heads_stride = L.tiles_cap * 16;
-  job.cand_stride = L.tiles_cap * CSA_TOPK;
+  job.heads_stride = L.tiles_cap * kMaxTileHeads;
   int64_t total = 0;
   for (int i = 0; i < n_sessions; ++i) total += job.n_rows[i];
   job.tile_rows = choose_tile_rows(total);
+  for (int i = 0; i < n_sessions; ++i)
+    job.hd[i] = heads_per_tile((job.n_rows[i] + job.tile_rows - 1) / job.tile_rows);
+}
+
+// The selection that follows a tile launch.
+void fill_select(SelectJob &sj, const TileJob &job, int k) {
+  sj.n_sessions = job.n_sessions;
+  sj.tile_rows = job.tile_rows;
+  sj.k = k;
+  sj.slices = choose_slices(job.n_sessions);
+  sj.array_scores = job.mode == TileJob::kArraySelect;
+  for (int i = 0; i < job.n_sessions; ++i) {
+    sj.scores[i] = sj.array_scores ? job.scores_in[i] : job.scores_out[i];
+    sj.n_rows[i] = job.n_rows[i];
+    sj.hd[i] = job.hd[i];
+    sj.kv_rows[i] = nullptr;
+    sj.q_attn[i] = nullptr;
+  }
+  sj.heads = job.heads;
+  sj.heads_stride = job.heads_stride;
+  sj.logits = nullptr;
+  sj.n_heads = 0;
+  sj.softmax_scale = 0.0f;
 }
 
 }  // namespace
@@ -145,6 +175,7 @@ int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const
   job.scores_out[0] = scores;
   job.n_rows[0] = n_rows;
   fill_job(job, L, ws, 1);
+  if (n_rows == 0) return CSA_OK;
   hipError_t e = launch_q_split(&q_idx, &w_idx, 1, n_idx_heads, const_cast<uint32_t *>(job.qsplit), st);
   if (e == hipSuccess) e = launch_tiles(job, st);
   return status_of(e);
@@ -168,8 +199,12 @@ int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float
   job.scores_out[0] = nullptr;
   job.n_rows[0] = n_rows;
   fill_job(job, L, ws, 1);
+  SelectJob sj;
+  fill_select(sj, job, k);
+  sj.sel_idx[0] = sel_idx;
+  sj.sel_score[0] = sel_score;
   hipError_t e = launch_tiles(job, st);
-  if (e == hipSuccess) e = launch_merge(job, &sel_idx, &sel_score, k, st);
+  if (e == hipSuccess) e = launch_select(sj, st);
   return status_of(e);
 }
 
@@ -185,8 +220,10 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   rc = check_device();
   if (rc != CSA_OK) return rc;
   AttnSession s{kv_rows, sel_idx, q_attn, out, lse, n_rows, n_sel};
-  return status_of(launch_attention(&s, 1, n_heads, softmax_scale, at<float>(ws, L.part_off),
-                                    (hipStream_t)hip_stream));
+  float *logits = at<float>(ws, L.logits_off);
+  hipError_t e = launch_logits(&s, 1, n_heads, softmax_scale, logits, (hipStream_t)hip_stream);
+  if (e == hipSuccess) e = launch_pv(&s, 1, n_heads, logits, (hipStream_t)hip_stream);
+  return status_of(e);
 }
 
 static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
@@ -216,11 +253,12 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   int32_t *sel[CSA_MAX_SESSIONS];
   float *sel_score[CSA_MAX_SESSIONS];
   AttnSession at_s[CSA_MAX_SESSIONS];
+  float *scores = at<float>(ws, L.scores_off);
   for (int i = 0; i < n_sessions; ++i) {
     const csa_session &s = sessions[i];
     job.idx_rows[i] = s.idx_rows;
     job.scores_in[i] = nullptr;
-    job.scores_out[i] = nullptr;
+    job.scores_out[i] = scores + (size_t)i * L.rows_cap;
     job.n_rows[i] = s.n_rows;
     q[i] = s.q_idx;
     w[i] = s.w_idx;
@@ -230,6 +268,18 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     at_s[i] = AttnSession{s.kv_rows, s.sel_idx, s.q_attn, s.out, s.lse, s.n_rows, n_sel};
   }
   fill_job(job, L, ws, n_sessions);
+  float *logits = at<float>(ws, L.logits_off);
+  SelectJob sj;
+  fill_select(sj, job, CSA_TOPK);
+  sj.logits = logits;
+  sj.n_heads = n_heads;
+  sj.softmax_scale = softmax_scale;
+  for (int i = 0; i < n_sessions; ++i) {
+    sj.sel_idx[i] = sel[i];
+    sj.sel_score[i] = sel_score[i];
+    sj.kv_rows[i] = sessions[i].kv_rows;
+    sj.q_attn[i] = sessions[i].q_attn;
+  }
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
   };
@@ -240,10 +290,10 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   if (e == hipSuccess) e = launch_tiles(job, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess) e = launch_merge(job, sel, sel_score, CSA_TOPK, st);
+  if (e == hipSuccess) e = launch_select(sj, st);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
-  if (e == hipSuccess) e = launch_attention(at_s, n_sessions, n_heads, softmax_scale, at<float>(ws, L.part_off), st);
+  if (e == hipSuccess) e = launch_pv(at_s, n_sessions, n_heads, logits, st);
   if (e == hipSuccess) e = mark(7);
   return status_of(e);
 }

@@ -1,228 +1,201 @@
-// csa_attn.hip -- softmax attention over the selected packed KV rows
-// (csa_sparse_attn; the DS4X page's "indexed attention" kernel group).
-//
-// Split-K over the selection: workgroup (split, head group, session) decodes
-// its 16 selected rows into LDS (the decoded rows never reach HBM), computes
-// the 16 heads x 16 rows logits, the per-head running max m and sum l of
-// exp(logit - m), and the partial sums acc[h][:] = sum_t exp(l_t - m) kv_t.
-// A second kernel rescales the partials by exp(m_s - M) and divides, the
-// usual log-sum-exp recombination.  The decoded row is both key and value.
+// csa_attn.hip -- softmax attention over the selected packed KV rows (DS4X
+// page, kernel group "indexed attention"; row layout from "Packed cache
+// ABI"): the decoded 512-value row is both key and value,
+//   l[h][j] = scale * q_h . kv_j,   out[h] = sum_j softmax(l[h])_j kv_j,
+//   lse[h] = log sum_j exp(l[h][j]).
+// Two kernels:
+//   logits_kernel  the logits of rows sel_idx[0..n_sel) (csa_attn.hpp), for
+//                  csa_sparse_attn; the decode step computes the same values
+//                  inside its selection kernel;
+//   pv_kernel      grid (32 dimension tiles of 16, sessions), 4 waves = 4
+//                  head groups: the softmax of each head over its logits,
+//                  then out = P V on the bf16 matrix cores, with P = hi + lo
+//                  (two bf16 terms, residual below 2^-17 of each weight) and
+//                  V exact (one bf16 term, two for the FP16 RoPE values).
+// Entries of sel_idx outside [0, n_rows) contribute nothing; with no valid
+// entry out = 0 and lse = -inf.
+#include "csa_attn.hpp"
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
 namespace csa {
 
-struct AttnPartSession {
-  const uint8_t *kv_rows;
-  const int32_t *sel_idx;
-  const float *q_attn;
-  int64_t n_rows;
-  int32_t n_sel;
-};
-
-struct AttnPartArgs {
-  AttnPartSession s[CSA_MAX_SESSIONS];
-  float *part;  // [session][split][head][514]
+struct AttnArgs {
+  AttnSession s[CSA_MAX_SESSIONS];
+  float *logits;  // [session][64][512]
   int n_heads;
-  float scale;
+  float softmax_scale;
 };
+static_assert(sizeof(AttnArgs) <= 4096, "kernel argument block");
 
-struct AttnCombSession {
-  float *out;
-  float *lse;
-  int32_t n_sel;
-};
+__device__ __forceinline__ bool valid_row(int32_t r, int64_t n) { return r >= 0 && (int64_t)r < n; }
 
-struct AttnCombArgs {
-  AttnCombSession s[CSA_MAX_SESSIONS];
-  const float *part;
-  int n_heads;
-};
+// ---------------------------------------------------------------- logits
 
-static_assert(sizeof(AttnPartArgs) <= 4096, "kernel argument block");
-static_assert(sizeof(AttnCombArgs) <= 4096, "kernel argument block");
+constexpr int kLogitBatches = CSA_TOPK / kLogitRows;  // 32
 
-constexpr int kR = kAttnRowsPerSplit;    // 16 rows per split
-constexpr int kHG = kAttnHeadsPerGroup;  // 16 heads per group
-constexpr int kPartStride = CSA_KV_DIM + 2;
-constexpr int kLdsStride = CSA_KV_DIM + 4;  // rows 4 banks apart
-
-__device__ __forceinline__ float decode_kv_elem(const uint8_t *r, int i) {
-  if (i < kKvNope) return e4m3_value(r[i]) * ue8m0_scale(r[576 + (i >> 6)]);
-  const int o = kKvNope + 2 * (i - kKvNope);
-  return f16_value((uint32_t)r[o] | ((uint32_t)r[o + 1] << 8));
-}
-
-__global__ void __launch_bounds__(256) attn_partial_kernel(const AttnPartArgs a) {
-  const int split = blockIdx.x, hg = blockIdx.y, sess = blockIdx.z;
-  const AttnPartSession &S = a.s[sess];
+__global__ void __launch_bounds__(kLogitThreads) logits_kernel(const AttnArgs a) {
+  const int sess = blockIdx.y;
+  const AttnSession &S = a.s[sess];
+  const int p0 = blockIdx.x * kLogitRows;
+  if (p0 >= S.n_sel) return;
+  const int nb = S.n_sel - p0 < kLogitRows ? S.n_sel - p0 : kLogitRows;
+  __shared__ LogitShared sh;
+  LogitQueryRaw qraw;
+  load_logit_query(qraw, S.q_attn, a.n_heads);
   const int tid = threadIdx.x;
-  __shared__ float kv[kR][kLdsStride];
-  __shared__ float prob[kHG][kR];
-  __shared__ int64_t rowid[kR];
-
-  const int r0 = split * kR;
-  int nr = S.n_sel - r0;
-  nr = nr < 0 ? 0 : (nr > kR ? kR : nr);
-  if (tid < kR) {
-    int64_t idx = -1;
-    if (tid < nr) {
-      const int32_t v = S.sel_idx[r0 + tid];
-      if (v >= 0 && (int64_t)v < S.n_rows) idx = v;
-    }
-    rowid[tid] = idx;
+  if (tid < kLogitRows) {
+    const int32_t r = tid < nb ? S.sel_idx[p0 + tid] : -1;
+    sh.row[tid] = valid_row(r, S.n_rows) ? r : -1;
+    sh.pos[tid] = p0 + tid;
   }
   __syncthreads();
-  // thread -> elements tid and tid + 256 of all 16 rows; every byte load is
-  // issued before any is used.  Invalid rows load nothing (the history may
-  // be empty, with no row to read) and decode to zero.
-  {
-    uint32_t lo[kR][2], hi[kR][2], sc[kR][2];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int64_t idx = rowid[r];  // workgroup-uniform
-      if (idx < 0) {
-        lo[r][0] = lo[r][1] = hi[r][0] = hi[r][1] = sc[r][0] = sc[r][1] = 0;
-        continue;
-      }
-      const uint8_t *row = S.kv_rows + idx * kKvRowBytes;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int i = tid + 256 * hh;
-        if (i < kKvNope) {
-          lo[r][hh] = row[i];
-          sc[r][hh] = row[576 + (i >> 6)];
-          hi[r][hh] = 0;
-        } else {
-          const int o = kKvNope + 2 * (i - kKvNope);
-          lo[r][hh] = row[o];
-          hi[r][hh] = row[o + 1];
-          sc[r][hh] = 0;
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int i = tid + 256 * hh;
-        const float v = (i < kKvNope) ? e4m3_value(lo[r][hh]) * ue8m0_scale(sc[r][hh])
-                                      : f16_value(lo[r][hh] | (hi[r][hh] << 8));
-        kv[r][i] = rowid[r] >= 0 ? v : 0.0f;
-      }
-    }
-  }
+  decode_logit_rows(S.kv_rows, S.n_rows > 0, sh, nb);
+  LogitQuery q;
+  split_logit_query(q, qraw);
   __syncthreads();
-
-  // logits: thread -> (head h, row r)
-  const int h = tid / kR, r = tid % kR;
-  const int hglob = hg * kHG + h;
-  float logit = -__builtin_inff();
-  if (hglob < a.n_heads && rowid[r] >= 0) {
-    const float4 *q4 = reinterpret_cast<const float4 *>(S.q_attn + (size_t)hglob * CSA_KV_DIM);
-    const float4 *k4 = reinterpret_cast<const float4 *>(&kv[r][0]);
-    float dot = 0.0f;
-    for (int i = 0; i < CSA_KV_DIM / 4; ++i) {
-      const float4 qv = q4[i], kk = k4[i];
-      dot = __builtin_fmaf(qv.x, kk.x, dot);
-      dot = __builtin_fmaf(qv.y, kk.y, dot);
-      dot = __builtin_fmaf(qv.z, kk.z, dot);
-      dot = __builtin_fmaf(qv.w, kk.w, dot);
-    }
-    logit = a.scale * dot;
-  }
-  float m = logit;
-#pragma unroll
-  for (int off = kR / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kR));
-  const float p = (m == -__builtin_inff()) ? 0.0f : __expf(logit - m);
-  float l = p;
-#pragma unroll
-  for (int off = kR / 2; off > 0; off >>= 1) l += __shfl_xor(l, off, kR);
-  prob[h][r] = p;
-  float *part = a.part + ((size_t)(sess * kAttnSplits + split) * CSA_MAX_HEADS) * kPartStride;
-  if (r == 0 && hglob < a.n_heads) {
-    part[(size_t)hglob * kPartStride + CSA_KV_DIM] = m;
-    part[(size_t)hglob * kPartStride + CSA_KV_DIM + 1] = l;
-  }
-  __syncthreads();
-
-  // partial P.V: thread -> dims tid and tid + 256, all heads of the group
-  for (int hh = 0; hh < kHG; ++hh) {
-    const int hgl = hg * kHG + hh;
-    if (hgl >= a.n_heads) break;
-    float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-    for (int rr = 0; rr < kR; ++rr) {
-      const float pr = prob[hh][rr];
-      acc0 = __builtin_fmaf(pr, kv[rr][tid], acc0);
-      acc1 = __builtin_fmaf(pr, kv[rr][tid + 256], acc1);
-    }
-    part[(size_t)hgl * kPartStride + tid] = acc0;
-    part[(size_t)hgl * kPartStride + tid + 256] = acc1;
-  }
+  batch_logits(q, sh, nb, a.n_heads, a.softmax_scale, a.logits + (size_t)sess * kLogitFloats);
 }
 
-__global__ void __launch_bounds__(256) attn_combine_kernel(const AttnCombArgs a) {
-  const int h = blockIdx.x, sess = blockIdx.y, tid = threadIdx.x;
-  const AttnCombSession &S = a.s[sess];
-  const int nsplit = (S.n_sel + kR - 1) / kR;
-  const float *base = a.part + (size_t)sess * kAttnSplits * CSA_MAX_HEADS * kPartStride + (size_t)h * kPartStride;
-  const size_t sstride = (size_t)CSA_MAX_HEADS * kPartStride;
-  // every partial load is issued up front (fixed trip counts, clamped)
-  float ms[kAttnSplits], ls[kAttnSplits], a0[kAttnSplits], a1[kAttnSplits];
-#pragma unroll
-  for (int s = 0; s < kAttnSplits; ++s) {
-    const float *ps = base + (s < nsplit ? s : 0) * sstride;
-    ms[s] = ps[CSA_KV_DIM];
-    ls[s] = ps[CSA_KV_DIM + 1];
-    a0[s] = ps[tid];
-    a1[s] = ps[tid + 256];
+// ---------------------------------------------------------------- softmax + PV
+
+constexpr int kPvThreads = 256;
+constexpr int kPvTileDims = 16;
+constexpr int kPvTiles = kKvDim / kPvTileDims;  // 32
+constexpr int kPvStride = kPvTileDims + 1;
+
+struct PvShared {
+  float v[CSA_TOPK][kPvStride];  // value tile: selected row x 16 dimensions
+  int32_t row[CSA_TOPK];
+};
+
+__global__ void __launch_bounds__(kPvThreads) pv_kernel(const AttnArgs a) {
+  const int sess = blockIdx.y;
+  const AttnSession &S = a.s[sess];
+  const int dt = blockIdx.x;
+  const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63;
+  const int n_sel = S.n_sel;
+  __shared__ PvShared sh;
+  for (int j = tid; j < CSA_TOPK; j += kPvThreads) {
+    const int32_t r = j < n_sel ? S.sel_idx[j] : -1;
+    sh.row[j] = valid_row(r, S.n_rows) ? r : -1;
   }
-  float M = -__builtin_inff();
+  // this lane's logits: head 16g + l%16, rows 32 s + 8 (l/16) + i
+  const int h = 16 * g + (lane & 15);
+  const bool head_ok = h < a.n_heads;
+  const float *lg = a.logits + (size_t)sess * kLogitFloats + (size_t)(head_ok ? h : 0) * CSA_TOPK;
+  // every slot of the logits buffer is readable: load all 512 without
+  // conditions (a condition would let the compiler put each load behind its
+  // own branch and wait), mask after the barrier
+  float p[16][8];
 #pragma unroll
-  for (int s = 0; s < kAttnSplits; ++s) M = (s < nsplit) ? fmaxf(M, ms[s]) : M;
-  float *out = S.out + (size_t)h * CSA_KV_DIM;
-  if (M == -__builtin_inff()) {
-    out[tid] = 0.0f;
-    out[tid + 256] = 0.0f;
-    if (tid == 0 && S.lse) S.lse[h] = -__builtin_inff();
-    return;
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[s][i] = lg[32 * s + 8 * (lane >> 4) + i];
+  __syncthreads();
+  // value tile: 512 rows x 16 dimensions, 32 per thread
+  const int d0 = kPvTileDims * dt;
+  if (S.n_rows > 0) {
+    constexpr int U = CSA_TOPK * kPvTileDims / kPvThreads;
+    int32_t r[U];
+    uint32_t b0[U], b1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = sh.row[(tid + kPvThreads * u) / kPvTileDims];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = tid + kPvThreads * u;
+      kv_load(S.kv_rows + (size_t)(uint32_t)max(r[u], 0) * kKvRowBytes, d0 + e % kPvTileDims, b0[u], b1[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = tid + kPvThreads * u;
+      const float x = kv_decode(d0 + e % kPvTileDims, b0[u], b1[u]);
+      sh.v[e / kPvTileDims][e % kPvTileDims] = r[u] >= 0 ? x : 0.0f;
+    }
+  } else {
+    for (int e = tid; e < CSA_TOPK * kPvTileDims; e += kPvThreads) sh.v[e / kPvTileDims][e % kPvTileDims] = 0.0f;
   }
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  // invalid entries (and entries past n_sel, and absent heads) carry no weight
 #pragma unroll
-  for (int s = 0; s < kAttnSplits; ++s) {
-    if (s < nsplit && ms[s] != -__builtin_inff()) {
-      const float wgt = __expf(ms[s] - M);
-      L = __builtin_fmaf(wgt, ls[s], L);
-      o0 = __builtin_fmaf(wgt, a0[s], o0);
-      o1 = __builtin_fmaf(wgt, a1[s], o1);
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+    {
+      const bool bad = (sh.row[32 * s + 8 * (lane >> 4) + i] < 0) | !head_ok;
+      p[s][i] = bad ? -__builtin_inff() : p[s][i];
+    }
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, p[s][i]);
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const float mref = m == -__builtin_inff() ? 0.0f : m;
+  float sum = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[s][i] = __expf(p[s][i] - mref);
+      sum += p[s][i];
+    }
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  __syncthreads();  // value tile complete
+  const bool rope = d0 >= kKvNope;
+  v4f_attn c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    v8bf ph, pl, vh, vl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ph[i] = (__bf16)p[s][i];
+      pl[i] = (__bf16)(p[s][i] - (float)ph[i]);
+      const float v = sh.v[32 * s + 8 * (lane >> 4) + i][lane & 15];
+      vh[i] = (__bf16)v;
+      vl[i] = (__bf16)(v - (float)vh[i]);
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vh, c, 0, 0, 0);
+    if (rope) {
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vl, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vl, c, 0, 0, 0);
     }
   }
-  const float inv = 1.0f / L;
-  out[tid] = o0 * inv;
-  out[tid + 256] = o1 * inv;
-  if (tid == 0 && S.lse) S.lse[h] = M + __logf(L);
+  // lane l holds heads 16g + 4(l/16) + v, dimension d0 + l%16; the sum and
+  // maximum of head 16g + x sit in lane x
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int src = 4 * (lane >> 4) + v;
+    const float sv = __shfl(sum, src, 64);
+    const int hv = 16 * g + src;
+    if (hv < a.n_heads) S.out[(size_t)hv * kKvDim + d0 + (lane & 15)] = sv > 0.0f ? c[v] / sv : 0.0f;
+  }
+  if (dt == 0 && lane < 16 && head_ok && S.lse) S.lse[h] = sum > 0.0f ? mref + logf(sum) : -__builtin_inff();
 }
 
-hipError_t launch_attention(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale,
-                            float *part, hipStream_t st) {
-  AttnPartArgs pa;
-  AttnCombArgs ca;
-  for (int i = 0; i < n_sessions; ++i) {
-    pa.s[i] = AttnPartSession{s[i].kv_rows, s[i].sel_idx, s[i].q_attn, s[i].n_rows, s[i].n_sel};
-    ca.s[i] = AttnCombSession{s[i].out, s[i].lse, s[i].n_sel};
-  }
-  pa.part = part;
-  ca.part = part;
-  pa.n_heads = n_heads;
-  ca.n_heads = n_heads;
-  pa.scale = softmax_scale;
-  dim3 g1(kAttnSplits, (n_heads + kHG - 1) / kHG, n_sessions);
-  attn_partial_kernel<<<g1, 256, 0, st>>>(pa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 g2(n_heads, n_sessions);
-  attn_combine_kernel<<<g2, 256, 0, st>>>(ca);
+// ---------------------------------------------------------------- launchers
+
+static AttnArgs attn_args(const AttnSession *s, int n_sessions, int n_heads, float scale, const float *logits) {
+  AttnArgs a;
+  for (int i = 0; i < n_sessions; ++i) a.s[i] = s[i];
+  a.logits = const_cast<float *>(logits);
+  a.n_heads = n_heads;
+  a.softmax_scale = scale;
+  return a;
+}
+
+hipError_t launch_logits(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale, float *logits,
+                         hipStream_t st) {
+  const AttnArgs a = attn_args(s, n_sessions, n_heads, softmax_scale, logits);
+  logits_kernel<<<dim3(kLogitBatches, n_sessions), kLogitThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pv(const AttnSession *s, int n_sessions, int n_heads, const float *logits, hipStream_t st) {
+  const AttnArgs a = attn_args(s, n_sessions, n_heads, 0.0f, logits);
+  pv_kernel<<<dim3(kPvTiles, n_sessions), kPvThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

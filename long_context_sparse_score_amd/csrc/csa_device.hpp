@@ -33,21 +33,25 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
   return __uint_as_float(mag | ((c & 8u) << 28));
 }
 
-// E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN) byte -> fp32.
+// E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN) byte -> fp32.  Both
+// cases are computed and selected (no branch: decoders sit in unrolled
+// gathers whose loads must stay in flight together).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  if ((c & 0x7Fu) == 0x7Fu) return __uint_as_float(0x7FC00000u);
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+  const float norm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0x1p-9f;
+  const float v = __uint_as_float(__float_as_uint(e ? norm : sub) | ((c & 0x80u) << 24));
+  return ((c & 0x7Fu) == 0x7Fu) ? __uint_as_float(0x7FC00000u) : v;
 }
 
-// IEEE binary16 bits -> fp32 (exact, subnormals included).
+// IEEE binary16 bits -> fp32 (exact, subnormals included), branch-free.
 __device__ __forceinline__ float f16_value(uint32_t h) {
   const uint32_t s = (h & 0x8000u) << 16;
   const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
-  if (e == 0u) return __uint_as_float(__float_as_uint((float)m * 0x1p-24f) | s);
+  const float sub = __uint_as_float(__float_as_uint((float)m * 0x1p-24f) | s);
   const uint32_t bits = (e == 31u) ? (0x7F800000u | (m << 13)) : (((e + 112u) << 23) | (m << 13));
-  return __uint_as_float(bits | s);
+  const float nrm = __uint_as_float(bits | s);
+  return e == 0u ? sub : nrm;
 }
 
 // Monotone map of a score to 32 bits: larger score -> larger value, -0 == +0,

@@ -11,28 +11,60 @@
 
 namespace csa {
 
-// Largest tile of the score/select kernel (rows kept in LDS as 32-bit
-// order keys) and the smallest (the tile's top-512 needs >= 512 rows).
+// Tile of the score kernel: rows scored by one workgroup and kept in LDS.
 constexpr int kMaxTileRows = 4096;
 constexpr int kMinTileRows = 512;
+// Heads per tile: the tile's exact top-H keys, H in {16, 32, 64}.
+constexpr int kMaxTileHeads = 64;
 
-// One launch of the tile kernel (and of the merge that follows it).
+// Heads per tile for a session of nt tiles: enough that the heads of all
+// tiles number at least ~2048 (so few tiles hold more winners than heads).
+inline int heads_per_tile(int64_t nt) {
+  int hd = 16;
+  while (hd < kMaxTileHeads && nt * hd < 2048) hd *= 2;
+  return hd;
+}
+
+// One launch of the score kernel.
 struct TileJob {
   enum Mode { kScore, kScoreSelect, kArraySelect } mode;
   int n_sessions;
   int n_idx_heads;
   int tile_rows;
   const uint8_t *idx_rows[CSA_MAX_SESSIONS];
-  const float *scores_in[CSA_MAX_SESSIONS];
-  float *scores_out[CSA_MAX_SESSIONS];
+  const float *scores_in[CSA_MAX_SESSIONS];  // kArraySelect
+  float *scores_out[CSA_MAX_SESSIONS];       // kScore, kScoreSelect
   int64_t n_rows[CSA_MAX_SESSIONS];
+  int hd[CSA_MAX_SESSIONS];
   const uint32_t *qsplit;  // query split, [session][kQSplitBytes / 4]
-  uint64_t *cand;          // per tile: its top-512 keys
-  uint64_t *heads;         // per tile: its top-16 keys, sorted
-  int64_t cand_stride, heads_stride;  // keys per session
+  uint64_t *heads;         // [session][heads_stride]: per tile its top-hd keys, sorted
+  int64_t heads_stride;
 };
 
-// Per-session pointers for the attention stages.
+// One launch of the global selection (and, optionally, of the attention
+// logits of the selected rows).
+struct SelectJob {
+  int n_sessions;
+  int tile_rows;
+  int k;
+  int slices;          // workgroups per session
+  bool array_scores;   // sel_score from the score array (csa_topk) or the key
+  const float *scores[CSA_MAX_SESSIONS];
+  int64_t n_rows[CSA_MAX_SESSIONS];
+  int hd[CSA_MAX_SESSIONS];
+  int32_t *sel_idx[CSA_MAX_SESSIONS];
+  float *sel_score[CSA_MAX_SESSIONS];
+  const uint64_t *heads;
+  int64_t heads_stride;
+  // logits of the selected rows (nullptr: none)
+  float *logits;  // [session][64][512]
+  const uint8_t *kv_rows[CSA_MAX_SESSIONS];
+  const float *q_attn[CSA_MAX_SESSIONS];
+  int n_heads;
+  float softmax_scale;
+};
+
+// Per-session pointers of the attention stages.
 struct AttnSession {
   const uint8_t *kv_rows;
   const int32_t *sel_idx;
@@ -43,12 +75,8 @@ struct AttnSession {
   int32_t n_sel;
 };
 
-// Attention split: rows of the selection handled by one workgroup.
-constexpr int kAttnRowsPerSplit = 16;
-constexpr int kAttnSplits = CSA_TOPK / kAttnRowsPerSplit;  // 32
-constexpr int kAttnHeadsPerGroup = 16;
-// Floats of split partials per session: [split][head][512 acc + m + l].
-constexpr size_t kAttnPartFloats = (size_t)kAttnSplits * CSA_MAX_HEADS * (CSA_KV_DIM + 2);
+// Logits per session in the workspace: [head][selected row].
+constexpr size_t kLogitFloats = (size_t)CSA_MAX_HEADS * CSA_TOPK;
 
 hipError_t launch_dequant_idx(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
 hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
@@ -56,10 +84,11 @@ hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStre
 hipError_t launch_q_split(const float *const *q, const float *const *w, int n_sessions, int n_heads,
                           uint32_t *out, hipStream_t st);
 hipError_t launch_tiles(const TileJob &job, hipStream_t st);
-hipError_t launch_merge(const TileJob &job, int32_t *const *sel_idx, float *const *sel_score, int k,
-                        hipStream_t st);
-// part: workspace of n_sessions * kAttnPartFloats floats (session-major).
-hipError_t launch_attention(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale,
-                            float *part, hipStream_t st);
+hipError_t launch_select(const SelectJob &job, hipStream_t st);
+// Logits of the rows sel_idx[0..n_sel) of every session (csa_sparse_attn).
+hipError_t launch_logits(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale, float *logits,
+                         hipStream_t st);
+// Softmax over the logits and the value sum: out, lse.
+hipError_t launch_pv(const AttnSession *s, int n_sessions, int n_heads, const float *logits, hipStream_t st);
 
 }  // namespace csa

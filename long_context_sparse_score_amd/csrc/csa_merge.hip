@@ -1,0 +1,387 @@
+// csa_merge.hip -- the global exact top-k of a session from its tiles' heads
+// (DS4X page, "CSA score/top-512 fusion": merge the per-tile selections into
+// the model's exact top-512 with the same float order and lower-index tie
+// break as a separate top-k pass), and optionally the attention logits of
+// the selected rows.
+//
+// Every workgroup of a session (grid.x = slices) runs the same selection:
+//   1. G: a lower bound on the 512th-largest head, found with one or two
+//      histogram passes over the heads: at least 512 heads are >= G, and at
+//      most kSelTarget are (or exactly 512).  Since every head is a key, at
+//      least 512 keys are >= G, so G also bounds the global 512th key, and
+//      the top-k (k <= 512) lies among the keys >= G.
+//   2. A tile is "full" when its hd-th (smallest) head is >= G: it may hold
+//      keys >= G that are not heads.  Any other tile holds no key >= G beyond
+//      its heads.  Candidates = heads >= G of tiles that are not full, plus
+//      every key >= G of the full tiles, read from the score array.  (Few
+//      heads per tile hold at least hd keys >= G, so at most kSelTarget / hd
+//      tiles are full.)
+//   3. If the candidates overflow the LDS buffer (many ties, crowded
+//      winners), the exact k_eff-th key among them replaces G.
+//   4. The candidates are ranked exactly (rank = number of larger
+//      candidates).  Workgroup b ranks the candidates whose row hashes to b,
+//      writes sel_idx[rank] / sel_score[rank] for ranks < k_eff, and (when
+//      asked) computes the attention logits of those rows (csa_attn.hpp).
+// Selection keys are (ord32(score) << 32) | (2^32 - 1 - row): distinct,
+// larger = better; 0 means "no key".
+#include "csa_attn.hpp"
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+#include "csa_select.hpp"
+
+namespace csa {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelKPT = 8;                            // heads per thread in registers
+constexpr int kSelRegHeads = kSelThreads * kSelKPT;  // 8192
+constexpr int kSelBins = 2 * kSelThreads;             // histogram bins per pass
+constexpr int kSelCap = 4096;                         // candidates held in LDS
+constexpr int kSelTarget = 1024;                      // candidates at which G is good enough
+constexpr int kSelMaxFull = 128;                      // full tiles listed (at most kSelTarget / 16)
+constexpr int kSelMaxRegTiles = kSelRegHeads / 16;
+
+struct SelSessionArgs {
+  const float *scores;
+  int32_t *sel_idx;
+  float *sel_score;
+  const uint8_t *kv_rows;
+  const float *q_attn;
+  int64_t n_rows;
+  int hd;
+};
+
+struct SelArgs {
+  SelSessionArgs s[CSA_MAX_SESSIONS];
+  const uint64_t *heads;
+  float *logits;
+  int64_t heads_stride;
+  int tile_rows;
+  int k;
+  int n_heads;
+  float softmax_scale;
+  int array_scores;
+};
+static_assert(sizeof(SelArgs) <= 4096, "kernel argument block");
+
+struct SelShared {
+  uint64_t cand[kSelCap + 4 * 64];  // + over-read slack of the rank scan
+  uint32_t hist[kSelBins];
+  uint64_t red_lo[kSelWaves], red_hi[kSelWaves];
+  uint32_t red_n[kSelWaves];
+  uint32_t full_list[kSelMaxFull];
+  uint8_t full_flag[kSelMaxRegTiles];
+  uint16_t mine[kSelCap];
+  int32_t loc_rank[CSA_TOPK], loc_row[CSA_TOPK];
+  uint32_t ccnt, nfull, nmine, nloc;
+  uint32_t bin, ca, cb;
+  LogitShared lg;
+};
+
+// Lower bound G on the need-th largest of the keys that `visit` enumerates
+// (every thread visits its share, calling f(key) for each nonzero key): at
+// least need keys are >= G, and at most max(target, need) are.  Returns 1
+// (every key) when there are at most need keys.  All threads call it.
+template <class Visit>
+__device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32_t target, SelShared &sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint64_t mn = ~0ull, mx = 0;
+  uint32_t cnt = 0;
+  visit([&](uint64_t x) __attribute__((always_inline)) {
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
+    ++cnt;
+  });
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t a = shfl_xor_u64(mn, m), b = shfl_xor_u64(mx, m);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+    cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
+  }
+  if (lane == 0) { sh.red_lo[wave] = mn; sh.red_hi[wave] = mx; sh.red_n[wave] = cnt; }
+  __syncthreads();
+  uint64_t lo = ~0ull, hi = 0;
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    lo = sh.red_lo[w] < lo ? sh.red_lo[w] : lo;
+    hi = sh.red_hi[w] > hi ? sh.red_hi[w] : hi;
+    total += sh.red_n[w];
+  }
+  __syncthreads();
+  if (total <= need) return 1ull;
+  if (total <= target) return lo;
+  uint32_t above = 0;  // keys above the current range [lo, hi]
+  for (;;) {
+    const uint64_t span = hi - lo;
+    const int hb = span ? 63 - __clzll((long long)span) : 0;
+    const int shift = hb > 10 ? hb - 10 : 0;  // span >> shift < kSelBins
+    for (int i = tid; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    visit([&](uint64_t x) __attribute__((always_inline)) {
+      if (x >= lo && x <= hi) atomicAdd(&sh.hist[(uint32_t)((x - lo) >> shift)], 1u);
+    });
+    __syncthreads();
+    const uint32_t need_here = need - above;
+    const uint32_t h0 = sh.hist[2 * tid], h1 = sh.hist[2 * tid + 1];
+    const uint32_t s = h0 + h1;
+    uint32_t suf = s;  // inclusive suffix sum over the lanes of the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_down((int)suf, d, 64);
+      if (lane + d < 64) suf += v;
+    }
+    if (lane == 0) sh.red_n[wave] = suf;
+    __syncthreads();
+    uint32_t after = 0;
+    for (int w = wave + 1; w < kSelWaves; ++w) after += sh.red_n[w];
+    const uint32_t X = suf - s + after;  // keys in bins above 2 tid + 1
+    if (X < need_here && need_here <= X + h1) {
+      sh.bin = 2 * tid + 1; sh.ca = X; sh.cb = h1;
+    } else if (X + h1 < need_here && need_here <= X + s) {
+      sh.bin = 2 * tid; sh.ca = X + h1; sh.cb = h0;
+    }
+    __syncthreads();
+    const uint32_t b = sh.bin, ca = sh.ca, cb = sh.cb;
+    __syncthreads();
+    const uint64_t gb = lo + ((uint64_t)b << shift);
+    if (above + ca + cb <= target || shift == 0) return gb;
+    above += ca;
+    const uint64_t top = gb + ((1ull << shift) - 1);
+    lo = gb;
+    hi = top < hi ? top : hi;
+  }
+}
+
+// Row of a key -> workgroup of the session that ranks it.
+__device__ __forceinline__ uint32_t row_slice(uint32_t row, int slices) {
+  return (uint32_t)(((uint64_t)(row * 0x9E3779B1u) * (uint32_t)slices) >> 32);
+}
+
+// REG: every session's heads fit in registers (at most kSelRegHeads), chosen
+// on the host for the whole launch; otherwise they are re-read per pass.
+template <bool LOGITS, bool REG>
+__global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
+  const int sess = blockIdx.y;
+  // fields used inside lambdas are copied first: a lambda taking the address
+  // of the kernel argument block would force a private copy of it
+  const float *const scores = a.s[sess].scores;
+  int32_t *const sel_idx = a.s[sess].sel_idx;
+  float *const sel_score = a.s[sess].sel_score;
+  const int64_t n = a.s[sess].n_rows;
+  const int k = a.k;
+  const int k_eff = (int)(n < k ? n : k);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ SelShared sh;
+
+  if (blockIdx.x == 0)
+    for (int r = k_eff + tid; r < k; r += kSelThreads) {
+      sel_idx[r] = -1;
+      if (sel_score) sel_score[r] = -__builtin_inff();
+    }
+  if (k_eff == 0) return;
+
+  const int T = a.tile_rows;
+  const int hd = a.s[sess].hd;
+  const int64_t nt = (n + T - 1) / T;
+  const int64_t nh = nt * hd;
+  const uint64_t *heads = a.heads + (size_t)sess * a.heads_stride;
+  constexpr bool reg = REG;
+  if (tid == 0) { sh.ccnt = 0; sh.nfull = 0; sh.nmine = 0; sh.nloc = 0; }
+
+  // heads in registers: slot j of thread tid is head tid + 1024 j
+  uint64_t h[kSelKPT];
+  if constexpr (reg) {
+#pragma unroll
+    for (int j = 0; j < kSelKPT; ++j) {
+      const int64_t i = tid + (int64_t)kSelThreads * j;
+      const uint64_t y = heads[i < nh ? i : nh - 1];  // clamped: no branch around the load
+      h[j] = i < nh ? y : 0ull;
+    }
+  }
+  auto visit_heads = [&](auto f) __attribute__((always_inline)) {
+    if constexpr (reg) {
+#pragma unroll
+      for (int j = 0; j < kSelKPT; ++j)
+        if (h[j] != 0) f(h[j]);
+    } else {
+      for (int64_t i0 = tid; i0 < nh; i0 += (int64_t)kSelThreads * 8) {
+        uint64_t y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i = i0 + (int64_t)kSelThreads * u;
+          const uint64_t z = heads[i < nh ? i : nh - 1];
+          y[u] = i < nh ? z : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (y[u] != 0) f(y[u]);
+      }
+    }
+  };
+
+  // 1. the bound G
+  const uint64_t G = sel_bound(visit_heads, (uint32_t)kTopK, (uint32_t)kSelTarget, sh);
+
+  // 2. full tiles
+  auto tile_is_full = [&](int64_t t) __attribute__((always_inline)) {
+    const uint64_t last = heads[t * hd + hd - 1];
+    return last != 0 && last >= G;
+  };
+  if constexpr (reg) {
+#pragma unroll
+    for (int j = 0; j < kSelKPT; ++j) {
+      const int64_t i = tid + (int64_t)kSelThreads * j;
+      if (i < nh && (int)(i % hd) == hd - 1) {
+        const bool full = h[j] != 0 && h[j] >= G;
+        sh.full_flag[i / hd] = full ? 1 : 0;
+        if (full) {
+          const uint32_t p = atomicAdd(&sh.nfull, 1u);
+          if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)(i / hd);
+        }
+      }
+    }
+  } else {
+    for (int64_t t = tid; t < nt; t += kSelThreads)
+      if (tile_is_full(t)) {
+        const uint32_t p = atomicAdd(&sh.nfull, 1u);
+        if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)t;
+      }
+  }
+  __syncthreads();
+  const int nfull = (int)(sh.nfull < kSelMaxFull ? sh.nfull : kSelMaxFull);
+
+  // candidates: heads >= lb of tiles that are not full, keys >= lb of full tiles
+  auto visit_cand = [&](uint64_t lb, auto f) __attribute__((always_inline)) {
+    if constexpr (reg) {
+#pragma unroll
+      for (int j = 0; j < kSelKPT; ++j) {
+        const int64_t i = tid + (int64_t)kSelThreads * j;
+        if (h[j] != 0 && h[j] >= lb && !sh.full_flag[i / hd]) f(h[j]);
+      }
+    } else {
+      visit_heads([&](uint64_t x) __attribute__((always_inline)) {
+        if (x >= lb) {
+          // the tile of this head: keys carry the row, tiles are T rows
+          const int64_t t = (int64_t)key_row(x) / T;
+          if (!tile_is_full(t)) f(x);
+        }
+      });
+    }
+    const int64_t nfr = (int64_t)nfull * T;
+    for (int64_t i0 = tid; i0 < nfr; i0 += (int64_t)kSelThreads * 8) {
+      float v[8];
+      int64_t row[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + (int64_t)kSelThreads * u;
+        row[u] = i < nfr ? (int64_t)sh.full_list[i / T] * T + (i % T) : n;
+        v[u] = scores[row[u] < n ? row[u] : n - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (row[u] < n) {
+          const uint64_t x = ((uint64_t)score_ord(v[u]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row[u]);
+          if (x >= lb) f(x);
+        }
+      }
+    }
+  };
+  auto append = [&](uint64_t x) __attribute__((always_inline)) {
+    const uint32_t p = atomicAdd(&sh.ccnt, 1u);
+    if (p < kSelCap) sh.cand[p] = x;
+  };
+  visit_cand(G, append);
+  __syncthreads();
+  int C = (int)sh.ccnt;
+  if (C > kSelCap) {
+    // 3. too many candidates: the exact k_eff-th key among them
+    const uint64_t thr = sel_bound([&](auto f) __attribute__((always_inline)) { visit_cand(G, f); }, (uint32_t)k_eff, (uint32_t)k_eff, sh);
+    if (tid == 0) sh.ccnt = 0;
+    __syncthreads();
+    visit_cand(thr, append);
+    __syncthreads();
+    C = (int)sh.ccnt;
+  }
+
+  // 4. rank this workgroup's candidates
+  for (int i0 = 0; i0 < C; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    if (i < C && row_slice(key_row(sh.cand[i]), gridDim.x) == blockIdx.x) sh.mine[atomicAdd(&sh.nmine, 1u)] = (uint16_t)i;
+  }
+  __syncthreads();
+  const int nm = (int)sh.nmine;
+  for (int m = wave; m < nm; m += kSelWaves) {
+    const uint64_t x = sh.cand[sh.mine[m]];
+    uint32_t r = 0;
+    for (int j0 = 0; j0 < C; j0 += 4 * 64) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + 64 * u + lane;
+        const uint64_t y = sh.cand[j];
+        r += (uint32_t)__popcll(__ballot(j < C && y > x));
+      }
+    }
+    if (lane == 0 && r < (uint32_t)k_eff) {
+      const uint32_t row = key_row(x);
+      sel_idx[r] = (int32_t)row;
+      if (sel_score) sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+      const uint32_t p = atomicAdd(&sh.nloc, 1u);
+      sh.loc_rank[p] = (int32_t)r;
+      sh.loc_row[p] = (int32_t)row;
+    }
+  }
+  if constexpr (!LOGITS) return;
+
+  // 5. attention logits of this workgroup's selected rows
+  __syncthreads();
+  const int nl = (int)sh.nloc;
+  if (nl == 0) return;
+  LogitQueryRaw qraw;  // loads in flight together with the first batch's rows
+  load_logit_query(qraw, a.s[sess].q_attn, a.n_heads);
+  LogitQuery q;
+  split_logit_query(q, qraw);
+  float *logits = a.logits + (size_t)sess * kLogitFloats;
+  for (int b0 = 0; b0 < nl; b0 += kLogitRows) {
+    const int nb = nl - b0 < kLogitRows ? nl - b0 : kLogitRows;
+    if (tid < kLogitRows) {
+      sh.lg.row[tid] = tid < nb ? sh.loc_row[b0 + tid] : -1;
+      sh.lg.pos[tid] = tid < nb ? sh.loc_rank[b0 + tid] : 0;
+    }
+    __syncthreads();
+    decode_logit_rows(a.s[sess].kv_rows, true, sh.lg, nb);
+    __syncthreads();
+    batch_logits(q, sh.lg, nb, a.n_heads, a.softmax_scale, logits);
+  }
+}
+
+hipError_t launch_select(const SelectJob &job, hipStream_t st) {
+  SelArgs a;
+  for (int i = 0; i < job.n_sessions; ++i)
+    a.s[i] = SelSessionArgs{job.scores[i], job.sel_idx[i], job.sel_score[i],
+                            job.logits ? job.kv_rows[i] : nullptr, job.logits ? job.q_attn[i] : nullptr,
+                            job.n_rows[i], job.hd[i]};
+  a.heads = job.heads;
+  a.logits = job.logits;
+  a.heads_stride = job.heads_stride;
+  a.tile_rows = job.tile_rows;
+  a.k = job.k;
+  a.n_heads = job.n_heads;
+  a.softmax_scale = job.softmax_scale;
+  a.array_scores = job.array_scores ? 1 : 0;
+  const dim3 grid((unsigned)job.slices, (unsigned)job.n_sessions);
+  bool reg = true;
+  for (int i = 0; i < job.n_sessions; ++i)
+    reg = reg && ((job.n_rows[i] + job.tile_rows - 1) / job.tile_rows) * job.hd[i] <= kSelRegHeads;
+  if (job.logits) {
+    if (reg) select_kernel<true, true><<<grid, kSelThreads, 0, st>>>(a);
+    else select_kernel<true, false><<<grid, kSelThreads, 0, st>>>(a);
+  } else {
+    if (reg) select_kernel<false, true><<<grid, kSelThreads, 0, st>>>(a);
+    else select_kernel<false, false><<<grid, kSelThreads, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

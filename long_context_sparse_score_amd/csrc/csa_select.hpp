@@ -18,6 +18,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, 64);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 template <int NW>  // waves per workgroup
 struct SelScratch {
   uint32_t hist[NW][256];
@@ -218,59 +224,6 @@ __device__ uint64_t block_kth_largest_reg(const uint64_t (&x)[KPT], int nj, int 
     if (done) return prefix > lb ? prefix : lb;
     hi = shift - 1;
   }
-}
-
-// Descending order of up to NT*ranks distinct keys in LDS by counting: the
-// rank of a key is the number of larger keys.  keys[0..n) -> out[0..n).
-// No barrier inside the counting; n <= 1024.
-template <int NT>
-__device__ void block_rank_sort_desc(const uint64_t *keys, int n, uint64_t *out) {
-  constexpr int PER = NT >= 1024 ? 1 : 1024 / NT;
-  for (int base = 0; base < PER; ++base) {
-    const int i = threadIdx.x + base * NT;
-    if (i < n) {
-      const uint64_t x = keys[i];
-      int r = 0;
-      for (int j = 0; j < n; ++j) r += keys[j] > x ? 1 : 0;
-      out[r] = x;
-    }
-  }
-  __syncthreads();
-}
-
-// Bitonic sort of n2 (a power of two) keys in LDS, descending.
-template <int NT>
-__device__ void block_sort_desc(uint64_t *keys, int n2) {
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < (n2 >> 1); t += NT) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = ((lo & size) == 0);
-        const uint64_t a = keys[lo], b = keys[hi];
-        if ((a < b) == desc) { keys[lo] = b; keys[hi] = a; }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// One wave sorts the 16 keys held by lanes 0..15 (descending); other lanes'
-// values are ignored.  Returns this lane's sorted key (lanes 0..15).
-__device__ __forceinline__ uint64_t wave_sort16_desc(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 16; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t o = shfl_xor_u64(v, stride);
-      const bool desc = ((lane & size) == 0) || size == 16;
-      const bool lower = (lane & stride) == 0;
-      const bool take_max = (lower == desc);
-      v = take_max ? (o > v ? o : v) : (o < v ? o : v);
-    }
-  }
-  return v;
 }
 
 }  // namespace csa

@@ -1,22 +1,20 @@
-// csa_topk_tile.hip -- fused score + exact top-512 selection, without a
-// full score array (DS4X page, "CSA score/top-512 fusion": per-CTA exact
-// local top-512 lists of sortable (score, index) keys, then merges that keep
-// float order and lower-index tie break).
+// csa_topk_tile.hip -- fused score + per-tile heads (DS4X page, "CSA
+// score/top-512 fusion": the scorer keeps exact local selections of sortable
+// (score, index) keys per tile of rows, so no separate pass over a score
+// array is needed to find the winners).
 //
 // tile_kernel (one workgroup per T-row tile of one session):
 //   1. scores the tile's rows on the matrix cores (csa_score.hpp) into LDS
-//      (or reads a given score array, or only writes the scores);
-//   2. selects the tile's exact top-min(512, rows) keys -> cand[tile][512]
-//      (unordered, 0-padded) and its top-16 sorted descending ->
-//      heads[tile][16] (0-padded).
-// merge_kernel (one workgroup per session):
-//   3. G = the 512th largest head over all tiles (or "everything" if there are
-//      fewer).  At least 512 keys are >= G, so G lower-bounds the global
-//      512th key.  A tile whose 16th head is below G holds at most 15 keys
-//      >= G, all among its heads; any other ("full") tile contributes its
-//      cand list.  At most 32 tiles can be full, so the candidates number at
-//      most 32*512 + 512 and fit in LDS.
-//   4. exact top-k_eff of the candidates, sorted -> sel_idx / sel_score.
+//      and writes them out (or reads a given score array);
+//   2. finds the tile's exact top-hd keys ("heads", hd in {16, 32, 64}) and
+//      writes them sorted descending to heads[tile][hd] (0-padded).
+// Step 2 first bounds the hd-th key from below without sorting the tile:
+// every wave sorts the 64 per-lane maxima of its keys, and the hd-th largest
+// of them is a key with at least hd keys above or at it; the largest such
+// bound over the waves is theta.  Only keys >= theta can be heads.  At most
+// hd lanes per wave hold such keys, so there are at most 4 * hd * (T / 256)
+// of them (typically 2-4 hd); they are ranked exactly against each other.
+// The global selection over the heads is in csa_merge.hip.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "csa_score.hpp"
@@ -30,14 +28,14 @@ struct TileSession {
   const float *scores_in;
   float *scores_out;
   int64_t n_rows;
+  int hd;
 };
 
 struct TileArgs {
   TileSession s[CSA_MAX_SESSIONS];
   const uint32_t *qsplit;  // [session][kQSplitBytes / 4]
-  uint64_t *cand;          // [session][cand_stride]
   uint64_t *heads;         // [session][heads_stride]
-  int64_t cand_stride, heads_stride;
+  int64_t heads_stride;
   int tile_rows;
 };
 static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
@@ -49,51 +47,85 @@ constexpr int kTileWaves = kTileThreads / 64;
 
 constexpr int kTileKPT = kMaxTileRows / kTileThreads;  // keys per thread, at most
 constexpr int kRingDepth = 3;                            // chunks in flight per wave
+constexpr int kTileCandCap = 256;                        // keys >= theta ranked directly
 
 struct TileShared {
   uint8_t ring[kTileWaves][kRingDepth][kChunkSlot];  // per-wave chunk ring
   float score[kMaxTileRows];                          // scores by tile position
-  uint64_t sel[kTopK];
-  uint64_t top16[16];
-  uint32_t cnt, cnt16;
+  uint64_t cand[kTileCandCap + 16];                   // keys >= theta (+ over-read slack)
+  uint64_t theta[kTileWaves];
+  uint32_t ccnt;
   SelScratch<kTileWaves> sc;
 };
 
-// Step 2 on keys held in registers (slot j of thread tid is tile position
-// tid + 256 j; nj slots are live): the tile's top-512 set and sorted top-16.
-__device__ void tile_select(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj, int rows,
-                            uint64_t *__restrict__ cand_out, uint64_t *__restrict__ heads_out) {
-  const int tid = threadIdx.x;
-  const int k_loc = rows < kTopK ? rows : kTopK;
-  if (tid == 0) { sh.cnt = 0; sh.cnt16 = 0; }
-  const uint64_t thr = block_kth_largest_reg<kTileWaves, kTileKPT>(x, nj, k_loc, 1ull, sh.sc);
+// Bitonic sort of one key per lane across the wave, descending: lane l
+// returns the l-th largest.
+__device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < kTileKPT; ++j) {
-    if (j < nj && x[j] != 0 && x[j] >= thr) {
-      const uint32_t p = atomicAdd(&sh.cnt, 1u);
-      sh.sel[p] = x[j];
-      cand_out[p] = x[j];
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, stride);
+      const bool desc = ((lane & size) == 0) || size == 64;
+      const bool lower = (lane & stride) == 0;
+      v = (lower == desc) ? (o > v ? o : v) : (o < v ? o : v);
     }
   }
-  for (int p = k_loc + tid; p < kTopK; p += kTileThreads) cand_out[p] = 0ull;
-  __syncthreads();
-  const int kh = k_loc < 16 ? k_loc : 16;
-  uint64_t y[kTopK / kTileThreads];
+  return v;
+}
+
+// Step 2: keys in registers (slot j of thread tid is tile position tid +
+// 256 j, 0 = none) -> the tile's top-hd keys, sorted, at heads_out[0..hd).
+__device__ void tile_heads(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj, int hd,
+                           uint64_t *__restrict__ heads_out) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint64_t lmax = 0;
 #pragma unroll
-  for (int j = 0; j < kTopK / kTileThreads; ++j) {
-    const int i = tid + kTileThreads * j;
-    y[j] = i < k_loc ? sh.sel[i] : 0ull;
-  }
-  const uint64_t thr16 = block_kth_largest_reg<kTileWaves, kTopK / kTileThreads>(y, kTopK / kTileThreads, kh,
-                                                                                  1ull, sh.sc);
-#pragma unroll
-  for (int j = 0; j < kTopK / kTileThreads; ++j)
-    if (y[j] != 0 && y[j] >= thr16) sh.top16[atomicAdd(&sh.cnt16, 1u)] = y[j];
+  for (int j = 0; j < kTileKPT; ++j)
+    if (j < nj) lmax = x[j] > lmax ? x[j] : lmax;
+  const uint64_t srt = wave_sort64_desc(lmax);
+  const uint64_t tw = shfl_u64(srt, hd - 1);
+  if (lane == 0) sh.theta[wave] = tw;
+  if (tid == 0) sh.ccnt = 0;
   __syncthreads();
-  if (tid < 64) {
-    const uint64_t v = wave_sort16_desc(tid < kh ? sh.top16[tid] : 0ull);
-    if (tid < 16) heads_out[tid] = v;
+  uint64_t theta = 1;
+#pragma unroll
+  for (int w = 0; w < kTileWaves; ++w) theta = sh.theta[w] > theta ? sh.theta[w] : theta;
+#pragma unroll
+  for (int j = 0; j < kTileKPT; ++j) {
+    if (j < nj && x[j] >= theta) {
+      const uint32_t p = atomicAdd(&sh.ccnt, 1u);
+      if (p < kTileCandCap) sh.cand[p] = x[j];
+    }
   }
+  __syncthreads();
+  int C = (int)sh.ccnt;
+  if (C > kTileCandCap) {
+    // many keys tie with or crowd above the bound: select exactly instead
+    const uint64_t thr = block_kth_largest_reg<kTileWaves, kTileKPT>(x, nj, hd, theta, sh.sc);
+    if (tid == 0) sh.ccnt = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTileKPT; ++j)
+      if (j < nj && x[j] != 0 && x[j] >= thr) sh.cand[atomicAdd(&sh.ccnt, 1u)] = x[j];
+    __syncthreads();
+    C = (int)sh.ccnt;
+  }
+  // rank = number of larger candidates = sorted position
+  for (int i = tid; i < C; i += kTileThreads) {
+    const uint64_t key = sh.cand[i];
+    int r = 0;
+    for (int j0 = 0; j0 < C; j0 += 16) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint64_t y = sh.cand[j0 + u];
+        r += (j0 + u < C && y > key) ? 1 : 0;
+      }
+    }
+    if (r < hd) heads_out[r] = key;
+  }
+  for (int r = C + tid; r < hd; r += kTileThreads) heads_out[r] = 0ull;
 }
 
 // Score every row of the tile: wave w takes chunks w, w + 4, ... (64 rows
@@ -107,12 +139,10 @@ __device__ __forceinline__ void score_stream(const QFrag<G> &q, const uint8_t *_
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
   const int nfull = rows / kChunkRows;  // chunks with all 64 rows present
   const int cnt = nfull > wave ? (nfull - wave + kTileWaves - 1) / kTileWaves : 0;
+  // lanes 0..15 hold rows pos0 + lane of operand 0, lanes 16..31 rows
+  // pos0 + lane of operand 1
   auto emit2 = [&](int pos0, const float (&s2)[2]) {
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int pos = pos0 + 16 * v + lane;
-      if (lane < 16 && pos < rows) sh.score[pos] = score_finish(s2[v], 0.0f);
-    }
+    if (lane < 32 && pos0 + lane < rows) sh.score[pos0 + lane] = score_finish(lane < 16 ? s2[0] : s2[1], 0.0f);
   };
   if (cnt > 0) {
     auto slot = [&](int k) { return (uint32_t)(uintptr_t)&sh.ring[wave][k][0]; };
@@ -168,28 +198,27 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   if (row0 >= n) return;
   const int rows = (int)((n - row0) < T ? (n - row0) : T);
   __shared__ TileShared sh;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int nj = (rows + kTileThreads - 1) / kTileThreads;
   uint64_t x[kTileKPT];
-  auto key_of = [&](int i, uint32_t ord) -> uint64_t {
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(row0 + i));
+  auto key_of = [&](int i, float sc) -> uint64_t {
+    return ((uint64_t)score_ord(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(row0 + i));
   };
 
   if constexpr (MODE != kModeArraySelect) {
     QFrag<G> q;
     load_qfrag<G>(q, a.qsplit + (size_t)sess * (kQSplitBytes / 4), lane, 0);
     wait_vmcnt<0>();  // the query is resident before the chunk loads start
-    score_stream<G>(q, S.idx_rows, row0, n, rows, sh, wave, lane);
+    score_stream<G>(q, S.idx_rows, row0, n, rows, sh, tid >> 6, lane);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kTileKPT; ++j) {
       const int i = tid + kTileThreads * j;
+      x[j] = 0ull;
       if (j < nj && i < rows) {
         const float sc = sh.score[i];
-        if constexpr (MODE == kModeScore) S.scores_out[row0 + i] = sc;
-        else x[j] = key_of(i, score_ord(sc));
-      } else {
-        x[j] = 0ull;
+        S.scores_out[row0 + i] = sc;
+        x[j] = key_of(i, sc);
       }
     }
     if constexpr (MODE == kModeScore) return;
@@ -204,171 +233,13 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
 #pragma unroll
     for (int j = 0; j < kTileKPT; ++j) {
       const int i = tid + kTileThreads * j;
-      x[j] = (j < nj && i < rows) ? key_of(i, score_ord(v[j])) : 0ull;
+      x[j] = (j < nj && i < rows) ? key_of(i, v[j]) : 0ull;
     }
   }
-  tile_select(sh, x, nj, rows, a.cand + (size_t)sess * a.cand_stride + (size_t)blockIdx.x * kTopK,
-              a.heads + (size_t)sess * a.heads_stride + (size_t)blockIdx.x * 16);
+  tile_heads(sh, x, nj, S.hd, a.heads + (size_t)sess * a.heads_stride + (size_t)blockIdx.x * S.hd);
 }
 
-// ---------------------------------------------------------------- merge
-
-struct MergeSession {
-  const float *scores;  // score array (csa_topk) or nullptr (fused path)
-  int32_t *sel_idx;
-  float *sel_score;
-  int64_t n_rows;
-};
-
-struct MergeArgs {
-  MergeSession s[CSA_MAX_SESSIONS];
-  const uint64_t *cand;
-  const uint64_t *heads;
-  int64_t cand_stride, heads_stride;
-  int tile_rows;
-  int k;
-};
-static_assert(sizeof(MergeArgs) <= 4096, "kernel argument block");
-
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeWaves = kMergeThreads / 64;
-constexpr int kMergeCap = 32 * kTopK + kTopK;  // candidate bound (see the file comment)
-constexpr int kHeadKPT = 16;                     // heads per thread held in registers
-constexpr int kMaxRegHeads = kHeadKPT * kMergeThreads;
-constexpr int kCandKPT = (kMergeCap + kMergeThreads - 1) / kMergeThreads;  // 17
-
-struct MergeShared {
-  // candidate buffer of the many-tile path; the register path keeps the
-  // tiles' 16th heads in it, and both reuse it for the sorted output
-  uint64_t buf[kMergeCap];
-  uint64_t out[kTopK];
-  uint32_t full_tiles[64];
-  uint32_t cnt, nfull;
-  SelScratch<kMergeWaves> sc;
-};
-static_assert(kMaxRegHeads / 16 <= kMergeCap && kTopK <= kMergeCap, "aliases fit in buf");
-
-__device__ void merge_write(const MergeSession &S, MergeShared &sh, int k, int k_eff) {
-  const int tid = threadIdx.x;
-  uint64_t *sorted = sh.buf;
-  if (k_eff > 0) block_rank_sort_desc<kMergeThreads>(sh.out, k_eff, sorted);
-  for (int t = tid; t < k; t += kMergeThreads) {
-    if (t < k_eff) {
-      const uint64_t x = sorted[t];
-      const uint32_t row = key_row(x);
-      S.sel_idx[t] = (int32_t)row;
-      if (S.sel_score) S.sel_score[t] = S.scores ? S.scores[row] : key_score(x);
-    } else {
-      S.sel_idx[t] = -1;
-      if (S.sel_score) S.sel_score[t] = -__builtin_inff();
-    }
-  }
-}
-
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeArgs a) {
-  const int sess = blockIdx.x;
-  const MergeSession &S = a.s[sess];
-  const int64_t n = S.n_rows;
-  const int k = a.k;
-  const int k_eff = (int)(n < k ? n : k);
-  const int tid = threadIdx.x;
-  __shared__ MergeShared sh;
-  if (k_eff == 0) {
-    merge_write(S, sh, k, 0);
-    return;
-  }
-  const int64_t nt = (n + a.tile_rows - 1) / a.tile_rows;
-  const uint64_t *heads = a.heads + (size_t)sess * a.heads_stride;
-  const uint64_t *cand = a.cand + (size_t)sess * a.cand_stride;
-  const int nh = (int)(nt * 16);
-  if (tid == 0) { sh.cnt = 0; sh.nfull = 0; }
-
-  if (nh <= kMaxRegHeads) {
-    uint64_t *tile16 = sh.buf;
-    // heads in registers: slot j of thread tid is head tid + 1024 j
-    const int nj = (nh + kMergeThreads - 1) / kMergeThreads;
-    uint64_t h[kHeadKPT];
-#pragma unroll
-    for (int j = 0; j < kHeadKPT; ++j) {
-      const int i = tid + kMergeThreads * j;
-      h[j] = heads[i < nh ? i : nh - 1];
-    }
-#pragma unroll
-    for (int j = 0; j < kHeadKPT; ++j) {
-      const int i = tid + kMergeThreads * j;
-      if (i >= nh) h[j] = 0ull;
-      else if ((i & 15) == 15) tile16[i >> 4] = h[j];
-    }
-    // 3. G: the 512th largest head (1 if there are fewer)
-    const uint64_t G = block_kth_largest_reg<kMergeWaves, kHeadKPT>(h, nj, kTopK, 1ull, sh.sc);
-    // candidates: heads >= G of tiles that are not full, in registers ...
-#pragma unroll
-    for (int j = 0; j < kHeadKPT; ++j) {
-      const int i = tid + kMergeThreads * j;
-      if (!(h[j] != 0 && h[j] >= G && tile16[i >> 4] < G)) h[j] = 0ull;
-    }
-    // ... and the cand lists of full tiles (at most 32 + 1 of them)
-    for (int64_t t = tid; t < nt; t += kMergeThreads)
-      if (tile16[t] >= G) sh.full_tiles[atomicAdd(&sh.nfull, 1u)] = (uint32_t)t;
-    __syncthreads();
-    const int ncand = (int)sh.nfull * kTopK;
-    uint64_t c[kCandKPT];
-#pragma unroll
-    for (int j = 0; j < kCandKPT; ++j) {
-      const int i = tid + kMergeThreads * j;
-      const int ii = i < ncand ? i : 0;
-      c[j] = ncand ? cand[(size_t)sh.full_tiles[ii / kTopK] * kTopK + (ii % kTopK)] : 0ull;
-    }
-#pragma unroll
-    for (int j = 0; j < kCandKPT; ++j) {
-      const int i = tid + kMergeThreads * j;
-      if (!(i < ncand && c[j] >= G)) c[j] = 0ull;
-    }
-    // 4. exact top-k_eff of the candidates (heads and cand slots together)
-    uint64_t u[kHeadKPT + kCandKPT];
-#pragma unroll
-    for (int j = 0; j < kHeadKPT; ++j) u[j] = h[j];
-#pragma unroll
-    for (int j = 0; j < kCandKPT; ++j) u[kHeadKPT + j] = c[j];
-    const uint64_t thr =
-        block_kth_largest_reg<kMergeWaves, kHeadKPT + kCandKPT>(u, kHeadKPT + kCandKPT, k_eff, G, sh.sc);
-    if (tid == 0) sh.cnt = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kHeadKPT + kCandKPT; ++j)
-      if (u[j] != 0 && u[j] >= thr) sh.out[atomicAdd(&sh.cnt, 1u)] = u[j];
-    __syncthreads();
-  } else {
-    // Many tiles: the same steps, reading the heads from memory each pass.
-    const uint64_t G =
-        block_kth_largest<kMergeWaves>([&](int i) { return heads[i]; }, nh, kTopK, 1ull, sh.sc);
-    for (int i = tid; i < nh; i += kMergeThreads) {
-      const uint64_t x = heads[i];
-      if (x >= G && heads[(i | 15)] < G) sh.buf[atomicAdd(&sh.cnt, 1u)] = x;
-    }
-    for (int64_t t = tid; t < nt; t += kMergeThreads)
-      if (heads[t * 16 + 15] >= G) sh.full_tiles[atomicAdd(&sh.nfull, 1u)] = (uint32_t)t;
-    __syncthreads();
-    const int nfull = (int)sh.nfull;
-    for (int i = tid; i < nfull * kTopK; i += kMergeThreads) {
-      const uint64_t x = cand[(size_t)sh.full_tiles[i / kTopK] * kTopK + (i % kTopK)];
-      if (x >= G) sh.buf[atomicAdd(&sh.cnt, 1u)] = x;
-    }
-    __syncthreads();
-    const int nc = (int)sh.cnt;
-    const uint64_t thr = block_kth_largest<kMergeWaves>([&](int i) { return sh.buf[i]; }, nc, k_eff, G, sh.sc);
-    if (tid == 0) sh.cnt = 0;
-    __syncthreads();
-    for (int i = tid; i < nc; i += kMergeThreads) {
-      const uint64_t x = sh.buf[i];
-      if (x >= thr) sh.out[atomicAdd(&sh.cnt, 1u)] = x;
-    }
-    __syncthreads();
-  }
-  merge_write(S, sh, k, k_eff);
-}
-
-// ---------------------------------------------------------------- launchers
+// ---------------------------------------------------------------- launcher
 
 template <int MODE>
 static hipError_t launch_tile_mode(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
@@ -385,14 +256,12 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   TileArgs a;
   int64_t max_rows = 0;
   for (int i = 0; i < job.n_sessions; ++i) {
-    a.s[i] = TileSession{job.idx_rows[i], job.scores_in[i], job.scores_out[i], job.n_rows[i]};
+    a.s[i] = TileSession{job.idx_rows[i], job.scores_in[i], job.scores_out[i], job.n_rows[i], job.hd[i]};
     max_rows = job.n_rows[i] > max_rows ? job.n_rows[i] : max_rows;
   }
   if (max_rows == 0) return hipSuccess;
   a.qsplit = job.qsplit;
-  a.cand = job.cand;
   a.heads = job.heads;
-  a.cand_stride = job.cand_stride;
   a.heads_stride = job.heads_stride;
   a.tile_rows = job.tile_rows;
   const int groups = (job.n_idx_heads + 15) / 16;
@@ -404,22 +273,6 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
       tile_kernel<1, kModeArraySelect><<<grid, kTileThreads, 0, st>>>(a);
       return hipGetLastError();
   }
-}
-
-hipError_t launch_merge(const TileJob &job, int32_t *const *sel_idx, float *const *sel_score, int k,
-                        hipStream_t st) {
-  MergeArgs a;
-  for (int i = 0; i < job.n_sessions; ++i)
-    a.s[i] = MergeSession{job.mode == TileJob::kArraySelect ? job.scores_in[i] : nullptr, sel_idx[i], sel_score[i],
-                          job.n_rows[i]};
-  a.cand = job.cand;
-  a.heads = job.heads;
-  a.cand_stride = job.cand_stride;
-  a.heads_stride = job.heads_stride;
-  a.tile_rows = job.tile_rows;
-  a.k = k;
-  merge_kernel<<<job.n_sessions, kMergeThreads, 0, st>>>(a);
-  return hipGetLastError();
 }
 
 }  // namespace csa
