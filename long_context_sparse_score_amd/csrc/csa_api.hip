@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "../../include/csa.h"
+#include "csa_attn.hpp"
 #include "csa_internal.hpp"
 #include "csa_score.hpp"
 
@@ -19,11 +20,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout for (max rows per session, sessions); sized for the
 // smallest tile so that it grows monotonically with max_rows:
-//   [query split][tile heads][scores][attention logits]
+//   [query split][attention query split][tile heads][scores]
+//   [attention partials][attention (m, l)]
 struct Layout {
   int64_t tiles_cap;  // tiles per session at the smallest tile size
   int64_t rows_cap;   // score slots per session
-  size_t qsplit_off, heads_off, scores_off, logits_off, total;
+  size_t qsplit_off, attn_q_off, heads_off, scores_off, part_off, ml_off, total;
 };
 
 Layout make_layout(int64_t max_rows, int n_sessions) {
@@ -32,10 +34,12 @@ Layout make_layout(int64_t max_rows, int n_sessions) {
   L.rows_cap = (max_rows + 63) & ~(int64_t)63;
   const size_t ns = (size_t)n_sessions;
   L.qsplit_off = 0;
-  L.heads_off = align_up(ns * kQSplitBytes);
+  L.attn_q_off = align_up(ns * kQSplitBytes);
+  L.heads_off = L.attn_q_off + align_up(ns * kAttnQBytes);
   L.scores_off = L.heads_off + align_up(ns * (size_t)L.tiles_cap * kMaxTileHeads * sizeof(uint64_t));
-  L.logits_off = L.scores_off + align_up(ns * (size_t)L.rows_cap * sizeof(float));
-  L.total = L.logits_off + align_up(ns * kLogitFloats * sizeof(float));
+  L.part_off = L.scores_off + align_up(ns * (size_t)L.rows_cap * sizeof(float));
+  L.ml_off = L.part_off + align_up(ns * kAttnPartFloats * sizeof(float));
+  L.total = L.ml_off + align_up(ns * kAttnMlFloats * sizeof(float));
   return L;
 }
 
@@ -112,11 +116,12 @@ void fill_select(SelectJob &sj, const TileJob &job, int k) {
     sj.n_rows[i] = job.n_rows[i];
     sj.hd[i] = job.hd[i];
     sj.kv_rows[i] = nullptr;
-    sj.q_attn[i] = nullptr;
   }
   sj.heads = job.heads;
   sj.heads_stride = job.heads_stride;
-  sj.logits = nullptr;
+  sj.attn_q = nullptr;
+  sj.attn_part = nullptr;
+  sj.attn_ml = nullptr;
   sj.n_heads = 0;
   sj.softmax_scale = 0.0f;
 }
@@ -176,7 +181,8 @@ int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const
   job.n_rows[0] = n_rows;
   fill_job(job, L, ws, 1);
   if (n_rows == 0) return CSA_OK;
-  hipError_t e = launch_q_split(&q_idx, &w_idx, 1, n_idx_heads, const_cast<uint32_t *>(job.qsplit), st);
+  hipError_t e = launch_q_split(&q_idx, &w_idx, 1, n_idx_heads, const_cast<uint32_t *>(job.qsplit), nullptr, 0,
+                                nullptr, st);
   if (e == hipSuccess) e = launch_tiles(job, st);
   return status_of(e);
 }
@@ -220,9 +226,12 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   rc = check_device();
   if (rc != CSA_OK) return rc;
   AttnSession s{kv_rows, sel_idx, q_attn, out, lse, n_rows, n_sel};
-  float *logits = at<float>(ws, L.logits_off);
-  hipError_t e = launch_logits(&s, 1, n_heads, softmax_scale, logits, (hipStream_t)hip_stream);
-  if (e == hipSuccess) e = launch_pv(&s, 1, n_heads, logits, (hipStream_t)hip_stream);
+  hipStream_t st = (hipStream_t)hip_stream;
+  uint4 *aq = at<uint4>(ws, L.attn_q_off);
+  float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
+  hipError_t e = launch_q_split(nullptr, nullptr, 1, 0, nullptr, &q_attn, n_heads, aq, st);
+  if (e == hipSuccess) e = launch_attn_rows(&s, 1, n_heads, softmax_scale, aq, part, ml, st);
+  if (e == hipSuccess) e = launch_attn_combine(&s, 1, n_heads, part, ml, st);
   return status_of(e);
 }
 
@@ -249,7 +258,7 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   TileJob job;
   job.mode = TileJob::kScoreSelect;
   job.n_idx_heads = n_idx_heads;
-  const float *q[CSA_MAX_SESSIONS], *w[CSA_MAX_SESSIONS];
+  const float *q[CSA_MAX_SESSIONS], *w[CSA_MAX_SESSIONS], *qa[CSA_MAX_SESSIONS];
   int32_t *sel[CSA_MAX_SESSIONS];
   float *sel_score[CSA_MAX_SESSIONS];
   AttnSession at_s[CSA_MAX_SESSIONS];
@@ -262,29 +271,34 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     job.n_rows[i] = s.n_rows;
     q[i] = s.q_idx;
     w[i] = s.w_idx;
+    qa[i] = s.q_attn;
     sel[i] = s.sel_idx;
     sel_score[i] = s.sel_score;
     const int32_t n_sel = (int32_t)(s.n_rows < CSA_TOPK ? s.n_rows : CSA_TOPK);
     at_s[i] = AttnSession{s.kv_rows, s.sel_idx, s.q_attn, s.out, s.lse, s.n_rows, n_sel};
   }
   fill_job(job, L, ws, n_sessions);
-  float *logits = at<float>(ws, L.logits_off);
+  uint4 *aq = at<uint4>(ws, L.attn_q_off);
+  float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
   SelectJob sj;
   fill_select(sj, job, CSA_TOPK);
-  sj.logits = logits;
+  sj.slices = kAttnGroupCount;
+  sj.attn_q = aq;
+  sj.attn_part = part;
+  sj.attn_ml = ml;
   sj.n_heads = n_heads;
   sj.softmax_scale = softmax_scale;
   for (int i = 0; i < n_sessions; ++i) {
     sj.sel_idx[i] = sel[i];
     sj.sel_score[i] = sel_score[i];
     sj.kv_rows[i] = sessions[i].kv_rows;
-    sj.q_attn[i] = sessions[i].q_attn;
   }
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_q_split(q, w, n_sessions, n_idx_heads, const_cast<uint32_t *>(job.qsplit), st);
+  if (e == hipSuccess)
+    e = launch_q_split(q, w, n_sessions, n_idx_heads, const_cast<uint32_t *>(job.qsplit), qa, n_heads, aq, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_tiles(job, st);
@@ -293,7 +307,7 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   if (e == hipSuccess) e = launch_select(sj, st);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
-  if (e == hipSuccess) e = launch_pv(at_s, n_sessions, n_heads, logits, st);
+  if (e == hipSuccess) e = launch_attn_combine(at_s, n_sessions, n_heads, part, ml, st);
   if (e == hipSuccess) e = mark(7);
   return status_of(e);
 }

@@ -1,27 +1,42 @@
-// csa_attn.hpp -- attention logits of selected KV rows on the gfx950 bf16
-// matrix cores (V_MFMA_F32_16X16X32_BF16), shared by the fused selection
-// kernel and the stand-alone logits kernel so both give identical values.
+// csa_attn.hpp -- softmax attention over a group of selected KV rows on the
+// gfx950 bf16 matrix cores (V_MFMA_F32_16X16X32_BF16), the flash-decoding
+// split used by both the fused selection kernel and csa_sparse_attn.
 //
-// l[h][j] = scale * sum_d q[h][d] * kv_j[d] (DS4X page, "Packed cache ABI"
-// for the row; the decoded 512-value row is both key and value).  Every
-// operand enters exactly:
+// The selected rows are partitioned into kAttnGroups fixed groups by a hash
+// of the row index; a workgroup takes one group, visits its rows in rank
+// (position) order, 16 at a time, and keeps for every head h
+//   m_h = max logit seen, l_h = sum exp(l - m_h), acc_h[d] = sum exp(l - m_h) kv[d]
+// (rescaled when m_h grows).  It writes (m, l, acc) as the group's partial;
+// attn_combine merges the groups:
+//   out[h] = sum_b e^{m_b - M} acc_b / sum_b e^{m_b - M} l_b,
+//   lse[h] = M + log sum_b e^{m_b - M} l_b,   M = max_b m_b.
+// Logits l[h][j] = scale * q_h . kv_j and values use the decoded 512-value
+// row for both (DS4X page, "Packed cache ABI").  Every operand enters the
+// matrix cores exactly:
 //   * a decoded non-RoPE value is an E4M3 value times 2^(s-127): at most 4
-//     significant bits, exact in bf16;
-//   * a RoPE value is FP16 (11 bits): hi = bf16(v), lo = v - hi (exact, <= 3
-//     bits), two bf16 terms;
-//   * the fp32 query is q0 + q1 + q2 with q_t = bf16(q - q0 - ... - q_{t-1})
-//     (round to nearest even), leaving a residual below 2^-26 |q|.
-// Products of bf16 values are exact in fp32 and accumulate in fp32.  The
-// value of l[h][j] depends only on head h and row j, never on the other rows
-// of the batch.
+//     significant bits, one bf16 term (exact for magnitudes >= 2^-133);
+//   * a RoPE value is FP16 (11 bits): hi = bf16(v), lo = v - hi, two terms;
+//   * the fp32 query is q0 + q1 + q2, q_t = bf16(q - q0 - ... - q_{t-1})
+//     (round to nearest even), residual below 2^-26 |q|; it is split once
+//     per call by the query-split kernel;
+//   * a softmax weight p in [0, 1] is hi + lo (two bf16 terms, residual
+//     below 2^-17 p).
+// Products of bf16 values are exact in fp32; sums are fp32.  Everything a
+// group computes depends only on its rows and their order, so the fused and
+// the stand-alone paths give identical bits.
 //
 // Lane layout of the 16x16x32 instruction (verified on MI355X): lane l holds
 // A[m = l%16][k = 8(l/16) .. +8) and B[k = 8(l/16) .. +8][n = l%16]; the
-// result gives lane l C[m = 4(l/16) + v][n = l%16], v < 4.  Here m = head,
-// n = row, k = dimension.  The 1024 threads of a workgroup are 16 waves:
-// wave w takes head group g = w%4 (heads 16g..16g+15) and the dimension
-// quarter kq = w/4 (dimensions 128kq..128kq+127, four K steps of 32); the
-// four quarters are summed in order through LDS.
+// result gives lane l C[m = 4(l/16) + v][n = l%16], v < 4.
+// A workgroup is 8 waves; wave w takes head group g = w%4 (heads
+// 16g..16g+15) and half hv = w/4:
+//   logits: m = head, n = row, k = dimension; the wave covers dimension
+//           quarters 2hv and 2hv+1 (four K steps of 32 each) for the 16 rows
+//           of the batch; per row the four quarters are summed as
+//           (q0 + q1) + (q2 + q3), the second pair through LDS.
+//   P V:    m = head, n = dimension, k = row (the batch's 16 rows in k < 16,
+//           zeros above); the wave covers the 128 dimensions of chunks 2hv
+//           and 2hv+1 (eight 16-wide tiles each).
 #pragma once
 
 #include "../../include/csa.h"
@@ -33,22 +48,36 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f_attn __attribute__((ext_vector_type(4)));
 
 constexpr int kKvDim = 512;
-constexpr int kLogitThreads = 1024;
-constexpr int kLogitRows = 16;  // rows per matrix-core batch
+constexpr int kAttnThreads = 512;
+constexpr int kAttnGroups = 32;
+constexpr int kAttnBatch = 16;  // rows per matrix-core batch
 constexpr int kKvLdsStride = kKvDim + 4;
 
-struct LogitShared {
-  float kv[kLogitRows][kKvLdsStride];  // decoded rows of the batch
-  float red[4][4][64][4];              // [quarter][head group][lane][v] partials
-  int32_t row[kLogitRows];             // KV row, or -1 (the logit is -inf)
-  int32_t pos[kLogitRows];             // output column (rank / position)
+// Group of a selected row (also the workgroup of the fused selection that
+// ranks it): the top 5 bits of a multiplicative hash.
+__device__ __forceinline__ uint32_t attn_group(uint32_t row) { return (row * 0x9E3779B1u) >> 27; }
+
+// Attention query split in the workspace, per session:
+// [g + 4 kq][K step 4][term 3][lane 64] x 8 bf16 (16 bytes).
+constexpr int kAttnQVecs = 16 * 4 * 3 * 64;
+constexpr size_t kAttnQBytes = (size_t)kAttnQVecs * 16;
+// Partials per session: acc [group][head][512] and (m, l) [group][head][2].
+constexpr size_t kAttnPartFloats = (size_t)kAttnGroups * CSA_MAX_HEADS * kKvDim;
+constexpr size_t kAttnMlFloats = (size_t)kAttnGroups * CSA_MAX_HEADS * 2;
+
+__device__ __forceinline__ size_t attn_q_index(int wave, int s, int t, int lane) {
+  return ((size_t)(wave * 4 + s) * 3 + t) * 64 + lane;
+}
+
+struct AttnStage {
+  float kv[kAttnBatch][kKvLdsStride];       // decoded rows of the batch
+  float lg[CSA_MAX_HEADS][kAttnBatch + 1];  // logits of the batch
+  float red[4][64][4];                      // logits of quarters 2 + 3 [g]
+  int32_t row[kAttnBatch];                  // KV row, or -1 (padding)
 };
 
-// This lane's query terms: K step s of its quarter, term t.
-struct LogitQuery {
-  v8bf a[4][3];
-};
-
+// x = t0 + t1 + t2 + r: three bf16 terms, each the round-to-nearest-even of
+// what the previous ones leave (the subtractions are exact in fp32).
 __device__ __forceinline__ void split3_bf16(float x, __bf16 &t0, __bf16 &t1, __bf16 &t2) {
   t0 = (__bf16)x;
   const float r1 = x - (float)t0;
@@ -56,33 +85,23 @@ __device__ __forceinline__ void split3_bf16(float x, __bf16 &t0, __bf16 &t1, __b
   t2 = (__bf16)(r1 - (float)t1);
 }
 
-// Raw query values of this lane: q[16g + l%16][128kq + 32s + 8(l/16) + i].
-struct LogitQueryRaw {
-  float v[4][8];
+// This lane's query terms: quarter 2hv + kl, K step s, term t.
+struct AttnQuery {
+  v8bf a[2][4][3];
 };
 
-__device__ __forceinline__ void load_logit_query(LogitQueryRaw &r, const float *__restrict__ q_attn, int n_heads) {
+__device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *__restrict__ qs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = wave & 3, kq = wave >> 2;
-  const int h = 16 * g + (lane & 15);
-  const float *src = q_attn + (size_t)h * kKvDim + 128 * kq + 8 * (lane >> 4);
+  const int g = wave & 3, hv = wave >> 2;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[s][i] = (h < n_heads) ? src[32 * s + i] : 0.0f;
-}
-
-__device__ __forceinline__ void split_logit_query(LogitQuery &q, const LogitQueryRaw &r) {
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __bf16 t0, t1, t2;
-      split3_bf16(r.v[s][i], t0, t1, t2);
-      q.a[s][0][i] = t0;
-      q.a[s][1][i] = t1;
-      q.a[s][2][i] = t2;
-    }
+      for (int t = 0; t < 3; ++t) {
+        const uint4 v = qs[attn_q_index(g + 4 * (2 * hv + kl), s, t, lane)];
+        q.a[kl][s][t] = __builtin_bit_cast(v8bf, v);
+      }
 }
 
 // The two bytes that determine decoded value i of a packed KV row (code and
@@ -101,79 +120,236 @@ __device__ __forceinline__ float kv_decode(int i, uint32_t b0, uint32_t b1) {
   return i < kKvNope ? vn : vr;
 }
 
-// Decode the rows sh.row[0..nb) into sh.kv (0 for rows < 0 and past nb).
-// Invalid rows read row 0 and discard it; have_rows = false (an empty
-// history, possibly no buffer) skips every load.  All kLogitThreads threads
-// call it.
-__device__ __forceinline__ void decode_logit_rows(const uint8_t *__restrict__ kv_rows, bool have_rows,
-                                                  LogitShared &sh, int nb) {
-  constexpr int U = kLogitRows * kKvDim / kLogitThreads;
-  uint32_t b0[U], b1[U];
-  int32_t row[U];
+// Per-wave state of a group: accumulator tiles (heads 16g + 4(l/16) + v,
+// dimensions 128(2hv + cl) + 16t + l%16) and the running max / sum of head
+// 16g + l%16.
+struct AttnState {
+  v4f_attn acc[2][8];
+  float m, l;
+};
+
+__device__ __forceinline__ void attn_init(AttnState &S) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int e = threadIdx.x + kLogitThreads * u;
-    const int r = e / kKvDim;
-    row[u] = r < nb ? sh.row[r] : -1;
-  }
-  if (have_rows) {
+  for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S.acc[cl][t] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
+  S.m = -__builtin_inff();
+  S.l = 0.0f;
+}
+
+// One batch: rows st.row[0..kAttnBatch) (-1 = padding) are decoded into
+// st.kv, their logits go to st.lg, and this wave's running softmax state and
+// accumulators are updated.  All kAttnThreads threads call it; it starts and
+// ends with a barrier.
+__device__ __forceinline__ void attn_batch(const uint4 *__restrict__ qsplit, AttnState &S, AttnStage &st,
+                                           const uint8_t *__restrict__ kv_rows, float scale) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __syncthreads();  // st.row written
+  // the query terms (L2-resident, shared by every group) are loaded with the
+  // rows' bytes and live only through the logits
+  AttnQuery q;
+  load_attn_query(q, qsplit);
+  {
+    // decode: 32 rows x 512 values, 16 per thread, all loads first.  A wave
+    // covers 64 consecutive values of one row, so the row (and the RoPE
+    // test) is uniform per wave and lives in scalar registers.
+    constexpr int U = kAttnBatch * kKvDim / kAttnThreads;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t bb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = threadIdx.x + kLogitThreads * u;
-      kv_load(kv_rows + (size_t)(uint32_t)max(row[u], 0) * kKvRowBytes, e % kKvDim, b0[u], b1[u]);
+      const int e0 = 64 * wv + kAttnThreads * u;  // first value of this wave
+      const int32_t r = __builtin_amdgcn_readfirstlane(st.row[e0 / kKvDim]);
+      uint32_t b0, b1;
+      kv_load(kv_rows + (size_t)(uint32_t)max(r, 0) * kKvRowBytes, e0 % kKvDim + lane, b0, b1);
+      bb[u] = b0 | (b1 << 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e0 = 64 * wv + kAttnThreads * u;
+      const int32_t r = __builtin_amdgcn_readfirstlane(st.row[e0 / kKvDim]);
+      const float x = kv_decode(e0 % kKvDim + lane, bb[u] & 255u, bb[u] >> 8);
+      st.kv[e0 / kKvDim][e0 % kKvDim + lane] = r >= 0 ? x : 0.0f;
     }
   }
+  __syncthreads();
+  const int g = wave & 3, hv = wave >> 2;
+  // logits of the batch's 16 rows, this wave's two dimension quarters
+  v4f_attn c[2];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int e = threadIdx.x + kLogitThreads * u;
-    const float x = have_rows ? kv_decode(e % kKvDim, b0[u], b1[u]) : 0.0f;
-    sh.kv[e / kKvDim][e % kKvDim] = row[u] >= 0 ? x : 0.0f;
+  for (int kl = 0; kl < 2; ++kl) {
+    const int kq = 2 * hv + kl;
+    c[kl] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float *src = &st.kv[lane & 15][128 * kq + 32 * s + 8 * (lane >> 4)];
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = src[i];
+      v8bf hi;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hi[i] = (__bf16)f[i];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], hi, c[kl], 0, 0, 0);
+      if (kq == 3 && s >= 2) {  // RoPE dimensions 448..511: the FP16 remainder
+        v8bf lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(f[i] - (float)hi[i]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], lo, c[kl], 0, 0, 0);
+      }
+    }
+  }
+  const v4f_attn cw = c[0] + c[1];
+  if (hv == 1) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) st.red[g][lane][v] = cw[v];
+  }
+  __syncthreads();
+  if (hv == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float sum = cw[v] + st.red[g][lane][v];
+      const int n = lane & 15;
+      st.lg[16 * g + 4 * (lane >> 4) + v][n] = st.row[n] >= 0 ? scale * sum : -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  // online softmax of this lane's head over the batch's rows: lanes with
+  // l/16 < 2 hold rows 8(l/16)..+8, the others the zero rows 16..31
+  const int hh = 16 * g + (lane & 15);
+  const bool real = (lane >> 4) < 2;
+  float pl[8];
+  float mb = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = st.lg[hh][(8 * (lane >> 4) + i) & 15];  // in range for every lane: no branch
+    pl[i] = real ? x : -__builtin_inff();
+    mb = fmaxf(mb, pl[i]);
+  }
+  mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+  mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+  const float m_new = fmaxf(S.m, mb);
+  const float mref = m_new == -__builtin_inff() ? 0.0f : m_new;
+  const float alpha = __expf(S.m - mref);
+  float ps = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pl[i] = __expf(pl[i] - mref);
+    ps += pl[i];
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  S.l = S.l * alpha + ps;
+  S.m = m_new;
+  v8bf ph, plo;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ph[i] = (__bf16)pl[i];
+    plo[i] = (__bf16)(pl[i] - (float)ph[i]);
+  }
+  // rescale the accumulators: element v of a tile is head 16g + 4(l/16) + v,
+  // whose factor sits in lane 4(l/16) + v
+  float av[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * (lane >> 4) + v, 64);
+#pragma unroll
+  for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S.acc[cl][t][v] *= av[v];
+  // acc += P V over the batch's 32 rows
+#pragma unroll
+  for (int cl = 0; cl < 2; ++cl) {
+    const int cc = 2 * hv + cl;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int d = 128 * cc + 16 * t + (lane & 15);
+      v8bf vh, vl;
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = st.kv[(8 * (lane >> 4) + i) & 15][d];
+        vf[i] = real ? x : 0.0f;
+        vh[i] = (__bf16)vf[i];
+      }
+      S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vh, S.acc[cl][t], 0, 0, 0);
+      S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vh, S.acc[cl][t], 0, 0, 0);
+      if (cc == 3 && t >= 4) {  // RoPE dimensions: the FP16 remainder
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vl[i] = (__bf16)(vf[i] - (float)vh[i]);
+        S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vl, S.acc[cl][t], 0, 0, 0);
+        S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vl, S.acc[cl][t], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // the stage is reused by the next batch
+}
+
+// Write the group's partial: acc [head][512] and (m, l) [head][2].
+__device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, float *__restrict__ part,
+                                           float *__restrict__ ml) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = wave & 3, hv = wave >> 2;
+  if (16 * g + 15 < n_heads) {  // every head of the wave exists (uniform)
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int h = 16 * g + 4 * (lane >> 4) + v;
+          part[(size_t)h * kKvDim + 128 * (2 * hv + cl) + 16 * t + (lane & 15)] = S.acc[cl][t][v];
+        }
+  } else if (16 * g < n_heads) {
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int h = 16 * g + 4 * (lane >> 4) + v;
+          if (h < n_heads) part[(size_t)h * kKvDim + 128 * (2 * hv + cl) + 16 * t + (lane & 15)] = S.acc[cl][t][v];
+        }
+  }
+  const int hh = 16 * g + (lane & 15);
+  if (hv == 0 && lane < 16 && hh < n_heads) {
+    ml[2 * hh] = S.m;
+    ml[2 * hh + 1] = S.l;
   }
 }
 
-// logits[h * 512 + sh.pos[n]] for rows n < nb and heads h < n_heads (rows
-// with sh.row[n] < 0 get -inf).  sh.kv must hold the decoded batch; all
-// kLogitThreads threads call it; it ends with a barrier.
-__device__ __forceinline__ void batch_logits(const LogitQuery &q, LogitShared &sh, int nb, int n_heads,
-                                             float scale, float *__restrict__ logits) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = wave & 3, kq = wave >> 2;
-  v4f_attn c = {0.0f, 0.0f, 0.0f, 0.0f};
+// Order a group's entries by their key (rank or position, distinct),
+// ascending: out_rows[i] = row of the i-th.  keys/rows[0..m) in LDS; all
+// threads call it; ends with a barrier.
+__device__ __forceinline__ void attn_order(const int32_t *keys, const int32_t *rows, int m, int32_t *out_rows) {
+  for (int i = threadIdx.x; i < m; i += kAttnThreads) {
+    const int32_t k = keys[i];
+    int r = 0;
+    for (int j0 = 0; j0 < m; j0 += 16) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const float *src = &sh.kv[lane & 15][128 * kq + 32 * s + 8 * (lane >> 4)];
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = src[i];
-    v8bf hi;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi[i] = (__bf16)f[i];
-#pragma unroll
-    for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[s][t], hi, c, 0, 0, 0);
-    if (kq == 3 && s >= 2) {  // RoPE dimensions 448..511: the FP16 remainder
-      v8bf lo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(f[i] - (float)hi[i]);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[s][t], lo, c, 0, 0, 0);
+      for (int u = 0; u < 16; ++u) r += (j0 + u < m && keys[j0 + u] < k) ? 1 : 0;
     }
-  }
-  if (kq != 0) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sh.red[kq][g][lane][v] = c[v];
+    out_rows[r] = rows[i];
   }
   __syncthreads();
-  if (kq == 0) {
-    const int n = lane & 15;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float sum = ((c[v] + sh.red[1][g][lane][v]) + sh.red[2][g][lane][v]) + sh.red[3][g][lane][v];
-      const int h = 16 * g + 4 * (lane >> 4) + v;
-      if (n < nb && h < n_heads)
-        logits[(size_t)h * CSA_TOPK + sh.pos[n]] = sh.row[n] >= 0 ? scale * sum : -__builtin_inff();
-    }
+}
+
+// Attention over a group's rows (in order) -> its partial.  All threads
+// call it.
+__device__ __forceinline__ void attn_group_rows(const uint4 *__restrict__ qsplit, AttnStage &st, const int32_t *rows,
+                                                int m,
+                                                const uint8_t *__restrict__ kv_rows, float scale, int n_heads,
+                                                float *__restrict__ part, float *__restrict__ ml) {
+  AttnState S;
+  attn_init(S);
+  for (int b0 = 0; b0 < m; b0 += kAttnBatch) {
+    if (threadIdx.x < kAttnBatch)
+      st.row[threadIdx.x] = b0 + (int)threadIdx.x < m ? rows[b0 + threadIdx.x] : -1;
+    attn_batch(qsplit, S, st, kv_rows, scale);
   }
-  __syncthreads();
+  attn_store(S, n_heads, part, ml);
 }
 
 }  // namespace csa

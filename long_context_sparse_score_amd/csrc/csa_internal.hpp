@@ -42,7 +42,7 @@ struct TileJob {
 };
 
 // One launch of the global selection (and, optionally, of the attention
-// logits of the selected rows).
+// attention of the selected rows).
 struct SelectJob {
   int n_sessions;
   int tile_rows;
@@ -56,10 +56,12 @@ struct SelectJob {
   float *sel_score[CSA_MAX_SESSIONS];
   const uint64_t *heads;
   int64_t heads_stride;
-  // logits of the selected rows (nullptr: none)
-  float *logits;  // [session][64][512]
+  // attention partials of the selected rows (attn_part == nullptr: none);
+  // then slices must equal the number of attention groups (32)
+  const uint4 *attn_q;  // [session][attention query split]
+  float *attn_part;     // [session][group][64][512]
+  float *attn_ml;       // [session][group][64][2]
   const uint8_t *kv_rows[CSA_MAX_SESSIONS];
-  const float *q_attn[CSA_MAX_SESSIONS];
   int n_heads;
   float softmax_scale;
 };
@@ -75,20 +77,24 @@ struct AttnSession {
   int32_t n_sel;
 };
 
-// Logits per session in the workspace: [head][selected row].
-constexpr size_t kLogitFloats = (size_t)CSA_MAX_HEADS * CSA_TOPK;
+// Attention groups (flash-decoding split of the selected rows).
+constexpr int kAttnGroupCount = 32;
 
 hipError_t launch_dequant_idx(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
 hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
-// Query split of every session (csa_qsplit.hip): q[i], w[i] -> out.
+// Query split of every session (csa_qsplit.hip): q[i], w[i] -> out (skipped
+// when q is null) and, when q_attn is given, the attention query -> attn_out.
 hipError_t launch_q_split(const float *const *q, const float *const *w, int n_sessions, int n_heads,
-                          uint32_t *out, hipStream_t st);
+                          uint32_t *out, const float *const *q_attn, int n_attn_heads, uint4 *attn_out,
+                          hipStream_t st);
 hipError_t launch_tiles(const TileJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);
-// Logits of the rows sel_idx[0..n_sel) of every session (csa_sparse_attn).
-hipError_t launch_logits(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale, float *logits,
-                         hipStream_t st);
-// Softmax over the logits and the value sum: out, lse.
-hipError_t launch_pv(const AttnSession *s, int n_sessions, int n_heads, const float *logits, hipStream_t st);
+// Attention partials of the rows sel_idx[0..n_sel) of every session, one
+// workgroup per group (csa_sparse_attn).
+hipError_t launch_attn_rows(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale,
+                            const uint4 *qsplit, float *part, float *ml, hipStream_t st);
+// Merge of the group partials: out, lse.
+hipError_t launch_attn_combine(const AttnSession *s, int n_sessions, int n_heads, const float *part,
+                               const float *ml, hipStream_t st);
 
 }  // namespace csa

@@ -1,7 +1,7 @@
 // csa_merge.hip -- the global exact top-k of a session from its tiles' heads
 // (DS4X page, "CSA score/top-512 fusion": merge the per-tile selections into
 // the model's exact top-512 with the same float order and lower-index tie
-// break as a separate top-k pass), and optionally the attention logits of
+// break as a separate top-k pass), and optionally the attention of
 // the selected rows.
 //
 // Every workgroup of a session (grid.x = slices) runs the same selection:
@@ -21,7 +21,9 @@
 //   4. The candidates are ranked exactly (rank = number of larger
 //      candidates).  Workgroup b ranks the candidates whose row hashes to b,
 //      writes sel_idx[rank] / sel_score[rank] for ranks < k_eff, and (when
-//      asked) computes the attention logits of those rows (csa_attn.hpp).
+//      asked) runs the attention of those rows in rank order and writes the
+//      group's partial (csa_attn.hpp; the workgroup index is the row's
+//      attention group, so the partials equal csa_sparse_attn's).
 // Selection keys are (ord32(score) << 32) | (2^32 - 1 - row): distinct,
 // larger = better; 0 means "no key".
 #include "csa_attn.hpp"
@@ -31,9 +33,9 @@
 
 namespace csa {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = kAttnThreads;  // 512
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelKPT = 8;                            // heads per thread in registers
+constexpr int kSelKPT = 16;                           // heads per thread in registers
 constexpr int kSelRegHeads = kSelThreads * kSelKPT;  // 8192
 constexpr int kSelBins = 2 * kSelThreads;             // histogram bins per pass
 constexpr int kSelCap = 4096;                         // candidates held in LDS
@@ -46,7 +48,6 @@ struct SelSessionArgs {
   int32_t *sel_idx;
   float *sel_score;
   const uint8_t *kv_rows;
-  const float *q_attn;
   int64_t n_rows;
   int hd;
 };
@@ -54,7 +55,9 @@ struct SelSessionArgs {
 struct SelArgs {
   SelSessionArgs s[CSA_MAX_SESSIONS];
   const uint64_t *heads;
-  float *logits;
+  const uint4 *attn_q;
+  float *attn_part;
+  float *attn_ml;
   int64_t heads_stride;
   int tile_rows;
   int k;
@@ -65,17 +68,21 @@ struct SelArgs {
 static_assert(sizeof(SelArgs) <= 4096, "kernel argument block");
 
 struct SelShared {
-  uint64_t cand[kSelCap + 4 * 64];  // + over-read slack of the rank scan
-  uint32_t hist[kSelBins];
+  union {
+    struct {
+      uint64_t cand[kSelCap + 4 * 64];  // + over-read slack of the rank scan
+      uint32_t hist[kSelBins];
+      uint16_t mine[kSelCap];
+    } s;
+    AttnStage st;  // used after the ranks are written
+  } u;
   uint64_t red_lo[kSelWaves], red_hi[kSelWaves];
   uint32_t red_n[kSelWaves];
   uint32_t full_list[kSelMaxFull];
   uint8_t full_flag[kSelMaxRegTiles];
-  uint16_t mine[kSelCap];
-  int32_t loc_rank[CSA_TOPK], loc_row[CSA_TOPK];
+  int32_t loc_rank[CSA_TOPK + 16], loc_row[CSA_TOPK], ordered[CSA_TOPK];
   uint32_t ccnt, nfull, nmine, nloc;
   uint32_t bin, ca, cb;
-  LogitShared lg;
 };
 
 // Lower bound G on the need-th largest of the keys that `visit` enumerates
@@ -116,15 +123,15 @@ __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32
   for (;;) {
     const uint64_t span = hi - lo;
     const int hb = span ? 63 - __clzll((long long)span) : 0;
-    const int shift = hb > 10 ? hb - 10 : 0;  // span >> shift < kSelBins
-    for (int i = tid; i < kSelBins; i += kSelThreads) sh.hist[i] = 0;
+    const int shift = hb > 9 ? hb - 9 : 0;  // span >> shift < kSelBins (1024)
+    for (int i = tid; i < kSelBins; i += kSelThreads) sh.u.s.hist[i] = 0;
     __syncthreads();
     visit([&](uint64_t x) __attribute__((always_inline)) {
-      if (x >= lo && x <= hi) atomicAdd(&sh.hist[(uint32_t)((x - lo) >> shift)], 1u);
+      if (x >= lo && x <= hi) atomicAdd(&sh.u.s.hist[(uint32_t)((x - lo) >> shift)], 1u);
     });
     __syncthreads();
     const uint32_t need_here = need - above;
-    const uint32_t h0 = sh.hist[2 * tid], h1 = sh.hist[2 * tid + 1];
+    const uint32_t h0 = sh.u.s.hist[2 * tid], h1 = sh.u.s.hist[2 * tid + 1];
     const uint32_t s = h0 + h1;
     uint32_t suf = s;  // inclusive suffix sum over the lanes of the wave
 #pragma unroll
@@ -161,7 +168,7 @@ __device__ __forceinline__ uint32_t row_slice(uint32_t row, int slices) {
 
 // REG: every session's heads fit in registers (at most kSelRegHeads), chosen
 // on the host for the whole launch; otherwise they are re-read per pass.
-template <bool LOGITS, bool REG>
+template <bool ATTN, bool REG>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   const int sess = blockIdx.y;
   // fields used inside lambdas are copied first: a lambda taking the address
@@ -180,11 +187,21 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       sel_idx[r] = -1;
       if (sel_score) sel_score[r] = -__builtin_inff();
     }
-  if (k_eff == 0) return;
+  if (k_eff == 0) {
+    if constexpr (ATTN) {  // an empty group partial: m = -inf, l = 0
+      float *ml = a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)blockIdx.x * CSA_MAX_HEADS * 2;
+      if (tid < a.n_heads) {
+        ml[2 * tid] = -__builtin_inff();
+        ml[2 * tid + 1] = 0.0f;
+      }
+    }
+    return;
+  }
 
   const int T = a.tile_rows;
   const int hd = a.s[sess].hd;
-  const int64_t nt = (n + T - 1) / T;
+  const int lT = __builtin_ctz((unsigned)T), lhd = __builtin_ctz((unsigned)hd);  // both powers of two
+  const int64_t nt = (n + T - 1) >> lT;
   const int64_t nh = nt * hd;
   const uint64_t *heads = a.heads + (size_t)sess * a.heads_stride;
   constexpr bool reg = REG;
@@ -232,13 +249,13 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   if constexpr (reg) {
 #pragma unroll
     for (int j = 0; j < kSelKPT; ++j) {
-      const int64_t i = tid + (int64_t)kSelThreads * j;
-      if (i < nh && (int)(i % hd) == hd - 1) {
+      const int i = tid + kSelThreads * j;  // < kSelRegHeads
+      if (i < nh && (i & (hd - 1)) == hd - 1) {
         const bool full = h[j] != 0 && h[j] >= G;
-        sh.full_flag[i / hd] = full ? 1 : 0;
+        sh.full_flag[i >> lhd] = full ? 1 : 0;
         if (full) {
           const uint32_t p = atomicAdd(&sh.nfull, 1u);
-          if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)(i / hd);
+          if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)(i >> lhd);
         }
       }
     }
@@ -257,26 +274,26 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
     if constexpr (reg) {
 #pragma unroll
       for (int j = 0; j < kSelKPT; ++j) {
-        const int64_t i = tid + (int64_t)kSelThreads * j;
-        if (h[j] != 0 && h[j] >= lb && !sh.full_flag[i / hd]) f(h[j]);
+        const int i = tid + kSelThreads * j;
+        if (h[j] != 0 && h[j] >= lb && !sh.full_flag[i >> lhd]) f(h[j]);
       }
     } else {
       visit_heads([&](uint64_t x) __attribute__((always_inline)) {
         if (x >= lb) {
           // the tile of this head: keys carry the row, tiles are T rows
-          const int64_t t = (int64_t)key_row(x) / T;
+          const int64_t t = (int64_t)(key_row(x) >> lT);
           if (!tile_is_full(t)) f(x);
         }
       });
     }
-    const int64_t nfr = (int64_t)nfull * T;
-    for (int64_t i0 = tid; i0 < nfr; i0 += (int64_t)kSelThreads * 8) {
+    const int nfr = nfull << lT;  // at most kSelMaxFull * 4096
+    for (int i0 = tid; i0 < nfr; i0 += kSelThreads * 8) {
       float v[8];
       int64_t row[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + (int64_t)kSelThreads * u;
-        row[u] = i < nfr ? (int64_t)sh.full_list[i / T] * T + (i % T) : n;
+        const int i = i0 + kSelThreads * u;
+        row[u] = i < nfr ? ((int64_t)sh.full_list[i >> lT] << lT) + (i & (T - 1)) : n;
         v[u] = scores[row[u] < n ? row[u] : n - 1];
       }
 #pragma unroll
@@ -290,7 +307,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   };
   auto append = [&](uint64_t x) __attribute__((always_inline)) {
     const uint32_t p = atomicAdd(&sh.ccnt, 1u);
-    if (p < kSelCap) sh.cand[p] = x;
+    if (p < kSelCap) sh.u.s.cand[p] = x;
   };
   visit_cand(G, append);
   __syncthreads();
@@ -308,62 +325,67 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   // 4. rank this workgroup's candidates
   for (int i0 = 0; i0 < C; i0 += kSelThreads) {
     const int i = i0 + tid;
-    if (i < C && row_slice(key_row(sh.cand[i]), gridDim.x) == blockIdx.x) sh.mine[atomicAdd(&sh.nmine, 1u)] = (uint16_t)i;
+    if (i < C && row_slice(key_row(sh.u.s.cand[i]), gridDim.x) == blockIdx.x) sh.u.s.mine[atomicAdd(&sh.nmine, 1u)] = (uint16_t)i;
   }
   __syncthreads();
   const int nm = (int)sh.nmine;
+  // warm the L2 with the KV rows of this workgroup's candidates (a superset
+  // of the rows it will attend over) while the ranks are computed
+  uint32_t warm = 0;
+  if constexpr (ATTN) {
+    const uint8_t *kv = a.s[sess].kv_rows;
+    for (int t = tid; t < nm * 6; t += kSelThreads) {
+      const uint32_t row = key_row(sh.u.s.cand[sh.u.s.mine[t / 6]]);
+      const int off = 128 * (t % 6) < kKvRowBytes - 1 ? 128 * (t % 6) : kKvRowBytes - 1;
+      warm ^= kv[(size_t)row * kKvRowBytes + off];
+    }
+  }
   for (int m = wave; m < nm; m += kSelWaves) {
-    const uint64_t x = sh.cand[sh.mine[m]];
+    const uint64_t x = sh.u.s.cand[sh.u.s.mine[m]];
     uint32_t r = 0;
     for (int j0 = 0; j0 < C; j0 += 4 * 64) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = j0 + 64 * u + lane;
-        const uint64_t y = sh.cand[j];
+        const uint64_t y = sh.u.s.cand[j];
         r += (uint32_t)__popcll(__ballot(j < C && y > x));
       }
     }
     if (lane == 0 && r < (uint32_t)k_eff) {
       const uint32_t row = key_row(x);
       sel_idx[r] = (int32_t)row;
-      if (sel_score) sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+      if (sel_score) {
+        if constexpr (ATTN)  // the fused path: the key holds the score
+          sel_score[r] = key_score(x);
+        else
+          sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+      }
       const uint32_t p = atomicAdd(&sh.nloc, 1u);
       sh.loc_rank[p] = (int32_t)r;
       sh.loc_row[p] = (int32_t)row;
     }
   }
-  if constexpr (!LOGITS) return;
+  if constexpr (!ATTN) return;
+  if (warm == 0x5A5A5A5Au && a.k < 0) sel_idx[0] = 0;  // never true (k >= 1): keeps the warming loads
 
-  // 5. attention logits of this workgroup's selected rows
+  // 5. attention over this workgroup's selected rows, in rank order
   __syncthreads();
   const int nl = (int)sh.nloc;
-  if (nl == 0) return;
-  LogitQueryRaw qraw;  // loads in flight together with the first batch's rows
-  load_logit_query(qraw, a.s[sess].q_attn, a.n_heads);
-  LogitQuery q;
-  split_logit_query(q, qraw);
-  float *logits = a.logits + (size_t)sess * kLogitFloats;
-  for (int b0 = 0; b0 < nl; b0 += kLogitRows) {
-    const int nb = nl - b0 < kLogitRows ? nl - b0 : kLogitRows;
-    if (tid < kLogitRows) {
-      sh.lg.row[tid] = tid < nb ? sh.loc_row[b0 + tid] : -1;
-      sh.lg.pos[tid] = tid < nb ? sh.loc_rank[b0 + tid] : 0;
-    }
-    __syncthreads();
-    decode_logit_rows(a.s[sess].kv_rows, true, sh.lg, nb);
-    __syncthreads();
-    batch_logits(q, sh.lg, nb, a.n_heads, a.softmax_scale, logits);
-  }
+  attn_order(sh.loc_rank, sh.loc_row, nl, sh.ordered);
+  attn_group_rows(a.attn_q + (size_t)sess * kAttnQVecs, sh.u.st, sh.ordered, nl, a.s[sess].kv_rows, a.softmax_scale, a.n_heads,
+                  a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)blockIdx.x * CSA_MAX_HEADS * kKvDim,
+                  a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)blockIdx.x * CSA_MAX_HEADS * 2);
 }
 
 hipError_t launch_select(const SelectJob &job, hipStream_t st) {
   SelArgs a;
   for (int i = 0; i < job.n_sessions; ++i)
     a.s[i] = SelSessionArgs{job.scores[i], job.sel_idx[i], job.sel_score[i],
-                            job.logits ? job.kv_rows[i] : nullptr, job.logits ? job.q_attn[i] : nullptr,
-                            job.n_rows[i], job.hd[i]};
+                            job.attn_part ? job.kv_rows[i] : nullptr, job.n_rows[i], job.hd[i]};
   a.heads = job.heads;
-  a.logits = job.logits;
+  a.attn_q = job.attn_q;
+  a.attn_part = job.attn_part;
+  a.attn_ml = job.attn_ml;
   a.heads_stride = job.heads_stride;
   a.tile_rows = job.tile_rows;
   a.k = job.k;
@@ -374,7 +396,7 @@ hipError_t launch_select(const SelectJob &job, hipStream_t st) {
   bool reg = true;
   for (int i = 0; i < job.n_sessions; ++i)
     reg = reg && ((job.n_rows[i] + job.tile_rows - 1) / job.tile_rows) * job.hd[i] <= kSelRegHeads;
-  if (job.logits) {
+  if (job.attn_part) {
     if (reg) select_kernel<true, true><<<grid, kSelThreads, 0, st>>>(a);
     else select_kernel<true, false><<<grid, kSelThreads, 0, st>>>(a);
   } else {

@@ -10,6 +10,11 @@
 // every term.  The fragment of head h, block b becomes MFMA lane 16b + h%16
 // of group h/16.  Eight threads share a fragment, four values each: a term
 // costs one three-step maximum and three byte stores per thread.
+//
+// The same launch also splits the attention query into three bf16 terms per
+// value, stored in the matrix-core operand order of csa_attn.hpp (extra
+// workgroups, when an attention query is given).
+#include "csa_attn.hpp"
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "csa_score.hpp"
@@ -34,16 +39,50 @@ __device__ __forceinline__ uint32_t e2m3_mag(float a, float *val) {
 struct QSplitArgs {
   const float *q[CSA_MAX_SESSIONS];
   const float *w[CSA_MAX_SESSIONS];
-  uint32_t *out;  // [session][kQSplitBytes / 4]
-  int n_heads;
+  const float *q_attn[CSA_MAX_SESSIONS];
+  uint32_t *out;    // [session][kQSplitBytes / 4]
+  uint4 *attn_out;  // [session][kAttnQVecs]
+  int n_heads;      // indexer heads (0: no indexer split)
+  int n_attn_heads;
+  int idx_blocks;   // workgroups of the indexer split per session
 };
 
 constexpr int kSplitThreads = 256;
 constexpr int kSplitSub = 8;                                                   // threads per fragment
 constexpr int kSplitBlocks = kMaxGroups * 16 * 4 * kSplitSub / kSplitThreads;  // 8 per session
 
+constexpr int kAttnSplitBlocks = 16 * 4 * 64 / kSplitThreads;  // 16 per session
+
+// Attention query: thread (wave w, step s, lane l) writes the three terms of
+// q[16(w%4) + l%16][128(w/4) + 32s + 8(l/16) + i], i < 8.
+__device__ void attn_q_split(const QSplitArgs &a, int sess, int t) {
+  const int lane = t % 64, s = (t / 64) % 4, wave = t / 256;
+  const int h = 16 * (wave & 3) + (lane & 15);
+  const int d0 = 128 * (wave >> 2) + 32 * s + 8 * (lane >> 4);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = h < a.n_attn_heads ? a.q_attn[sess][h * 512 + d0 + i] : 0.0f;
+  v8bf t0, t1, t2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __bf16 a0, a1, a2;
+    split3_bf16(x[i], a0, a1, a2);
+    t0[i] = a0;
+    t1[i] = a1;
+    t2[i] = a2;
+  }
+  uint4 *dst = a.attn_out + (size_t)sess * kAttnQVecs;
+  dst[attn_q_index(wave, s, 0, lane)] = __builtin_bit_cast(uint4, t0);
+  dst[attn_q_index(wave, s, 1, lane)] = __builtin_bit_cast(uint4, t1);
+  dst[attn_q_index(wave, s, 2, lane)] = __builtin_bit_cast(uint4, t2);
+}
+
 __global__ void __launch_bounds__(kSplitThreads) q_split_kernel(const QSplitArgs a) {
   const int sess = blockIdx.y;
+  if ((int)blockIdx.x >= a.idx_blocks) {
+    attn_q_split(a, sess, (blockIdx.x - a.idx_blocks) * kSplitThreads + threadIdx.x);
+    return;
+  }
   const int gt = blockIdx.x * kSplitThreads + threadIdx.x;
   const int frag = gt / kSplitSub, sub = gt % kSplitSub;
   const int h = frag >> 2, blk = frag & 3;
@@ -95,15 +134,22 @@ __global__ void __launch_bounds__(kSplitThreads) q_split_kernel(const QSplitArgs
 }
 
 hipError_t launch_q_split(const float *const *q, const float *const *w, int n_sessions, int n_heads,
-                          uint32_t *out, hipStream_t st) {
+                          uint32_t *out, const float *const *q_attn, int n_attn_heads, uint4 *attn_out,
+                          hipStream_t st) {
   QSplitArgs a;
   for (int i = 0; i < n_sessions; ++i) {
-    a.q[i] = q[i];
-    a.w[i] = w[i];
+    a.q[i] = q ? q[i] : nullptr;
+    a.w[i] = w ? w[i] : nullptr;
+    a.q_attn[i] = q_attn ? q_attn[i] : nullptr;
   }
   a.out = out;
+  a.attn_out = attn_out;
   a.n_heads = n_heads;
-  q_split_kernel<<<dim3(kSplitBlocks, n_sessions), kSplitThreads, 0, st>>>(a);
+  a.n_attn_heads = n_attn_heads;
+  a.idx_blocks = q ? kSplitBlocks : 0;
+  const int blocks = a.idx_blocks + (q_attn ? kAttnSplitBlocks : 0);
+  if (blocks == 0) return hipSuccess;
+  q_split_kernel<<<dim3(blocks, n_sessions), kSplitThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
