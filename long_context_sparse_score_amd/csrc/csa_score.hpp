@@ -120,7 +120,8 @@ __device__ __forceinline__ float row_butterfly(float p) {
 // Partial score of one half of the head groups for NS 16-row tiles: for each
 // operand r (this lane's 16 code bytes of row l%16 and its scale byte),
 //   part_r = butterfly( fma-chain over groups g, then the lane's heads v, of
-//                       w_gv * max(0, d_gv) ),
+//                       w_gv * max(0, d_gv) ),  (a NaN d_gv, impossible for
+//                       valid rows, is not zeroed)
 // d the matrix-core dot product of the query terms (in order) with the row.
 // Every lane returns its row's value.  The full score of a row is
 // part(first half) + part(second half), -0 stored as +0 (score_finish).
@@ -144,8 +145,10 @@ __device__ __forceinline__ void score_part(const QFrag<G> &q, const RowOperand (
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float d = c[r][g][v];
-        p = __builtin_fmaf(q.w[g][v], d > 0.0f ? d : 0.0f, p);
+        // ReLU as a signed-integer max of the bits: one instruction, and
+        // -0 -> +0 (a float max would add an IEEE quieting step)
+        const float d = __int_as_float(max(__float_as_int(c[r][g][v]), 0));
+        p = __builtin_fmaf(q.w[g][v], d, p);
       }
     }
     out[r] = row_butterfly(p);

@@ -9,9 +9,9 @@
 //   2. finds the tile's exact top-hd keys ("heads", hd in {16, 32, 64}) and
 //      writes them sorted descending to heads[tile][hd] (0-padded).
 // Step 2 first bounds the hd-th key from below without sorting the tile:
-// every wave sorts the 64 per-lane maxima of its keys, and the hd-th largest
-// of them is a key with at least hd keys above or at it; the largest such
-// bound over the waves is theta.  Only keys >= theta can be heads.  At most
+// every wave finds, from the 64 per-lane maxima of its keys, a value with at
+// least hd of them at or above it (a bit-by-bit search on the top 24 bits,
+// one ballot per bit); the largest such bound over the waves is theta.  Only keys >= theta can be heads.  At most
 // hd lanes per wave hold such keys, so there are at most 4 * hd * (T / 256)
 // of them (typically 2-4 hd); they are ranked exactly against each other.
 // The global selection over the heads is in csa_merge.hip.
@@ -58,23 +58,6 @@ struct TileShared {
   SelScratch<kTileWaves> sc;
 };
 
-// Bitonic sort of one key per lane across the wave, descending: lane l
-// returns the l-th largest.
-__device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t o = shfl_xor_u64(v, stride);
-      const bool desc = ((lane & size) == 0) || size == 64;
-      const bool lower = (lane & stride) == 0;
-      v = (lower == desc) ? (o > v ? o : v) : (o < v ? o : v);
-    }
-  }
-  return v;
-}
-
 // Step 2: keys in registers (slot j of thread tid is tile position tid +
 // 256 j, 0 = none) -> the tile's top-hd keys, sorted, at heads_out[0..hd).
 __device__ void tile_heads(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj, int hd,
@@ -84,8 +67,16 @@ __device__ void tile_heads(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj
 #pragma unroll
   for (int j = 0; j < kTileKPT; ++j)
     if (j < nj) lmax = x[j] > lmax ? x[j] : lmax;
-  const uint64_t srt = wave_sort64_desc(lmax);
-  const uint64_t tw = shfl_u64(srt, hd - 1);
+  // the largest 24-bit prefix p of the key with at least hd lane maxima at
+  // or above p << 40: those hd keys are >= p << 40, a valid bound
+  const uint32_t o = (uint32_t)(lmax >> 40);
+  uint32_t p = 0;
+#pragma unroll
+  for (int b = 23; b >= 0; --b) {
+    const uint32_t c = p | (1u << b);
+    if (__popcll(__ballot(o >= c)) >= hd) p = c;
+  }
+  const uint64_t tw = (uint64_t)p << 40;
   if (lane == 0) sh.theta[wave] = tw;
   if (tid == 0) sh.ccnt = 0;
   __syncthreads();
@@ -133,27 +124,48 @@ __device__ void tile_heads(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj
 // LDS ring kRingDepth - 1 chunks ahead; a final partial chunk (the buffer
 // end need not be 16-byte aligned) is read with per-lane row-clamped loads.
 // Each row's score goes to sh.score[position].
+// Chunks of this wave that lie wholly inside the buffer.
+__device__ __forceinline__ int stream_chunks(int rows, int wave) {
+  const int nfull = rows / kChunkRows;  // chunks with all 64 rows present
+  return nfull > wave ? (nfull - wave + kTileWaves - 1) / kTileWaves : 0;
+}
+
+// Chunk c of this wave into its ring slot (c past the last chunk reloads the
+// last one: the loop keeps a fixed number of loads in flight).
+__device__ __forceinline__ void stream_issue(const uint8_t *__restrict__ idx_rows, int64_t row0, int cnt, int c,
+                                             TileShared &sh, int wave, int lane) {
+  const int cc = c < cnt ? c : cnt - 1;
+  issue_chunk(idx_rows, row0 + (int64_t)kChunkRows * (wave + kTileWaves * cc),
+              (uint32_t)(uintptr_t)&sh.ring[wave][c % kRingDepth][0], lane);
+}
+
+// The first kRingDepth - 1 chunks, issued before the query fragments are
+// loaded so that both latencies overlap.
+__device__ __forceinline__ void stream_prologue(const uint8_t *__restrict__ idx_rows, int64_t row0, int rows,
+                                                TileShared &sh, int wave, int lane) {
+  const int cnt = stream_chunks(rows, wave);
+  if (cnt > 0) {
+#pragma unroll
+    for (int c = 0; c < kRingDepth - 1; ++c) stream_issue(idx_rows, row0, cnt, c, sh, wave, lane);
+  }
+}
+
+// Requires stream_prologue() and then no outstanding vector memory loads but
+// those chunks.
 template <int G>
 __device__ __forceinline__ void score_stream(const QFrag<G> &q, const uint8_t *__restrict__ idx_rows, int64_t row0,
                                              int64_t n, int rows, TileShared &sh, int wave, int lane) {
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
   const int nfull = rows / kChunkRows;  // chunks with all 64 rows present
-  const int cnt = nfull > wave ? (nfull - wave + kTileWaves - 1) / kTileWaves : 0;
+  const int cnt = stream_chunks(rows, wave);
   // lanes 0..15 hold rows pos0 + lane of operand 0, lanes 16..31 rows
   // pos0 + lane of operand 1
   auto emit2 = [&](int pos0, const float (&s2)[2]) {
     if (lane < 32 && pos0 + lane < rows) sh.score[pos0 + lane] = score_finish(lane < 16 ? s2[0] : s2[1], 0.0f);
   };
   if (cnt > 0) {
-    auto slot = [&](int k) { return (uint32_t)(uintptr_t)&sh.ring[wave][k][0]; };
-    auto issue = [&](int c) {
-      const int cc = c < cnt ? c : cnt - 1;
-      issue_chunk(idx_rows, row0 + (int64_t)kChunkRows * (wave + kTileWaves * cc), slot(c % kRingDepth), lane);
-    };
-#pragma unroll
-    for (int c = 0; c < kRingDepth - 1; ++c) issue(c);
     for (int c = 0; c < cnt; ++c) {
-      issue(c + kRingDepth - 1);
+      stream_issue(idx_rows, row0, cnt, c + kRingDepth - 1, sh, wave, lane);
       wait_vmcnt<kChunkDma * (kRingDepth - 1)>();
       const uint8_t *base = &sh.ring[wave][c % kRingDepth][0];
       const int pos0 = kChunkRows * (wave + kTileWaves * c);
@@ -206,9 +218,10 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   };
 
   if constexpr (MODE != kModeArraySelect) {
+    stream_prologue(S.idx_rows, row0, rows, sh, tid >> 6, lane);
     QFrag<G> q;
     load_qfrag<G>(q, a.qsplit + (size_t)sess * (kQSplitBytes / 4), lane, 0);
-    wait_vmcnt<0>();  // the query is resident before the chunk loads start
+    wait_vmcnt<0>();  // query and first chunks resident: the loop's own waits count chunks only
     score_stream<G>(q, S.idx_rows, row0, n, rows, sh, tid >> 6, lane);
     __syncthreads();
 #pragma unroll
