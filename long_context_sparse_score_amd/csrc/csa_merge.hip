@@ -92,31 +92,33 @@ struct SelShared {
 template <class Visit>
 __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32_t target, SelShared &sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint64_t mn = ~0ull, mx = 0;
+  auto umin = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  auto uadd = [](uint32_t a, uint32_t b) { return a + b; };
+  // range of the score parts (key >> 32), and the count
+  uint32_t mn = ~0u, mx = 0;
   uint32_t cnt = 0;
   visit([&](uint64_t x) __attribute__((always_inline)) {
-    mn = x < mn ? x : mn;
-    mx = x > mx ? x : mx;
+    const uint32_t o = (uint32_t)(x >> 32);
+    mn = o < mn ? o : mn;
+    mx = o > mx ? o : mx;
     ++cnt;
   });
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint64_t a = shfl_xor_u64(mn, m), b = shfl_xor_u64(mx, m);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-    cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
-  }
+  mn = wave_reduce_u32(mn, ~0u, umin);
+  mx = wave_reduce_u32(mx, 0u, umax);
+  cnt = wave_reduce_u32(cnt, 0u, uadd);
   if (lane == 0) { sh.red_lo[wave] = mn; sh.red_hi[wave] = mx; sh.red_n[wave] = cnt; }
   __syncthreads();
-  uint64_t lo = ~0ull, hi = 0;
+  uint32_t omin = ~0u, omax = 0;
   uint32_t total = 0;
 #pragma unroll
   for (int w = 0; w < kSelWaves; ++w) {
-    lo = sh.red_lo[w] < lo ? sh.red_lo[w] : lo;
-    hi = sh.red_hi[w] > hi ? sh.red_hi[w] : hi;
+    omin = (uint32_t)sh.red_lo[w] < omin ? (uint32_t)sh.red_lo[w] : omin;
+    omax = (uint32_t)sh.red_hi[w] > omax ? (uint32_t)sh.red_hi[w] : omax;
     total += sh.red_n[w];
   }
   __syncthreads();
+  uint64_t lo = (uint64_t)omin << 32, hi = ((uint64_t)omax << 32) | 0xFFFFFFFFull;
   if (total <= need) return 1ull;
   if (total <= target) return lo;
   uint32_t above = 0;  // keys above the current range [lo, hi]
@@ -131,23 +133,21 @@ __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32
     });
     __syncthreads();
     const uint32_t need_here = need - above;
-    const uint32_t h0 = sh.u.s.hist[2 * tid], h1 = sh.u.s.hist[2 * tid + 1];
+    // thread t owns the upper bin kSelBins-1-2t and the lower bin
+    // kSelBins-2-2t, so "bins above" is a prefix over threads
+    const uint32_t bu = kSelBins - 1 - 2 * tid;
+    const uint32_t h1 = sh.u.s.hist[bu], h0 = sh.u.s.hist[bu - 1];
     const uint32_t s = h0 + h1;
-    uint32_t suf = s;  // inclusive suffix sum over the lanes of the wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t v = (uint32_t)__shfl_down((int)suf, d, 64);
-      if (lane + d < 64) suf += v;
-    }
-    if (lane == 0) sh.red_n[wave] = suf;
+    const uint32_t incl = wave_scan_u32(s, 0u, uadd);
+    if (lane == 63) sh.red_n[wave] = incl;
     __syncthreads();
-    uint32_t after = 0;
-    for (int w = wave + 1; w < kSelWaves; ++w) after += sh.red_n[w];
-    const uint32_t X = suf - s + after;  // keys in bins above 2 tid + 1
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += sh.red_n[w];
+    const uint32_t X = incl - s + before;  // keys in bins above bu
     if (X < need_here && need_here <= X + h1) {
-      sh.bin = 2 * tid + 1; sh.ca = X; sh.cb = h1;
+      sh.bin = bu; sh.ca = X; sh.cb = h1;
     } else if (X + h1 < need_here && need_here <= X + s) {
-      sh.bin = 2 * tid; sh.ca = X + h1; sh.cb = h0;
+      sh.bin = bu - 1; sh.ca = X + h1; sh.cb = h0;
     }
     __syncthreads();
     const uint32_t b = sh.bin, ca = sh.ca, cb = sh.cb;
@@ -217,25 +217,30 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       h[j] = i < nh ? y : 0ull;
     }
   }
-  auto visit_heads = [&](auto f) __attribute__((always_inline)) {
+  // every head slot of this thread, in control flow uniform over the wave:
+  // f(ok, x), ok = "x is a head"
+  auto scan_heads = [&](auto f) __attribute__((always_inline)) {
     if constexpr (reg) {
 #pragma unroll
-      for (int j = 0; j < kSelKPT; ++j)
-        if (h[j] != 0) f(h[j]);
+      for (int j = 0; j < kSelKPT; ++j) f(h[j] != 0, h[j]);
     } else {
-      for (int64_t i0 = tid; i0 < nh; i0 += (int64_t)kSelThreads * 8) {
+      for (int64_t i0 = 0; i0 < nh; i0 += (int64_t)kSelThreads * 8) {
         uint64_t y[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int64_t i = i0 + (int64_t)kSelThreads * u;
+          const int64_t i = i0 + tid + (int64_t)kSelThreads * u;
           const uint64_t z = heads[i < nh ? i : nh - 1];
           y[u] = i < nh ? z : 0ull;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (y[u] != 0) f(y[u]);
+        for (int u = 0; u < 8; ++u) f(y[u] != 0, y[u]);
       }
     }
+  };
+  auto visit_heads = [&](auto f) __attribute__((always_inline)) {
+    scan_heads([&](bool ok, uint64_t x) __attribute__((always_inline)) {
+      if (ok) f(x);
+    });
   };
 
   // 1. the bound G
@@ -269,47 +274,92 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   __syncthreads();
   const int nfull = (int)(sh.nfull < kSelMaxFull ? sh.nfull : kSelMaxFull);
 
-  // candidates: heads >= lb of tiles that are not full, keys >= lb of full tiles
-  auto visit_cand = [&](uint64_t lb, auto f) __attribute__((always_inline)) {
+  // candidates: heads >= lb of tiles that are not full, keys >= lb of full
+  // tiles, in batches of 8 slots per thread: fb(ok[8], x[8]) in control flow
+  // uniform over the wave
+  auto scan_cand = [&](uint64_t lb, auto fb) __attribute__((always_inline)) {
     if constexpr (reg) {
 #pragma unroll
-      for (int j = 0; j < kSelKPT; ++j) {
-        const int i = tid + kSelThreads * j;
-        if (h[j] != 0 && h[j] >= lb && !sh.full_flag[i >> lhd]) f(h[j]);
+      for (int j0 = 0; j0 < kSelKPT; j0 += 8) {
+        bool ok[8];
+        uint64_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = tid + kSelThreads * (j0 + u);
+          x[u] = h[j0 + u];
+          ok[u] = x[u] != 0 && x[u] >= lb && !sh.full_flag[i >> lhd];
+        }
+        fb(ok, x);
       }
     } else {
-      visit_heads([&](uint64_t x) __attribute__((always_inline)) {
-        if (x >= lb) {
-          // the tile of this head: keys carry the row, tiles are T rows
-          const int64_t t = (int64_t)(key_row(x) >> lT);
-          if (!tile_is_full(t)) f(x);
+      for (int64_t i0 = 0; i0 < nh; i0 += (int64_t)kSelThreads * 8) {
+        bool ok[8];
+        uint64_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i = i0 + tid + (int64_t)kSelThreads * u;
+          const uint64_t z = heads[i < nh ? i : nh - 1];
+          x[u] = i < nh ? z : 0ull;
         }
-      });
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          // the tile of a head: keys carry the row, tiles are T rows
+          const int64_t t = x[u] != 0 ? (int64_t)(key_row(x[u]) >> lT) : 0;
+          ok[u] = x[u] != 0 && x[u] >= lb && !tile_is_full(t);
+        }
+        fb(ok, x);
+      }
     }
     const int nfr = nfull << lT;  // at most kSelMaxFull * 4096
-    for (int i0 = tid; i0 < nfr; i0 += kSelThreads * 8) {
+    for (int i0 = 0; i0 < nfr; i0 += kSelThreads * 8) {
       float v[8];
       int64_t row[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + kSelThreads * u;
+        const int i = i0 + tid + kSelThreads * u;
         row[u] = i < nfr ? ((int64_t)sh.full_list[i >> lT] << lT) + (i & (T - 1)) : n;
         v[u] = scores[row[u] < n ? row[u] : n - 1];
       }
+      bool ok[8];
+      uint64_t x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (row[u] < n) {
-          const uint64_t x = ((uint64_t)score_ord(v[u]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row[u]);
-          if (x >= lb) f(x);
-        }
+        x[u] = ((uint64_t)score_ord(v[u]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row[u]);
+        ok[u] = row[u] < n && x[u] >= lb;
       }
+      fb(ok, x);
     }
   };
-  auto append = [&](uint64_t x) __attribute__((always_inline)) {
-    const uint32_t p = atomicAdd(&sh.ccnt, 1u);
-    if (p < kSelCap) sh.u.s.cand[p] = x;
+  auto visit_cand = [&](uint64_t lb, auto f) __attribute__((always_inline)) {
+    scan_cand(lb, [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ok[u]) f(x[u]);
+    });
   };
-  visit_cand(G, append);
+  // one LDS atomic per wave and batch: the wave's selected slots take
+  // consecutive positions
+  auto append = [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
+    uint64_t m[8];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      m[u] = __ballot(ok[u]);
+      tot += (uint32_t)__popcll(m[u]);
+    }
+    if (tot == 0) return;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&sh.ccnt, tot);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t p =
+          base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[u], 0u));
+      if (ok[u] && p < (uint32_t)kSelCap) sh.u.s.cand[p] = x[u];
+      base += (uint32_t)__popcll(m[u]);
+    }
+  };
+  scan_cand(G, append);
   __syncthreads();
   int C = (int)sh.ccnt;
   if (C > kSelCap) {
@@ -317,7 +367,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
     const uint64_t thr = sel_bound([&](auto f) __attribute__((always_inline)) { visit_cand(G, f); }, (uint32_t)k_eff, (uint32_t)k_eff, sh);
     if (tid == 0) sh.ccnt = 0;
     __syncthreads();
-    visit_cand(thr, append);
+    scan_cand(thr, append);
     __syncthreads();
     C = (int)sh.ccnt;
   }

@@ -24,6 +24,32 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Cross-lane steps on the DPP network (GFX9 row_shr:n = 0x110 + n,
+// row_bcast:15 = 0x142 into rows 1 and 3, row_bcast:31 = 0x143 into rows 2
+// and 3).  Lanes without a source keep `ident`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t ident, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive scan of v over the lanes of the wave in lane order with an
+// associative op whose identity is ident (lane 63 ends with the total).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v, uint32_t ident, Op op) {
+  v = op(v, dpp_u32<0x111, 0xF>(ident, v));
+  v = op(v, dpp_u32<0x112, 0xF>(ident, v));
+  v = op(v, dpp_u32<0x114, 0xF>(ident, v));
+  v = op(v, dpp_u32<0x118, 0xF>(ident, v));
+  v = op(v, dpp_u32<0x142, 0xA>(ident, v));
+  v = op(v, dpp_u32<0x143, 0xC>(ident, v));
+  return v;
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t ident, Op op) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v, ident, op), 63);
+}
+
 template <int NW>  // waves per workgroup
 struct SelScratch {
   uint32_t hist[NW][256];
