@@ -76,6 +76,24 @@ __device__ __forceinline__ void load_qfrag(QFrag<G> &q, const uint32_t *__restri
   }
 }
 
+// Complete the query loads at this point: an empty asm statement that reads
+// and writes every fragment register makes the compiler wait for the loads
+// here.  Without it the scheduler may sink the loads past an explicit wait
+// and the compiler's own waits then sit inside the streaming loop, where a
+// load-counter wait also drains the chunks in flight.
+template <int G>
+__device__ __forceinline__ void pin_qfrag(QFrag<G> &q) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int t = 0; t < kTerms; ++t) asm volatile("" : "+v"(q.a[g][t]));
+#pragma unroll
+    for (int w = 0; w < kScaleWords; ++w) asm volatile("" : "+v"(q.scw[g][w]));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(q.w[g][v]));
+  }
+}
+
 struct RowOperand {
   uint4 codes;
   int sb;
@@ -107,52 +125,52 @@ __device__ __forceinline__ void mfma_terms(const QFrag<G> &q, const v8i (&b)[NS]
   (mfma_term<G, NS, Ts>(q, b, sb, c), ...);
 }
 
-// Sum over the four lanes l, l^16, l^32, l^48 as (p0 + p1) + (p2 + p3), p_r
-// the value of lane row r, the same association in every lane
-// (v_permlane16_swap / v_permlane32_swap exchange 16-lane rows).
-__device__ __forceinline__ float row_butterfly(float p) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
-  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Partial score of one half of the head groups for NS 16-row tiles: for each
-// operand r (this lane's 16 code bytes of row l%16 and its scale byte),
-//   part_r = butterfly( fma-chain over groups g, then the lane's heads v, of
-//                       w_gv * max(0, d_gv) ),  (a NaN d_gv, impossible for
-//                       valid rows, is not zeroed)
-// d the matrix-core dot product of the query terms (in order) with the row.
-// Every lane returns its row's value.  The full score of a row is
-// part(first half) + part(second half), -0 stored as +0 (score_finish).
-template <int G, int NS>
-__device__ __forceinline__ void score_part(const QFrag<G> &q, const RowOperand (&ops)[NS], float (&out)[NS]) {
+// The kTerms matrix-core products of NS row operands with one 16-head
+// group's query: c[r] = sum over terms t, in order, of (term t) x (operand r),
+// each operand r being this lane's 16 code bytes of row l%16 and its scale
+// byte.  Lane l receives heads 4(l/16) + v, v < 4, of row l%16.
+template <int NS>
+__device__ __forceinline__ void group_dots(const QFrag<1> &q, const RowOperand (&ops)[NS], v4f (&c)[NS][1]) {
   v8i b[NS];
   int sb[NS];
-  v4f c[NS][G];
 #pragma unroll
   for (int r = 0; r < NS; ++r) {
     b[r] = as_b(ops[r]);
     sb[r] = ops[r].sb;
-#pragma unroll
-    for (int g = 0; g < G; ++g) c[r][g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    c[r][0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  mfma_terms<G, NS>(q, b, sb, c, std::make_integer_sequence<int, kTerms>{});
+  mfma_terms<1, NS>(q, b, sb, c, std::make_integer_sequence<int, kTerms>{});
+}
+
+// The group's part of the score for four operands (64 rows):
+//   part = sum over the group's 16 heads h of w_h * max(0, d_h)
+// (a NaN d, impossible for valid rows, is not zeroed).  Each lane first sums
+// its four heads (an fma chain over v); the four lane-rows are then summed
+// by a reduce-scatter: a 32-lane swap pairs operands (0, 2) and (1, 3)
+// across the lane halves, a 16-lane swap pairs the results across adjacent
+// lane-rows.  Lane l returns the part of row l%16 of operand l/16 (that is,
+// of row l of the 64), as (lane-row 0 + lane-row 2) + (lane-row 1 + lane-row 3).
+// v_permlane32_swap(x, y) -> (x0, x1, y0, y1), (x2, x3, y2, y3) and
+// v_permlane16_swap(x, y) -> (x0, y0, x2, y2), (x1, y1, x3, y3) in 16-lane rows.
+__device__ __forceinline__ float group_part4(const QFrag<1> &q, const v4f (&c)[4][1]) {
+  float p[4];
 #pragma unroll
-  for (int r = 0; r < NS; ++r) {
-    float p = 0.0f;
+  for (int r = 0; r < 4; ++r) {
+    p[r] = 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        // ReLU as a signed-integer max of the bits: one instruction, and
-        // -0 -> +0 (a float max would add an IEEE quieting step)
-        const float d = __int_as_float(max(__float_as_int(c[r][g][v]), 0));
-        p = __builtin_fmaf(q.w[g][v], d, p);
-      }
+    for (int v = 0; v < 4; ++v) {
+      // ReLU as a signed-integer max of the bits: one instruction, and
+      // -0 -> +0 (a float max would add an IEEE quieting step)
+      const float d = __int_as_float(max(__float_as_int(c[r][0][v]), 0));
+      p[r] = __builtin_fmaf(q.w[0][v], d, p[r]);
     }
-    out[r] = row_butterfly(p);
   }
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float b = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // The score of a row from its two half partials (first + second).

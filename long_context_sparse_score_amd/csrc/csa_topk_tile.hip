@@ -9,11 +9,12 @@
 //   2. finds the tile's exact top-hd keys ("heads", hd in {16, 32, 64}) and
 //      writes them sorted descending to heads[tile][hd] (0-padded).
 // Step 2 first bounds the hd-th key from below without sorting the tile:
-// every wave finds, from the 64 per-lane maxima of its keys, a value with at
-// least hd of them at or above it (a bit-by-bit search on the top 24 bits,
-// one ballot per bit); the largest such bound over the waves is theta.  Only keys >= theta can be heads.  At most
-// hd lanes per wave hold such keys, so there are at most 4 * hd * (T / 256)
-// of them (typically 2-4 hd); they are ranked exactly against each other.
+// every wave splits its 64 lanes into hd groups and takes the smallest group
+// maximum of the lanes' largest keys (score part), a value with at least hd
+// keys at or above it; the largest such bound over the waves is theta.  Only
+// keys >= theta can be heads: typically a few times hd of them, ranked
+// exactly against each other (an exact k-th selection replaces theta when
+// they overflow the candidate buffer).
 // The global selection over the heads is in csa_merge.hip.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
@@ -45,72 +46,108 @@ enum { kModeScore = 0, kModeScoreSelect = 1, kModeArraySelect = 2 };
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
 
-constexpr int kTileKPT = kMaxTileRows / kTileThreads;  // keys per thread, at most
-constexpr int kRingDepth = 3;                            // chunks in flight per wave
+constexpr int kStepChunks = kTileWaves;                  // one 64-row chunk per wave and step
+constexpr int kStepRows = kStepChunks * kChunkRows;      // 256
+constexpr int kStepBytes = kStepChunks * kChunkBytes;    // 17408 (16-byte multiple)
+constexpr int kRingDepth = 3;                            // steps resident: D - 1 in flight
 constexpr int kTileCandCap = 256;                        // keys >= theta ranked directly
+static_assert(kRingDepth >= 2 && kRingDepth <= 4, "ring depth");
+static_assert(kStepBytes % 16 == 0 && kChunkBytes % 16 == 0, "direct-to-LDS pieces stay aligned");
 
 struct TileShared {
-  uint8_t ring[kTileWaves][kRingDepth][kChunkSlot];  // per-wave chunk ring
+  alignas(16) uint8_t ring[kRingDepth][kStepBytes];  // workgroup ring of steps
   float score[kMaxTileRows];                          // scores by tile position
-  uint64_t cand[kTileCandCap + 16];                   // keys >= theta (+ over-read slack)
-  uint64_t theta[kTileWaves];
-  uint32_t ccnt;
-  SelScratch<kTileWaves> sc;
+  union {
+    float part[2][kMaxGroups][kStepRows];  // head-group partials of the last two steps
+    struct {
+      uint64_t cand[kTileCandCap + 16];  // keys >= theta (+ over-read slack)
+      uint64_t theta[kTileWaves];
+      uint32_t ccnt;
+      SelScratch<kTileWaves> sc;
+    } h;  // step 2
+  } u;
 };
+static_assert(sizeof(TileShared) <= 80 * 1024, "two workgroups per compute unit");
 
-// Step 2: keys in registers (slot j of thread tid is tile position tid +
-// 256 j, 0 = none) -> the tile's top-hd keys, sorted, at heads_out[0..hd).
-__device__ void tile_heads(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj, int hd,
+// Step 2: the tile's scores in sh.score[0..rows) and, per thread, the
+// largest score part (score_ord) over its positions tid + 256 j -> the
+// tile's top-hd keys, sorted, at heads_out[0..hd).
+__device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, int hd,
                            uint64_t *__restrict__ heads_out) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint64_t lmax = 0;
-#pragma unroll
-  for (int j = 0; j < kTileKPT; ++j)
-    if (j < nj) lmax = x[j] > lmax ? x[j] : lmax;
-  // the largest 24-bit prefix p of the key with at least hd lane maxima at
-  // or above p << 40: those hd keys are >= p << 40, a valid bound
-  const uint32_t o = (uint32_t)(lmax >> 40);
+  auto key_at = [&](int i) __attribute__((always_inline)) {
+    return make_key(sh.score[i], (uint32_t)(row0 + i));
+  };
+  // the largest 24-bit prefix p with at least hd lane maxima at or above
+  // p << 8 (two bits per step): those hd keys are >= p << 40
+  const uint32_t o24 = o >> 8;
   uint32_t p = 0;
 #pragma unroll
-  for (int b = 23; b >= 0; --b) {
-    const uint32_t c = p | (1u << b);
-    if (__popcll(__ballot(o >= c)) >= hd) p = c;
+  for (int b = 22; b >= 0; b -= 2) {
+    const uint32_t c1 = p | (1u << b), c2 = p | (2u << b), c3 = p | (3u << b);
+    const int n1 = __popcll(__ballot(o24 >= c1));
+    const int n2 = __popcll(__ballot(o24 >= c2));
+    const int n3 = __popcll(__ballot(o24 >= c3));
+    p = n3 >= hd ? c3 : (n2 >= hd ? c2 : (n1 >= hd ? c1 : p));
   }
-  const uint64_t tw = (uint64_t)p << 40;
-  if (lane == 0) sh.theta[wave] = tw;
-  if (tid == 0) sh.ccnt = 0;
+  if (lane == 0) sh.u.h.theta[wave] = (uint64_t)p << 40;
+  if (tid == 0) sh.u.h.ccnt = 0;
   __syncthreads();
-  uint64_t theta = 1;
+  uint64_t theta = 1;  // also excludes empty positions
 #pragma unroll
-  for (int w = 0; w < kTileWaves; ++w) theta = sh.theta[w] > theta ? sh.theta[w] : theta;
+  for (int w = 0; w < kTileWaves; ++w) theta = sh.u.h.theta[w] > theta ? sh.u.h.theta[w] : theta;
+  // keys >= lb, four positions per thread at a time, one LDS atomic per wave
+  // and batch: the wave's keys take consecutive positions
+  const int nj = (rows + kTileThreads - 1) / kTileThreads;
+  auto gather = [&](uint64_t lb, uint32_t cap) __attribute__((always_inline)) {
+    for (int j0 = 0; j0 < nj; j0 += 4) {
+      bool ok[4];
+      uint64_t kx[4], m[4];
+      uint32_t tot = 0;
 #pragma unroll
-  for (int j = 0; j < kTileKPT; ++j) {
-    if (j < nj && x[j] >= theta) {
-      const uint32_t p = atomicAdd(&sh.ccnt, 1u);
-      if (p < kTileCandCap) sh.cand[p] = x[j];
+      for (int u = 0; u < 4; ++u) {
+        const int i = tid + kTileThreads * (j0 + u);
+        const bool in = i < rows;
+        kx[u] = key_at(in ? i : 0);
+        ok[u] = in && kx[u] >= lb;
+        m[u] = __ballot(ok[u]);
+        tot += (uint32_t)__popcll(m[u]);
+      }
+      if (tot != 0) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sh.u.h.ccnt, tot);
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t q = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m[u] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m[u], 0u));
+          if (ok[u] && q < cap) sh.u.h.cand[q] = kx[u];
+          base += (uint32_t)__popcll(m[u]);
+        }
+      }
     }
-  }
+  };
+  gather(theta, (uint32_t)kTileCandCap);
   __syncthreads();
-  int C = (int)sh.ccnt;
+  int C = (int)sh.u.h.ccnt;
   if (C > kTileCandCap) {
     // many keys tie with or crowd above the bound: select exactly instead
-    const uint64_t thr = block_kth_largest_reg<kTileWaves, kTileKPT>(x, nj, hd, theta, sh.sc);
-    if (tid == 0) sh.ccnt = 0;
+    // (exactly hd keys are >= the hd-th largest)
+    const uint64_t thr = block_kth_largest<kTileWaves>(key_at, rows, hd, theta, sh.u.h.sc);
+    if (tid == 0) sh.u.h.ccnt = 0;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kTileKPT; ++j)
-      if (j < nj && x[j] != 0 && x[j] >= thr) sh.cand[atomicAdd(&sh.ccnt, 1u)] = x[j];
+    gather(thr, (uint32_t)kTileCandCap);
     __syncthreads();
-    C = (int)sh.ccnt;
+    C = (int)sh.u.h.ccnt;
   }
   // rank = number of larger candidates = sorted position
   for (int i = tid; i < C; i += kTileThreads) {
-    const uint64_t key = sh.cand[i];
+    const uint64_t key = sh.u.h.cand[i];
     int r = 0;
     for (int j0 = 0; j0 < C; j0 += 16) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const uint64_t y = sh.cand[j0 + u];
+        const uint64_t y = sh.u.h.cand[j0 + u];
         r += (j0 + u < C && y > key) ? 1 : 0;
       }
     }
@@ -119,85 +156,137 @@ __device__ void tile_heads(TileShared &sh, const uint64_t (&x)[kTileKPT], int nj
   for (int r = C + tid; r < hd; r += kTileThreads) heads_out[r] = 0ull;
 }
 
-// Score every row of the tile: wave w takes chunks w, w + 4, ... (64 rows
-// each).  Chunks lying wholly inside the buffer stream through the wave's
-// LDS ring kRingDepth - 1 chunks ahead; a final partial chunk (the buffer
-// end need not be 16-byte aligned) is read with per-lane row-clamped loads.
-// Each row's score goes to sh.score[position].
-// Chunks of this wave that lie wholly inside the buffer.
-__device__ __forceinline__ int stream_chunks(int rows, int wave) {
-  const int nfull = rows / kChunkRows;  // chunks with all 64 rows present
-  return nfull > wave ? (nfull - wave + kTileWaves - 1) / kTileWaves : 0;
-}
-
-// Chunk c of this wave into its ring slot (c past the last chunk reloads the
-// last one: the loop keeps a fixed number of loads in flight).
-__device__ __forceinline__ void stream_issue(const uint8_t *__restrict__ idx_rows, int64_t row0, int cnt, int c,
-                                             TileShared &sh, int wave, int lane) {
-  const int cc = c < cnt ? c : cnt - 1;
-  issue_chunk(idx_rows, row0 + (int64_t)kChunkRows * (wave + kTileWaves * cc),
-              (uint32_t)(uintptr_t)&sh.ring[wave][c % kRingDepth][0], lane);
-}
-
-// The first kRingDepth - 1 chunks, issued before the query fragments are
-// loaded so that both latencies overlap.
-__device__ __forceinline__ void stream_prologue(const uint8_t *__restrict__ idx_rows, int64_t row0, int rows,
-                                                TileShared &sh, int wave, int lane) {
-  const int cnt = stream_chunks(rows, wave);
-  if (cnt > 0) {
+// Rows [r0, r0 + 64) of a chunk that ends past the buffer: lane l copies
+// row min(r0 + l, n - 1) to dst + 68 l with ordinary loads (the compiler
+// waits for them before the LDS stores; rows past n are scored and dropped).
+__device__ __forceinline__ void copy_chunk_clamped(const uint8_t *__restrict__ rows, int64_t r0, int64_t n,
+                                                   uint8_t *dst, int lane) {
+  int64_t r = r0 + lane;
+  r = r < n ? r : n - 1;
+  const uint32_t *src = reinterpret_cast<const uint32_t *>(rows + r * kIdxRowBytes);
+  uint32_t v[kIdxRowBytes / 4];
 #pragma unroll
-    for (int c = 0; c < kRingDepth - 1; ++c) stream_issue(idx_rows, row0, cnt, c, sh, wave, lane);
+  for (int i = 0; i < kIdxRowBytes / 4; ++i) v[i] = src[i];
+  uint32_t *d = reinterpret_cast<uint32_t *>(dst + lane * kIdxRowBytes);
+#pragma unroll
+  for (int i = 0; i < kIdxRowBytes / 4; ++i) d[i] = v[i];
+}
+
+// Wait until this wave's chunk of the current step is in LDS, `later` being
+// the number of later steps whose chunk this wave has already issued
+// direct-to-LDS.  Vector loads complete in order, so at most
+// later * kChunkDma outstanding loads means the current chunk is done; a
+// score store still outstanding only lengthens the wait.
+__device__ __forceinline__ void wait_chunk(int later) {
+  if (kRingDepth > 3 && later >= 2)
+    wait_vmcnt<2 * kChunkDma>();
+  else if (kRingDepth > 2 && later >= 1)
+    wait_vmcnt<kChunkDma>();
+  else
+    wait_vmcnt<0>();
+}
+
+// This lane's operands of chunk b of a step in LDS: operand i is rows
+// 64 b + 16 i .. + 16, the lane taking row l%16's code bytes [16(l/16), +16)
+// and scale byte l/16.
+__device__ __forceinline__ void load_ops(const uint8_t *base, int b, RowOperand (&ops)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t *rb = base + (kChunkRows * b + 16 * i + (lane & 15)) * kIdxRowBytes;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(rb + 16 * (lane >> 4));
+    ops[i].codes = uint4{w[0], w[1], w[2], w[3]};
+    ops[i].sb = rb[64 + (lane >> 4)];
   }
 }
 
-// Requires stream_prologue() and then no outstanding vector memory loads but
-// those chunks.
+// Score the tile's rows into sh.score[0..rows) (and out[0..rows)).
+// Step s covers tile positions [256 s, 256 s + 256): wave w brings chunk
+// 4s + w into the step's ring slot (direct-to-LDS when the chunk lies wholly
+// inside the buffer, kRingDepth - 1 steps ahead; a chunk cut by the buffer
+// end by clamped per-lane loads).  After one barrier per step every wave
+// scores its share of the step for ITS head group only: wave w takes group
+// w % G and chunks [G (w / G), G (w / G) + G) of the step, so a wave holds
+// the query terms of 16 heads.  The group partials meet in LDS and are
+// summed, group by group in a fixed association, one step later.
 template <int G>
-__device__ __forceinline__ void score_stream(const QFrag<G> &q, const uint8_t *__restrict__ idx_rows, int64_t row0,
-                                             int64_t n, int rows, TileShared &sh, int wave, int lane) {
+__device__ __forceinline__ uint32_t score_tile(const uint32_t *__restrict__ qsplit, const uint8_t *__restrict__ idx_rows,
+                                           int64_t row0, int64_t n, int rows, float *__restrict__ out,
+                                           TileShared &sh) {
+  static_assert(G == 1 || G == 2 || G == 4, "head groups per workgroup");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = wave % G, rl = wave / G;
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
-  const int nfull = rows / kChunkRows;  // chunks with all 64 rows present
-  const int cnt = stream_chunks(rows, wave);
-  // lanes 0..15 hold rows pos0 + lane of operand 0, lanes 16..31 rows
-  // pos0 + lane of operand 1
-  auto emit2 = [&](int pos0, const float (&s2)[2]) {
-    if (lane < 32 && pos0 + lane < rows) sh.score[pos0 + lane] = score_finish(lane < 16 ? s2[0] : s2[1], 0.0f);
+  const int nfc = rows / kChunkRows;  // chunks wholly inside the buffer
+  const int ns = (nch + kStepChunks - 1) / kStepChunks;
+  auto fill = [&](int s) __attribute__((always_inline)) {
+    const int c = kStepChunks * s + wave;
+    uint8_t *dst = &sh.ring[s % kRingDepth][wave * kChunkBytes];
+    if (c < nfc)
+      issue_chunk(idx_rows, row0 + (int64_t)kChunkRows * c, (uint32_t)(uintptr_t)dst, lane);
+    else if (c < nch)
+      copy_chunk_clamped(idx_rows, row0 + (int64_t)kChunkRows * c, n, dst, lane);
   };
-  if (cnt > 0) {
-    for (int c = 0; c < cnt; ++c) {
-      stream_issue(idx_rows, row0, cnt, c + kRingDepth - 1, sh, wave, lane);
-      wait_vmcnt<kChunkDma * (kRingDepth - 1)>();
-      const uint8_t *base = &sh.ring[wave][c % kRingDepth][0];
-      const int pos0 = kChunkRows * (wave + kTileWaves * c);
-#pragma unroll
-      for (int sp = 0; sp < kChunkRows / 32; ++sp) {
-        RowOperand ops[2];
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const uint8_t *rb = base + (32 * sp + 16 * v + (lane & 15)) * kIdxRowBytes;
-          const uint32_t *w = reinterpret_cast<const uint32_t *>(rb + 16 * (lane >> 4));
-          ops[v].codes = uint4{w[0], w[1], w[2], w[3]};
-          ops[v].sb = rb[64 + (lane >> 4)];
-        }
-        float s2[2];
-        score_part<G, 2>(q, ops, s2);
-        emit2(pos0 + 32 * sp, s2);
-      }
+  auto direct = [&](int s) __attribute__((always_inline)) { return s < ns && kStepChunks * s + wave < nfc; };
+  uint32_t omax = 0;  // largest score part of this thread's rows
+  auto combine = [&](int s) __attribute__((always_inline)) {
+    const int p = kStepRows * s + tid;
+    if (p < rows) {
+      const float *pp = &sh.u.part[s & 1][0][tid];
+      float v;
+      if constexpr (G == 4)
+        v = (pp[0] + pp[kStepRows]) + (pp[2 * kStepRows] + pp[3 * kStepRows]);
+      else if constexpr (G == 2)
+        v = pp[0] + pp[kStepRows];
+      else
+        v = pp[0];
+      v = score_finish(v, 0.0f);
+      sh.score[p] = v;
+      out[p] = v;
+      const uint32_t so = score_ord(v);
+      omax = so > omax ? so : omax;
     }
-    wait_vmcnt<0>();  // no chunk load may still be writing LDS past this point
-  }
-  if (nch > nfull && (nch - 1) % kTileWaves == wave) {
-    const int pos0 = kChunkRows * (nch - 1);
+  };
+
 #pragma unroll
-    for (int sp = 0; sp < kChunkRows / 32; ++sp) {
-      RowOperand ops[2];
+  for (int s = 0; s < kRingDepth - 1; ++s)
+    if (s < ns) fill(s);
+  QFrag<1> q;
+  load_qfrag<1>(q, qsplit, lane, grp);
+  pin_qfrag<1>(q);  // no wait for the query inside the loop
+
+  for (int s = 0; s < ns; ++s) {
+    int later = 0;
 #pragma unroll
-      for (int v = 0; v < 2; ++v) ops[v] = load_row_operand(idx_rows, row0 + pos0 + 32 * sp + 16 * v, n, lane);
-      float s2[2];
-      score_part<G, 2>(q, ops, s2);
-      emit2(pos0 + 32 * sp, s2);
+    for (int t = 1; t <= kRingDepth - 2; ++t) later += direct(s + t) ? 1 : 0;
+    wait_chunk(later);
+    __syncthreads();  // step s complete in LDS; step s - 1 consumed by every wave
+    if (s + kRingDepth - 1 < ns) fill(s + kRingDepth - 1);  // into step s - 1's slot
+    if (s > 0) combine(s - 1);
+    const uint8_t *base = &sh.ring[s % kRingDepth][0];
+    // every chunk of the step is scored, also past the tile's rows in its
+    // last step (stale LDS bytes; those partials are never combined), and
+    // the products of the next chunk are issued before the current chunk's
+    // reduction, whose vector instructions then overlap the matrix cores
+    float *const part = &sh.u.part[s & 1][grp][0];
+    RowOperand ops[4];
+    v4f c[4][1], cn[4][1];
+    load_ops(base, G * rl, ops);
+    group_dots<4>(q, ops, c);
+#pragma unroll
+    for (int bb = 1; bb < G; ++bb) {
+      load_ops(base, G * rl + bb, ops);
+      group_dots<4>(q, ops, cn);
+      part[kChunkRows * (G * rl + bb - 1) + lane] = group_part4(q, c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
     }
+    part[kChunkRows * (G * rl + G - 1) + lane] = group_part4(q, c);
   }
+  __syncthreads();
+  if (ns > 0) combine(ns - 1);
+  __syncthreads();
+  return omax;
 }
 
 template <int G, int MODE>
@@ -211,55 +300,44 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   const int rows = (int)((n - row0) < T ? (n - row0) : T);
   __shared__ TileShared sh;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int nj = (rows + kTileThreads - 1) / kTileThreads;
-  uint64_t x[kTileKPT];
-  auto key_of = [&](int i, float sc) -> uint64_t {
-    return ((uint64_t)score_ord(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(row0 + i));
-  };
-
+  uint32_t o = 0;  // largest score part of this thread's positions
   if constexpr (MODE != kModeArraySelect) {
-    stream_prologue(S.idx_rows, row0, rows, sh, tid >> 6, lane);
-    QFrag<G> q;
-    load_qfrag<G>(q, a.qsplit + (size_t)sess * (kQSplitBytes / 4), lane, 0);
-    wait_vmcnt<0>();  // query and first chunks resident: the loop's own waits count chunks only
-    score_stream<G>(q, S.idx_rows, row0, n, rows, sh, tid >> 6, lane);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kTileKPT; ++j) {
-      const int i = tid + kTileThreads * j;
-      x[j] = 0ull;
-      if (j < nj && i < rows) {
-        const float sc = sh.score[i];
-        S.scores_out[row0 + i] = sc;
-        x[j] = key_of(i, sc);
-      }
-    }
+    o = score_tile<G>(a.qsplit + (size_t)sess * (kQSplitBytes / 4), S.idx_rows, row0, n, rows, S.scores_out + row0, sh);
     if constexpr (MODE == kModeScore) return;
   } else {
-    // all loads first (clamped addresses), then the keys
-    float v[kTileKPT];
+    // the given scores into LDS, four loads in flight per thread
+    const float *src = S.scores_in + row0;
+    for (int j0 = 0; j0 < rows; j0 += 4 * kTileThreads) {
+      float v[4];
 #pragma unroll
-    for (int j = 0; j < kTileKPT; ++j) {
-      const int i = tid + kTileThreads * j;
-      v[j] = S.scores_in[row0 + (i < rows ? i : rows - 1)];
-    }
+      for (int u = 0; u < 4; ++u) {
+        const int i = j0 + kTileThreads * u + tid;
+        v[u] = src[i < rows ? i : rows - 1];
+      }
 #pragma unroll
-    for (int j = 0; j < kTileKPT; ++j) {
-      const int i = tid + kTileThreads * j;
-      x[j] = (j < nj && i < rows) ? key_of(i, v[j]) : 0ull;
+      for (int u = 0; u < 4; ++u) {
+        const int i = j0 + kTileThreads * u + tid;
+        if (i < rows) {
+          sh.score[i] = v[u];
+          const uint32_t so = score_ord(v[u]);
+          o = so > o ? so : o;
+        }
+      }
     }
+    __syncthreads();
   }
-  tile_heads(sh, x, nj, S.hd, a.heads + (size_t)sess * a.heads_stride + (size_t)blockIdx.x * S.hd);
+  tile_heads(sh, o, rows, row0, S.hd, a.heads + (size_t)sess * a.heads_stride + (size_t)blockIdx.x * S.hd);
 }
 
 // ---------------------------------------------------------------- launcher
 
 template <int MODE>
 static hipError_t launch_tile_mode(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
+  // three groups run as four: the query split holds zero terms and weights
+  // for heads past n_idx_heads, which add exact zeros
   switch (groups) {
     case 1: tile_kernel<1, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
     case 2: tile_kernel<2, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
-    case 3: tile_kernel<3, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
     default: tile_kernel<4, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
   }
   return hipGetLastError();
