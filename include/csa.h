@@ -143,7 +143,7 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Stages of csa_decode_step, in launch order. */
-#define CSA_STAGES 4 /* 0 query split, 1 score + tile heads, 2 select + logits, 3 softmax + PV */
+#define CSA_STAGES 3 /* 0 query split + score + tile heads, 1 select + attention partials, 2 merge */
 
 /* csa_decode_step that also records events[2*s] right before and
  * events[2*s+1] right after the launches of stage s on hip_stream, so a

@@ -24,7 +24,7 @@ TOPK = 512
 MAX_HEADS = 64
 MAX_SESSIONS = 64
 ABI_VERSION = 1
-STAGES = ("query split", "score + tile heads", "select + logits", "softmax + PV")
+STAGES = ("score + tile heads", "select + attention", "merge")
 
 OK, EINVAL, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4
 

@@ -20,12 +20,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout for (max rows per session, sessions); sized for the
 // smallest tile so that it grows monotonically with max_rows:
-//   [query split][attention query split][tile heads][scores]
-//   [attention partials][attention (m, l)]
+//   [attention query split][tile heads][scores][attention partials]
+//   [attention (m, l)]
 struct Layout {
   int64_t tiles_cap;  // tiles per session at the smallest tile size
   int64_t rows_cap;   // score slots per session
-  size_t qsplit_off, attn_q_off, heads_off, scores_off, part_off, ml_off, total;
+  size_t attn_q_off, heads_off, scores_off, part_off, ml_off, total;
 };
 
 Layout make_layout(int64_t max_rows, int n_sessions) {
@@ -33,8 +33,7 @@ Layout make_layout(int64_t max_rows, int n_sessions) {
   L.tiles_cap = (max_rows + kMinTileRows - 1) / kMinTileRows;
   L.rows_cap = (max_rows + 63) & ~(int64_t)63;
   const size_t ns = (size_t)n_sessions;
-  L.qsplit_off = 0;
-  L.attn_q_off = align_up(ns * kQSplitBytes);
+  L.attn_q_off = 0;
   L.heads_off = L.attn_q_off + align_up(ns * kAttnQBytes);
   L.scores_off = L.heads_off + align_up(ns * (size_t)L.tiles_cap * kMaxTileHeads * sizeof(uint64_t));
   L.part_off = L.scores_off + align_up(ns * (size_t)L.rows_cap * sizeof(float));
@@ -94,7 +93,8 @@ T *at(void *ws, size_t off) {
 
 void fill_job(TileJob &job, const Layout &L, void *ws, int n_sessions) {
   job.n_sessions = n_sessions;
-  job.qsplit = at<uint32_t>(ws, L.qsplit_off);
+  job.attn_q = nullptr;
+  job.n_attn_heads = 0;
   job.heads = at<uint64_t>(ws, L.heads_off);
   job.heads_stride = L.tiles_cap * kMaxTileHeads;
   int64_t total = 0;
@@ -179,12 +179,12 @@ int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const
   job.scores_in[0] = nullptr;
   job.scores_out[0] = scores;
   job.n_rows[0] = n_rows;
+  job.q[0] = q_idx;
+  job.w[0] = w_idx;
+  job.q_attn[0] = nullptr;
   fill_job(job, L, ws, 1);
   if (n_rows == 0) return CSA_OK;
-  hipError_t e = launch_q_split(&q_idx, &w_idx, 1, n_idx_heads, const_cast<uint32_t *>(job.qsplit), nullptr, 0,
-                                nullptr, st);
-  if (e == hipSuccess) e = launch_tiles(job, st);
-  return status_of(e);
+  return status_of(launch_tiles(job, st));
 }
 
 int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float *sel_score,
@@ -204,6 +204,7 @@ int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float
   job.scores_in[0] = scores;
   job.scores_out[0] = nullptr;
   job.n_rows[0] = n_rows;
+  job.q[0] = job.w[0] = job.q_attn[0] = nullptr;
   fill_job(job, L, ws, 1);
   SelectJob sj;
   fill_select(sj, job, k);
@@ -229,7 +230,7 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   hipStream_t st = (hipStream_t)hip_stream;
   uint4 *aq = at<uint4>(ws, L.attn_q_off);
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
-  hipError_t e = launch_q_split(nullptr, nullptr, 1, 0, nullptr, &q_attn, n_heads, aq, st);
+  hipError_t e = launch_attn_q_split(&q_attn, 1, n_heads, aq, st);
   if (e == hipSuccess) e = launch_attn_rows(&s, 1, n_heads, softmax_scale, aq, part, ml, st);
   if (e == hipSuccess) e = launch_attn_combine(&s, 1, n_heads, part, ml, st);
   return status_of(e);
@@ -258,7 +259,6 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   TileJob job;
   job.mode = TileJob::kScoreSelect;
   job.n_idx_heads = n_idx_heads;
-  const float *q[CSA_MAX_SESSIONS], *w[CSA_MAX_SESSIONS], *qa[CSA_MAX_SESSIONS];
   int32_t *sel[CSA_MAX_SESSIONS];
   float *sel_score[CSA_MAX_SESSIONS];
   AttnSession at_s[CSA_MAX_SESSIONS];
@@ -269,9 +269,9 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     job.scores_in[i] = nullptr;
     job.scores_out[i] = scores + (size_t)i * L.rows_cap;
     job.n_rows[i] = s.n_rows;
-    q[i] = s.q_idx;
-    w[i] = s.w_idx;
-    qa[i] = s.q_attn;
+    job.q[i] = s.q_idx;
+    job.w[i] = s.w_idx;
+    job.q_attn[i] = s.q_attn;
     sel[i] = s.sel_idx;
     sel_score[i] = s.sel_score;
     const int32_t n_sel = (int32_t)(s.n_rows < CSA_TOPK ? s.n_rows : CSA_TOPK);
@@ -279,6 +279,8 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   }
   fill_job(job, L, ws, n_sessions);
   uint4 *aq = at<uint4>(ws, L.attn_q_off);
+  job.attn_q = aq;  // split by the score kernel
+  job.n_attn_heads = n_heads;
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
   SelectJob sj;
   fill_select(sj, job, CSA_TOPK);
@@ -297,18 +299,14 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
-    e = launch_q_split(q, w, n_sessions, n_idx_heads, const_cast<uint32_t *>(job.qsplit), qa, n_heads, aq, st);
+  if (e == hipSuccess) e = launch_tiles(job, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_tiles(job, st);
+  if (e == hipSuccess) e = launch_select(sj, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess) e = launch_select(sj, st);
-  if (e == hipSuccess) e = mark(5);
-  if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess) e = launch_attn_combine(at_s, n_sessions, n_heads, part, ml, st);
-  if (e == hipSuccess) e = mark(7);
+  if (e == hipSuccess) e = mark(5);
   return status_of(e);
 }
 

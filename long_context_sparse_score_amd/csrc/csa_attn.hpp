@@ -85,6 +85,39 @@ __device__ __forceinline__ void split3_bf16(float x, __bf16 &t0, __bf16 &t1, __b
   t2 = (__bf16)(r1 - (float)t1);
 }
 
+// Split task t < kAttnQVecs / 3 of a session's attention query q[n][512]
+// (n = n_heads; heads past n are zero): the three terms of
+//   q[16(w%4) + l%16][128(w/4) + 32s + 8(l/16) + i], i < 8,
+// for w = t / 256, s = (t / 64) % 4, l = t % 64, stored at
+// dst[attn_q_index(w, s, term, l)].
+__device__ __forceinline__ void attn_q_split_task(const float *__restrict__ qa, int n_heads, uint4 *__restrict__ dst,
+                                                  int t) {
+  const int lane = t % 64, s = (t / 64) % 4, wave = t / 256;
+  const int h = 16 * (wave & 3) + (lane & 15);
+  const int d0 = 128 * (wave >> 2) + 32 * s + 8 * (lane >> 4);
+  const bool live = h < n_heads;
+  const float *src = qa + (size_t)(live ? h : 0) * kKvDim + d0;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = src[i];
+    x[i] = live ? v : 0.0f;
+  }
+  v8bf t0, t1, t2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __bf16 a0, a1, a2;
+    split3_bf16(x[i], a0, a1, a2);
+    t0[i] = a0;
+    t1[i] = a1;
+    t2[i] = a2;
+  }
+  dst[attn_q_index(wave, s, 0, lane)] = __builtin_bit_cast(uint4, t0);
+  dst[attn_q_index(wave, s, 1, lane)] = __builtin_bit_cast(uint4, t1);
+  dst[attn_q_index(wave, s, 2, lane)] = __builtin_bit_cast(uint4, t2);
+}
+constexpr int kAttnQTasks = kAttnQVecs / 3;  // 4096
+
 // This lane's query terms: quarter 2hv + kl, K step s, term t.
 struct AttnQuery {
   v8bf a[2][4][3];

@@ -36,8 +36,12 @@ struct TileJob {
   float *scores_out[CSA_MAX_SESSIONS];       // kScore, kScoreSelect
   int64_t n_rows[CSA_MAX_SESSIONS];
   int hd[CSA_MAX_SESSIONS];
-  const uint32_t *qsplit;  // query split, [session][kQSplitBytes / 4]
-  uint64_t *heads;         // [session][heads_stride]: per tile its top-hd keys, sorted
+  const float *q[CSA_MAX_SESSIONS];       // indexer query [n_idx_heads][128] (scoring modes)
+  const float *w[CSA_MAX_SESSIONS];       // indexer head weights
+  const float *q_attn[CSA_MAX_SESSIONS];  // attention query [n_attn_heads][512] (when attn_q)
+  uint4 *attn_q;                          // attention query split, [session][kAttnQVecs], or null
+  int n_attn_heads;
+  uint64_t *heads;  // [session][heads_stride]: per tile its top-hd keys, sorted
   int64_t heads_stride;
 };
 
@@ -82,11 +86,10 @@ constexpr int kAttnGroupCount = 32;
 
 hipError_t launch_dequant_idx(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
 hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
-// Query split of every session (csa_qsplit.hip): q[i], w[i] -> out (skipped
-// when q is null) and, when q_attn is given, the attention query -> attn_out.
-hipError_t launch_q_split(const float *const *q, const float *const *w, int n_sessions, int n_heads,
-                          uint32_t *out, const float *const *q_attn, int n_attn_heads, uint4 *attn_out,
-                          hipStream_t st);
+// Attention query split of every session (csa_qsplit.hip): q_attn[i] ->
+// attn_out + i * kAttnQVecs.
+hipError_t launch_attn_q_split(const float *const *q_attn, int n_sessions, int n_attn_heads, uint4 *attn_out,
+                               hipStream_t st);
 hipError_t launch_tiles(const TileJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);
 // Attention partials of the rows sel_idx[0..n_sel) of every session, one

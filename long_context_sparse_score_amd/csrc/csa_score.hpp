@@ -14,8 +14,8 @@
 // split into kTerms fp6 (E2M3) terms with their own E8M0 block scales,
 //     q = sum_t qt + r,   |r| <= 2^-19.6 * blockmax|q| per element,
 // and the dot product is the fp32 accumulation of the kTerms exact-product
-// MFMAs (q_split_kernel builds the terms once per call).  Every product is
-// exact; accumulation is fp32 inside the matrix core.
+// MFMAs.  Every product is exact; accumulation is fp32 inside the matrix
+// core.  Each lane splits its own fragment in registers (split_qfrag).
 //
 // Lane layout of the 16x16x128 instruction (verified on MI355X): lane l holds
 // A row l%16 and B column l%16, for K elements [32*(l/16), 32*(l/16)+32),
@@ -40,11 +40,6 @@ constexpr int kMaxGroups = 4;    // 16-head groups (64 indexer heads)
 constexpr int kFmtFp6 = 2;       // MFMA operand format codes: E2M3
 constexpr int kFmtFp4 = 4;       // E2M1
 
-// Per-session query split in the workspace: [group][term][lane][8 dwords],
-// dwords 0..5 = 32 fp6 codes, dword 6 = E8M0 scale byte; then 64 weights.
-constexpr int kQSplitDwords = kMaxGroups * kTerms * 64 * 8;
-constexpr int kQSplitBytes = kQSplitDwords * 4 + 64 * 4;
-
 constexpr int kScaleWords = (kTerms + 3) / 4;  // A scale bytes packed four per register
 
 template <int G>
@@ -54,43 +49,64 @@ struct QFrag {
   float w[G][4];
 };
 
-// Load this lane's query fragments of groups [g0, g0 + G) (written by
-// q_split_kernel).
-template <int G>
-__device__ __forceinline__ void load_qfrag(QFrag<G> &q, const uint32_t *__restrict__ qs, int lane, int g0) {
-  const float *wp = reinterpret_cast<const float *>(qs + kQSplitDwords) + 16 * g0;
-  qs += g0 * kTerms * 64 * 8;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int w = 0; w < kScaleWords; ++w) q.scw[g][w] = 0;
-#pragma unroll
-    for (int t = 0; t < kTerms; ++t) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(qs + ((g * kTerms + t) * 64 + lane) * 8);
-      const uint4 lo = p[0], hi = p[1];
-      q.a[g][t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
-      q.scw[g][t / 4] |= (int)((hi.z & 255u) << (8 * (t % 4)));
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) q.w[g][v] = wp[16 * g + 4 * (lane >> 4) + v];
-  }
-}
+typedef float v16f_q __attribute__((ext_vector_type(16)));
+typedef float v32f_q __attribute__((ext_vector_type(32)));
+typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 
-// Complete the query loads at this point: an empty asm statement that reads
-// and writes every fragment register makes the compiler wait for the loads
-// here.  Without it the scheduler may sink the loads past an explicit wait
-// and the compiler's own waits then sit inside the streaming loop, where a
-// load-counter wait also drains the chunks in flight.
-template <int G>
-__device__ __forceinline__ void pin_qfrag(QFrag<G> &q) {
+// This lane's query fragment of head group g, split from the fp32 query
+// q[n_heads][128] and weights w[n_heads]: head h = 16 g + l%16, values
+// [32(l/16), +32) (the lane's A operand rows and K slice), and the weights
+// of heads 16 g + 4(l/16) + v (the lane's result rows).  Heads past n_heads
+// get zero terms and weights.  With r the residual (initially the values):
+//   E   = smallest exponent with max|r| / 2^E <= 7.5 (E2M3's largest value),
+//         at least -126,
+//   q_t = RNE_E2M3(r / 2^E) * 2^E,   r <- r - q_t   (exact in fp32),
+// repeated kTerms times: the block maximum of r shrinks by at least 2^-3.9
+// per term, so after 5 terms every element is within 2^-19.6 of the block
+// maximum of q.  The conversions are gfx950's scaled fp6 instructions
+// (round to nearest even, saturating; verified on MI355X): the packing one
+// interleaves its two 16-value inputs (even, odd positions), so value i
+// lands at bit 6i, the MFMA operand order; the unpacking one returns the
+// exact term values for the residual.
+__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float *__restrict__ qh,
+                                            const float *__restrict__ wh, int n_heads, int g, int lane) {
+  const int h = 16 * g + (lane & 15);
+  const bool live = h < n_heads;
+  const float *src = qh + (size_t)(live ? h : 0) * 128 + 32 * (lane >> 4);
+  v16f_q re, ro;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int i = 0; i < 16; ++i) {
+    const float a = src[2 * i], b = src[2 * i + 1];  // clamped head: no branch around the loads
+    re[i] = live ? a : 0.0f;
+    ro[i] = live ? b : 0.0f;
+  }
 #pragma unroll
-    for (int t = 0; t < kTerms; ++t) asm volatile("" : "+v"(q.a[g][t]));
+  for (int w = 0; w < kScaleWords; ++w) q.scw[0][w] = 0;
 #pragma unroll
-    for (int w = 0; w < kScaleWords; ++w) asm volatile("" : "+v"(q.scw[g][w]));
+  for (int t = 0; t < kTerms; ++t) {
+    float amax = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(q.w[g][v]));
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(re[i]), fabsf(ro[i])));
+    const float am = amax > 0.0f ? amax : 1.0f;  // a zero block keeps scale 2^0 and zero codes
+    int E = ilogbf(am) - 2;                         // am / 2^E in [4, 8)
+    if (ldexpf(am, -E) > 7.5f) E += 1;
+    E = E < -126 ? -126 : (E > 127 ? 127 : E);
+    const float sc = ldexpf(1.0f, E);
+    const v6u_q c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(re, ro, sc);
+    const v32f_q d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      re[i] -= d[2 * i];
+      ro[i] -= d[2 * i + 1];
+    }
+    q.a[0][t] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4], (int)c[5], 0, 0};
+    q.scw[0][t / 4] |= (E + 127) << (8 * (t % 4));
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int hw = 16 * g + 4 * (lane >> 4) + v;
+    const float x = wh[hw < n_heads ? hw : n_heads - 1];
+    q.w[0][v] = hw < n_heads ? x : 0.0f;
   }
 }
 

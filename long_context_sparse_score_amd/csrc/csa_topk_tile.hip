@@ -16,6 +16,7 @@
 // exactly against each other (an exact k-th selection replaces theta when
 // they overflow the candidate buffer).
 // The global selection over the heads is in csa_merge.hip.
+#include "csa_attn.hpp"
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "csa_score.hpp"
@@ -26,22 +27,24 @@ namespace csa {
 
 struct TileSession {
   const uint8_t *idx_rows;
-  const float *scores_in;
-  float *scores_out;
+  float *scores;        // written (scoring modes) or read (array mode)
+  const float *q, *w;   // indexer query and head weights
+  const float *q_attn;  // attention query
   int64_t n_rows;
   int hd;
 };
 
 struct TileArgs {
   TileSession s[CSA_MAX_SESSIONS];
-  const uint32_t *qsplit;  // [session][kQSplitBytes / 4]
-  uint64_t *heads;         // [session][heads_stride]
+  uint4 *attn_q;  // attention query split [session][kAttnQVecs], or null
+  uint64_t *heads;  // [session][heads_stride]
   int64_t heads_stride;
   int tile_rows;
+  int n_idx_heads, n_attn_heads;
+  int write_heads;  // scoring launches: also find and write the tile heads
 };
 static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
 
-enum { kModeScore = 0, kModeScoreSelect = 1, kModeArraySelect = 2 };
 
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
@@ -209,10 +212,12 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, int b, RowOperand 
 // w % G and chunks [G (w / G), G (w / G) + G) of the step, so a wave holds
 // the query terms of 16 heads.  The group partials meet in LDS and are
 // summed, group by group in a fixed association, one step later.
-template <int G>
-__device__ __forceinline__ uint32_t score_tile(const uint32_t *__restrict__ qsplit, const uint8_t *__restrict__ idx_rows,
-                                           int64_t row0, int64_t n, int rows, float *__restrict__ out,
-                                           TileShared &sh) {
+// `pre` runs once the first steps are in flight.
+template <int G, class Pre>
+__device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
+                                               int n_idx_heads, const uint8_t *__restrict__ idx_rows, int64_t row0,
+                                               int64_t n, int rows, float *__restrict__ out, TileShared &sh,
+                                               Pre pre) {
   static_assert(G == 1 || G == 2 || G == 4, "head groups per workgroup");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = wave % G, rl = wave / G;
@@ -251,9 +256,11 @@ __device__ __forceinline__ uint32_t score_tile(const uint32_t *__restrict__ qspl
 #pragma unroll
   for (int s = 0; s < kRingDepth - 1; ++s)
     if (s < ns) fill(s);
+  pre();
+  // the query terms, split while the first steps are in flight (the
+  // query loads complete before the loop, so no wait for them sits inside)
   QFrag<1> q;
-  load_qfrag<1>(q, qsplit, lane, grp);
-  pin_qfrag<1>(q);  // no wait for the query inside the loop
+  split_qfrag(q, qh, wh, n_idx_heads, grp, lane);
 
   for (int s = 0; s < ns; ++s) {
     int later = 0;
@@ -289,7 +296,11 @@ __device__ __forceinline__ uint32_t score_tile(const uint32_t *__restrict__ qspl
   return omax;
 }
 
-template <int G, int MODE>
+// ARRAY: the scores are given (csa_topk).  The scoring launches of csa_score
+// and of the decode step run the same code (the heads are a runtime choice),
+// so both produce the same bits: the scaled matrix-core accumulation may
+// round differently under a different instruction schedule.
+template <int G, bool ARRAY>
 __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a) {
   const int sess = blockIdx.y;
   const TileSession &S = a.s[sess];
@@ -301,12 +312,25 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   __shared__ TileShared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t o = 0;  // largest score part of this thread's positions
-  if constexpr (MODE != kModeArraySelect) {
-    o = score_tile<G>(a.qsplit + (size_t)sess * (kQSplitBytes / 4), S.idx_rows, row0, n, rows, S.scores_out + row0, sh);
-    if constexpr (MODE == kModeScore) return;
+  if constexpr (!ARRAY) {
+    uint4 *const aq = a.attn_q ? a.attn_q + (size_t)sess * kAttnQVecs : nullptr;
+    const float *const qa = S.q_attn;
+    const int n_attn_heads = a.n_attn_heads;
+    auto attn_split = [=]() __attribute__((always_inline)) {
+      if (aq) {
+        // this workgroup's share of the session's attention query split
+        // (read by the selection kernel that follows)
+        const int nt = (int)((n + T - 1) / T);
+        const int per = (kAttnQTasks + nt - 1) / nt;
+        const int t1 = ((int)blockIdx.x + 1) * per < kAttnQTasks ? ((int)blockIdx.x + 1) * per : kAttnQTasks;
+        for (int t = (int)blockIdx.x * per + tid; t < t1; t += kTileThreads) attn_q_split_task(qa, n_attn_heads, aq, t);
+      }
+    };
+    o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, S.scores + row0, sh, attn_split);
+    if (!a.write_heads) return;
   } else {
     // the given scores into LDS, four loads in flight per thread
-    const float *src = S.scores_in + row0;
+    const float *src = S.scores + row0;
     for (int j0 = 0; j0 < rows; j0 += 4 * kTileThreads) {
       float v[4];
 #pragma unroll
@@ -331,14 +355,13 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
 
 // ---------------------------------------------------------------- launcher
 
-template <int MODE>
-static hipError_t launch_tile_mode(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
+static hipError_t launch_scoring(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
   // three groups run as four: the query split holds zero terms and weights
   // for heads past n_idx_heads, which add exact zeros
   switch (groups) {
-    case 1: tile_kernel<1, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
-    case 2: tile_kernel<2, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
-    default: tile_kernel<4, MODE><<<grid, kTileThreads, 0, st>>>(a); break;
+    case 1: tile_kernel<1, false><<<grid, kTileThreads, 0, st>>>(a); break;
+    case 2: tile_kernel<2, false><<<grid, kTileThreads, 0, st>>>(a); break;
+    default: tile_kernel<4, false><<<grid, kTileThreads, 0, st>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -347,21 +370,29 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   TileArgs a;
   int64_t max_rows = 0;
   for (int i = 0; i < job.n_sessions; ++i) {
-    a.s[i] = TileSession{job.idx_rows[i], job.scores_in[i], job.scores_out[i], job.n_rows[i], job.hd[i]};
+    float *scores = job.mode == TileJob::kArraySelect ? const_cast<float *>(job.scores_in[i]) : job.scores_out[i];
+    a.s[i] = TileSession{job.idx_rows[i], scores, job.q[i], job.w[i], job.q_attn[i], job.n_rows[i], job.hd[i]};
     max_rows = job.n_rows[i] > max_rows ? job.n_rows[i] : max_rows;
   }
   if (max_rows == 0) return hipSuccess;
-  a.qsplit = job.qsplit;
+  a.attn_q = job.mode == TileJob::kScoreSelect ? job.attn_q : nullptr;
+  a.n_idx_heads = job.n_idx_heads;
+  a.n_attn_heads = job.n_attn_heads;
   a.heads = job.heads;
   a.heads_stride = job.heads_stride;
   a.tile_rows = job.tile_rows;
   const int groups = (job.n_idx_heads + 15) / 16;
   dim3 grid((unsigned)((max_rows + job.tile_rows - 1) / job.tile_rows), (unsigned)job.n_sessions);
   switch (job.mode) {
-    case TileJob::kScore: return launch_tile_mode<kModeScore>(a, grid, groups, st);
-    case TileJob::kScoreSelect: return launch_tile_mode<kModeScoreSelect>(a, grid, groups, st);
+    case TileJob::kScore:
+      a.write_heads = 0;
+      return launch_scoring(a, grid, groups, st);
+    case TileJob::kScoreSelect:
+      a.write_heads = 1;
+      return launch_scoring(a, grid, groups, st);
     default:
-      tile_kernel<1, kModeArraySelect><<<grid, kTileThreads, 0, st>>>(a);
+      a.write_heads = 1;
+      tile_kernel<1, true><<<grid, kTileThreads, 0, st>>>(a);
       return hipGetLastError();
   }
 }
