@@ -69,11 +69,17 @@ __device__ __forceinline__ size_t attn_q_index(int wave, int s, int t, int lane)
   return ((size_t)(wave * 4 + s) * 3 + t) * 64 + lane;
 }
 
+// Packed rows staged in LDS, realigned: slot i holds its row's 583 bytes
+// from byte 0.
+constexpr int kRawStride = 592;  // bytes per slot: 148 dwords
+constexpr int kRawRows = 32;     // rows staged at once
+
 struct AttnStage {
   float kv[kAttnBatch][kKvLdsStride];       // decoded rows of the batch
   float lg[CSA_MAX_HEADS][kAttnBatch + 1];  // logits of the batch
   float red[4][64][4];                      // logits of quarters 2 + 3 [g]
   int32_t row[kAttnBatch];                  // KV row, or -1 (padding)
+  uint32_t raw[kRawRows][kRawStride / 4];   // staged packed rows
 };
 
 // x = t0 + t1 + t2 + r: three bf16 terms, each the round-to-nearest-even of
@@ -123,7 +129,7 @@ struct AttnQuery {
   v8bf a[2][4][3];
 };
 
-__device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *__restrict__ qs) {
+__device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *qs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = wave & 3, hv = wave >> 2;
 #pragma unroll
@@ -135,22 +141,6 @@ __device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *__res
         const uint4 v = qs[attn_q_index(g + 4 * (2 * hv + kl), s, t, lane)];
         q.a[kl][s][t] = __builtin_bit_cast(v8bf, v);
       }
-}
-
-// The two bytes that determine decoded value i of a packed KV row (code and
-// block scale, or the two bytes of an FP16 RoPE value), and the value from
-// them.  Callers load the bytes of all their values first and decode after,
-// so the loads are in flight together.
-__device__ __forceinline__ void kv_load(const uint8_t *__restrict__ p, int i, uint32_t &b0, uint32_t &b1) {
-  const bool nope = i < kKvNope;
-  const int t = 2 * (i - kKvNope);
-  b0 = p[nope ? i : kKvNope + t];
-  b1 = p[nope ? kKvNope + 128 + (i >> 6) : kKvNope + t + 1];
-}
-__device__ __forceinline__ float kv_decode(int i, uint32_t b0, uint32_t b1) {
-  const float vn = e4m3_value(b0) * ue8m0_scale(b1);
-  const float vr = f16_value(b0 | (b1 << 8));
-  return i < kKvNope ? vn : vr;
 }
 
 // Per-wave state of a group: accumulator tiles (heads 16g + 4(l/16) + v,
@@ -170,12 +160,56 @@ __device__ __forceinline__ void attn_init(AttnState &S) {
   S.l = 0.0f;
 }
 
+// Stage rows[0..m) (valid KV row indices, m <= kRawRows) into st.raw: slot
+// i receives row rows[i]'s bytes from byte 0 (146 dwords).  Lane j of the
+// wave builds dwords j, j + 64, j + 128 of a row from the two aligned dwords
+// that hold them (v_alignbyte); only dwords holding a byte of the row are
+// read, so nothing past the buffer's last byte is touched.  Wave w copies
+// rows w, w + 8, ..., two rows per pass, all loads first.  All threads call
+// it; the caller synchronizes before reading the slots.
+constexpr int kRawDwords = (kKvRowBytes + 3) / 4;  // 146
+__device__ __forceinline__ void attn_stage_raw(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
+                                               AttnStage &st) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kWaves = kAttnThreads / 64;
+  constexpr int kPass = 2;
+  for (int i0 = wave; i0 < m; i0 += kPass * kWaves) {
+    uint32_t lo[kPass][3], hi[kPass][3], sh[kPass];
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int i = i0 + kWaves * u;
+      const int32_t r = __builtin_amdgcn_readfirstlane(rows[i < m ? i : i0]);
+      const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
+      const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
+      const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);  // stays a global pointer
+      const int last = (int)(mis + kKvRowBytes - 1) >> 2;                 // dword of the last byte
+      sh[u] = 8u * mis;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        lo[u][k] = a0[j < last ? j : last];  // clamped: no branch around the loads
+        hi[u][k] = a0[j + 1 < last ? j + 1 : last];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int i = i0 + kWaves * u;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        const uint32_t w = (uint32_t)(((uint64_t)hi[u][k] << 32 | lo[u][k]) >> sh[u]);
+        if (i < m && j < kRawDwords) st.raw[i][j] = w;
+      }
+    }
+  }
+}
+
 // One batch: rows st.row[0..kAttnBatch) (-1 = padding) are decoded into
 // st.kv, their logits go to st.lg, and this wave's running softmax state and
 // accumulators are updated.  All kAttnThreads threads call it; it starts and
 // ends with a barrier.
-__device__ __forceinline__ void attn_batch(const uint4 *__restrict__ qsplit, AttnState &S, AttnStage &st,
-                                           const uint8_t *__restrict__ kv_rows, float scale) {
+__device__ __forceinline__ void attn_batch(const uint4 *qsplit, AttnState &S, AttnStage &st, int slot0,
+                                           float scale) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __syncthreads();  // st.row written
   // the query terms (L2-resident, shared by every group) are loaded with the
@@ -183,26 +217,42 @@ __device__ __forceinline__ void attn_batch(const uint4 *__restrict__ qsplit, Att
   AttnQuery q;
   load_attn_query(q, qsplit);
   {
-    // decode: 32 rows x 512 values, 16 per thread, all loads first.  A wave
-    // covers 64 consecutive values of one row, so the row (and the RoPE
-    // test) is uniform per wave and lives in scalar registers.
+    // decode: 16 rows x 512 values, 16 per thread, all LDS reads first.  Wave
+    // w takes values [64w, 64w + 64) of every row (one per lane): waves 0..6
+    // hold E4M3 values of one scale block per row, wave 7 the FP16 RoPE
+    // values, so the branch is uniform.  The conversions are gfx950's
+    // v_cvt_scalef32_f32_fp8 (code x scale, exact; checked on MI355X on all
+    // 256 codes, scale bytes 0..255 included) and v_cvt_f32_f16 (exact).
     constexpr int U = kAttnBatch * kKvDim / kAttnThreads;
+    static_assert(U == kAttnBatch, "one value per lane and row");
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t bb[U];
+    const int col = 64 * wv + lane;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(&st.raw[slot0][0]);
+    float x[U];
+    if (wv < kKvNope / 64) {
+      uint32_t code[U], sb[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e0 = 64 * wv + kAttnThreads * u;  // first value of this wave
-      const int32_t r = __builtin_amdgcn_readfirstlane(st.row[e0 / kKvDim]);
-      uint32_t b0, b1;
-      kv_load(kv_rows + (size_t)(uint32_t)max(r, 0) * kKvRowBytes, e0 % kKvDim + lane, b0, b1);
-      bb[u] = b0 | (b1 << 8);
+      for (int u = 0; u < U; ++u) {
+        code[u] = base[u * kRawStride + col];
+        sb[u] = base[u * kRawStride + kKvNope + 128 + wv];  // the block's scale byte (same in every lane)
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t e = __builtin_amdgcn_readfirstlane(sb[u]);
+        x[u] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)code[u], ue8m0_scale(e), 0);
+      }
+    } else {
+      uint32_t h[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        h[u] = *reinterpret_cast<const uint16_t *>(base + u * kRawStride + kKvNope + 2 * (col - kKvNope));
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)h[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e0 = 64 * wv + kAttnThreads * u;
-      const int32_t r = __builtin_amdgcn_readfirstlane(st.row[e0 / kKvDim]);
-      const float x = kv_decode(e0 % kKvDim + lane, bb[u] & 255u, bb[u] >> 8);
-      st.kv[e0 / kKvDim][e0 % kKvDim + lane] = r >= 0 ? x : 0.0f;
+      const int32_t r = __builtin_amdgcn_readfirstlane(st.row[u]);
+      st.kv[u][col] = r >= 0 ? x[u] : 0.0f;
     }
   }
   __syncthreads();
@@ -371,16 +421,19 @@ __device__ __forceinline__ void attn_order(const int32_t *keys, const int32_t *r
 
 // Attention over a group's rows (in order) -> its partial.  All threads
 // call it.
-__device__ __forceinline__ void attn_group_rows(const uint4 *__restrict__ qsplit, AttnStage &st, const int32_t *rows,
+__device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &st, const int32_t *rows,
                                                 int m,
                                                 const uint8_t *__restrict__ kv_rows, float scale, int n_heads,
                                                 float *__restrict__ part, float *__restrict__ ml) {
   AttnState S;
   attn_init(S);
   for (int b0 = 0; b0 < m; b0 += kAttnBatch) {
-    if (threadIdx.x < kAttnBatch)
-      st.row[threadIdx.x] = b0 + (int)threadIdx.x < m ? rows[b0 + threadIdx.x] : -1;
-    attn_batch(qsplit, S, st, kv_rows, scale);
+    const int slot0 = b0 & (kRawRows - 1);
+    if (slot0 == 0)  // stage the next kRawRows rows (the previous batch ended with a barrier)
+      attn_stage_raw(kv_rows, rows + b0, m - b0 < kRawRows ? m - b0 : kRawRows, st);
+    if (threadIdx.x < kAttnBatch) st.row[threadIdx.x] = b0 + (int)threadIdx.x < m ? rows[b0 + threadIdx.x] : -1;
+    // starts with a barrier: rows staged, st.row written
+    attn_batch(qsplit, S, st, slot0, scale);
   }
   attn_store(S, n_heads, part, ml);
 }
