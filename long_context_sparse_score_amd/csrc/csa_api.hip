@@ -43,7 +43,9 @@ Layout make_layout(int64_t max_rows, int n_sessions) {
 }
 
 // Tile rows: as large as possible (fewer heads to merge) while the launch
-// keeps at least ~512 workgroups (two per compute unit).
+// keeps at least ~512 workgroups (two per compute unit).  More, smaller
+// tiles pay the per-tile start (query split, first loads) and heads twice
+// per slot, which costs more than they win back by balancing.
 int choose_tile_rows(int64_t total_rows) {
   int T = kMinTileRows;
   while (T < kMaxTileRows && total_rows / (2 * (int64_t)T) >= 512) T *= 2;

@@ -14,13 +14,14 @@ namespace csa {
 // Tile of the score kernel: rows scored by one workgroup and kept in LDS.
 constexpr int kMaxTileRows = 4096;
 constexpr int kMinTileRows = 512;
-// Heads per tile: the tile's exact top-H keys, H in {16, 32, 64}.
+// Heads per tile: the tile's exact top-H keys, H in {8, 16, 32, 64}.
+constexpr int kMinTileHeads = 8;
 constexpr int kMaxTileHeads = 64;
 
 // Heads per tile for a session of nt tiles: enough that the heads of all
 // tiles number at least ~2048 (so few tiles hold more winners than heads).
 inline int heads_per_tile(int64_t nt) {
-  int hd = 16;
+  int hd = kMinTileHeads;
   while (hd < kMaxTileHeads && nt * hd < 2048) hd *= 2;
   return hd;
 }

@@ -40,8 +40,8 @@ constexpr int kSelRegHeads = kSelThreads * kSelKPT;  // 8192
 constexpr int kSelBins = 2 * kSelThreads;             // histogram bins per pass
 constexpr int kSelCap = 4096;                         // candidates held in LDS
 constexpr int kSelTarget = 1024;                      // candidates at which G is good enough
-constexpr int kSelMaxFull = 128;                      // full tiles listed (at most kSelTarget / 16)
-constexpr int kSelMaxRegTiles = kSelRegHeads / 16;
+constexpr int kSelMaxFull = kSelTarget / kMinTileHeads;  // full tiles listed (each holds >= hd heads >= G)
+constexpr int kSelMaxRegTiles = kSelRegHeads / kMinTileHeads;
 
 struct SelSessionArgs {
   const float *scores;

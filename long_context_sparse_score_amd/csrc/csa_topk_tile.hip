@@ -6,7 +6,7 @@
 // tile_kernel (one workgroup per T-row tile of one session):
 //   1. scores the tile's rows on the matrix cores (csa_score.hpp) into LDS
 //      and writes them out (or reads a given score array);
-//   2. finds the tile's exact top-hd keys ("heads", hd in {16, 32, 64}) and
+//   2. finds the tile's exact top-hd keys ("heads", hd in {8, 16, 32, 64}) and
 //      writes them sorted descending to heads[tile][hd] (0-padded).
 // Step 2 first bounds the hd-th key from below without sorting the tile:
 // every wave splits its 64 lanes into hd groups and takes the smallest group
@@ -46,12 +46,14 @@ struct TileArgs {
 static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
 
 
+// Two 4-wave workgroups per compute unit.
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
 
 constexpr int kStepChunks = kTileWaves;                  // one 64-row chunk per wave and step
 constexpr int kStepRows = kStepChunks * kChunkRows;      // 256
 constexpr int kStepBytes = kStepChunks * kChunkBytes;    // 17408 (16-byte multiple)
+static_assert(kStepRows == kTileThreads, "one combined row per thread and step");
 constexpr int kRingDepth = 3;                            // steps resident: D - 1 in flight
 constexpr int kTileCandCap = 256;                        // keys >= theta ranked directly
 static_assert(kRingDepth >= 2 && kRingDepth <= 4, "ring depth");
