@@ -66,29 +66,9 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const Att
   const int e = blockIdx.x * kCombineThreads + threadIdx.x;  // head * 512 + dimension
   const int h = e / kKvDim;
   if (h >= a.n_heads) return;
-  const float *ml = a.ml + (size_t)sess * kAttnMlFloats;
-  const float *part = a.part + (size_t)sess * kAttnPartFloats;
-  float mb[kAttnGroups], lb[kAttnGroups], xb[kAttnGroups];
-#pragma unroll
-  for (int b = 0; b < kAttnGroups; ++b) {
-    mb[b] = ml[((size_t)b * CSA_MAX_HEADS + h) * 2];
-    lb[b] = ml[((size_t)b * CSA_MAX_HEADS + h) * 2 + 1];
-    xb[b] = part[(size_t)b * CSA_MAX_HEADS * kKvDim + e];
-  }
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int b = 0; b < kAttnGroups; ++b) M = fmaxf(M, mb[b]);
-  float L = 0.0f, X = 0.0f;
-  if (M != -__builtin_inff()) {
-#pragma unroll
-    for (int b = 0; b < kAttnGroups; ++b) {
-      const float w = mb[b] == -__builtin_inff() ? 0.0f : __expf(mb[b] - M);  // an empty group adds nothing
-      L += w * lb[b];
-      X += mb[b] == -__builtin_inff() ? 0.0f : w * xb[b];
-    }
-  }
-  S.out[e] = L > 0.0f ? X / L : 0.0f;
-  if (S.lse && e % kKvDim == 0) S.lse[h] = L > 0.0f ? M + logf(L) : -__builtin_inff();
+  float lse;
+  S.out[e] = attn_merge_element(a.ml + (size_t)sess * kAttnMlFloats, a.part + (size_t)sess * kAttnPartFloats, h, e, lse);
+  if (S.lse && e % kKvDim == 0) S.lse[h] = lse;
 }
 
 // ---------------------------------------------------------------- launchers

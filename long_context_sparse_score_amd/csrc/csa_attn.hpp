@@ -4,7 +4,7 @@
 //
 // The selected rows are partitioned into kAttnGroups fixed groups by a hash
 // of the row index; a workgroup takes one group, visits its rows in rank
-// (position) order, 16 at a time, and keeps for every head h
+// (position) order, 32 at a time, and keeps for every head h
 //   m_h = max logit seen, l_h = sum exp(l - m_h), acc_h[d] = sum exp(l - m_h) kv[d]
 // (rescaled when m_h grows).  It writes (m, l, acc) as the group's partial;
 // attn_combine merges the groups:
@@ -31,11 +31,11 @@
 // A workgroup is 8 waves; wave w takes head group g = w%4 (heads
 // 16g..16g+15) and half hv = w/4:
 //   logits: m = head, n = row, k = dimension; the wave covers dimension
-//           quarters 2hv and 2hv+1 (four K steps of 32 each) for the 16 rows
-//           of the batch; per row the four quarters are summed as
-//           (q0 + q1) + (q2 + q3), the second pair through LDS.
-//   P V:    m = head, n = dimension, k = row (the batch's 16 rows in k < 16,
-//           zeros above); the wave covers the 128 dimensions of chunks 2hv
+//           quarters 2hv and 2hv+1 (four K steps of 32 each) for the two
+//           16-row tiles of the batch; per row the four quarters are summed
+//           as (q0 + q1) + (q2 + q3), the pairs meeting in LDS.
+//   P V:    m = head, n = dimension, k = row (the batch's 32 rows); the
+//           wave covers the 128 dimensions of chunks 2hv
 //           and 2hv+1 (eight 16-wide tiles each).
 #pragma once
 
@@ -50,7 +50,7 @@ typedef float v4f_attn __attribute__((ext_vector_type(4)));
 constexpr int kKvDim = 512;
 constexpr int kAttnThreads = 512;
 constexpr int kAttnGroups = 32;
-constexpr int kAttnBatch = 16;  // rows per matrix-core batch
+constexpr int kAttnBatch = 32;  // rows per matrix-core batch (the K of the P V product)
 constexpr int kKvLdsStride = kKvDim + 4;
 
 // Group of a selected row (also the workgroup of the fused selection that
@@ -77,7 +77,7 @@ constexpr int kRawRows = 32;     // rows staged at once
 struct AttnStage {
   float kv[kAttnBatch][kKvLdsStride];       // decoded rows of the batch
   float lg[CSA_MAX_HEADS][kAttnBatch + 1];  // logits of the batch
-  float red[4][64][4];                      // logits of quarters 2 + 3 [g]
+  float red[2][4][64][4];                   // half-sums of the logits [half][g]
   int32_t row[kAttnBatch];                  // KV row, or -1 (padding)
   uint32_t raw[kRawRows][kRawStride / 4];   // staged packed rows
 };
@@ -217,97 +217,105 @@ __device__ __forceinline__ void attn_batch(const uint4 *qsplit, AttnState &S, At
   AttnQuery q;
   load_attn_query(q, qsplit);
   {
-    // decode: 16 rows x 512 values, 16 per thread, all LDS reads first.  Wave
+    // decode: 32 rows x 512 values in two passes of 16, all LDS reads of a
+    // pass first.  Wave
     // w takes values [64w, 64w + 64) of every row (one per lane): waves 0..6
     // hold E4M3 values of one scale block per row, wave 7 the FP16 RoPE
     // values, so the branch is uniform.  The conversions are gfx950's
     // v_cvt_scalef32_f32_fp8 (code x scale, exact; checked on MI355X on all
     // 256 codes, scale bytes 0..255 included) and v_cvt_f32_f16 (exact).
-    constexpr int U = kAttnBatch * kKvDim / kAttnThreads;
-    static_assert(U == kAttnBatch, "one value per lane and row");
+    static_assert(kAttnThreads == kKvDim, "one value per lane and row");
+    constexpr int U = 16;  // rows per pass
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int col = 64 * wv + lane;
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(&st.raw[slot0][0]);
-    float x[U];
-    if (wv < kKvNope / 64) {
-      uint32_t code[U], sb[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        code[u] = base[u * kRawStride + col];
-        sb[u] = base[u * kRawStride + kKvNope + 128 + wv];  // the block's scale byte (same in every lane)
+    for (int u0 = 0; u0 < kAttnBatch; u0 += U) {
+      const uint8_t *base = reinterpret_cast<const uint8_t *>(&st.raw[slot0 + u0][0]);
+      float x[U];
+      if (wv < kKvNope / 64) {
+        uint32_t code[U], sb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          code[u] = base[u * kRawStride + col];
+          sb[u] = base[u * kRawStride + kKvNope + 128 + wv];  // the block's scale byte (same in every lane)
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t e = __builtin_amdgcn_readfirstlane(sb[u]);
+          x[u] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)code[u], ue8m0_scale(e), 0);
+        }
+      } else {
+        uint32_t h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          h[u] = *reinterpret_cast<const uint16_t *>(base + u * kRawStride + kKvNope + 2 * (col - kKvNope));
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)h[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t e = __builtin_amdgcn_readfirstlane(sb[u]);
-        x[u] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)code[u], ue8m0_scale(e), 0);
+        const int32_t r = __builtin_amdgcn_readfirstlane(st.row[u0 + u]);
+        st.kv[u0 + u][col] = r >= 0 ? x[u] : 0.0f;
       }
-    } else {
-      uint32_t h[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        h[u] = *reinterpret_cast<const uint16_t *>(base + u * kRawStride + kKvNope + 2 * (col - kKvNope));
-#pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)h[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t r = __builtin_amdgcn_readfirstlane(st.row[u]);
-      st.kv[u][col] = r >= 0 ? x[u] : 0.0f;
     }
   }
   __syncthreads();
   const int g = wave & 3, hv = wave >> 2;
-  // logits of the batch's 16 rows, this wave's two dimension quarters
-  v4f_attn c[2];
+  // logits of the batch's 32 rows (two 16-row tiles nt), this wave's two
+  // dimension quarters; per row the four quarters are summed as
+  // (q0 + q1) + (q2 + q3), wave half hv finishing row tile nt = hv
+  v4f_attn cw[2];  // per row tile: quarters 2hv + 2hv+1
 #pragma unroll
-  for (int kl = 0; kl < 2; ++kl) {
-    const int kq = 2 * hv + kl;
-    c[kl] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nt = 0; nt < 2; ++nt) {
+    v4f_attn c[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float *src = &st.kv[lane & 15][128 * kq + 32 * s + 8 * (lane >> 4)];
-      float f[8];
+    for (int kl = 0; kl < 2; ++kl) {
+      const int kq = 2 * hv + kl;
+      c[kl] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = src[i];
-      v8bf hi;
+      for (int s = 0; s < 4; ++s) {
+        const float *src = &st.kv[16 * nt + (lane & 15)][128 * kq + 32 * s + 8 * (lane >> 4)];
+        float f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hi[i] = (__bf16)f[i];
+        for (int i = 0; i < 8; ++i) f[i] = src[i];
+        v8bf hi;
 #pragma unroll
-      for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], hi, c[kl], 0, 0, 0);
-      if (kq == 3 && s >= 2) {  // RoPE dimensions 448..511: the FP16 remainder
-        v8bf lo;
+        for (int i = 0; i < 8; ++i) hi[i] = (__bf16)f[i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(f[i] - (float)hi[i]);
+        for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], hi, c[kl], 0, 0, 0);
+        if (kq == 3 && s >= 2) {  // RoPE dimensions 448..511: the FP16 remainder
+          v8bf lo;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], lo, c[kl], 0, 0, 0);
+          for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(f[i] - (float)hi[i]);
+#pragma unroll
+          for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], lo, c[kl], 0, 0, 0);
+        }
       }
     }
+    cw[nt] = c[0] + c[1];
   }
-  const v4f_attn cw = c[0] + c[1];
-  if (hv == 1) {
+  {
+    const v4f_attn own = hv == 0 ? cw[0] : cw[1], other = hv == 0 ? cw[1] : cw[0];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) st.red[g][lane][v] = cw[v];
-  }
-  __syncthreads();
-  if (hv == 0) {
+    for (int v = 0; v < 4; ++v) st.red[hv][g][lane][v] = other[v];  // the partner's row tile
+    __syncthreads();
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float sum = cw[v] + st.red[g][lane][v];
-      const int n = lane & 15;
+      const float part = st.red[1 - hv][g][lane][v];
+      const float sum = hv == 0 ? own[v] + part : part + own[v];  // (q0 + q1) + (q2 + q3)
+      const int n = 16 * hv + (lane & 15);
       st.lg[16 * g + 4 * (lane >> 4) + v][n] = st.row[n] >= 0 ? scale * sum : -__builtin_inff();
     }
   }
   __syncthreads();
-  // online softmax of this lane's head over the batch's rows: lanes with
-  // l/16 < 2 hold rows 8(l/16)..+8, the others the zero rows 16..31
+  // online softmax of this lane's head over the batch's rows: lane l holds
+  // rows 8(l/16)..+8
   const int hh = 16 * g + (lane & 15);
-  const bool real = (lane >> 4) < 2;
   float pl[8];
   float mb = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float x = st.lg[hh][(8 * (lane >> 4) + i) & 15];  // in range for every lane: no branch
-    pl[i] = real ? x : -__builtin_inff();
+    pl[i] = st.lg[hh][8 * (lane >> 4) + i];
     mb = fmaxf(mb, pl[i]);
   }
   mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
@@ -342,7 +350,7 @@ __device__ __forceinline__ void attn_batch(const uint4 *qsplit, AttnState &S, At
     for (int t = 0; t < 8; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) S.acc[cl][t][v] *= av[v];
-  // acc += P V over the batch's 32 rows
+  // acc += P V over the batch's 32 rows (the K of the product)
 #pragma unroll
   for (int cl = 0; cl < 2; ++cl) {
     const int cc = 2 * hv + cl;
@@ -353,8 +361,7 @@ __device__ __forceinline__ void attn_batch(const uint4 *qsplit, AttnState &S, At
       float vf[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = st.kv[(8 * (lane >> 4) + i) & 15][d];
-        vf[i] = real ? x : 0.0f;
+        vf[i] = st.kv[8 * (lane >> 4) + i][d];
         vh[i] = (__bf16)vf[i];
       }
       S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vh, S.acc[cl][t], 0, 0, 0);
@@ -401,6 +408,35 @@ __device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, floa
     ml[2 * hh] = S.m;
     ml[2 * hh + 1] = S.l;
   }
+}
+
+// Merge of the group partials of one output element e = h * 512 + d:
+//   out = sum_b e^{m_b - M} acc_b / sum_b e^{m_b - M} l_b,  M = max_b m_b,
+//   lse = M + log sum_b e^{m_b - M} l_b
+// (groups with m = -inf are empty and add nothing; with no row at all,
+// out = 0 and lse = -inf).  ml, part: one session's partials.
+__device__ __forceinline__ float attn_merge_element(const float *ml, const float *part, int h, int e, float &lse) {
+  float mb[kAttnGroups], lb[kAttnGroups], xb[kAttnGroups];
+#pragma unroll
+  for (int b = 0; b < kAttnGroups; ++b) {
+    mb[b] = ml[((size_t)b * CSA_MAX_HEADS + h) * 2];
+    lb[b] = ml[((size_t)b * CSA_MAX_HEADS + h) * 2 + 1];
+    xb[b] = part[(size_t)b * CSA_MAX_HEADS * kKvDim + e];
+  }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int b = 0; b < kAttnGroups; ++b) M = fmaxf(M, mb[b]);
+  float L = 0.0f, X = 0.0f;
+  if (M != -__builtin_inff()) {
+#pragma unroll
+    for (int b = 0; b < kAttnGroups; ++b) {
+      const float w = mb[b] == -__builtin_inff() ? 0.0f : __expf(mb[b] - M);
+      L += w * lb[b];
+      X += mb[b] == -__builtin_inff() ? 0.0f : w * xb[b];
+    }
+  }
+  lse = L > 0.0f ? M + logf(L) : -__builtin_inff();
+  return L > 0.0f ? X / L : 0.0f;
 }
 
 // Order a group's entries by their key (rank or position, distinct),
