@@ -41,7 +41,6 @@ constexpr int kSelBins = 2 * kSelThreads;             // histogram bins per pass
 constexpr int kSelCap = 4096;                         // candidates held in LDS
 constexpr int kSelTarget = 1024;                      // candidates at which G is good enough
 constexpr int kSelMaxFull = kSelTarget / kMinTileHeads;  // full tiles listed (each holds >= hd heads >= G)
-constexpr int kSelMaxRegTiles = kSelRegHeads / kMinTileHeads;
 
 struct SelSessionArgs {
   const float *scores;
@@ -79,7 +78,6 @@ struct SelShared {
   uint64_t red_lo[kSelWaves], red_hi[kSelWaves];
   uint32_t red_n[kSelWaves];
   uint32_t full_list[kSelMaxFull];
-  uint8_t full_flag[kSelMaxRegTiles];
   int32_t loc_rank[CSA_TOPK + 16], loc_row[CSA_TOPK], ordered[CSA_TOPK];
   uint32_t ccnt, nfull, nmine, nloc;
   uint32_t bin, ca, cb;
@@ -246,38 +244,52 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   // 1. the bound G
   const uint64_t G = sel_bound(visit_heads, (uint32_t)kTopK, (uint32_t)kSelTarget, sh);
 
-  // 2. full tiles
+  // 2. full tiles (hd-th head >= G) and the candidates
   auto tile_is_full = [&](int64_t t) __attribute__((always_inline)) {
     const uint64_t last = heads[t * hd + hd - 1];
     return last != 0 && last >= G;
   };
+  // REG: a tile's hd heads sit in hd consecutive lanes of one slot (hd
+  // divides 64), so the lane of its last head decides "full" for all of
+  // them with one ballot, and lists the tile
+  bool fullbit[kSelKPT];
   if constexpr (reg) {
+    bool lists[kSelKPT];
+    uint64_t lm[kSelKPT];
+    uint32_t tot = 0;
 #pragma unroll
     for (int j = 0; j < kSelKPT; ++j) {
       const int i = tid + kSelThreads * j;  // < kSelRegHeads
-      if (i < nh && (i & (hd - 1)) == hd - 1) {
-        const bool full = h[j] != 0 && h[j] >= G;
-        sh.full_flag[i >> lhd] = full ? 1 : 0;
-        if (full) {
-          const uint32_t p = atomicAdd(&sh.nfull, 1u);
-          if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)(i >> lhd);
-        }
+      lists[j] = i < nh && (i & (hd - 1)) == hd - 1 && h[j] != 0 && h[j] >= G;
+      lm[j] = __ballot(lists[j]);
+      fullbit[j] = ((lm[j] >> (lane | (hd - 1))) & 1ull) != 0;
+      tot += (uint32_t)__popcll(lm[j]);
+    }
+    if (tot != 0) {  // one LDS atomic per wave
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sh.nfull, tot);
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+#pragma unroll
+      for (int j = 0; j < kSelKPT; ++j) {
+        const uint32_t p = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(lm[j] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)lm[j], 0u));
+        if (lists[j] && p < kSelMaxFull) sh.full_list[p] = (uint32_t)((tid + kSelThreads * j) >> lhd);
+        base += (uint32_t)__popcll(lm[j]);
       }
     }
   } else {
+#pragma unroll
+    for (int j = 0; j < kSelKPT; ++j) fullbit[j] = false;
     for (int64_t t = tid; t < nt; t += kSelThreads)
       if (tile_is_full(t)) {
         const uint32_t p = atomicAdd(&sh.nfull, 1u);
         if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)t;
       }
   }
-  __syncthreads();
-  const int nfull = (int)(sh.nfull < kSelMaxFull ? sh.nfull : kSelMaxFull);
 
-  // candidates: heads >= lb of tiles that are not full, keys >= lb of full
-  // tiles, in batches of 8 slots per thread: fb(ok[8], x[8]) in control flow
-  // uniform over the wave
-  auto scan_cand = [&](uint64_t lb, auto fb) __attribute__((always_inline)) {
+  // candidates >= lb, in batches of 8 slots per thread: fb(ok[8], x[8]) in
+  // control flow uniform over the wave.  Heads of tiles that are not full:
+  auto scan_head_cand = [&](uint64_t lb, auto fb) __attribute__((always_inline)) {
     if constexpr (reg) {
 #pragma unroll
       for (int j0 = 0; j0 < kSelKPT; j0 += 8) {
@@ -285,9 +297,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
         uint64_t x[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int i = tid + kSelThreads * (j0 + u);
           x[u] = h[j0 + u];
-          ok[u] = x[u] != 0 && x[u] >= lb && !sh.full_flag[i >> lhd];
+          ok[u] = x[u] != 0 && x[u] >= lb && !fullbit[j0 + u];
         }
         fb(ok, x);
       }
@@ -310,6 +321,9 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
         fb(ok, x);
       }
     }
+  };
+  // ... and every key of the full tiles (sh.full_list[0..nfull) complete)
+  auto scan_full_rows = [&](int nfull, uint64_t lb, auto fb) __attribute__((always_inline)) {
     const int nfr = nfull << lT;  // at most kSelMaxFull * 4096
     for (int i0 = 0; i0 < nfr; i0 += kSelThreads * 8) {
       float v[8];
@@ -329,13 +343,6 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       }
       fb(ok, x);
     }
-  };
-  auto visit_cand = [&](uint64_t lb, auto f) __attribute__((always_inline)) {
-    scan_cand(lb, [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (ok[u]) f(x[u]);
-    });
   };
   // one LDS atomic per wave and batch: the wave's selected slots take
   // consecutive positions
@@ -359,15 +366,30 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       base += (uint32_t)__popcll(m[u]);
     }
   };
-  scan_cand(G, append);
-  __syncthreads();
+  scan_head_cand(G, append);
+  __syncthreads();  // full tiles listed, head candidates appended
+  const int nfull = (int)(sh.nfull < kSelMaxFull ? sh.nfull : kSelMaxFull);
+  if (nfull > 0) {  // uniform
+    scan_full_rows(nfull, G, append);
+    __syncthreads();
+  }
   int C = (int)sh.ccnt;
   if (C > kSelCap) {
     // 3. too many candidates: the exact k_eff-th key among them
-    const uint64_t thr = sel_bound([&](auto f) __attribute__((always_inline)) { visit_cand(G, f); }, (uint32_t)k_eff, (uint32_t)k_eff, sh);
+    auto visit_cand = [&](auto f) __attribute__((always_inline)) {
+      auto each = [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (ok[u]) f(x[u]);
+      };
+      scan_head_cand(G, each);
+      scan_full_rows(nfull, G, each);
+    };
+    const uint64_t thr = sel_bound(visit_cand, (uint32_t)k_eff, (uint32_t)k_eff, sh);
     if (tid == 0) sh.ccnt = 0;
     __syncthreads();
-    scan_cand(thr, append);
+    scan_head_cand(thr, append);
+    scan_full_rows(nfull, thr, append);
     __syncthreads();
     C = (int)sh.ccnt;
   }
