@@ -71,7 +71,7 @@ typedef struct csa_session {
   const uint8_t *idx_rows; /* [n_rows][68] indexer rows, 16-byte aligned */
   const uint8_t *kv_rows;  /* [n_rows][583] KV rows */
   int64_t n_rows;          /* 0 <= n_rows <= CSA_MAX_ROWS */
-  const float *q_idx;      /* [n_idx_heads][128] indexer query */
+  const float *q_idx;      /* [n_idx_heads][128] indexer query, 16-byte aligned */
   const float *w_idx;      /* [n_idx_heads] per-head indexer weights */
   const float *q_attn;     /* [n_heads][512] attention query */
   int32_t *sel_idx;        /* out [512]: selected rows, best first, -1 padded */
@@ -103,8 +103,8 @@ size_t csa_workspace_bytes(int64_t max_rows_per_session, int n_sessions);
  * fp32.  The operation order is fixed, so a row's score does not depend on
  * its position; -0 is stored as +0.  The fused csa_decode_step computes
  * bit-identical scores.  n_idx_heads in [1, 64]; n_rows in [0, CSA_MAX_ROWS];
- * idx_rows must be 16-byte aligned (rows are streamed in 16-byte pieces;
- * CSA_EINVAL otherwise); ws sized by csa_workspace_bytes(n_rows, 1). */
+ * idx_rows and q_idx must be 16-byte aligned (both are streamed in 16-byte
+ * pieces; CSA_EINVAL otherwise); ws sized by csa_workspace_bytes(n_rows, 1). */
 int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
               int n_idx_heads, float *scores, void *ws, size_t ws_bytes, void *hip_stream);
 

@@ -166,7 +166,7 @@ int csa_dequant_kv(const uint8_t *kv_rows, int64_t n_rows, float *out, void *hip
 
 int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
               int n_idx_heads, float *scores, void *ws, size_t ws_bytes, void *hip_stream) {
-  if (!rows_ok(n_rows) || !heads_ok(n_idx_heads) || !q_idx || !w_idx) return CSA_EINVAL;
+  if (!rows_ok(n_rows) || !heads_ok(n_idx_heads) || !q_idx || !w_idx || !idx_aligned(q_idx)) return CSA_EINVAL;
   if (n_rows > 0 && (!idx_rows || !scores || !idx_aligned(idx_rows))) return CSA_EINVAL;
   Layout L;
   int rc = check_ws(ws, ws_bytes, n_rows, 1, &L);
@@ -248,6 +248,7 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   for (int i = 0; i < n_sessions; ++i) {
     const csa_session &s = sessions[i];
     if (!rows_ok(s.n_rows) || !s.q_idx || !s.w_idx || !s.q_attn || !s.sel_idx || !s.out) return CSA_EINVAL;
+    if (!idx_aligned(s.q_idx)) return CSA_EINVAL;
     if (s.n_rows > 0 && (!s.idx_rows || !s.kv_rows || !idx_aligned(s.idx_rows))) return CSA_EINVAL;
     if (s.n_rows > max_rows) max_rows = s.n_rows;
   }

@@ -53,11 +53,10 @@ typedef float v16f_q __attribute__((ext_vector_type(16)));
 typedef float v32f_q __attribute__((ext_vector_type(32)));
 typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 
-// This lane's query fragment of head group g, split from the fp32 query
-// q[n_heads][128] and weights w[n_heads]: head h = 16 g + l%16, values
-// [32(l/16), +32) (the lane's A operand rows and K slice), and the weights
-// of heads 16 g + 4(l/16) + v (the lane's result rows).  Heads past n_heads
-// get zero terms and weights.  With r the residual (initially the values):
+// This lane's query terms, split from its 32 fp32 query values at src (head
+// 16 g + l%16 of group g, values [32(l/16), +32): the lane's A operand row
+// and K slice); a head past the query's heads (live false) gets zero terms.
+// With r the residual (initially the values):
 //   E   = smallest exponent with max|r| / 2^E <= 7.5 (E2M3's largest value),
 //         at least -126,
 //   q_t = RNE_E2M3(r / 2^E) * 2^E,   r <- r - q_t   (exact in fp32),
@@ -68,15 +67,11 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 // interleaves its two 16-value inputs (even, odd positions), so value i
 // lands at bit 6i, the MFMA operand order; the unpacking one returns the
 // exact term values for the residual.
-__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float *__restrict__ qh,
-                                            const float *__restrict__ wh, int n_heads, int g, int lane) {
-  const int h = 16 * g + (lane & 15);
-  const bool live = h < n_heads;
-  const float *src = qh + (size_t)(live ? h : 0) * 128 + 32 * (lane >> 4);
+__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float *src, bool live) {
   v16f_q re, ro;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float a = src[2 * i], b = src[2 * i + 1];  // clamped head: no branch around the loads
+    const float a = src[2 * i], b = src[2 * i + 1];
     re[i] = live ? a : 0.0f;
     ro[i] = live ? b : 0.0f;
   }
@@ -102,6 +97,11 @@ __device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float *__restrict
     q.a[0][t] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4], (int)c[5], 0, 0};
     q.scw[0][t / 4] |= (E + 127) << (8 * (t % 4));
   }
+}
+
+// The weights of the heads whose results lane `lane` holds for group g:
+// heads 16 g + 4(l/16) + v, v < 4 (0 past n_heads).
+__device__ __forceinline__ void load_qweights(QFrag<1> &q, const float *wh, int n_heads, int g, int lane) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int hw = 16 * g + 4 * (lane >> 4) + v;

@@ -35,6 +35,10 @@ constexpr int kChunkSlot = kChunkBytes + 64;             // LDS bytes per ring s
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// 4 bytes per active lane from `g` to LDS address lds + 4 * lane (M0 = lds).
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Wait until at most N vector memory instructions are outstanding.

@@ -50,38 +50,37 @@ static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
 
-constexpr int kStepChunks = kTileWaves;                  // one 64-row chunk per wave and step
-constexpr int kStepRows = kStepChunks * kChunkRows;      // 256
-constexpr int kStepBytes = kStepChunks * kChunkBytes;    // 17408 (16-byte multiple)
-static_assert(kStepRows == kTileThreads, "one combined row per thread and step");
-constexpr int kRingDepth = 3;                            // steps resident: D - 1 in flight
-constexpr int kTileCandCap = 256;                        // keys >= theta ranked directly
+constexpr int kRingDepth = 3;     // chunks resident per wave: D - 1 in flight
+constexpr int kTileCandCap = 256; // keys >= theta ranked directly
+constexpr int kXchGroups = 2;     // query fragments exchanged per round
+constexpr int kXchWords = kTerms * 6 + kScaleWords;  // fp6 term registers + packed scales
 static_assert(kRingDepth >= 2 && kRingDepth <= 4, "ring depth");
-static_assert(kStepBytes % 16 == 0 && kChunkBytes % 16 == 0, "direct-to-LDS pieces stay aligned");
+static_assert(kChunkBytes % 16 == 0, "direct-to-LDS pieces stay aligned");
+static_assert(kXchGroups * kXchWords * 64 <= kMaxTileRows, "exchange fits the score array");
 
 struct TileShared {
-  alignas(16) uint8_t ring[kRingDepth][kStepBytes];  // workgroup ring of steps
-  float score[kMaxTileRows];                          // scores by tile position
+  alignas(16) uint8_t ring[kTileWaves][kRingDepth][kChunkBytes];  // one ring per wave
   union {
-    float part[2][kMaxGroups][kStepRows];  // head-group partials of the last two steps
-    struct {
-      uint64_t cand[kTileCandCap + 16];  // keys >= theta (+ over-read slack)
-      uint64_t theta[kTileWaves];
-      uint32_t ccnt;
-      SelScratch<kTileWaves> sc;
-    } h;  // step 2
-  } u;
+    float score[kMaxTileRows];                   // scores by tile position
+    uint32_t xch[kXchGroups][kXchWords][64];     // query fragments, before scoring
+  } a;
+  struct {
+    uint64_t cand[kTileCandCap + 16];  // keys >= theta (+ over-read slack)
+    uint64_t theta[kTileWaves];
+    uint32_t ccnt;
+    SelScratch<kTileWaves> sc;
+  } h;  // step 2
 };
 static_assert(sizeof(TileShared) <= 80 * 1024, "two workgroups per compute unit");
 
-// Step 2: the tile's scores in sh.score[0..rows) and, per thread, the
+// Step 2: the tile's scores in sh.a.score[0..rows) and, per thread, the
 // largest score part (score_ord) over its positions tid + 256 j -> the
 // tile's top-hd keys, sorted, at heads_out[0..hd).
 __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, int hd,
                            uint64_t *__restrict__ heads_out) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   auto key_at = [&](int i) __attribute__((always_inline)) {
-    return make_key(sh.score[i], (uint32_t)(row0 + i));
+    return make_key(sh.a.score[i], (uint32_t)(row0 + i));
   };
   // the largest 24-bit prefix p with at least hd lane maxima at or above
   // p << 8 (two bits per step): those hd keys are >= p << 40
@@ -95,12 +94,12 @@ __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, i
     const int n3 = __popcll(__ballot(o24 >= c3));
     p = n3 >= hd ? c3 : (n2 >= hd ? c2 : (n1 >= hd ? c1 : p));
   }
-  if (lane == 0) sh.u.h.theta[wave] = (uint64_t)p << 40;
-  if (tid == 0) sh.u.h.ccnt = 0;
+  if (lane == 0) sh.h.theta[wave] = (uint64_t)p << 40;
+  if (tid == 0) sh.h.ccnt = 0;
   __syncthreads();
   uint64_t theta = 1;  // also excludes empty positions
 #pragma unroll
-  for (int w = 0; w < kTileWaves; ++w) theta = sh.u.h.theta[w] > theta ? sh.u.h.theta[w] : theta;
+  for (int w = 0; w < kTileWaves; ++w) theta = sh.h.theta[w] > theta ? sh.h.theta[w] : theta;
   // keys >= lb, four positions per thread at a time, one LDS atomic per wave
   // and batch: the wave's keys take consecutive positions
   const int nj = (rows + kTileThreads - 1) / kTileThreads;
@@ -120,13 +119,13 @@ __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, i
       }
       if (tot != 0) {
         uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&sh.u.h.ccnt, tot);
+        if (lane == 0) base = atomicAdd(&sh.h.ccnt, tot);
         base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint32_t q = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m[u] >> 32),
                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m[u], 0u));
-          if (ok[u] && q < cap) sh.u.h.cand[q] = kx[u];
+          if (ok[u] && q < cap) sh.h.cand[q] = kx[u];
           base += (uint32_t)__popcll(m[u]);
         }
       }
@@ -134,25 +133,25 @@ __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, i
   };
   gather(theta, (uint32_t)kTileCandCap);
   __syncthreads();
-  int C = (int)sh.u.h.ccnt;
+  int C = (int)sh.h.ccnt;
   if (C > kTileCandCap) {
     // many keys tie with or crowd above the bound: select exactly instead
     // (exactly hd keys are >= the hd-th largest)
-    const uint64_t thr = block_kth_largest<kTileWaves>(key_at, rows, hd, theta, sh.u.h.sc);
-    if (tid == 0) sh.u.h.ccnt = 0;
+    const uint64_t thr = block_kth_largest<kTileWaves>(key_at, rows, hd, theta, sh.h.sc);
+    if (tid == 0) sh.h.ccnt = 0;
     __syncthreads();
     gather(thr, (uint32_t)kTileCandCap);
     __syncthreads();
-    C = (int)sh.u.h.ccnt;
+    C = (int)sh.h.ccnt;
   }
   // rank = number of larger candidates = sorted position
   for (int i = tid; i < C; i += kTileThreads) {
-    const uint64_t key = sh.u.h.cand[i];
+    const uint64_t key = sh.h.cand[i];
     int r = 0;
     for (int j0 = 0; j0 < C; j0 += 16) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const uint64_t y = sh.u.h.cand[j0 + u];
+        const uint64_t y = sh.h.cand[j0 + u];
         r += (j0 + u < C && y > key) ? 1 : 0;
       }
     }
@@ -191,109 +190,157 @@ __device__ __forceinline__ void wait_chunk(int later) {
     wait_vmcnt<0>();
 }
 
-// This lane's operands of chunk b of a step in LDS: operand i is rows
-// 64 b + 16 i .. + 16, the lane taking row l%16's code bytes [16(l/16), +16)
-// and scale byte l/16.
-__device__ __forceinline__ void load_ops(const uint8_t *base, int b, RowOperand (&ops)[4]) {
+// This lane's operands of the chunk at `base` in LDS: operand i is rows
+// 16 i .. + 16, the lane taking row l%16's code bytes [16(l/16), +16) and
+// scale byte l/16.
+__device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[4]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t *rb = base + (kChunkRows * b + 16 * i + (lane & 15)) * kIdxRowBytes;
+    const uint8_t *rb = base + (16 * i + (lane & 15)) * kIdxRowBytes;
     const uint32_t *w = reinterpret_cast<const uint32_t *>(rb + 16 * (lane >> 4));
     ops[i].codes = uint4{w[0], w[1], w[2], w[3]};
     ops[i].sb = rb[64 + (lane >> 4)];
   }
 }
 
-// Score the tile's rows into sh.score[0..rows) (and out[0..rows)).
-// Step s covers tile positions [256 s, 256 s + 256): wave w brings chunk
-// 4s + w into the step's ring slot (direct-to-LDS when the chunk lies wholly
-// inside the buffer, kRingDepth - 1 steps ahead; a chunk cut by the buffer
-// end by clamped per-lane loads).  After one barrier per step every wave
-// scores its share of the step for ITS head group only: wave w takes group
-// w % G and chunks [G (w / G), G (w / G) + G) of the step, so a wave holds
-// the query terms of 16 heads.  The group partials meet in LDS and are
-// summed, group by group in a fixed association, one step later.
-// `pre` runs once the first steps are in flight.
-template <int G, class Pre>
+// Score the tile's rows into sh.a.score[0..rows) (and out[0..rows)).
+// Wave w owns chunks w, w + 4, w + 8, ... of the tile (64 rows each) and
+// scores them for every head group, so each row is read from LDS once and
+// the group parts of a row meet in the lane that holds it; the waves run
+// without workgroup barriers.  A chunk wholly inside the buffer comes in
+// direct-to-LDS, kRingDepth - 1 chunks ahead, into the wave's own ring; a
+// chunk cut by the buffer end is copied with clamped per-lane loads.
+// Query terms: wave g brings the fp32 query of head group g (16 heads,
+// 8 KB) and all the weights direct-to-LDS into ring slots 1 and 2 ahead of
+// its first chunk, so they arrive first and the split runs while the chunk
+// is in flight; the groups are then exchanged through LDS, kXchGroups per
+// round.  Its second chunk is issued once the staging area has been read
+// (after the first exchange barrier).
+template <int G>
 __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
                                                int n_idx_heads, const uint8_t *__restrict__ idx_rows, int64_t row0,
-                                               int64_t n, int rows, float *__restrict__ out, TileShared &sh,
-                                               Pre pre) {
+                                               int64_t n, int rows, float *__restrict__ out, TileShared &sh) {
   static_assert(G == 1 || G == 2 || G == 4, "head groups per workgroup");
+  static_assert(kRingDepth >= 3, "the query is staged in ring slots 1 and 2");
+  static_assert(16 * 512 + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int grp = wave % G, rl = wave / G;
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
   const int nfc = rows / kChunkRows;  // chunks wholly inside the buffer
-  const int ns = (nch + kStepChunks - 1) / kStepChunks;
+  const int nmy = wave < nch ? (nch - wave + kTileWaves - 1) / kTileWaves : 0;  // this wave's chunks
+  auto chunk = [&](int s) __attribute__((always_inline)) { return wave + kTileWaves * s; };
   auto fill = [&](int s) __attribute__((always_inline)) {
-    const int c = kStepChunks * s + wave;
-    uint8_t *dst = &sh.ring[s % kRingDepth][wave * kChunkBytes];
+    const int c = chunk(s);
+    uint8_t *dst = &sh.ring[wave][s % kRingDepth][0];
     if (c < nfc)
       issue_chunk(idx_rows, row0 + (int64_t)kChunkRows * c, (uint32_t)(uintptr_t)dst, lane);
     else if (c < nch)
       copy_chunk_clamped(idx_rows, row0 + (int64_t)kChunkRows * c, n, dst, lane);
   };
-  auto direct = [&](int s) __attribute__((always_inline)) { return s < ns && kStepChunks * s + wave < nfc; };
-  uint32_t omax = 0;  // largest score part of this thread's rows
-  auto combine = [&](int s) __attribute__((always_inline)) {
-    const int p = kStepRows * s + tid;
-    if (p < rows) {
-      const float *pp = &sh.u.part[s & 1][0][tid];
-      float v;
-      if constexpr (G == 4)
-        v = (pp[0] + pp[kStepRows]) + (pp[2 * kStepRows] + pp[3 * kStepRows]);
-      else if constexpr (G == 2)
-        v = pp[0] + pp[kStepRows];
-      else
-        v = pp[0];
-      v = score_finish(v, 0.0f);
-      sh.score[p] = v;
-      out[p] = v;
-      const uint32_t so = score_ord(v);
-      omax = so > omax ? so : omax;
-    }
-  };
+  auto direct = [&](int s) __attribute__((always_inline)) { return s < nmy && chunk(s) < nfc; };
 
+  // staging: query rows of heads 16 wave + j at stage + 512 j (16-byte
+  // pieces, the head clamped to the last one), weights at stage + 8192
+  uint8_t *const stage = &sh.ring[wave][1][0];
+  const uint32_t stage_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage);
+  if (wave < G) {
 #pragma unroll
-  for (int s = 0; s < kRingDepth - 1; ++s)
-    if (s < ns) fill(s);
-  pre();
-  // the query terms, split while the first steps are in flight (the
-  // query loads complete before the loop, so no wait for them sits inside)
-  QFrag<1> q;
-  split_qfrag(q, qh, wh, n_idx_heads, grp, lane);
+    for (int i = 0; i < 8; ++i) {
+      const int piece = 64 * i + lane;  // 32 pieces per head
+      int h = 16 * wave + (piece >> 5);
+      h = h < n_idx_heads ? h : n_idx_heads - 1;
+      dma16(qh + (size_t)h * 128 + 4 * (piece & 31), stage_lds + 1024 * i);
+    }
+  }
+  dma4(wh + (lane < n_idx_heads ? lane : n_idx_heads - 1), stage_lds + 8192);
+  if (nmy > 0) fill(0);
+  if (direct(0))
+    wait_vmcnt<kChunkDma>();
+  else
+    wait_vmcnt<0>();
+  QFrag<1> q[G];
+  {
+    const float *wl = reinterpret_cast<const float *>(stage + 8192);
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_qweights(q[g], wl, n_idx_heads, g, lane);
+    QFrag<1> mine;
+    if (wave < G)
+      split_qfrag(mine, reinterpret_cast<const float *>(stage + 512 * (lane & 15) + 128 * (lane >> 4)),
+                  16 * wave + (lane & 15) < n_idx_heads);
+#pragma unroll
+    for (int r0 = 0; r0 < G; r0 += kXchGroups) {
+      if (wave >= r0 && wave < r0 + kXchGroups && wave < G) {
+        uint32_t *x = &sh.a.xch[wave - r0][0][lane];
+#pragma unroll
+        for (int t = 0; t < kTerms; ++t)
+#pragma unroll
+          for (int i = 0; i < 6; ++i) x[64 * (6 * t + i)] = (uint32_t)mine.a[0][t][i];
+#pragma unroll
+        for (int j = 0; j < kScaleWords; ++j) x[64 * (6 * kTerms + j)] = (uint32_t)mine.scw[0][j];
+      }
+      __syncthreads();  // (its wait for LDS reads also ends this wave's reads of the staging area)
+      if (r0 == 0 && 1 < nmy) fill(1);
+#pragma unroll
+      for (int g = r0; g < r0 + kXchGroups && g < G; ++g) {
+        const uint32_t *x = &sh.a.xch[g - r0][0][lane];
+#pragma unroll
+        for (int t = 0; t < kTerms; ++t) {
+          int v[6];
+#pragma unroll
+          for (int i = 0; i < 6; ++i) v[i] = (int)x[64 * (6 * t + i)];
+          q[g].a[0][t] = v8i{v[0], v[1], v[2], v[3], v[4], v[5], 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < kScaleWords; ++j) q[g].scw[0][j] = (int)x[64 * (6 * kTerms + j)];
+      }
+      __syncthreads();  // the exchange area is free again (it is the score array)
+    }
+  }
 
-  for (int s = 0; s < ns; ++s) {
+  uint32_t omax = 0;  // largest score part of this thread's rows
+  for (int s = 0; s < nmy; ++s) {
     int later = 0;
 #pragma unroll
     for (int t = 1; t <= kRingDepth - 2; ++t) later += direct(s + t) ? 1 : 0;
     wait_chunk(later);
-    __syncthreads();  // step s complete in LDS; step s - 1 consumed by every wave
-    if (s + kRingDepth - 1 < ns) fill(s + kRingDepth - 1);  // into step s - 1's slot
-    if (s > 0) combine(s - 1);
-    const uint8_t *base = &sh.ring[s % kRingDepth][0];
-    // every chunk of the step is scored, also past the tile's rows in its
-    // last step (stale LDS bytes; those partials are never combined), and
-    // the products of the next chunk are issued before the current chunk's
-    // reduction, whose vector instructions then overlap the matrix cores
-    float *const part = &sh.u.part[s & 1][grp][0];
+    // the slot refilled next held chunk s - 1, whose LDS reads completed
+    // before its products were formed
+    if (s + kRingDepth - 1 < nmy) fill(s + kRingDepth - 1);
+    // every row of the chunk is scored, also past the tile's rows in a last
+    // partial chunk (stale LDS bytes; those scores are dropped); the products
+    // of the next group are issued before the current group's reduction,
+    // whose vector instructions then overlap the matrix cores
+    const uint8_t *base = &sh.ring[wave][s % kRingDepth][0];
     RowOperand ops[4];
+    load_ops(base, ops);
+    float part[G];
     v4f c[4][1], cn[4][1];
-    load_ops(base, G * rl, ops);
-    group_dots<4>(q, ops, c);
+    group_dots<4>(q[0], ops, c);
 #pragma unroll
-    for (int bb = 1; bb < G; ++bb) {
-      load_ops(base, G * rl + bb, ops);
-      group_dots<4>(q, ops, cn);
-      part[kChunkRows * (G * rl + bb - 1) + lane] = group_part4(q, c);
+    for (int g = 1; g < G; ++g) {
+      group_dots<4>(q[g], ops, cn);
+      part[g - 1] = group_part4(q[g - 1], c);
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
     }
-    part[kChunkRows * (G * rl + G - 1) + lane] = group_part4(q, c);
+    part[G - 1] = group_part4(q[G - 1], c);
+    // lane l holds row l of the chunk: the groups summed in a fixed association
+    float v;
+    if constexpr (G == 4)
+      v = (part[0] + part[1]) + (part[2] + part[3]);
+    else if constexpr (G == 2)
+      v = part[0] + part[1];
+    else
+      v = part[0];
+    const int p = kChunkRows * chunk(s) + lane;
+    if (p < rows) {
+      v = score_finish(v, 0.0f);
+      sh.a.score[p] = v;
+      out[p] = v;
+      const uint32_t so = score_ord(v);
+      omax = so > omax ? so : omax;
+    }
   }
-  __syncthreads();
-  if (ns > 0) combine(ns - 1);
   __syncthreads();
   return omax;
 }
@@ -328,7 +375,8 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
         for (int t = (int)blockIdx.x * per + tid; t < t1; t += kTileThreads) attn_q_split_task(qa, n_attn_heads, aq, t);
       }
     };
-    o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, S.scores + row0, sh, attn_split);
+    o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, S.scores + row0, sh);
+    attn_split();
     if (!a.write_heads) return;
   } else {
     // the given scores into LDS, four loads in flight per thread
@@ -344,7 +392,7 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
       for (int u = 0; u < 4; ++u) {
         const int i = j0 + kTileThreads * u + tid;
         if (i < rows) {
-          sh.score[i] = v[u];
+          sh.a.score[i] = v[u];
           const uint32_t so = score_ord(v[u]);
           o = so > o ? so : o;
         }

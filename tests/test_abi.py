@@ -72,6 +72,7 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_score(fake, 10, fake, fake, 8, fake, fake, 16, None) == csa.EWORKSPACE
     odd = ctypes.c_void_p(4096 + 4)  # indexer rows must be 16-byte aligned
     assert L.csa_score(odd, 10, fake, fake, 8, fake, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score(fake, 10, odd, fake, 8, fake, fake, 1 << 30, None) == csa.EINVAL  # so must the query
     assert L.csa_topk(fake, 10, 0, fake, None, fake, 1 << 30, None) == csa.EINVAL
     assert L.csa_topk(fake, 10, 513, fake, None, fake, 1 << 30, None) == csa.EINVAL
     assert L.csa_topk(fake, 10, 8, None, None, fake, 1 << 30, None) == csa.EINVAL
@@ -92,4 +93,6 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_decode_step(sess, 2, 8, 0, 0.1, fake, 1 << 30, None) == csa.EINVAL
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 64, None) == csa.EWORKSPACE
     sess[1] = csa.Session(odd, fake, 100, fake, fake, fake, fake, None, fake, None)
+    assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
+    sess[1] = csa.Session(fake, fake, 100, odd, fake, fake, fake, None, fake, None)
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
