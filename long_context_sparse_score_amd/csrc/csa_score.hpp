@@ -158,21 +158,13 @@ __device__ __forceinline__ void group_dots(const QFrag<1> &q, const RowOperand (
   mfma_terms<1, NS>(q, b, sb, c, std::make_integer_sequence<int, kTerms>{});
 }
 
-// The group's part of the score for four operands (64 rows):
-//   part = sum over the group's 16 heads h of w_h * max(0, d_h)
-// (a NaN d, impossible for valid rows, is not zeroed).  Each lane first sums
-// its four heads (an fma chain over v); the four lane-rows are then summed
-// by a reduce-scatter: a 32-lane swap pairs operands (0, 2) and (1, 3)
-// across the lane halves, a 16-lane swap pairs the results across adjacent
-// lane-rows.  Lane l returns the part of row l%16 of operand l/16 (that is,
-// of row l of the 64), as (lane-row 0 + lane-row 2) + (lane-row 1 + lane-row 3).
-// v_permlane32_swap(x, y) -> (x0, x1, y0, y1), (x2, x3, y2, y3) and
-// v_permlane16_swap(x, y) -> (x0, y0, x2, y2), (x1, y1, x3, y3) in 16-lane rows.
-__device__ __forceinline__ float group_part4(const QFrag<1> &q, const v4f (&c)[4][1]) {
-  float p[4];
+// One head group's contribution to the score partials of four operands (64
+// rows): p[r] += w_h * max(0, d_h) over the lane's four heads of the group
+// (an fma chain over v, continued group after group), d_h = c[r][v].  A NaN
+// d, impossible for valid rows, is not zeroed.
+__device__ __forceinline__ void group_acc4(const QFrag<1> &q, const v4f (&c)[4][1], float (&p)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    p[r] = 0.0f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       // ReLU as a signed-integer max of the bits: one instruction, and
@@ -181,6 +173,16 @@ __device__ __forceinline__ float group_part4(const QFrag<1> &q, const v4f (&c)[4
       p[r] = __builtin_fmaf(q.w[0][v], d, p[r]);
     }
   }
+}
+
+// The four lane-rows of the partials summed by a reduce-scatter: a 32-lane
+// swap pairs operands (0, 2) and (1, 3) across the lane halves, a 16-lane
+// swap pairs the results across adjacent lane-rows.  Lane l returns the sum
+// for row l%16 of operand l/16 (that is, row l of the 64), as
+// (lane-row 0 + lane-row 2) + (lane-row 1 + lane-row 3).
+// v_permlane32_swap(x, y) -> (x0, x1, y0, y1), (x2, x3, y2, y3) and
+// v_permlane16_swap(x, y) -> (x0, y0, x2, y2), (x1, y1, x3, y3) in 16-lane rows.
+__device__ __forceinline__ float rows_reduce4(const float (&p)[4]) {
   const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
   const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
   const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);

@@ -76,8 +76,8 @@ static_assert(sizeof(TileShared) <= 80 * 1024, "two workgroups per compute unit"
 // Step 2: the tile's scores in sh.a.score[0..rows) and, per thread, the
 // largest score part (score_ord) over its positions tid + 256 j -> the
 // tile's top-hd keys, sorted, at heads_out[0..hd).
-__device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, int hd,
-                           uint64_t *__restrict__ heads_out) {
+__device__ __forceinline__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, int hd,
+                                           uint64_t *__restrict__ heads_out) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   auto key_at = [&](int i) __attribute__((always_inline)) {
     return make_key(sh.a.score[i], (uint32_t)(row0 + i));
@@ -100,20 +100,28 @@ __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, i
   uint64_t theta = 1;  // also excludes empty positions
 #pragma unroll
   for (int w = 0; w < kTileWaves; ++w) theta = sh.h.theta[w] > theta ? sh.h.theta[w] : theta;
-  // keys >= lb, four positions per thread at a time, one LDS atomic per wave
-  // and batch: the wave's keys take consecutive positions
+  // keys >= lb, eight positions per thread at a time (their loads issued
+  // together), one LDS atomic per wave and batch: the wave's keys take
+  // consecutive positions.  A wave whose largest score parts are all below
+  // the bound's holds no candidate and skips the scan.
   const int nj = (rows + kTileThreads - 1) / kTileThreads;
   auto gather = [&](uint64_t lb, uint32_t cap) __attribute__((always_inline)) {
-    for (int j0 = 0; j0 < nj; j0 += 4) {
-      bool ok[4];
-      uint64_t kx[4], m[4];
+    if (__ballot(o >= (uint32_t)(lb >> 32)) == 0) return;
+    for (int j0 = 0; j0 < nj; j0 += 8) {
+      bool ok[8];
+      uint64_t kx[8], m[8];
+      float sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = tid + kTileThreads * (j0 + u);
+        sv[u] = sh.a.score[i < rows ? i : 0];
+      }
       uint32_t tot = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = tid + kTileThreads * (j0 + u);
-        const bool in = i < rows;
-        kx[u] = key_at(in ? i : 0);
-        ok[u] = in && kx[u] >= lb;
+        kx[u] = make_key(sv[u], (uint32_t)(row0 + i));
+        ok[u] = i < rows && kx[u] >= lb;
         m[u] = __ballot(ok[u]);
         tot += (uint32_t)__popcll(m[u]);
       }
@@ -122,7 +130,7 @@ __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, i
         if (lane == 0) base = atomicAdd(&sh.h.ccnt, tot);
         base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           const uint32_t q = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m[u] >> 32),
                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m[u], 0u));
           if (ok[u] && q < cap) sh.h.cand[q] = kx[u];
@@ -149,11 +157,11 @@ __device__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, i
     const uint64_t key = sh.h.cand[i];
     int r = 0;
     for (int j0 = 0; j0 < C; j0 += 16) {
+      uint64_t y[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const uint64_t y = sh.h.cand[j0 + u];
-        r += (j0 + u < C && y > key) ? 1 : 0;
-      }
+      for (int u = 0; u < 16; ++u) y[u] = sh.h.cand[j0 + u];  // the slack covers j0 + u >= C
+#pragma unroll
+      for (int u = 0; u < 16; ++u) r += (j0 + u < C && y[u] > key) ? 1 : 0;
     }
     if (r < hd) heads_out[r] = key;
   }
@@ -308,30 +316,23 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     if (s + kRingDepth - 1 < nmy) fill(s + kRingDepth - 1);
     // every row of the chunk is scored, also past the tile's rows in a last
     // partial chunk (stale LDS bytes; those scores are dropped); the products
-    // of the next group are issued before the current group's reduction,
-    // whose vector instructions then overlap the matrix cores
+    // of the next group are issued before the current group's epilogue
     const uint8_t *base = &sh.ring[wave][s % kRingDepth][0];
     RowOperand ops[4];
     load_ops(base, ops);
-    float part[G];
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f c[4][1], cn[4][1];
     group_dots<4>(q[0], ops, c);
 #pragma unroll
     for (int g = 1; g < G; ++g) {
       group_dots<4>(q[g], ops, cn);
-      part[g - 1] = group_part4(q[g - 1], c);
+      group_acc4(q[g - 1], c, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
     }
-    part[G - 1] = group_part4(q[G - 1], c);
-    // lane l holds row l of the chunk: the groups summed in a fixed association
-    float v;
-    if constexpr (G == 4)
-      v = (part[0] + part[1]) + (part[2] + part[3]);
-    else if constexpr (G == 2)
-      v = part[0] + part[1];
-    else
-      v = part[0];
+    group_acc4(q[G - 1], c, acc);
+    // lane l: row l of the chunk, summed over every head
+    float v = rows_reduce4(acc);
     const int p = kChunkRows * chunk(s) + lane;
     if (p < rows) {
       v = score_finish(v, 0.0f);
@@ -368,11 +369,17 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
     auto attn_split = [=]() __attribute__((always_inline)) {
       if (aq) {
         // this workgroup's share of the session's attention query split
-        // (read by the selection kernel that follows)
+        // (read by the selection kernel that follows), spread over the
+        // first half of the tiles: they are dispatched first and finish
+        // while the second half still scores, so the split stays off the
+        // kernel's tail
         const int nt = (int)((n + T - 1) / T);
-        const int per = (kAttnQTasks + nt - 1) / nt;
-        const int t1 = ((int)blockIdx.x + 1) * per < kAttnQTasks ? ((int)blockIdx.x + 1) * per : kAttnQTasks;
-        for (int t = (int)blockIdx.x * per + tid; t < t1; t += kTileThreads) attn_q_split_task(qa, n_attn_heads, aq, t);
+        const int nw = nt > 1 ? nt / 2 : 1;
+        const int per = (kAttnQTasks + nw - 1) / nw;
+        const int b = (int)blockIdx.x;
+        const int t1 = (b + 1) * per < kAttnQTasks ? (b + 1) * per : kAttnQTasks;
+        if (b < nw)
+          for (int t = b * per + tid; t < t1; t += kTileThreads) attn_q_split_task(qa, n_attn_heads, aq, t);
       }
     };
     o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, S.scores + row0, sh);
