@@ -53,7 +53,7 @@ typedef float v16f_q __attribute__((ext_vector_type(16)));
 typedef float v32f_q __attribute__((ext_vector_type(32)));
 typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 
-// This lane's query terms, split from its 32 fp32 query values at src (head
+// This lane's query terms, split from its 32 fp32 query values x (head
 // 16 g + l%16 of group g, values [32(l/16), +32): the lane's A operand row
 // and K slice); a head past the query's heads (live false) gets zero terms.
 // With r the residual (initially the values):
@@ -67,13 +67,12 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 // interleaves its two 16-value inputs (even, odd positions), so value i
 // lands at bit 6i, the MFMA operand order; the unpacking one returns the
 // exact term values for the residual.
-__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float *src, bool live) {
+__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float (&x)[32], bool live) {
   v16f_q re, ro;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float a = src[2 * i], b = src[2 * i + 1];
-    re[i] = live ? a : 0.0f;
-    ro[i] = live ? b : 0.0f;
+    re[i] = live ? x[2 * i] : 0.0f;
+    ro[i] = live ? x[2 * i + 1] : 0.0f;
   }
 #pragma unroll
   for (int w = 0; w < kScaleWords; ++w) q.scw[0][w] = 0;

@@ -52,17 +52,14 @@ constexpr int kTileWaves = kTileThreads / 64;
 
 constexpr int kRingDepth = 3;     // chunks resident per wave: D - 1 in flight
 constexpr int kTileCandCap = 256; // keys >= theta ranked directly
-constexpr int kXchGroups = 2;     // query fragments exchanged per round
-constexpr int kXchWords = kTerms * 6 + kScaleWords;  // fp6 term registers + packed scales
+constexpr int kXchWords = kTerms * 6 + kScaleWords;  // fp6 term registers + packed scales per lane
 static_assert(kRingDepth >= 2 && kRingDepth <= 4, "ring depth");
 static_assert(kChunkBytes % 16 == 0, "direct-to-LDS pieces stay aligned");
-static_assert(kXchGroups * kXchWords * 64 <= kMaxTileRows, "exchange fits the score array");
 
 struct TileShared {
   alignas(16) uint8_t ring[kTileWaves][kRingDepth][kChunkBytes];  // one ring per wave
-  union {
-    float score[kMaxTileRows];                   // scores by tile position
-    uint32_t xch[kXchGroups][kXchWords][64];     // query fragments, before scoring
+  struct {
+    float score[kMaxTileRows];  // scores by tile position
   } a;
   struct {
     uint64_t cand[kTileCandCap + 16];  // keys >= theta (+ over-read slack)
@@ -220,18 +217,22 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[
 // direct-to-LDS, kRingDepth - 1 chunks ahead, into the wave's own ring; a
 // chunk cut by the buffer end is copied with clamped per-lane loads.
 // Query terms: wave g brings the fp32 query of head group g (16 heads,
-// 8 KB) and all the weights direct-to-LDS into ring slots 1 and 2 ahead of
-// its first chunk, so they arrive first and the split runs while the chunk
-// is in flight; the groups are then exchanged through LDS, kXchGroups per
-// round.  Its second chunk is issued once the staging area has been read
-// (after the first exchange barrier).
+// 8 KB) and all the weights direct-to-LDS into its ring slots 1 and 2 ahead
+// of its first chunk, so they arrive first and the split runs while the
+// chunk is in flight.  Each head's 512 bytes land at a 528-byte stride, so
+// the split's reads spread over the LDS banks; each wave then writes its group's terms over its own staging area (word d
+// of lane l at 4 (64 d + l)), and after one barrier every wave reads every
+// group's terms.  The second chunk is issued once a second barrier has
+// released the slots.
 template <int G>
 __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
                                                int n_idx_heads, const uint8_t *__restrict__ idx_rows, int64_t row0,
                                                int64_t n, int rows, float *__restrict__ out, TileShared &sh) {
   static_assert(G == 1 || G == 2 || G == 4, "head groups per workgroup");
   static_assert(kRingDepth >= 3, "the query is staged in ring slots 1 and 2");
-  static_assert(16 * 512 + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
+  constexpr int kStageHead = 528, kStageW = 16 * kStageHead;
+  static_assert(kStageW + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
+  static_assert(kXchWords * 64 * 4 <= kStageW, "the terms leave the weights alone");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
   const int nfc = rows / kChunkRows;  // chunks wholly inside the buffer
@@ -247,20 +248,19 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   };
   auto direct = [&](int s) __attribute__((always_inline)) { return s < nmy && chunk(s) < nfc; };
 
-  // staging: query rows of heads 16 wave + j at stage + 512 j (16-byte
-  // pieces, the head clamped to the last one), weights at stage + 8192
+  // staging: head 16 wave + j (clamped to the last one) at stage + 528 j,
+  // one 512-byte load per head (the 16-byte pad spreads the split's reads
+  // over the banks), the weights at stage + kStageW
   uint8_t *const stage = &sh.ring[wave][1][0];
   const uint32_t stage_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage);
-  if (wave < G) {
+  if (wave < G && lane < 32) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int piece = 64 * i + lane;  // 32 pieces per head
-      int h = 16 * wave + (piece >> 5);
-      h = h < n_idx_heads ? h : n_idx_heads - 1;
-      dma16(qh + (size_t)h * 128 + 4 * (piece & 31), stage_lds + 1024 * i);
+    for (int j = 0; j < 16; ++j) {
+      const int h = 16 * wave + j < n_idx_heads ? 16 * wave + j : n_idx_heads - 1;
+      dma16(qh + (size_t)h * 128 + 4 * lane, stage_lds + kStageHead * j);
     }
   }
-  dma4(wh + (lane < n_idx_heads ? lane : n_idx_heads - 1), stage_lds + 8192);
+  dma4(wh + (lane < n_idx_heads ? lane : n_idx_heads - 1), stage_lds + kStageW);
   if (nmy > 0) fill(0);
   if (direct(0))
     wait_vmcnt<kChunkDma>();
@@ -268,41 +268,49 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     wait_vmcnt<0>();
   QFrag<1> q[G];
   {
-    const float *wl = reinterpret_cast<const float *>(stage + 8192);
+    if (wave < G) {
+      float x[32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 v =
+            *reinterpret_cast<const float4 *>(stage + kStageHead * (lane & 15) + 128 * (lane >> 4) + 16 * i);
+        x[4 * i] = v.x;
+        x[4 * i + 1] = v.y;
+        x[4 * i + 2] = v.z;
+        x[4 * i + 3] = v.w;
+      }
+      QFrag<1> mine;
+      split_qfrag(mine, x, 16 * wave + (lane & 15) < n_idx_heads);
+      // the terms over the staging area (this wave's reads of it come first):
+      // word d of lane l at stage + 4 (64 d + l)
+      uint32_t *x4 = reinterpret_cast<uint32_t *>(stage) + lane;
+#pragma unroll
+      for (int t = 0; t < kTerms; ++t)
+#pragma unroll
+        for (int i = 0; i < 6; ++i) x4[64 * (6 * t + i)] = (uint32_t)mine.a[0][t][i];
+#pragma unroll
+      for (int j = 0; j < kScaleWords; ++j) x4[64 * (6 * kTerms + j)] = (uint32_t)mine.scw[0][j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t *x4 = reinterpret_cast<const uint32_t *>(&sh.ring[g][1][0]) + lane;
+#pragma unroll
+      for (int t = 0; t < kTerms; ++t) {
+        int v[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) v[i] = (int)x4[64 * (6 * t + i)];
+        q[g].a[0][t] = v8i{v[0], v[1], v[2], v[3], v[4], v[5], 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < kScaleWords; ++j) q[g].scw[0][j] = (int)x4[64 * (6 * kTerms + j)];
+    }
+    // the weights (in slot 2, which the exchange leaves alone)
+    const float *wl = reinterpret_cast<const float *>(stage + kStageW);
 #pragma unroll
     for (int g = 0; g < G; ++g) load_qweights(q[g], wl, n_idx_heads, g, lane);
-    QFrag<1> mine;
-    if (wave < G)
-      split_qfrag(mine, reinterpret_cast<const float *>(stage + 512 * (lane & 15) + 128 * (lane >> 4)),
-                  16 * wave + (lane & 15) < n_idx_heads);
-#pragma unroll
-    for (int r0 = 0; r0 < G; r0 += kXchGroups) {
-      if (wave >= r0 && wave < r0 + kXchGroups && wave < G) {
-        uint32_t *x = &sh.a.xch[wave - r0][0][lane];
-#pragma unroll
-        for (int t = 0; t < kTerms; ++t)
-#pragma unroll
-          for (int i = 0; i < 6; ++i) x[64 * (6 * t + i)] = (uint32_t)mine.a[0][t][i];
-#pragma unroll
-        for (int j = 0; j < kScaleWords; ++j) x[64 * (6 * kTerms + j)] = (uint32_t)mine.scw[0][j];
-      }
-      __syncthreads();  // (its wait for LDS reads also ends this wave's reads of the staging area)
-      if (r0 == 0 && 1 < nmy) fill(1);
-#pragma unroll
-      for (int g = r0; g < r0 + kXchGroups && g < G; ++g) {
-        const uint32_t *x = &sh.a.xch[g - r0][0][lane];
-#pragma unroll
-        for (int t = 0; t < kTerms; ++t) {
-          int v[6];
-#pragma unroll
-          for (int i = 0; i < 6; ++i) v[i] = (int)x[64 * (6 * t + i)];
-          q[g].a[0][t] = v8i{v[0], v[1], v[2], v[3], v[4], v[5], 0, 0};
-        }
-#pragma unroll
-        for (int j = 0; j < kScaleWords; ++j) q[g].scw[0][j] = (int)x[64 * (6 * kTerms + j)];
-      }
-      __syncthreads();  // the exchange area is free again (it is the score array)
-    }
+    __syncthreads();  // every wave has read the terms and weights: the slots are free
+    if (1 < nmy) fill(1);
   }
 
   uint32_t omax = 0;  // largest score part of this thread's rows
