@@ -35,8 +35,8 @@ namespace csa {
 
 constexpr int kSelThreads = kAttnThreads;  // 512
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelKPT = 16;                           // heads per thread in registers
-constexpr int kSelRegHeads = kSelThreads * kSelKPT;  // 8192
+constexpr int kSelKPT = 8;                            // heads per thread in registers
+constexpr int kSelRegHeads = kSelThreads * kSelKPT;  // 4096
 constexpr int kSelBins = 2 * kSelThreads;             // histogram bins per pass
 constexpr int kSelCap = 4096;                         // candidates held in LDS
 constexpr int kSelTarget = 1024;                      // candidates at which G is good enough

@@ -60,7 +60,7 @@ def _tricky_scores(n, seed):
     return s
 
 
-@pytest.mark.parametrize("n", [0, 1, 2, 100, 511, 512, 513, 2047, 2048, 2049, 5000, 70001])
+@pytest.mark.parametrize("n", [0, 1, 2, 100, 511, 512, 513, 2047, 2048, 2049, 5000, 70001, 3_000_001])
 def test_topk_matches_oracle_exactly(csa, orc, n):
     s = _tricky_scores(n, n)
     for k in (512, 1, 37):
@@ -205,8 +205,10 @@ def test_decode_step_ragged_sessions(csa, orc):
         _check_session(orc, s, g)
 
 
-def test_fused_equals_unfused(csa):
-    s = gen.session(1)
+@pytest.mark.parametrize("n_rows", [None, 2_500_000])
+def test_fused_equals_unfused(csa, n_rows):
+    # 2.5M rows: more tile heads than the selection holds in registers
+    s = gen.session(1) if n_rows is None else gen.session(1, n_rows=n_rows)
     d = gu.to_dev(s)
     step = csa.decode_step([dict(d)], s["softmax_scale"])[0]
     scores = csa.score(d["idx_rows"], d["q_idx"], d["w_idx"])
