@@ -12,8 +12,12 @@ HEADER = os.path.join(ROOT, "include", "csa.h")
 
 @pytest.fixture(scope="module")
 def csa():
-    from long_context_sparse_score_amd import _build
+    import importlib.util
 
+    spec = importlib.util.spec_from_file_location(
+        "_csa_build", os.path.join(ROOT, "long_context_sparse_score_amd", "_build.py"))
+    _build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(_build)  # by path: the package import needs the library
     if not os.path.exists(_build.LIB):
         _build.build()
     import long_context_sparse_score_amd as m
