@@ -12,7 +12,7 @@
 namespace csa {
 
 // Tile of the score kernel: rows scored by one workgroup and kept in LDS.
-constexpr int kMaxTileRows = 4096;
+constexpr int kMaxTileRows = 2048;
 constexpr int kMinTileRows = 512;
 // Heads per tile: the tile's exact top-H keys, H in {8, 16, 32, 64}.
 constexpr int kMinTileHeads = 8;

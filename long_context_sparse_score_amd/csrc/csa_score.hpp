@@ -12,7 +12,7 @@
 // four UE8M0 bytes are the B block scales (one per 32 values, exactly the
 // row's block structure).  The fp32 query cannot be an MX operand, so it is
 // split into kTerms fp6 (E2M3) terms with their own E8M0 block scales,
-//     q = sum_t qt + r,   |r| <= 2^-19.6 * blockmax|q| per element,
+//     q = sum_t qt + r,   |r| <= 2^-19.9 * blockmax|q| per element,
 // and the dot product is the fp32 accumulation of the kTerms exact-product
 // MFMAs.  Every product is exact; accumulation is fp32 inside the matrix
 // core.  Each lane splits its own fragment in registers (split_qfrag).
@@ -55,43 +55,50 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 
 // This lane's query terms, split from its 32 fp32 query values x (head
 // 16 g + l%16 of group g, values [32(l/16), +32): the lane's A operand row
-// and K slice); a head past the query's heads (live false) gets zero terms.
-// With r the residual (initially the values):
-//   E   = smallest exponent with max|r| / 2^E <= 7.5 (E2M3's largest value),
-//         at least -126,
-//   q_t = RNE_E2M3(r / 2^E) * 2^E,   r <- r - q_t   (exact in fp32),
-// repeated kTerms times: the block maximum of r shrinks by at least 2^-3.9
-// per term, so after 5 terms every element is within 2^-19.6 of the block
-// maximum of q.  The conversions are gfx950's scaled fp6 instructions
-// (round to nearest even, saturating; verified on MI355X): the packing one
-// interleaves its two 16-value inputs (even, odd positions), so value i
-// lands at bit 6i, the MFMA operand order; the unpacking one returns the
-// exact term values for the residual.
-__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float (&x)[32], bool live) {
+// and K slice).  With r the residual (initially the values):
+//   E_0 = smallest exponent with max|x| / 2^E <= 7.5 (E2M3's largest
+//         value), E_t = max(E_0 - 4t, -126),
+//   q_t = RNE_E2M3(r / 2^E_t) * 2^E_t,   r <- r - q_t   (exact in fp32),
+// for t < kTerms.  A term's rounding error is at most a quarter of its
+// scale (half the 0.5 spacing of E2M3's top binade), which the next term's
+// range 7.5 * 2^(E_t - 4) holds without saturating; after 5 terms
+// |r| <= 2^-2 * 2^(E_0 - 16) < 2^-19.9 * max|x|, since max|x| > 3.75 * 2^E_0.
+// Heads past the query's heads carry a zero weight (load_qweights), so
+// their terms (split from a clamped head) add exact zeros to the score.
+// The conversions are gfx950's scaled fp6 instructions (round to nearest
+// even, saturating; verified on MI355X): the packing one interleaves its
+// two 16-value inputs (even, odd positions), so value i lands at bit 6i,
+// the MFMA operand order; the unpacking one returns the exact term values
+// for the residual.
+__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float (&x)[32]) {
   v16f_q re, ro;
+  float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    re[i] = live ? x[2 * i] : 0.0f;
-    ro[i] = live ? x[2 * i + 1] : 0.0f;
+    re[i] = x[2 * i];
+    ro[i] = x[2 * i + 1];
+    amax = fmaxf(amax, fmaxf(fabsf(re[i]), fabsf(ro[i])));
   }
+  // amax = m 2^e, m in [1, 2): amax / 2^(e-2) = 4m is in [4, 8), above 7.5
+  // when m > 1.875; a zero block keeps scale 2^0 (its codes are zero)
+  const uint32_t ab = __float_as_uint(amax);
+  int E0 = (int)(ab >> 23) - 129 + ((ab & 0x7FFFFFu) > 0x700000u ? 1 : 0);
+  E0 = amax == 0.0f ? 0 : E0;
+  E0 = E0 < -126 ? -126 : (E0 > 127 ? 127 : E0);
 #pragma unroll
   for (int w = 0; w < kScaleWords; ++w) q.scw[0][w] = 0;
 #pragma unroll
   for (int t = 0; t < kTerms; ++t) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(re[i]), fabsf(ro[i])));
-    const float am = amax > 0.0f ? amax : 1.0f;  // a zero block keeps scale 2^0 and zero codes
-    int E = ilogbf(am) - 2;                         // am / 2^E in [4, 8)
-    if (ldexpf(am, -E) > 7.5f) E += 1;
-    E = E < -126 ? -126 : (E > 127 ? 127 : E);
-    const float sc = ldexpf(1.0f, E);
+    const int E = E0 - 4 * t < -126 ? -126 : E0 - 4 * t;
+    const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
     const v6u_q c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(re, ro, sc);
-    const v32f_q d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
+    if (t + 1 < kTerms) {
+      const v32f_q d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      re[i] -= d[2 * i];
-      ro[i] -= d[2 * i + 1];
+      for (int i = 0; i < 16; ++i) {
+        re[i] -= d[2 * i];
+        ro[i] -= d[2 * i + 1];
+      }
     }
     q.a[0][t] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4], (int)c[5], 0, 0};
     q.scw[0][t / 4] |= (E + 127) << (8 * (t % 4));

@@ -50,23 +50,26 @@ static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
 
-constexpr int kRingDepth = 3;     // chunks resident per wave: D - 1 in flight
+constexpr int kRingDepth = 4;     // chunks resident per wave: D - 1 in flight
 constexpr int kTileCandCap = 256; // keys >= theta ranked directly
 constexpr int kXchWords = kTerms * 6 + kScaleWords;  // fp6 term registers + packed scales per lane
+constexpr int kXchQuads = (kXchWords + 3) / 4;       // ... exchanged as 16-byte quads
 static_assert(kRingDepth >= 2 && kRingDepth <= 4, "ring depth");
 static_assert(kChunkBytes % 16 == 0, "direct-to-LDS pieces stay aligned");
 
 struct TileShared {
-  alignas(16) uint8_t ring[kTileWaves][kRingDepth][kChunkBytes];  // one ring per wave
+  union {
+    alignas(16) uint8_t ring[kTileWaves][kRingDepth][kChunkBytes];  // one ring per wave (step 1)
+    struct {
+      uint64_t cand[kTileCandCap + 16];  // keys >= theta (+ over-read slack)
+      uint64_t theta[kTileWaves];
+      uint32_t ccnt;
+      SelScratch<kTileWaves> sc;
+    } h;  // step 2: the ring is drained by then
+  };
   struct {
     float score[kMaxTileRows];  // scores by tile position
   } a;
-  struct {
-    uint64_t cand[kTileCandCap + 16];  // keys >= theta (+ over-read slack)
-    uint64_t theta[kTileWaves];
-    uint32_t ccnt;
-    SelScratch<kTileWaves> sc;
-  } h;  // step 2
 };
 static_assert(sizeof(TileShared) <= 80 * 1024, "two workgroups per compute unit");
 
@@ -220,9 +223,10 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[
 // 8 KB) and all the weights direct-to-LDS into its ring slots 1 and 2 ahead
 // of its first chunk, so they arrive first and the split runs while the
 // chunk is in flight.  Each head's 512 bytes land at a 528-byte stride, so
-// the split's reads spread over the LDS banks; each wave then writes its group's terms over its own staging area (word d
-// of lane l at 4 (64 d + l)), and after one barrier every wave reads every
-// group's terms.  The second chunk is issued once a second barrier has
+// the split's reads spread over the LDS banks; each wave then writes its
+// group's terms over its own staging area (16-byte quad j of lane l at
+// 16 (64 j + l)), and after one barrier every wave reads every group's
+// terms.  The chunks after the first are issued once a second barrier has
 // released the slots.
 template <int G>
 __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
@@ -232,7 +236,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   static_assert(kRingDepth >= 3, "the query is staged in ring slots 1 and 2");
   constexpr int kStageHead = 528, kStageW = 16 * kStageHead;
   static_assert(kStageW + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
-  static_assert(kXchWords * 64 * 4 <= kStageW, "the terms leave the weights alone");
+  static_assert(kXchQuads * 64 * 16 <= kStageW, "the terms leave the weights alone");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
   const int nfc = rows / kChunkRows;  // chunks wholly inside the buffer
@@ -280,37 +284,51 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
         x[4 * i + 3] = v.w;
       }
       QFrag<1> mine;
-      split_qfrag(mine, x, 16 * wave + (lane & 15) < n_idx_heads);
+      split_qfrag(mine, x);
       // the terms over the staging area (this wave's reads of it come first):
-      // word d of lane l at stage + 4 (64 d + l)
-      uint32_t *x4 = reinterpret_cast<uint32_t *>(stage) + lane;
+      // the lane's 32 words (6 per term, then the packed scales) as eight
+      // 16-byte quads, quad j of lane l at stage + 16 (64 j + l)
+      uint32_t w[kXchQuads * 4];
 #pragma unroll
       for (int t = 0; t < kTerms; ++t)
 #pragma unroll
-        for (int i = 0; i < 6; ++i) x4[64 * (6 * t + i)] = (uint32_t)mine.a[0][t][i];
+        for (int i = 0; i < 6; ++i) w[6 * t + i] = (uint32_t)mine.a[0][t][i];
 #pragma unroll
-      for (int j = 0; j < kScaleWords; ++j) x4[64 * (6 * kTerms + j)] = (uint32_t)mine.scw[0][j];
+      for (int j = 0; j < kScaleWords; ++j) w[6 * kTerms + j] = (uint32_t)mine.scw[0][j];
+#pragma unroll
+      for (int j = 6 * kTerms + kScaleWords; j < kXchQuads * 4; ++j) w[j] = 0u;
+      uint4 *x16 = reinterpret_cast<uint4 *>(stage) + lane;
+#pragma unroll
+      for (int j = 0; j < kXchQuads; ++j) x16[64 * j] = uint4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
     }
     __syncthreads();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint32_t *x4 = reinterpret_cast<const uint32_t *>(&sh.ring[g][1][0]) + lane;
+      const uint4 *x16 = reinterpret_cast<const uint4 *>(&sh.ring[g][1][0]) + lane;
+      uint32_t w[kXchQuads * 4];
 #pragma unroll
-      for (int t = 0; t < kTerms; ++t) {
-        int v[6];
-#pragma unroll
-        for (int i = 0; i < 6; ++i) v[i] = (int)x4[64 * (6 * t + i)];
-        q[g].a[0][t] = v8i{v[0], v[1], v[2], v[3], v[4], v[5], 0, 0};
+      for (int j = 0; j < kXchQuads; ++j) {
+        const uint4 v = x16[64 * j];
+        w[4 * j] = v.x;
+        w[4 * j + 1] = v.y;
+        w[4 * j + 2] = v.z;
+        w[4 * j + 3] = v.w;
       }
 #pragma unroll
-      for (int j = 0; j < kScaleWords; ++j) q[g].scw[0][j] = (int)x4[64 * (6 * kTerms + j)];
+      for (int t = 0; t < kTerms; ++t)
+        q[g].a[0][t] = v8i{(int)w[6 * t], (int)w[6 * t + 1], (int)w[6 * t + 2], (int)w[6 * t + 3],
+                           (int)w[6 * t + 4], (int)w[6 * t + 5], 0, 0};
+#pragma unroll
+      for (int j = 0; j < kScaleWords; ++j) q[g].scw[0][j] = (int)w[6 * kTerms + j];
     }
     // the weights (in slot 2, which the exchange leaves alone)
     const float *wl = reinterpret_cast<const float *>(stage + kStageW);
 #pragma unroll
     for (int g = 0; g < G; ++g) load_qweights(q[g], wl, n_idx_heads, g, lane);
     __syncthreads();  // every wave has read the terms and weights: the slots are free
-    if (1 < nmy) fill(1);
+#pragma unroll
+    for (int t = 1; t <= kRingDepth - 2; ++t)
+      if (t < nmy) fill(t);
   }
 
   uint32_t omax = 0;  // largest score part of this thread's rows
