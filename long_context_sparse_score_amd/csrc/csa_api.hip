@@ -287,7 +287,7 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
   SelectJob sj;
   fill_select(sj, job, CSA_TOPK);
-  sj.slices = kAttnGroupCount;
+  sj.slices = kAttnSlices;
   sj.attn_q = aq;
   sj.attn_part = part;
   sj.attn_ml = ml;

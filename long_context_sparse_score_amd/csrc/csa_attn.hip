@@ -3,8 +3,9 @@
 //   l[h][j] = scale * q_h . kv_j,   out[h] = sum_j softmax(l[h])_j kv_j,
 //   lse[h] = log sum_j exp(l[h][j]),
 // split over kAttnGroups groups of rows (csa_attn.hpp) and merged here.
-//   attn_rows_kernel  grid (kAttnGroups, sessions): the partial of group b
-//                     over the entries of sel_idx[0..n_sel) that belong to it
+//   attn_rows_kernel  grid (kAttnSlices, sessions): the partial of row group
+//                     b % 32 for head group b / 32, over the entries of
+//                     sel_idx[0..n_sel) that belong to the row group
 //                     (csa_sparse_attn; the decode step computes the same
 //                     partials inside its selection kernel);
 //   attn_combine      one thread per (head, dimension): merges the groups.
@@ -35,7 +36,7 @@ struct RowsShared {
 };
 
 __global__ void __launch_bounds__(kAttnThreads) attn_rows_kernel(const AttnArgs a) {
-  const int sess = blockIdx.y, grp = blockIdx.x;
+  const int sess = blockIdx.y, grp = blockIdx.x % kAttnGroups, hg = blockIdx.x / kAttnGroups;
   const AttnSession &S = a.s[sess];
   __shared__ RowsShared sh;
   if (threadIdx.x == 0) sh.cnt = 0;
@@ -51,7 +52,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_rows_kernel(const AttnArgs 
   __syncthreads();
   const int m = (int)sh.cnt;
   attn_order(sh.key, sh.row, m, sh.ordered);
-  attn_group_rows(a.qsplit + (size_t)sess * kAttnQVecs, sh.st, sh.ordered, m, S.kv_rows, a.softmax_scale, a.n_heads,
+  attn_group_rows(a.qsplit + (size_t)sess * kAttnQVecs, sh.st, sh.ordered, m, S.kv_rows, a.softmax_scale, a.n_heads, hg,
                   a.part + (size_t)sess * kAttnPartFloats + (size_t)grp * CSA_MAX_HEADS * kKvDim,
                   a.ml + (size_t)sess * kAttnMlFloats + (size_t)grp * CSA_MAX_HEADS * 2);
 }
@@ -88,7 +89,7 @@ static AttnArgs attn_args(const AttnSession *s, int n_sessions, int n_heads, flo
 hipError_t launch_attn_rows(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale,
                             const uint4 *qsplit, float *part, float *ml, hipStream_t st) {
   const AttnArgs a = attn_args(s, n_sessions, n_heads, softmax_scale, qsplit, part, ml);
-  attn_rows_kernel<<<dim3(kAttnGroups, n_sessions), kAttnThreads, 0, st>>>(a);
+  attn_rows_kernel<<<dim3(kAttnSlices, n_sessions), kAttnThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

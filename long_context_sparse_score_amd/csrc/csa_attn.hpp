@@ -1,42 +1,45 @@
 // csa_attn.hpp -- softmax attention over a group of selected KV rows on the
-// gfx950 bf16 matrix cores (V_MFMA_F32_16X16X32_BF16), the flash-decoding
-// split used by both the fused selection kernel and csa_sparse_attn.
+// gfx950 bf16 matrix cores, the flash-decoding split used by both the fused
+// selection kernel and csa_sparse_attn.
 //
-// The selected rows are partitioned into kAttnGroups fixed groups by a hash
-// of the row index; a workgroup takes one group, visits its rows in rank
-// (position) order, 32 at a time, and keeps for every head h
+// The selected rows are partitioned into kAttnGroups fixed row groups by a
+// hash of the row index, and the 64 heads into kAttnHeadGroups groups of 16;
+// a workgroup takes one (row group, head group) pair, visits the group's
+// rows in rank (position) order, 16 at a time, and keeps for every head h
 //   m_h = max logit seen, l_h = sum exp(l - m_h), acc_h[d] = sum exp(l - m_h) kv[d]
-// (rescaled when m_h grows).  It writes (m, l, acc) as the group's partial;
-// attn_combine merges the groups:
+// (rescaled when m_h grows).  It writes (m, l, acc) as the row group's
+// partial of its heads; attn_combine merges the row groups:
 //   out[h] = sum_b e^{m_b - M} acc_b / sum_b e^{m_b - M} l_b,
 //   lse[h] = M + log sum_b e^{m_b - M} l_b,   M = max_b m_b.
 // Logits l[h][j] = scale * q_h . kv_j and values use the decoded 512-value
 // row for both (DS4X page, "Packed cache ABI").  Every operand enters the
 // matrix cores exactly:
 //   * a decoded non-RoPE value is an E4M3 value times 2^(s-127): at most 4
-//     significant bits, one bf16 term (exact for magnitudes >= 2^-133);
+//     significant bits, one bf16 term (exact for magnitudes >= 2^-133),
+//     converted from the packed byte by gfx950's scaled fp8 conversion;
 //   * a RoPE value is FP16 (11 bits): hi = bf16(v), lo = v - hi, two terms;
 //   * the fp32 query is q0 + q1 + q2, q_t = bf16(q - q0 - ... - q_{t-1})
 //     (round to nearest even), residual below 2^-26 |q|; it is split once
-//     per call by the query-split kernel;
+//     per call (by the score kernel or the query-split kernel);
 //   * a softmax weight p in [0, 1] is hi + lo (two bf16 terms, residual
 //     below 2^-17 p).
-// Products of bf16 values are exact in fp32; sums are fp32.  Everything a
-// group computes depends only on its rows and their order, so the fused and
-// the stand-alone paths give identical bits.
+// Products of bf16 values are exact in fp32; sums are fp32 in a fixed
+// order.  Everything a workgroup computes depends only on its rows and their
+// order, so the fused and the stand-alone paths give identical bits.
 //
-// Lane layout of the 16x16x32 instruction (verified on MI355X): lane l holds
-// A[m = l%16][k = 8(l/16) .. +8) and B[k = 8(l/16) .. +8][n = l%16]; the
-// result gives lane l C[m = 4(l/16) + v][n = l%16], v < 4.
-// A workgroup is 8 waves; wave w takes head group g = w%4 (heads
-// 16g..16g+15) and half hv = w/4:
-//   logits: m = head, n = row, k = dimension; the wave covers dimension
-//           quarters 2hv and 2hv+1 (four K steps of 32 each) for the two
-//           16-row tiles of the batch; per row the four quarters are summed
-//           as (q0 + q1) + (q2 + q3), the pairs meeting in LDS.
-//   P V:    m = head, n = dimension, k = row (the batch's 32 rows); the
-//           wave covers the 128 dimensions of chunks 2hv
-//           and 2hv+1 (eight 16-wide tiles each).
+// Matrix-core shapes (lane layouts verified on MI355X):
+//   logits  V_MFMA_F32_16X16X32_BF16 with M = 16 rows, N = 16 heads,
+//           K = 32 dimensions: lane l holds A[row l%16][k 8(l/16) .. +8],
+//           B[k 8(l/16) .. +8][head l%16] and receives C[rows 4(l/16) + v][head l%16];
+//   P V     V_MFMA_F32_16X16X16_BF16 with M = 16 heads, N = 16 dimensions,
+//           K = 16 rows: lane l holds A[head l%16][rows 4(l/16) .. +4] --
+//           exactly the softmax weights it computed from its logits, so no
+//           transpose is needed -- and B[rows 4(l/16) .. +4][dim l%16], and
+//           receives C[heads 4(l/16) + v][dim l%16].
+// A workgroup is 8 waves: wave w forms the logits' K steps 2w and 2w + 1
+// (dimensions 64w .. 64w + 63) for all 16 rows and heads; the eight partial
+// logit tiles meet in LDS and every wave sums them in the same fixed order,
+// then runs the same softmax; for P V wave w owns dimensions 64w .. +64.
 #pragma once
 
 #include "../../include/csa.h"
@@ -47,11 +50,17 @@ namespace csa {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f_attn __attribute__((ext_vector_type(4)));
 
+typedef short v4s_attn __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf_attn __attribute__((ext_vector_type(2)));
+
 constexpr int kKvDim = 512;
 constexpr int kAttnThreads = 512;
-constexpr int kAttnGroups = 32;
-constexpr int kAttnBatch = 32;  // rows per matrix-core batch (the K of the P V product)
-constexpr int kKvLdsStride = kKvDim + 4;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kAttnGroups = 32;     // row groups
+constexpr int kAttnHeadGroups = 4;  // 16 heads each
+constexpr int kAttnSlices = kAttnGroups * kAttnHeadGroups;  // workgroups per session
+constexpr int kAttnBatch = 16;      // rows per matrix-core batch
+static_assert(kAttnWaves * 64 == kKvDim, "one 64-dimension block per wave");
 
 // Group of a selected row (also the workgroup of the fused selection that
 // ranks it): the top 5 bits of a multiplicative hash.
@@ -72,14 +81,12 @@ __device__ __forceinline__ size_t attn_q_index(int wave, int s, int t, int lane)
 // Packed rows staged in LDS, realigned: slot i holds its row's 583 bytes
 // from byte 0.
 constexpr int kRawStride = 592;  // bytes per slot: 148 dwords
-constexpr int kRawRows = 32;     // rows staged at once
+constexpr int kRawRows = 32;     // rows staged at once (two batches)
+static_assert(kRawRows % kAttnBatch == 0, "batches do not straddle a staging round");
 
 struct AttnStage {
-  float kv[kAttnBatch][kKvLdsStride];       // decoded rows of the batch
-  float lg[CSA_MAX_HEADS][kAttnBatch + 1];  // logits of the batch
-  float red[2][4][64][4];                   // half-sums of the logits [half][g]
-  int32_t row[kAttnBatch];                  // KV row, or -1 (padding)
-  uint32_t raw[kRawRows][kRawStride / 4];   // staged packed rows
+  uint32_t raw[kRawRows][kRawStride / 4];  // staged packed rows
+  float lgp[kAttnWaves][4][64];            // partial logit tiles [wave][v][lane]
 };
 
 // x = t0 + t1 + t2 + r: three bf16 terms, each the round-to-nearest-even of
@@ -124,40 +131,212 @@ __device__ __forceinline__ void attn_q_split_task(const float *__restrict__ qa, 
 }
 constexpr int kAttnQTasks = kAttnQVecs / 3;  // 4096
 
-// This lane's query terms: quarter 2hv + kl, K step s, term t.
+// This wave's query terms for head group g: K steps 2w and 2w + 1, three
+// terms each, in the B operand layout of the logits (lane l: head 16g +
+// l%16, dimensions 32 ks + 8(l/16) .. +8).
 struct AttnQuery {
-  v8bf a[2][4][3];
+  v8bf b[2][3];
 };
 
-__device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *qs) {
+__device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *qs, int g) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = wave & 3, hv = wave >> 2;
 #pragma unroll
-  for (int kl = 0; kl < 2; ++kl)
+  for (int j = 0; j < 2; ++j) {
+    const int ks = 2 * wave + j;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        const uint4 v = qs[attn_q_index(g + 4 * (2 * hv + kl), s, t, lane)];
-        q.a[kl][s][t] = __builtin_bit_cast(v8bf, v);
-      }
+    for (int t = 0; t < 3; ++t)
+      q.b[j][t] = __builtin_bit_cast(v8bf, qs[attn_q_index(g + 4 * (ks >> 2), ks & 3, t, lane)]);
+  }
 }
 
-// Per-wave state of a group: accumulator tiles (heads 16g + 4(l/16) + v,
-// dimensions 128(2hv + cl) + 16t + l%16) and the running max / sum of head
-// 16g + l%16.
+// Per-wave state of a workgroup: P V accumulator tiles (heads 4(l/16) + v of
+// the head group, dimensions 64w + 16i + l%16) and the running max / sum of
+// head l%16 (the same in every lane of that head and in every wave).
 struct AttnState {
-  v4f_attn acc[2][8];
+  v4f_attn acc[4];
   float m, l;
 };
 
 __device__ __forceinline__ void attn_init(AttnState &S) {
 #pragma unroll
-  for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) S.acc[cl][t] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < 4; ++i) S.acc[i] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
   S.m = -__builtin_inff();
   S.l = 0.0f;
+}
+
+__device__ __forceinline__ short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+
+// fp16 bits -> (bf16 hi, bf16 lo) with hi + lo == the fp16 value exactly.
+__device__ __forceinline__ void f16_split(uint32_t h, short &hi, short &lo) {
+  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  const __bf16 b = (__bf16)f;
+  hi = __builtin_bit_cast(short, b);
+  lo = bf16_bits(f - (float)b);
+}
+
+// Logits A operand of K step ks (dimensions 32 ks .. +32) for the row in
+// slot `slot`: the lane's 8 values at dimensions 32 ks + 8(l/16) .. +8, as
+// bf16 (lo: the RoPE remainder; zero for E4M3 steps).  Zero for a padding
+// row.
+__device__ __forceinline__ void attn_row_operand(const AttnStage &st, int slot, int ks, bool valid, v8bf &hi,
+                                                 v8bf &lo) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t *rb = reinterpret_cast<const uint8_t *>(&st.raw[slot][0]);
+  if (ks < kKvNope / 32) {
+    const uint2 c = *reinterpret_cast<const uint2 *>(rb + 32 * ks + 8 * (lane >> 4));
+    const float sc = ue8m0_scale(rb[kKvNope + 128 + (ks >> 1)]);
+    const v2bf_attn p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false);
+    const v2bf_attn p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true);
+    const v2bf_attn p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false);
+    const v2bf_attn p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true);
+    hi = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    if (!valid) hi = v8bf{};
+    lo = v8bf{};
+  } else {
+    const uint4 h4 = *reinterpret_cast<const uint4 *>(rb + kKvNope + 64 * (ks - kKvNope / 32) + 16 * (lane >> 4));
+    const uint32_t w[4] = {h4.x, h4.y, h4.z, h4.w};
+    short sh[8], sl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f16_split((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu, sh[i], sl[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hi[i] = valid ? __builtin_bit_cast(__bf16, sh[i]) : (__bf16)0.0f;
+      lo[i] = valid ? __builtin_bit_cast(__bf16, sl[i]) : (__bf16)0.0f;
+    }
+  }
+}
+
+// One batch: the rows in slots slot0 .. slot0 + 15, of which the first
+// `nvalid` (>= 1) are rows and the rest padding.  Updates this wave's
+// running softmax state and accumulators.  All kAttnThreads threads call it;
+// it ends with a barrier (the partial tiles and the staged rows are reused).
+__device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, AttnStage &st, int slot0, int nvalid,
+                                           float scale) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  // partial logits of the 16 rows x 16 heads over dimensions 64w .. +64
+  v4f_attn c = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ks = 2 * wave + j;  // uniform
+    v8bf hi, lo;
+    attn_row_operand(st, slot0 + lr, ks, lr < nvalid, hi, lo);
+#pragma unroll
+    for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, q.b[j][t], c, 0, 0, 0);
+    if (ks >= kKvNope / 32) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, q.b[j][t], c, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) st.lgp[wave][v][lane] = c[v];
+  __syncthreads();
+  // the full logits of rows 4(l/16) + v for head l%16, summed in a fixed order
+  float lg4[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float p[kAttnWaves];
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) p[w] = st.lgp[w][v][lane];
+    const float sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    lg4[v] = 4 * lg + v < nvalid ? scale * sum : -__builtin_inff();
+  }
+  // online softmax of head l%16 over the batch's rows (held by the lanes of
+  // that head in the four lane groups)
+  float mb = fmaxf(fmaxf(lg4[0], lg4[1]), fmaxf(lg4[2], lg4[3]));
+  mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+  mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+  const float m_new = fmaxf(S.m, mb);  // finite: the batch holds a row
+  const float alpha = __expf(S.m - m_new);
+  float pv[4], ps = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    pv[v] = __expf(lg4[v] - m_new);
+    ps += pv[v];
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  S.l = S.l * alpha + ps;
+  S.m = m_new;
+  v4s_attn ph, pl;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const __bf16 b = (__bf16)pv[v];
+    ph[v] = __builtin_bit_cast(short, b);
+    pl[v] = bf16_bits(pv[v] - (float)b);
+  }
+  // rescale: accumulator element v is head 4(l/16) + v, whose factor sits
+  // in lane 4(l/16) + v
+  float av[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * lg + v, 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) S.acc[i][v] *= av[v];
+  // acc += P V over this wave's 64 dimensions (4 tiles of 16)
+  const uint8_t *rb[4];
+  bool rv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rb[i] = reinterpret_cast<const uint8_t *>(&st.raw[slot0 + 4 * lg + i][0]);
+    rv[i] = 4 * lg + i < nvalid;
+  }
+  if (wave < kKvNope / 64) {  // E4M3 block `wave`: one scale per row
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = ue8m0_scale(rb[i][kKvNope + 128 + wave]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int d = 64 * wave + 16 * t + lr;
+      v4s_attn vb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)rb[i][d], sc[i], 0);
+        vb[i] = bf16_bits(rv[i] ? f : 0.0f);
+      }
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, S.acc[t], 0, 0, 0);
+    }
+  } else {  // the RoPE values
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int d = 16 * t + lr;  // RoPE index
+      v4s_attn vh, vl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        short h, l;
+        f16_split(*reinterpret_cast<const uint16_t *>(rb[i] + kKvNope + 2 * d), h, l);
+        vh[i] = rv[i] ? h : (short)0;
+        vl[i] = rv[i] ? l : (short)0;
+      }
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vh, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vh, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vl, S.acc[t], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // the partial tiles and staged rows are reused
+}
+
+// Write the workgroup's partial: acc [head][512] and (m, l) [head][2] of
+// head group g (part and ml point at the row group's partial).
+__device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, int g, float *__restrict__ part,
+                                           float *__restrict__ ml) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * g + 4 * lg + v;
+      if (h < n_heads) part[(size_t)h * kKvDim + 64 * wave + 16 * t + lr] = S.acc[t][v];
+    }
+  const int hh = 16 * g + lr;
+  if (wave == 0 && lg == 0 && hh < n_heads) {
+    ml[2 * hh] = S.m;
+    ml[2 * hh + 1] = S.l;
+  }
 }
 
 // Stage rows[0..m) (valid KV row indices, m <= kRawRows) into st.raw: slot
@@ -201,212 +380,6 @@ __device__ __forceinline__ void attn_stage_raw(const uint8_t *__restrict__ kv_ro
         if (i < m && j < kRawDwords) st.raw[i][j] = w;
       }
     }
-  }
-}
-
-// One batch: rows st.row[0..kAttnBatch) (-1 = padding) are decoded into
-// st.kv, their logits go to st.lg, and this wave's running softmax state and
-// accumulators are updated.  All kAttnThreads threads call it; it starts and
-// ends with a barrier.
-__device__ __forceinline__ void attn_batch(const uint4 *qsplit, AttnState &S, AttnStage &st, int slot0,
-                                           float scale) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  __syncthreads();  // st.row written
-  // the query terms (L2-resident, shared by every group) are loaded with the
-  // rows' bytes and live only through the logits
-  AttnQuery q;
-  load_attn_query(q, qsplit);
-  {
-    // decode: 32 rows x 512 values in two passes of 16, all LDS reads of a
-    // pass first.  Wave
-    // w takes values [64w, 64w + 64) of every row (one per lane): waves 0..6
-    // hold E4M3 values of one scale block per row, wave 7 the FP16 RoPE
-    // values, so the branch is uniform.  The conversions are gfx950's
-    // v_cvt_scalef32_f32_fp8 (code x scale, exact; checked on MI355X on all
-    // 256 codes, scale bytes 0..255 included) and v_cvt_f32_f16 (exact).
-    static_assert(kAttnThreads == kKvDim, "one value per lane and row");
-    constexpr int U = 16;  // rows per pass
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int col = 64 * wv + lane;
-#pragma unroll
-    for (int u0 = 0; u0 < kAttnBatch; u0 += U) {
-      const uint8_t *base = reinterpret_cast<const uint8_t *>(&st.raw[slot0 + u0][0]);
-      float x[U];
-      if (wv < kKvNope / 64) {
-        uint32_t code[U], sb[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          code[u] = base[u * kRawStride + col];
-          sb[u] = base[u * kRawStride + kKvNope + 128 + wv];  // the block's scale byte (same in every lane)
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t e = __builtin_amdgcn_readfirstlane(sb[u]);
-          x[u] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)code[u], ue8m0_scale(e), 0);
-        }
-      } else {
-        uint32_t h[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          h[u] = *reinterpret_cast<const uint16_t *>(base + u * kRawStride + kKvNope + 2 * (col - kKvNope));
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)h[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int32_t r = __builtin_amdgcn_readfirstlane(st.row[u0 + u]);
-        st.kv[u0 + u][col] = r >= 0 ? x[u] : 0.0f;
-      }
-    }
-  }
-  __syncthreads();
-  const int g = wave & 3, hv = wave >> 2;
-  // logits of the batch's 32 rows (two 16-row tiles nt), this wave's two
-  // dimension quarters; per row the four quarters are summed as
-  // (q0 + q1) + (q2 + q3), wave half hv finishing row tile nt = hv
-  v4f_attn cw[2];  // per row tile: quarters 2hv + 2hv+1
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    v4f_attn c[2];
-#pragma unroll
-    for (int kl = 0; kl < 2; ++kl) {
-      const int kq = 2 * hv + kl;
-      c[kl] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float *src = &st.kv[16 * nt + (lane & 15)][128 * kq + 32 * s + 8 * (lane >> 4)];
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = src[i];
-        v8bf hi;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hi[i] = (__bf16)f[i];
-#pragma unroll
-        for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], hi, c[kl], 0, 0, 0);
-        if (kq == 3 && s >= 2) {  // RoPE dimensions 448..511: the FP16 remainder
-          v8bf lo;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(f[i] - (float)hi[i]);
-#pragma unroll
-          for (int t = 0; t < 3; ++t) c[kl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[kl][s][t], lo, c[kl], 0, 0, 0);
-        }
-      }
-    }
-    cw[nt] = c[0] + c[1];
-  }
-  {
-    const v4f_attn own = hv == 0 ? cw[0] : cw[1], other = hv == 0 ? cw[1] : cw[0];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) st.red[hv][g][lane][v] = other[v];  // the partner's row tile
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float part = st.red[1 - hv][g][lane][v];
-      const float sum = hv == 0 ? own[v] + part : part + own[v];  // (q0 + q1) + (q2 + q3)
-      const int n = 16 * hv + (lane & 15);
-      st.lg[16 * g + 4 * (lane >> 4) + v][n] = st.row[n] >= 0 ? scale * sum : -__builtin_inff();
-    }
-  }
-  __syncthreads();
-  // online softmax of this lane's head over the batch's rows: lane l holds
-  // rows 8(l/16)..+8
-  const int hh = 16 * g + (lane & 15);
-  float pl[8];
-  float mb = -__builtin_inff();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    pl[i] = st.lg[hh][8 * (lane >> 4) + i];
-    mb = fmaxf(mb, pl[i]);
-  }
-  mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-  mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-  const float m_new = fmaxf(S.m, mb);
-  const float mref = m_new == -__builtin_inff() ? 0.0f : m_new;
-  const float alpha = __expf(S.m - mref);
-  float ps = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    pl[i] = __expf(pl[i] - mref);
-    ps += pl[i];
-  }
-  ps += __shfl_xor(ps, 16, 64);
-  ps += __shfl_xor(ps, 32, 64);
-  S.l = S.l * alpha + ps;
-  S.m = m_new;
-  v8bf ph, plo;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ph[i] = (__bf16)pl[i];
-    plo[i] = (__bf16)(pl[i] - (float)ph[i]);
-  }
-  // rescale the accumulators: element v of a tile is head 16g + 4(l/16) + v,
-  // whose factor sits in lane 4(l/16) + v
-  float av[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * (lane >> 4) + v, 64);
-#pragma unroll
-  for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) S.acc[cl][t][v] *= av[v];
-  // acc += P V over the batch's 32 rows (the K of the product)
-#pragma unroll
-  for (int cl = 0; cl < 2; ++cl) {
-    const int cc = 2 * hv + cl;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int d = 128 * cc + 16 * t + (lane & 15);
-      v8bf vh, vl;
-      float vf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        vf[i] = st.kv[8 * (lane >> 4) + i][d];
-        vh[i] = (__bf16)vf[i];
-      }
-      S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vh, S.acc[cl][t], 0, 0, 0);
-      S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vh, S.acc[cl][t], 0, 0, 0);
-      if (cc == 3 && t >= 4) {  // RoPE dimensions: the FP16 remainder
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vl[i] = (__bf16)(vf[i] - (float)vh[i]);
-        S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vl, S.acc[cl][t], 0, 0, 0);
-        S.acc[cl][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vl, S.acc[cl][t], 0, 0, 0);
-      }
-    }
-  }
-  __syncthreads();  // the stage is reused by the next batch
-}
-
-// Write the group's partial: acc [head][512] and (m, l) [head][2].
-__device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, float *__restrict__ part,
-                                           float *__restrict__ ml) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = wave & 3, hv = wave >> 2;
-  if (16 * g + 15 < n_heads) {  // every head of the wave exists (uniform)
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int h = 16 * g + 4 * (lane >> 4) + v;
-          part[(size_t)h * kKvDim + 128 * (2 * hv + cl) + 16 * t + (lane & 15)] = S.acc[cl][t][v];
-        }
-  } else if (16 * g < n_heads) {
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int h = 16 * g + 4 * (lane >> 4) + v;
-          if (h < n_heads) part[(size_t)h * kKvDim + 128 * (2 * hv + cl) + 16 * t + (lane & 15)] = S.acc[cl][t][v];
-        }
-  }
-  const int hh = 16 * g + (lane & 15);
-  if (hv == 0 && lane < 16 && hh < n_heads) {
-    ml[2 * hh] = S.m;
-    ml[2 * hh + 1] = S.l;
   }
 }
 
@@ -455,23 +428,24 @@ __device__ __forceinline__ void attn_order(const int32_t *keys, const int32_t *r
   __syncthreads();
 }
 
-// Attention over a group's rows (in order) -> its partial.  All threads
-// call it.
-__device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &st, const int32_t *rows,
-                                                int m,
-                                                const uint8_t *__restrict__ kv_rows, float scale, int n_heads,
+// Attention over a row group's rows (in order) for head group g -> the
+// partial of those heads.  All threads call it.
+__device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &st, const int32_t *rows, int m,
+                                                const uint8_t *__restrict__ kv_rows, float scale, int n_heads, int g,
                                                 float *__restrict__ part, float *__restrict__ ml) {
+  AttnQuery q;
+  load_attn_query(q, qsplit, g);
   AttnState S;
   attn_init(S);
   for (int b0 = 0; b0 < m; b0 += kAttnBatch) {
-    const int slot0 = b0 & (kRawRows - 1);
-    if (slot0 == 0)  // stage the next kRawRows rows (the previous batch ended with a barrier)
+    const int slot0 = b0 % kRawRows;
+    if (slot0 == 0) {  // the previous batch ended with a barrier
       attn_stage_raw(kv_rows, rows + b0, m - b0 < kRawRows ? m - b0 : kRawRows, st);
-    if (threadIdx.x < kAttnBatch) st.row[threadIdx.x] = b0 + (int)threadIdx.x < m ? rows[b0 + threadIdx.x] : -1;
-    // starts with a barrier: rows staged, st.row written
-    attn_batch(qsplit, S, st, slot0, scale);
+      __syncthreads();
+    }
+    attn_batch(q, S, st, slot0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
   }
-  attn_store(S, n_heads, part, ml);
+  attn_store(S, n_heads, g, part, ml);
 }
 
 }  // namespace csa

@@ -62,7 +62,7 @@ struct SelectJob {
   const uint64_t *heads;
   int64_t heads_stride;
   // attention partials of the selected rows (attn_part == nullptr: none);
-  // then slices must equal the number of attention groups (32)
+  // then slices must equal kAttnSlices (row groups x head groups)
   const uint4 *attn_q;  // [session][attention query split]
   float *attn_part;     // [session][group][64][512]
   float *attn_ml;       // [session][group][64][2]
@@ -82,8 +82,6 @@ struct AttnSession {
   int32_t n_sel;
 };
 
-// Attention groups (flash-decoding split of the selected rows).
-constexpr int kAttnGroupCount = 32;
 
 hipError_t launch_dequant_idx(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
 hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStream_t st);

@@ -19,11 +19,13 @@
 //   3. If the candidates overflow the LDS buffer (many ties, crowded
 //      winners), the exact k_eff-th key among them replaces G.
 //   4. The candidates are ranked exactly (rank = number of larger
-//      candidates).  Workgroup b ranks the candidates whose row hashes to b,
-//      writes sel_idx[rank] / sel_score[rank] for ranks < k_eff, and (when
-//      asked) runs the attention of those rows in rank order and writes the
-//      group's partial (csa_attn.hpp; the workgroup index is the row's
-//      attention group, so the partials equal csa_sparse_attn's).
+//      candidates).  Workgroup b ranks the candidates whose row hashes to
+//      slice b and writes sel_idx[rank] / sel_score[rank] for ranks < k_eff.
+//      With attention, the slices are the kAttnGroups row groups and four
+//      workgroups (one per 16-head group) share each: all four rank the
+//      row group's candidates, the first writes the selection, and each runs
+//      the attention of those rows in rank order for its heads and writes
+//      their partial (csa_attn.hpp; the same partials as csa_sparse_attn's).
 // Selection keys are (ord32(score) << 32) | (2^32 - 1 - row): distinct,
 // larger = better; 0 means "no key".
 #include "csa_attn.hpp"
@@ -185,12 +187,20 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       sel_idx[r] = -1;
       if (sel_score) sel_score[r] = -__builtin_inff();
     }
+  // ATTN: workgroup b ranks (and attends over) the rows of row group
+  // b % kAttnGroups, for head group b / kAttnGroups; the head-group-0
+  // workgroups write the selection
+  const int nslice = ATTN ? kAttnGroups : (int)gridDim.x;
+  const uint32_t myslice = ATTN ? blockIdx.x % kAttnGroups : blockIdx.x;
+  const int hgroup = ATTN ? (int)(blockIdx.x / kAttnGroups) : 0;
+  const bool writer = hgroup == 0;
   if (k_eff == 0) {
     if constexpr (ATTN) {  // an empty group partial: m = -inf, l = 0
-      float *ml = a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)blockIdx.x * CSA_MAX_HEADS * 2;
-      if (tid < a.n_heads) {
-        ml[2 * tid] = -__builtin_inff();
-        ml[2 * tid + 1] = 0.0f;
+      float *ml = a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)myslice * CSA_MAX_HEADS * 2;
+      const int h = 16 * hgroup + tid;
+      if (tid < 16 && h < a.n_heads) {
+        ml[2 * h] = -__builtin_inff();
+        ml[2 * h + 1] = 0.0f;
       }
     }
     return;
@@ -397,7 +407,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   // 4. rank this workgroup's candidates
   for (int i0 = 0; i0 < C; i0 += kSelThreads) {
     const int i = i0 + tid;
-    if (i < C && row_slice(key_row(sh.u.s.cand[i]), gridDim.x) == blockIdx.x) sh.u.s.mine[atomicAdd(&sh.nmine, 1u)] = (uint16_t)i;
+    if (i < C && row_slice(key_row(sh.u.s.cand[i]), nslice) == myslice) sh.u.s.mine[atomicAdd(&sh.nmine, 1u)] = (uint16_t)i;
   }
   __syncthreads();
   const int nm = (int)sh.nmine;
@@ -425,12 +435,14 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
     }
     if (lane == 0 && r < (uint32_t)k_eff) {
       const uint32_t row = key_row(x);
-      sel_idx[r] = (int32_t)row;
-      if (sel_score) {
-        if constexpr (ATTN)  // the fused path: the key holds the score
-          sel_score[r] = key_score(x);
-        else
-          sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+      if (writer) {
+        sel_idx[r] = (int32_t)row;
+        if (sel_score) {
+          if constexpr (ATTN)  // the fused path: the key holds the score
+            sel_score[r] = key_score(x);
+          else
+            sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+        }
       }
       const uint32_t p = atomicAdd(&sh.nloc, 1u);
       sh.loc_rank[p] = (int32_t)r;
@@ -445,8 +457,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   const int nl = (int)sh.nloc;
   attn_order(sh.loc_rank, sh.loc_row, nl, sh.ordered);
   attn_group_rows(a.attn_q + (size_t)sess * kAttnQVecs, sh.u.st, sh.ordered, nl, a.s[sess].kv_rows, a.softmax_scale, a.n_heads,
-                  a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)blockIdx.x * CSA_MAX_HEADS * kKvDim,
-                  a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)blockIdx.x * CSA_MAX_HEADS * 2);
+                  hgroup, a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)myslice * CSA_MAX_HEADS * kKvDim,
+                  a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)myslice * CSA_MAX_HEADS * 2);
 }
 
 hipError_t launch_select(const SelectJob &job, hipStream_t st) {
