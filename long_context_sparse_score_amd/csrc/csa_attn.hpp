@@ -206,12 +206,20 @@ __device__ __forceinline__ void attn_row_operand(const AttnStage &st, int slot, 
   }
 }
 
-// One batch: the rows in slots slot0 .. slot0 + 15, of which the first
-// `nvalid` (>= 1) are rows and the rest padding.  Updates this wave's
-// running softmax state and accumulators.  All kAttnThreads threads call it;
-// it ends with a barrier (the partial tiles and the staged rows are reused).
-__device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, AttnStage &st, int slot0, int nvalid,
-                                           float scale) {
+// Staging slot of row b0 + i of a group's ordered rows: slotmap[b0 + i], or
+// (b0 + i) % kRawRows without a map; slot 0 for padding (i >= nvalid).
+__device__ __forceinline__ int attn_slot(const int32_t *slotmap, int b0, int i, int nvalid) {
+  if (i >= nvalid) return 0;
+  return slotmap ? slotmap[b0 + i] : (b0 + i) % kRawRows;
+}
+
+// One batch: rows b0 .. b0 + 15 of the group's ordered rows, of which the
+// first `nvalid` (>= 1) exist and the rest are padding; row b0 + i is staged
+// in slot attn_slot(slotmap, b0, i, nvalid).  Updates this wave's running
+// softmax state and accumulators.  All kAttnThreads threads call it; it ends
+// with a barrier (the partial tiles and the staged rows are reused).
+__device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, AttnStage &st, const int32_t *slotmap,
+                                           int b0, int nvalid, float scale) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   // partial logits of the 16 rows x 16 heads over dimensions 64w .. +64
@@ -220,7 +228,7 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
   for (int j = 0; j < 2; ++j) {
     const int ks = 2 * wave + j;  // uniform
     v8bf hi, lo;
-    attn_row_operand(st, slot0 + lr, ks, lr < nvalid, hi, lo);
+    attn_row_operand(st, attn_slot(slotmap, b0, lr, nvalid), ks, lr < nvalid, hi, lo);
 #pragma unroll
     for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, q.b[j][t], c, 0, 0, 0);
     if (ks >= kKvNope / 32) {
@@ -279,7 +287,7 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
   bool rv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    rb[i] = reinterpret_cast<const uint8_t *>(&st.raw[slot0 + 4 * lg + i][0]);
+    rb[i] = reinterpret_cast<const uint8_t *>(&st.raw[attn_slot(slotmap, b0, 4 * lg + i, nvalid)][0]);
     rv[i] = 4 * lg + i < nvalid;
   }
   if (wave < kKvNope / 64) {  // E4M3 block `wave`: one scale per row
@@ -383,6 +391,53 @@ __device__ __forceinline__ void attn_stage_raw(const uint8_t *__restrict__ kv_ro
   }
 }
 
+// Staging in two phases, so that other work runs while the rows are in
+// flight: attn_stage_issue loads rows rows[i] (i < m <= kRawRows; wave w
+// takes i = w, w + 8, ...) into registers, attn_stage_finish writes them
+// realigned into slots i, exactly as attn_stage_raw does.
+struct AttnStageRegs {
+  uint32_t lo[kRawRows / kAttnWaves][3], hi[kRawRows / kAttnWaves][3], sh[kRawRows / kAttnWaves];
+};
+
+__device__ __forceinline__ void attn_stage_issue(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
+                                                 AttnStageRegs &R) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
+    const int i = wave + kAttnWaves * u;
+    if (i < m) {  // uniform
+      const int32_t r = __builtin_amdgcn_readfirstlane(rows[i]);
+      const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
+      const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
+      const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);
+      const int last = (int)(mis + kKvRowBytes - 1) >> 2;
+      R.sh[u] = 8u * mis;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        R.lo[u][k] = a0[j < last ? j : last];
+        R.hi[u][k] = a0[j + 1 < last ? j + 1 : last];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void attn_stage_finish(const AttnStageRegs &R, int m, AttnStage &st) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
+    const int i = wave + kAttnWaves * u;
+    if (i < m) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        const uint32_t w = (uint32_t)(((uint64_t)R.hi[u][k] << 32 | R.lo[u][k]) >> R.sh[u]);
+        if (j < kRawDwords) st.raw[i][j] = w;
+      }
+    }
+  }
+}
+
 // Merge of the group partials of one output element e = h * 512 + d:
 //   out = sum_b e^{m_b - M} acc_b / sum_b e^{m_b - M} l_b,  M = max_b m_b,
 //   lse = M + log sum_b e^{m_b - M} l_b
@@ -443,8 +498,23 @@ __device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &
       attn_stage_raw(kv_rows, rows + b0, m - b0 < kRawRows ? m - b0 : kRawRows, st);
       __syncthreads();
     }
-    attn_batch(q, S, st, slot0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
+    attn_batch(q, S, st, nullptr, b0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
   }
+  attn_store(S, n_heads, g, part, ml);
+}
+
+// The same attention over m <= kRawRows rows that are already staged: the
+// i-th row in order sits in slot slotmap[i].  Same bits as attn_group_rows
+// over those rows in that order.  All threads call it.
+__device__ __forceinline__ void attn_staged_rows(const uint4 *qsplit, AttnStage &st, const int32_t *slotmap, int m,
+                                                 float scale, int n_heads, int g, float *__restrict__ part,
+                                                 float *__restrict__ ml) {
+  AttnQuery q;
+  load_attn_query(q, qsplit, g);
+  AttnState S;
+  attn_init(S);
+  for (int b0 = 0; b0 < m; b0 += kAttnBatch)
+    attn_batch(q, S, st, slotmap, b0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
   attn_store(S, n_heads, g, part, ml);
 }
 

@@ -68,6 +68,11 @@ struct SelArgs {
 };
 static_assert(sizeof(SelArgs) <= 4096, "kernel argument block");
 
+// The early attention stage (at most k_eff <= 512 candidates, read with the
+// rank scan's slack) starts this many bytes into the selection union.
+constexpr int kEarlyStageOff = 8192;
+static_assert((CSA_TOPK + 4 * 64) * 8 <= kEarlyStageOff, "the stage leaves the live candidates alone");
+
 struct SelShared {
   union {
     struct {
@@ -84,6 +89,8 @@ struct SelShared {
   uint32_t ccnt, nfull, nmine, nloc;
   uint32_t bin, ca, cb;
 };
+static_assert(kEarlyStageOff + sizeof(AttnStage) <= offsetof(SelShared, u.s.mine) - offsetof(SelShared, u),
+              "the early stage ends before the group list");
 
 // Lower bound G on the need-th largest of the keys that `visit` enumerates
 // (every thread visits its share, calling f(key) for each nonzero key): at
@@ -411,6 +418,57 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   }
   __syncthreads();
   const int nm = (int)sh.nmine;
+  if constexpr (ATTN) {
+    if (C <= k_eff && nm <= kRawRows) {  // uniform
+      // C >= k_eff always (G bounds the k_eff-th key), so here every
+      // candidate is selected: the row group attends over its candidates in
+      // key order (= rank order).  Their rows are staged while that order
+      // and the global ranks are formed; the stage sits in the union past
+      // the live candidates and before the group list.
+      AttnStage &est = *reinterpret_cast<AttnStage *>(reinterpret_cast<char *>(&sh.u) + kEarlyStageOff);
+      if (tid < nm) sh.loc_row[tid] = (int32_t)key_row(sh.u.s.cand[sh.u.s.mine[tid]]);
+      __syncthreads();
+      AttnStageRegs R;
+      attn_stage_issue(a.s[sess].kv_rows, sh.loc_row, nm, R);
+      if (wave == 0) {  // slot i (candidate mine[i]) -> its position in the group's key order
+        const uint64_t x = lane < nm ? sh.u.s.cand[sh.u.s.mine[lane]] : 0ull;
+        const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
+        int pos = 0;
+        for (int j = 0; j < nm; ++j) {
+          const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xhi, j) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)xlo, j);
+          pos += y > x ? 1 : 0;
+        }
+        if (lane < nm) sh.ordered[pos] = lane;
+      }
+      // the global ranks: the row group's four workgroups split its
+      // candidates by row index (each workgroup lists and numbers its
+      // candidates in its own order), waves taking list entries in turn
+      for (int i = wave; i < nm; i += kSelWaves) {
+        const uint64_t x = sh.u.s.cand[sh.u.s.mine[i]];
+        if ((int)(key_row(x) % kAttnHeadGroups) != hgroup) continue;  // uniform over the wave
+        uint32_t r = 0;
+        for (int j0 = 0; j0 < C; j0 += 4 * 64) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 64 * u + lane;
+            const uint64_t y = sh.u.s.cand[j];
+            r += (uint32_t)__popcll(__ballot(j < C && y > x));
+          }
+        }
+        if (lane == 0) {
+          sel_idx[r] = (int32_t)key_row(x);
+          if (sel_score) sel_score[r] = key_score(x);
+        }
+      }
+      attn_stage_finish(R, nm, est);
+      __syncthreads();
+      attn_staged_rows(a.attn_q + (size_t)sess * kAttnQVecs, est, sh.ordered, nm, a.softmax_scale, a.n_heads, hgroup,
+                       a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)myslice * CSA_MAX_HEADS * kKvDim,
+                       a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)myslice * CSA_MAX_HEADS * 2);
+      return;
+    }
+  }
   // warm the L2 with the KV rows of this workgroup's candidates (a superset
   // of the rows it will attend over) while the ranks are computed
   uint32_t warm = 0;
