@@ -237,16 +237,20 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   constexpr int kStageHead = 528, kStageW = 16 * kStageHead;
   static_assert(kStageW + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
   static_assert(kXchQuads * 64 * 16 <= kStageW, "the terms leave the weights alone");
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: chunk bookkeeping stays scalar
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
   const int nfc = rows / kChunkRows;  // chunks wholly inside the buffer
   const int nmy = wave < nch ? (nch - wave + kTileWaves - 1) / kTileWaves : 0;  // this wave's chunks
   auto chunk = [&](int s) __attribute__((always_inline)) { return wave + kTileWaves * s; };
+  // this wave's first chunk (uniform) and the lanes' piece offsets
+  const uint8_t *const wave_rows = uniform_ptr(idx_rows + (row0 + (int64_t)kChunkRows * wave) * kIdxRowBytes);
+  const ChunkLanes cl = chunk_lanes(lane);
   auto fill = [&](int s) __attribute__((always_inline)) {
     const int c = chunk(s);
     uint8_t *dst = &sh.ring[wave][s % kRingDepth][0];
     if (c < nfc)
-      issue_chunk(idx_rows, row0 + (int64_t)kChunkRows * c, (uint32_t)(uintptr_t)dst, lane);
+      issue_chunk_s(wave_rows + (size_t)s * (kTileWaves * kChunkBytes), cl, (uint32_t)(uintptr_t)dst, lane);
     else if (c < nch)
       copy_chunk_clamped(idx_rows, row0 + (int64_t)kChunkRows * c, n, dst, lane);
   };
