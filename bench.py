@@ -41,6 +41,9 @@ def parse():
                    help="repeat the oracle step until this much CPU time has been measured")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (scale for the HBM byte counters)")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the per-history-length figures of the other workloads")
+    p.add_argument("--sweep-steps", type=int, default=20)
     return p.parse_args()
 
 
@@ -104,6 +107,73 @@ def algorithmic_bytes(n_rows: int, n_idx_heads: int, n_heads: int) -> dict:
     return {"score": score, "attention": attn, "step": score + attn}
 
 
+def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host):
+    """Cold / warm / per-stage timing of `steps` decode steps of workload wl."""
+    t0 = time.time()
+    sess_np = [gen.session(wl.cid, s=i) for i in range(wl.n_sessions)]
+    sess = []
+    for s in sess_np:
+        sess.append({k: torch.from_numpy(s[k]).to(dev) for k in ("idx_rows", "kv_rows", "q_idx", "w_idx", "q_attn")})
+    scale = sess_np[0]["softmax_scale"]
+    print(f"[bench] workload {wl.name}: {wl.n_sessions} x {wl.n_rows} rows, generated in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    step = csa.DecodeStep(sess, scale)
+    stream = torch.cuda.current_stream()
+
+    def do_flush():
+        flush.sum()
+
+    for _ in range(warmup):
+        do_flush()
+        step()
+    torch.cuda.synchronize()
+
+    # cold steps: events bracket the decode step only
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for e0, e1 in ev:
+        do_flush()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    cold = [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    # warm steps: back to back
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(steps):
+        step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm = w0.elapsed_time(w1) / steps
+
+    # per-stage times (same work; events recorded between the stage launches
+    # on the launching stream)
+    nst = len(csa.STAGES)
+    st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(steps)]
+    for evs in st_ev:
+        do_flush()
+        step.timed(evs)
+    torch.cuda.synchronize()
+    stage_ms = [statistics.mean(evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in st_ev) for i in range(nst)]
+    r = {
+        "mean_ms": statistics.mean(cold),
+        "median_ms": statistics.median(cold),
+        "p10_ms": float(np.percentile(cold, 10)),
+        "p90_ms": float(np.percentile(cold, 90)),
+        "warm_ms": warm,
+        "wall_ms": wall * 1e3 / steps,
+        "stage_ms": stage_ms,
+        "score_ms": stage_ms[0],  # the score kernel's launch
+    }
+    del step, sess
+    torch.cuda.synchronize()
+    return (sess_np if keep_host else None), r
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -121,68 +191,18 @@ def main():
     import gen
     import long_context_sparse_score_amd as csa
 
-    wl = {w.name: w for w in gen.WORKLOADS}[a.workload]
+    workloads = {w.name: w for w in gen.WORKLOADS}
+    wl = workloads[a.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB: evicts the MALL and the L2s
 
-    t0 = time.time()
-    sess_np = [gen.session(wl.cid, s=i) for i in range(wl.n_sessions)]
-    sess = []
-    for s in sess_np:
-        sess.append({k: torch.from_numpy(s[k]).to(dev) for k in ("idx_rows", "kv_rows", "q_idx", "w_idx", "q_attn")})
+    sess_np, r = measure(wl, a.steps, a.warmup, flush, dev, csa, gen, np, torch, keep_host=True)
     scale = sess_np[0]["softmax_scale"]
-    print(f"[bench] workload {wl.name}: {wl.n_sessions} x {wl.n_rows} rows, generated in {time.time() - t0:.1f}s",
-          file=sys.stderr, flush=True)
-
-    step = csa.DecodeStep(sess, scale)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-    stream = torch.cuda.current_stream()
-
-    def do_flush():
-        flush.sum()
-
-    for _ in range(a.warmup):
-        do_flush()
-        step()
-    torch.cuda.synchronize()
-
-    # cold steps: events bracket the decode step only
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for e0, e1 in ev:
-        do_flush()
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    cold = [e0.elapsed_time(e1) for e0, e1 in ev]
-
-    # warm steps: back to back
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record(stream)
-    for _ in range(a.steps):
-        step()
-    w1.record(stream)
-    torch.cuda.synchronize()
-    warm = w0.elapsed_time(w1) / a.steps
-
-    # per-stage times (same work, events recorded between the stage launches)
-    nst = len(csa.STAGES)
-    st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(a.steps)]
-    for evs in st_ev:
-        do_flush()
-        step.timed(evs)
-    torch.cuda.synchronize()
-    stage_ms = [statistics.mean(evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in st_ev) for i in range(nst)]
-    score_ms = stage_ms[0]  # the score kernel's launch
-
     ab = algorithmic_bytes(wl.n_rows, wl.n_idx_heads, wl.n_heads)
-    ms = statistics.mean(cold)
-    med = statistics.median(cold)
+    ms = r["mean_ms"]
     step_bytes = ab["step"] * wl.n_sessions
-    score_gbs = ab["score"] * wl.n_sessions / (score_ms * 1e-3) / 1e9
+    score_gbs = ab["score"] * wl.n_sessions / (r["score_ms"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(ms, 5),
@@ -205,14 +225,14 @@ def main():
             "topk": 512,
             "cache": "cold: MALL and L2 flushed before each step, outside its events",
         },
-        "median_ms": round(med, 5),
-        "p10_ms": round(float(np.percentile(cold, 10)), 5),
-        "p90_ms": round(float(np.percentile(cold, 90)), 5),
-        "warm_ms_per_step": round(warm, 5),
-        "wall_ms_per_step_incl_flush": round(wall * 1e3 / a.steps, 5),
+        "median_ms": round(r["median_ms"], 5),
+        "p10_ms": round(r["p10_ms"], 5),
+        "p90_ms": round(r["p90_ms"], 5),
+        "warm_ms_per_step": round(r["warm_ms"], 5),
+        "wall_ms_per_step_incl_flush": round(r["wall_ms"], 5),
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2),
-        "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, stage_ms)},
+        "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, r["stage_ms"])},
         "roofline": {
             "kernel": "tile_kernel: query split + score + tile heads (all sessions, one launch)",
             "bound": "hbm",
@@ -221,10 +241,34 @@ def main():
             "unit": "GB/s",
             "frac": round(score_gbs / HBM_PEAK_GBS, 5),
             "traffic": measured_traffic(wl.name),
-            "launch_ms": round(score_ms, 5),
+            "launch_ms": round(r["score_ms"], 5),
             "algorithmic_bytes_per_launch": ab["score"] * wl.n_sessions,
         },
     }
+
+    if not a.no_sweep:
+        # every history length of the workload set: cold step latency, the
+        # score kernel's HBM fraction and the whole step's algorithmic GB/s
+        by = {}
+        for w in gen.WORKLOADS:
+            if w.name == wl.name:
+                rw = r
+            else:
+                _, rw = measure(w, a.sweep_steps, 2, flush, dev, csa, gen, np, torch, keep_host=False)
+            abw = algorithmic_bytes(w.n_rows, w.n_idx_heads, w.n_heads)
+            sg = abw["score"] * w.n_sessions / (rw["score_ms"] * 1e-3) / 1e9
+            by[w.name] = {
+                "rows_per_session": w.n_rows,
+                "sessions": w.n_sessions,
+                "cold_median_ms": round(rw["median_ms"], 5),
+                "warm_ms": round(rw["warm_ms"], 5),
+                "step_hbm_gbs": round(abw["step"] * w.n_sessions / (rw["median_ms"] * 1e-3) / 1e9, 2),
+                "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, rw["stage_ms"])},
+                "score_kernel_ms": round(rw["score_ms"], 5),
+                "score_kernel_hbm_frac": round(sg / HBM_PEAK_GBS, 5),
+            }
+            print(f"[bench] {w.name}: {by[w.name]}", file=sys.stderr, flush=True)
+        line["by_workload"] = by
 
     if not a.no_cpu_baseline:
         import oracle

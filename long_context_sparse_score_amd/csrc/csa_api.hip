@@ -52,6 +52,18 @@ int choose_tile_rows(int64_t total_rows) {
   return T;
 }
 
+// Largest selection grid that also runs the attention (about one
+// workgroup per compute unit).
+constexpr int kFusedAttnMaxWorkgroups = 256;
+
+// log2 of the row groups per session of the attention when it runs as its
+// own launch: about 512 workgroups (4 head groups each) over all sessions.
+int separate_groups_lg(int n_sessions) {
+  int lg = kAttnGroupsLg;
+  while (lg > 0 && n_sessions * (kAttnHeadGroups << lg) > 512) --lg;
+  return lg;
+}
+
 // Workgroups per session of the selection kernel: about one per compute
 // unit in total.
 int choose_slices(int n_sessions) {
@@ -233,8 +245,8 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   uint4 *aq = at<uint4>(ws, L.attn_q_off);
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
   hipError_t e = launch_attn_q_split(&q_attn, 1, n_heads, aq, st);
-  if (e == hipSuccess) e = launch_attn_rows(&s, 1, n_heads, softmax_scale, aq, part, ml, st);
-  if (e == hipSuccess) e = launch_attn_combine(&s, 1, n_heads, part, ml, st);
+  if (e == hipSuccess) e = launch_attn_rows(&s, 1, n_heads, softmax_scale, aq, part, ml, kAttnGroupsLg, st);
+  if (e == hipSuccess) e = launch_attn_combine(&s, 1, n_heads, part, ml, kAttnGroupsLg, st);
   return status_of(e);
 }
 
@@ -287,12 +299,22 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
   SelectJob sj;
   fill_select(sj, job, CSA_TOPK);
-  sj.slices = kAttnSlices;
-  sj.attn_q = aq;
-  sj.attn_part = part;
-  sj.attn_ml = ml;
-  sj.n_heads = n_heads;
-  sj.softmax_scale = softmax_scale;
+  // One session's selection workgroups also run its attention (one
+  // workgroup per row group and head group).  With many sessions that grid
+  // would take several rounds of the chip, so the selection runs alone and
+  // the attention follows as its own launch (same partials, same bits).
+  const bool fused_attn = n_sessions * kAttnSlices <= kFusedAttnMaxWorkgroups;
+  // separate attention: the sessions supply the parallelism, so fewer row
+  // groups (longer groups, smaller partials) per session
+  const int groups_lg = fused_attn ? kAttnGroupsLg : separate_groups_lg(n_sessions);
+  if (fused_attn) {
+    sj.slices = kAttnSlices;
+    sj.attn_q = aq;
+    sj.attn_part = part;
+    sj.attn_ml = ml;
+    sj.n_heads = n_heads;
+    sj.softmax_scale = softmax_scale;
+  }
   for (int i = 0; i < n_sessions; ++i) {
     sj.sel_idx[i] = sel[i];
     sj.sel_score[i] = sel_score[i];
@@ -306,9 +328,11 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_select(sj, st);
+  if (e == hipSuccess && !fused_attn)
+    e = launch_attn_rows(at_s, n_sessions, n_heads, softmax_scale, aq, part, ml, groups_lg, st);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess) e = launch_attn_combine(at_s, n_sessions, n_heads, part, ml, st);
+  if (e == hipSuccess) e = launch_attn_combine(at_s, n_sessions, n_heads, part, ml, groups_lg, st);
   if (e == hipSuccess) e = mark(5);
   return status_of(e);
 }

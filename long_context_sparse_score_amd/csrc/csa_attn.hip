@@ -3,9 +3,10 @@
 //   l[h][j] = scale * q_h . kv_j,   out[h] = sum_j softmax(l[h])_j kv_j,
 //   lse[h] = log sum_j exp(l[h][j]),
 // split over kAttnGroups groups of rows (csa_attn.hpp) and merged here.
-//   attn_rows_kernel  grid (kAttnSlices, sessions): the partial of row group
-//                     b % 32 for head group b / 32, over the entries of
-//                     sel_idx[0..n_sel) that belong to the row group
+//   attn_rows_kernel  grid (4 G, sessions), G = 2^groups_lg row groups: the
+//                     partial of row group b % G for head group b / G, over
+//                     the entries of sel_idx[0..n_sel) that belong to the
+//                     row group
 //                     (csa_sparse_attn; the decode step computes the same
 //                     partials inside its selection kernel);
 //   attn_combine      one thread per (head, dimension): merges the groups.
@@ -24,6 +25,7 @@ struct AttnArgs {
   float *ml;            // [session][kAttnMlFloats]
   int n_heads;
   float softmax_scale;
+  int groups_lg;  // 2^groups_lg row groups per session
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel argument block");
 
@@ -31,52 +33,98 @@ static_assert(sizeof(AttnArgs) <= 4096, "kernel argument block");
 
 struct RowsShared {
   AttnStage st;
-  int32_t key[CSA_TOPK + 16], row[CSA_TOPK], ordered[CSA_TOPK];
-  uint32_t cnt;
+  int32_t ordered[CSA_TOPK];
+  uint32_t wcnt[kAttnWaves];
 };
 
 __global__ void __launch_bounds__(kAttnThreads) attn_rows_kernel(const AttnArgs a) {
-  const int sess = blockIdx.y, grp = blockIdx.x % kAttnGroups, hg = blockIdx.x / kAttnGroups;
+  const int groups = 1 << a.groups_lg;
+  const int sess = blockIdx.y, grp = blockIdx.x % groups, hg = blockIdx.x / groups;
   const AttnSession &S = a.s[sess];
   __shared__ RowsShared sh;
-  if (threadIdx.x == 0) sh.cnt = 0;
+  // the row group's entries of sel_idx in position order: entry j goes to
+  // the number of the group's entries before it (n_sel <= 512 = one pass)
+  static_assert(kAttnThreads >= CSA_TOPK, "one entry per thread");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = tid;
+  const int32_t r = j < S.n_sel ? S.sel_idx[j] : -1;
+  const bool mine = r >= 0 && (int64_t)r < S.n_rows && attn_group((uint32_t)r, a.groups_lg) == (uint32_t)grp;
+  const uint64_t bal = __ballot(mine);
+  if (lane == 0) sh.wcnt[wave] = (uint32_t)__popcll(bal);
   __syncthreads();
-  for (int j = threadIdx.x; j < S.n_sel; j += kAttnThreads) {
-    const int32_t r = S.sel_idx[j];
-    if (r >= 0 && (int64_t)r < S.n_rows && attn_group((uint32_t)r) == (uint32_t)grp) {
-      const uint32_t p = atomicAdd(&sh.cnt, 1u);
-      sh.key[p] = j;
-      sh.row[p] = r;
-    }
+  uint32_t before = 0, m = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) {
+    before += w < wave ? sh.wcnt[w] : 0u;
+    m += sh.wcnt[w];
   }
+  if (mine) sh.ordered[before + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = r;
   __syncthreads();
-  const int m = (int)sh.cnt;
-  attn_order(sh.key, sh.row, m, sh.ordered);
-  attn_group_rows(a.qsplit + (size_t)sess * kAttnQVecs, sh.st, sh.ordered, m, S.kv_rows, a.softmax_scale, a.n_heads, hg,
+  attn_group_rows(a.qsplit + (size_t)sess * kAttnQVecs, sh.st, sh.ordered, (int)m, S.kv_rows, a.softmax_scale, a.n_heads, hg,
                   a.part + (size_t)sess * kAttnPartFloats + (size_t)grp * CSA_MAX_HEADS * kKvDim,
                   a.ml + (size_t)sess * kAttnMlFloats + (size_t)grp * CSA_MAX_HEADS * 2);
 }
 
 // ---------------------------------------------------------------- combine
 
-constexpr int kCombineThreads = 256;
+// Four workgroups per (head, session), one thread per dimension: the head's
+// group weights w_b = e^{m_b - M} and L = sum_b w_b l_b are formed once (in
+// group order, by one lane), then every dimension sums w_b acc_b in group
+// order:  out = (sum_b w_b acc_b) / L,  lse = M + log L.  Empty groups
+// (m = -inf) have weight 0; with no row at all out = 0 and lse = -inf.
+constexpr int kCombineThreads = 128;  // a quarter of the dimensions per workgroup
+constexpr int kCombineSplit = kKvDim / kCombineThreads;
 
 __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const AttnArgs a) {
-  const int sess = blockIdx.y;
+  const int sess = blockIdx.y, h = blockIdx.x / kCombineSplit;
+  const int d = (blockIdx.x % kCombineSplit) * kCombineThreads + threadIdx.x;
   const AttnSession &S = a.s[sess];
-  const int e = blockIdx.x * kCombineThreads + threadIdx.x;  // head * 512 + dimension
-  const int h = e / kKvDim;
-  if (h >= a.n_heads) return;
-  float lse;
-  S.out[e] = attn_merge_element(a.ml + (size_t)sess * kAttnMlFloats, a.part + (size_t)sess * kAttnPartFloats, h, e, lse);
-  if (S.lse && e % kKvDim == 0) S.lse[h] = lse;
+  const int groups = 1 << a.groups_lg;
+  const float *ml = a.ml + (size_t)sess * kAttnMlFloats;
+  const float *part = a.part + (size_t)sess * kAttnPartFloats + (size_t)h * kKvDim + d;
+  __shared__ float wgt[kAttnGroups];
+  __shared__ float s_l, s_lse;
+  // every group's value of this dimension, loaded with the (m, l) pairs
+  // (indices past the groups are clamped to group 0 and weigh nothing)
+  float xv[kAttnGroups];
+#pragma unroll
+  for (int b = 0; b < kAttnGroups; ++b) xv[b] = part[(size_t)(b < groups ? b : 0) * CSA_MAX_HEADS * kKvDim];
+  if (threadIdx.x < kAttnGroups) {  // lane b holds group b's (m, l)
+    const int b = threadIdx.x;
+    const float mb = b < groups ? ml[((size_t)b * CSA_MAX_HEADS + h) * 2] : -__builtin_inff();
+    const float lb = b < groups ? ml[((size_t)b * CSA_MAX_HEADS + h) * 2 + 1] : 0.0f;
+    float M = mb;
+#pragma unroll
+    for (int o = 1; o < kAttnGroups; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kAttnGroups));
+    const float w = (M == -__builtin_inff() || mb == -__builtin_inff()) ? 0.0f : __expf(mb - M);
+    wgt[b] = w;
+    // L in group order, by lane 0
+    const float wl = w * lb;
+    float L = 0.0f;
+    for (int c = 0; c < groups; ++c) L += __shfl(wl, c, kAttnGroups);
+    if (b == 0) {
+      s_l = L;
+      s_lse = L > 0.0f ? M + logf(L) : -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  float X = 0.0f;
+#pragma unroll
+  for (int b = 0; b < kAttnGroups; ++b) {
+    const float w = wgt[b];
+    X += w == 0.0f ? 0.0f : w * xv[b];
+  }
+  const float L = s_l;
+  S.out[(size_t)h * kKvDim + d] = L > 0.0f ? X / L : 0.0f;
+  if (S.lse && d == 0) S.lse[h] = s_lse;
 }
 
 // ---------------------------------------------------------------- launchers
 
 static AttnArgs attn_args(const AttnSession *s, int n_sessions, int n_heads, float scale, const uint4 *qsplit,
-                          float *part, float *ml) {
+                          float *part, float *ml, int groups_lg) {
   AttnArgs a;
+  a.groups_lg = groups_lg;
   for (int i = 0; i < n_sessions; ++i) a.s[i] = s[i];
   a.qsplit = qsplit;
   a.part = part;
@@ -87,18 +135,17 @@ static AttnArgs attn_args(const AttnSession *s, int n_sessions, int n_heads, flo
 }
 
 hipError_t launch_attn_rows(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale,
-                            const uint4 *qsplit, float *part, float *ml, hipStream_t st) {
-  const AttnArgs a = attn_args(s, n_sessions, n_heads, softmax_scale, qsplit, part, ml);
-  attn_rows_kernel<<<dim3(kAttnSlices, n_sessions), kAttnThreads, 0, st>>>(a);
+                            const uint4 *qsplit, float *part, float *ml, int groups_lg, hipStream_t st) {
+  const AttnArgs a = attn_args(s, n_sessions, n_heads, softmax_scale, qsplit, part, ml, groups_lg);
+  attn_rows_kernel<<<dim3((1u << groups_lg) * kAttnHeadGroups, n_sessions), kAttnThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_combine(const AttnSession *s, int n_sessions, int n_heads, const float *part,
-                               const float *ml, hipStream_t st) {
-  const AttnArgs a =
-      attn_args(s, n_sessions, n_heads, 0.0f, nullptr, const_cast<float *>(part), const_cast<float *>(ml));
-  const unsigned blocks = (unsigned)((n_heads * kKvDim + kCombineThreads - 1) / kCombineThreads);
-  attn_combine_kernel<<<dim3(blocks, n_sessions), kCombineThreads, 0, st>>>(a);
+                               const float *ml, int groups_lg, hipStream_t st) {
+  const AttnArgs a = attn_args(s, n_sessions, n_heads, 0.0f, nullptr, const_cast<float *>(part),
+                               const_cast<float *>(ml), groups_lg);
+  attn_combine_kernel<<<dim3((unsigned)(n_heads * kCombineSplit), n_sessions), kCombineThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

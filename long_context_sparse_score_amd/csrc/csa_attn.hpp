@@ -56,15 +56,19 @@ typedef __bf16 v2bf_attn __attribute__((ext_vector_type(2)));
 constexpr int kKvDim = 512;
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kAttnGroups = 32;     // row groups
+constexpr int kAttnGroupsLg = 5;
+constexpr int kAttnGroups = 1 << kAttnGroupsLg;  // row groups (at most)
 constexpr int kAttnHeadGroups = 4;  // 16 heads each
 constexpr int kAttnSlices = kAttnGroups * kAttnHeadGroups;  // workgroups per session
 constexpr int kAttnBatch = 16;      // rows per matrix-core batch
 static_assert(kAttnWaves * 64 == kKvDim, "one 64-dimension block per wave");
 
-// Group of a selected row (also the workgroup of the fused selection that
-// ranks it): the top 5 bits of a multiplicative hash.
-__device__ __forceinline__ uint32_t attn_group(uint32_t row) { return (row * 0x9E3779B1u) >> 27; }
+// Row group of a selected row among 2^lg row groups (lg <= 5): the top lg
+// bits of a multiplicative hash.  With lg = 5 it is also the workgroup of
+// the fused selection that ranks the row.
+__device__ __forceinline__ uint32_t attn_group(uint32_t row, int lg) {
+  return lg == 0 ? 0u : (row * 0x9E3779B1u) >> (32 - lg);
+}
 
 // Attention query split in the workspace, per session:
 // [g + 4 kq][K step 4][term 3][lane 64] x 8 bf16 (16 bytes).
@@ -347,64 +351,29 @@ __device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, int 
   }
 }
 
-// Stage rows[0..m) (valid KV row indices, m <= kRawRows) into st.raw: slot
-// i receives row rows[i]'s bytes from byte 0 (146 dwords).  Lane j of the
-// wave builds dwords j, j + 64, j + 128 of a row from the two aligned dwords
-// that hold them (v_alignbyte); only dwords holding a byte of the row are
-// read, so nothing past the buffer's last byte is touched.  Wave w copies
-// rows w, w + 8, ..., two rows per pass, all loads first.  All threads call
-// it; the caller synchronizes before reading the slots.
+// Staging of rows[0..m) (valid KV row indices, m <= kRawRows) into st.raw,
+// in two phases so that other work runs while the rows are in flight:
+// attn_stage_issue loads rows[i] (wave w takes i = first + w + 8u, u < U)
+// into registers, attn_stage_finish writes slot i realigned (the
+// row's 583 bytes from byte 0, 146 dwords).  Lane j builds dwords j, j + 64,
+// j + 128 of a row from the two aligned dwords that hold them; only dwords
+// holding a byte of the row are read, so nothing past the buffer's last
+// byte is touched.  The caller synchronizes before reading the slots.
 constexpr int kRawDwords = (kKvRowBytes + 3) / 4;  // 146
-__device__ __forceinline__ void attn_stage_raw(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
-                                               AttnStage &st) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  constexpr int kWaves = kAttnThreads / 64;
-  constexpr int kPass = 2;
-  for (int i0 = wave; i0 < m; i0 += kPass * kWaves) {
-    uint32_t lo[kPass][3], hi[kPass][3], sh[kPass];
-#pragma unroll
-    for (int u = 0; u < kPass; ++u) {
-      const int i = i0 + kWaves * u;
-      const int32_t r = __builtin_amdgcn_readfirstlane(rows[i < m ? i : i0]);
-      const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
-      const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
-      const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);  // stays a global pointer
-      const int last = (int)(mis + kKvRowBytes - 1) >> 2;                 // dword of the last byte
-      sh[u] = 8u * mis;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int j = lane + 64 * k;
-        lo[u][k] = a0[j < last ? j : last];  // clamped: no branch around the loads
-        hi[u][k] = a0[j + 1 < last ? j + 1 : last];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPass; ++u) {
-      const int i = i0 + kWaves * u;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int j = lane + 64 * k;
-        const uint32_t w = (uint32_t)(((uint64_t)hi[u][k] << 32 | lo[u][k]) >> sh[u]);
-        if (i < m && j < kRawDwords) st.raw[i][j] = w;
-      }
-    }
-  }
-}
-
-// Staging in two phases, so that other work runs while the rows are in
-// flight: attn_stage_issue loads rows rows[i] (i < m <= kRawRows; wave w
-// takes i = w, w + 8, ...) into registers, attn_stage_finish writes them
-// realigned into slots i, exactly as attn_stage_raw does.
-struct AttnStageRegs {
-  uint32_t lo[kRawRows / kAttnWaves][3], hi[kRawRows / kAttnWaves][3], sh[kRawRows / kAttnWaves];
+template <int U>  // rows per wave held at once
+struct AttnStageRegsT {
+  uint32_t lo[U][3], hi[U][3], sh[U];
 };
+using AttnStageRegs = AttnStageRegsT<kRawRows / kAttnWaves>;
 
+// Rows first + w + 8u (u < U) of rows[0..m), wave w.
+template <int U>
 __device__ __forceinline__ void attn_stage_issue(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
-                                                 AttnStageRegs &R) {
+                                                 AttnStageRegsT<U> &R, int first = 0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
-    const int i = wave + kAttnWaves * u;
+  for (int u = 0; u < U; ++u) {
+    const int i = first + wave + kAttnWaves * u;
     if (i < m) {  // uniform
       const int32_t r = __builtin_amdgcn_readfirstlane(rows[i]);
       const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
@@ -422,11 +391,12 @@ __device__ __forceinline__ void attn_stage_issue(const uint8_t *__restrict__ kv_
   }
 }
 
-__device__ __forceinline__ void attn_stage_finish(const AttnStageRegs &R, int m, AttnStage &st) {
+template <int U>
+__device__ __forceinline__ void attn_stage_finish(const AttnStageRegsT<U> &R, int m, AttnStage &st, int first = 0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
-    const int i = wave + kAttnWaves * u;
+  for (int u = 0; u < U; ++u) {
+    const int i = first + wave + kAttnWaves * u;
     if (i < m) {
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
@@ -436,35 +406,6 @@ __device__ __forceinline__ void attn_stage_finish(const AttnStageRegs &R, int m,
       }
     }
   }
-}
-
-// Merge of the group partials of one output element e = h * 512 + d:
-//   out = sum_b e^{m_b - M} acc_b / sum_b e^{m_b - M} l_b,  M = max_b m_b,
-//   lse = M + log sum_b e^{m_b - M} l_b
-// (groups with m = -inf are empty and add nothing; with no row at all,
-// out = 0 and lse = -inf).  ml, part: one session's partials.
-__device__ __forceinline__ float attn_merge_element(const float *ml, const float *part, int h, int e, float &lse) {
-  float mb[kAttnGroups], lb[kAttnGroups], xb[kAttnGroups];
-#pragma unroll
-  for (int b = 0; b < kAttnGroups; ++b) {
-    mb[b] = ml[((size_t)b * CSA_MAX_HEADS + h) * 2];
-    lb[b] = ml[((size_t)b * CSA_MAX_HEADS + h) * 2 + 1];
-    xb[b] = part[(size_t)b * CSA_MAX_HEADS * kKvDim + e];
-  }
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int b = 0; b < kAttnGroups; ++b) M = fmaxf(M, mb[b]);
-  float L = 0.0f, X = 0.0f;
-  if (M != -__builtin_inff()) {
-#pragma unroll
-    for (int b = 0; b < kAttnGroups; ++b) {
-      const float w = mb[b] == -__builtin_inff() ? 0.0f : __expf(mb[b] - M);
-      L += w * lb[b];
-      X += mb[b] == -__builtin_inff() ? 0.0f : w * xb[b];
-    }
-  }
-  lse = L > 0.0f ? M + logf(L) : -__builtin_inff();
-  return L > 0.0f ? X / L : 0.0f;
 }
 
 // Order a group's entries by their key (rank or position, distinct),
@@ -484,7 +425,8 @@ __device__ __forceinline__ void attn_order(const int32_t *keys, const int32_t *r
 }
 
 // Attention over a row group's rows (in order) for head group g -> the
-// partial of those heads.  All threads call it.
+// partial of those heads.  Rows are staged kRawRows at a time, in two
+// halves.  All threads call it.
 __device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &st, const int32_t *rows, int m,
                                                 const uint8_t *__restrict__ kv_rows, float scale, int n_heads, int g,
                                                 float *__restrict__ part, float *__restrict__ ml) {
@@ -493,9 +435,14 @@ __device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &
   AttnState S;
   attn_init(S);
   for (int b0 = 0; b0 < m; b0 += kAttnBatch) {
-    const int slot0 = b0 % kRawRows;
-    if (slot0 == 0) {  // the previous batch ended with a barrier
-      attn_stage_raw(kv_rows, rows + b0, m - b0 < kRawRows ? m - b0 : kRawRows, st);
+    if (b0 % kRawRows == 0) {  // the previous batch ended with a barrier
+      const int cnt = m - b0 < kRawRows ? m - b0 : kRawRows;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {  // two rows per wave at a time: fewer live registers
+        AttnStageRegsT<kRawRows / kAttnWaves / 2> R;
+        attn_stage_issue(kv_rows, rows + b0, cnt, R, half * kRawRows / 2);
+        attn_stage_finish(R, cnt, st, half * kRawRows / 2);
+      }
       __syncthreads();
     }
     attn_batch(q, S, st, nullptr, b0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);

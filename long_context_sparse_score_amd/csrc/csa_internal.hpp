@@ -19,10 +19,16 @@ constexpr int kMinTileHeads = 8;
 constexpr int kMaxTileHeads = 64;
 
 // Heads per tile for a session of nt tiles: enough that the heads of all
-// tiles number at least ~2048 (so few tiles hold more winners than heads).
+// tiles number at least ~2048 (so few tiles hold more winners than heads),
+// or ~1024 once a tile keeps 32 (the exact top-64 of a tile costs several
+// histogram passes, and 1024 heads still bound the 512th key well).  With
+// at most 512 heads possible the bound is 1 whatever hd is.
 inline int heads_per_tile(int64_t nt) {
+  // too few tiles for their heads to bound the 512th key: every tile is
+  // read back whole by the selection, so the cheapest heads will do
+  if (nt * kMaxTileHeads <= 512) return kMinTileHeads;
   int hd = kMinTileHeads;
-  while (hd < kMaxTileHeads && nt * hd < 2048) hd *= 2;
+  while (hd < kMaxTileHeads && nt * hd < 2048 && !(hd >= 32 && nt * hd >= 1024)) hd *= 2;
   return hd;
 }
 
@@ -93,10 +99,11 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);
 // Attention partials of the rows sel_idx[0..n_sel) of every session, one
 // workgroup per group (csa_sparse_attn).
+// 2^groups_lg row groups per session (at most 32; the fused selection uses 32).
 hipError_t launch_attn_rows(const AttnSession *s, int n_sessions, int n_heads, float softmax_scale,
-                            const uint4 *qsplit, float *part, float *ml, hipStream_t st);
+                            const uint4 *qsplit, float *part, float *ml, int groups_lg, hipStream_t st);
 // Merge of the group partials: out, lse.
 hipError_t launch_attn_combine(const AttnSession *s, int n_sessions, int n_heads, const float *part,
-                               const float *ml, hipStream_t st);
+                               const float *ml, int groups_lg, hipStream_t st);
 
 }  // namespace csa

@@ -94,8 +94,9 @@ static_assert(kEarlyStageOff + sizeof(AttnStage) <= offsetof(SelShared, u.s.mine
 
 // Lower bound G on the need-th largest of the keys that `visit` enumerates
 // (every thread visits its share, calling f(key) for each nonzero key): at
-// least need keys are >= G, and at most max(target, need) are.  Returns 1
-// (every key) when there are at most need keys.  All threads call it.
+// least need keys are >= G, and at most max(target, need) are, unless the
+// finest bin already holds more.  Returns 1 (every key) when there are at
+// most need keys.  All threads call it.
 template <class Visit>
 __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32_t target, SelShared &sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -127,7 +128,7 @@ __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32
   __syncthreads();
   uint64_t lo = (uint64_t)omin << 32, hi = ((uint64_t)omax << 32) | 0xFFFFFFFFull;
   if (total <= need) return 1ull;
-  if (total <= target) return lo;
+  // (even with few keys, G = the smallest would make every tile "full")
   uint32_t above = 0;  // keys above the current range [lo, hi]
   for (;;) {
     const uint64_t span = hi - lo;
