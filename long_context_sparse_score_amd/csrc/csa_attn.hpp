@@ -44,6 +44,7 @@
 
 #include "../../include/csa.h"
 #include "csa_device.hpp"
+#include "csa_stream.hpp"
 
 namespace csa {
 
@@ -371,22 +372,23 @@ template <int U>
 __device__ __forceinline__ void attn_stage_issue(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
                                                  AttnStageRegsT<U> &R, int first = 0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (m <= 0) return;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    // indices past m re-load row m - 1 (never written): no branch around the
+    // loads, so they all stay in flight
     const int i = first + wave + kAttnWaves * u;
-    if (i < m) {  // uniform
-      const int32_t r = __builtin_amdgcn_readfirstlane(rows[i]);
-      const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
-      const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
-      const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);
-      const int last = (int)(mis + kKvRowBytes - 1) >> 2;
-      R.sh[u] = 8u * mis;
+    const int32_t r = __builtin_amdgcn_readfirstlane(rows[i < m ? i : m - 1]);
+    const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
+    const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
+    const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);
+    const int last = (int)(mis + kKvRowBytes - 1) >> 2;
+    R.sh[u] = 8u * mis;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int j = lane + 64 * k;
-        R.lo[u][k] = a0[j < last ? j : last];
-        R.hi[u][k] = a0[j + 1 < last ? j + 1 : last];
-      }
+    for (int k = 0; k < 3; ++k) {
+      const int j = lane + 64 * k;
+      R.lo[u][k] = a0[j < last ? j : last];
+      R.hi[u][k] = a0[j + 1 < last ? j + 1 : last];
     }
   }
 }
@@ -403,6 +405,62 @@ __device__ __forceinline__ void attn_stage_finish(const AttnStageRegsT<U> &R, in
         const int j = lane + 64 * k;
         const uint32_t w = (uint32_t)(((uint64_t)R.hi[u][k] << 32 | R.lo[u][k]) >> R.sh[u]);
         if (j < kRawDwords) st.raw[i][j] = w;
+      }
+    }
+  }
+}
+
+// Staging by direct-to-LDS loads, for callers that have other work to do
+// while the rows are in flight and cannot hold them in registers:
+// attn_stage_dma_issue copies the 148 aligned dwords that contain row rows[i]
+// (i < m <= kRawRows; wave w takes i = w + 8u) into slot i as they lie in
+// memory (lanes past the row's last dword re-read it, lanes past the slot
+// are masked off); attn_stage_dma_finish, after the caller has waited for
+// the loads (wait_vmcnt<0>) and synchronized, shifts each slot in place so
+// the row starts at byte 0 (each wave reads all of a row's dwords before it
+// writes any).  The caller synchronizes again before reading the slots.
+__device__ __forceinline__ void attn_stage_dma_issue(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
+                                                     AttnStage &st) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
+    const int i = wave + kAttnWaves * u;
+    if (i < m) {  // uniform
+      const int32_t r = __builtin_amdgcn_readfirstlane(rows[i]);
+      const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
+      const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
+      const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);
+      const int last = (int)(mis + kKvRowBytes - 1) >> 2;  // <= 146
+      const uint32_t slot = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&st.raw[i][0]);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        if (j < kRawStride / 4) dma4(a0 + (j < last ? j : last), slot + 256 * k);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void attn_stage_dma_finish(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
+                                                      AttnStage &st) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
+    const int i = wave + kAttnWaves * u;
+    if (i < m) {  // uniform
+      const int32_t r = __builtin_amdgcn_readfirstlane(rows[i]);
+      const uint32_t sh = 8u * ((uint32_t)(uintptr_t)(kv_rows + (size_t)(uint32_t)r * kKvRowBytes) & 3u);
+      uint32_t lo[3], hi[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        lo[k] = st.raw[i][j < kRawDwords ? j : 0];
+        hi[k] = st.raw[i][j < kRawDwords ? j + 1 : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int j = lane + 64 * k;
+        if (j < kRawDwords) st.raw[i][j] = (uint32_t)(((uint64_t)hi[k] << 32 | lo[k]) >> sh);
       }
     }
   }
@@ -451,13 +509,12 @@ __device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &
 }
 
 // The same attention over m <= kRawRows rows that are already staged: the
-// i-th row in order sits in slot slotmap[i].  Same bits as attn_group_rows
-// over those rows in that order.  All threads call it.
-__device__ __forceinline__ void attn_staged_rows(const uint4 *qsplit, AttnStage &st, const int32_t *slotmap, int m,
+// i-th row in order sits in slot slotmap[i]; q holds the wave's query terms
+// (load_attn_query).  Same bits as attn_group_rows over those rows in that
+// order.  All threads call it.
+__device__ __forceinline__ void attn_staged_rows(const AttnQuery &q, AttnStage &st, const int32_t *slotmap, int m,
                                                  float scale, int n_heads, int g, float *__restrict__ part,
                                                  float *__restrict__ ml) {
-  AttnQuery q;
-  load_attn_query(q, qsplit, g);
   AttnState S;
   attn_init(S);
   for (int b0 = 0; b0 < m; b0 += kAttnBatch)

@@ -202,6 +202,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   const uint32_t myslice = ATTN ? blockIdx.x % kAttnGroups : blockIdx.x;
   const int hgroup = ATTN ? (int)(blockIdx.x / kAttnGroups) : 0;
   const bool writer = hgroup == 0;
+  // the attention query terms of this workgroup's head group, loaded now so
+  // they arrive during the selection
+  AttnQuery aq;
+  if constexpr (ATTN) load_attn_query(aq, a.attn_q + (size_t)sess * kAttnQVecs, hgroup);
   if (k_eff == 0) {
     if constexpr (ATTN) {  // an empty group partial: m = -inf, l = 0
       float *ml = a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)myslice * CSA_MAX_HEADS * 2;
@@ -429,8 +433,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       AttnStage &est = *reinterpret_cast<AttnStage *>(reinterpret_cast<char *>(&sh.u) + kEarlyStageOff);
       if (tid < nm) sh.loc_row[tid] = (int32_t)key_row(sh.u.s.cand[sh.u.s.mine[tid]]);
       __syncthreads();
-      AttnStageRegs R;
-      attn_stage_issue(a.s[sess].kv_rows, sh.loc_row, nm, R);
+      attn_stage_dma_issue(a.s[sess].kv_rows, sh.loc_row, nm, est);
       if (wave == 0) {  // slot i (candidate mine[i]) -> its position in the group's key order
         const uint64_t x = lane < nm ? sh.u.s.cand[sh.u.s.mine[lane]] : 0ull;
         const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
@@ -462,9 +465,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
           if (sel_score) sel_score[r] = key_score(x);
         }
       }
-      attn_stage_finish(R, nm, est);
+      wait_vmcnt<0>();  // this wave's row copies have landed
       __syncthreads();
-      attn_staged_rows(a.attn_q + (size_t)sess * kAttnQVecs, est, sh.ordered, nm, a.softmax_scale, a.n_heads, hgroup,
+      attn_stage_dma_finish(a.s[sess].kv_rows, sh.loc_row, nm, est);
+      __syncthreads();
+      attn_staged_rows(aq, est, sh.ordered, nm, a.softmax_scale, a.n_heads, hgroup,
                        a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)myslice * CSA_MAX_HEADS * kKvDim,
                        a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)myslice * CSA_MAX_HEADS * 2);
       return;
