@@ -205,6 +205,26 @@ def test_decode_step_ragged_sessions(csa, orc):
         _check_session(orc, s, g)
 
 
+@pytest.mark.parametrize("n_idx_heads,n_heads", [(1, 1), (13, 20), (40, 64), (64, 7)])
+def test_decode_step_head_counts(csa, orc, n_idx_heads, n_heads):
+    # head groups only partly filled: dead indexer heads weigh zero, dead
+    # attention heads are not written
+    s = gen.session(1, n_rows=20000, n_idx_heads=n_idx_heads, n_heads=n_heads)
+    got = _run_step(csa, [s], s["softmax_scale"])[0]
+    assert got["out"].shape == (n_heads, 512)
+    _check_session(orc, s, got)
+
+
+@pytest.mark.parametrize("sizes", [[3000, 700], [3000, 700, 0], [513, 40000, 511, 1, 9000]])
+def test_decode_step_session_counts(csa, orc, sizes):
+    # two sessions: attention inside the selection kernel; three or more:
+    # selection alone, then the attention with fewer row groups
+    ss = [gen.session(1, s=i, n_rows=n) for i, n in enumerate(sizes)]
+    got = _run_step(csa, ss, ss[0]["softmax_scale"])
+    for s, g in zip(ss, got):
+        _check_session(orc, s, g)
+
+
 @pytest.mark.parametrize("n_rows", [None, 2_500_000])
 def test_fused_equals_unfused(csa, n_rows):
     # 2.5M rows: more tile heads than the selection holds in registers
