@@ -67,56 +67,18 @@ __global__ void __launch_bounds__(kAttnThreads) attn_rows_kernel(const AttnArgs 
 
 // ---------------------------------------------------------------- combine
 
-// Four workgroups per (head, session), one thread per dimension: the head's
-// group weights w_b = e^{m_b - M} and L = sum_b w_b l_b are formed once (in
-// group order, by one lane), then every dimension sums w_b acc_b in group
-// order:  out = (sum_b w_b acc_b) / L,  lse = M + log L.  Empty groups
-// (m = -inf) have weight 0; with no row at all out = 0 and lse = -inf.
 constexpr int kCombineThreads = 128;  // a quarter of the dimensions per workgroup
 constexpr int kCombineSplit = kKvDim / kCombineThreads;
 
+// Four workgroups per (head, session), one thread per dimension
+// (attn_combine_head).
 __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const AttnArgs a) {
   const int sess = blockIdx.y, h = blockIdx.x / kCombineSplit;
-  const int d = (blockIdx.x % kCombineSplit) * kCombineThreads + threadIdx.x;
+  const int d0 = (blockIdx.x % kCombineSplit) * kCombineThreads;
   const AttnSession &S = a.s[sess];
-  const int groups = 1 << a.groups_lg;
-  const float *ml = a.ml + (size_t)sess * kAttnMlFloats;
-  const float *part = a.part + (size_t)sess * kAttnPartFloats + (size_t)h * kKvDim + d;
-  __shared__ float wgt[kAttnGroups];
-  __shared__ float s_l, s_lse;
-  // every group's value of this dimension, loaded with the (m, l) pairs
-  // (indices past the groups are clamped to group 0 and weigh nothing)
-  float xv[kAttnGroups];
-#pragma unroll
-  for (int b = 0; b < kAttnGroups; ++b) xv[b] = part[(size_t)(b < groups ? b : 0) * CSA_MAX_HEADS * kKvDim];
-  if (threadIdx.x < kAttnGroups) {  // lane b holds group b's (m, l)
-    const int b = threadIdx.x;
-    const float mb = b < groups ? ml[((size_t)b * CSA_MAX_HEADS + h) * 2] : -__builtin_inff();
-    const float lb = b < groups ? ml[((size_t)b * CSA_MAX_HEADS + h) * 2 + 1] : 0.0f;
-    float M = mb;
-#pragma unroll
-    for (int o = 1; o < kAttnGroups; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kAttnGroups));
-    const float w = (M == -__builtin_inff() || mb == -__builtin_inff()) ? 0.0f : __expf(mb - M);
-    wgt[b] = w;
-    // L in group order, by lane 0
-    const float wl = w * lb;
-    float L = 0.0f;
-    for (int c = 0; c < groups; ++c) L += __shfl(wl, c, kAttnGroups);
-    if (b == 0) {
-      s_l = L;
-      s_lse = L > 0.0f ? M + logf(L) : -__builtin_inff();
-    }
-  }
-  __syncthreads();
-  float X = 0.0f;
-#pragma unroll
-  for (int b = 0; b < kAttnGroups; ++b) {
-    const float w = wgt[b];
-    X += w == 0.0f ? 0.0f : w * xv[b];
-  }
-  const float L = s_l;
-  S.out[(size_t)h * kKvDim + d] = L > 0.0f ? X / L : 0.0f;
-  if (S.lse && d == 0) S.lse[h] = s_lse;
+  __shared__ CombineShared cs;
+  attn_combine_head(a.ml + (size_t)sess * kAttnMlFloats, a.part + (size_t)sess * kAttnPartFloats, 1 << a.groups_lg, h, d0,
+                    kCombineThreads, cs, S.out + (size_t)h * kKvDim, S.lse ? S.lse + h : nullptr);
 }
 
 // ---------------------------------------------------------------- launchers

@@ -466,6 +466,59 @@ __device__ __forceinline__ void attn_stage_dma_finish(const uint8_t *__restrict_
   }
 }
 
+// The merge of head h's row-group partials for dimensions d0 .. d0 + cnt
+// (one per thread t < cnt): threads 0..31 form the group weights
+// w_b = e^{m_b - M} (0 for empty groups), L = sum_b w_b l_b (in group order)
+// and lse = M + log L into cs; then out[d] = (sum_b w_b acc_b[d]) / L, summed
+// in group order (out = 0 and lse = -inf without any row).  ml, part: one
+// session's partials; out_h, lse_h: head h's output row and lse (lse_h may
+// be null; written by the thread of dimension 0).  All threads call it.
+struct CombineShared {
+  float wgt[kAttnGroups];
+  float l, lse;
+};
+
+__device__ __forceinline__ void attn_combine_head(const float *ml, const float *part, int groups, int h, int d0,
+                                                  int cnt, CombineShared &cs, float *out_h, float *lse_h) {
+  const int t = threadIdx.x;
+  const int d = d0 + (t < cnt ? t : 0);
+  // every group's value of this dimension, loaded with the (m, l) pairs
+  // (indices past the groups are clamped to group 0 and weigh nothing)
+  float xv[kAttnGroups];
+#pragma unroll
+  for (int b = 0; b < kAttnGroups; ++b)
+    xv[b] = part[((size_t)(b < groups ? b : 0) * CSA_MAX_HEADS + h) * kKvDim + d];
+  if (t < kAttnGroups) {  // lane b holds group b's (m, l)
+    const int b = t;
+    const float mb = b < groups ? ml[((size_t)b * CSA_MAX_HEADS + h) * 2] : -__builtin_inff();
+    const float lb = b < groups ? ml[((size_t)b * CSA_MAX_HEADS + h) * 2 + 1] : 0.0f;
+    float M = mb;
+#pragma unroll
+    for (int o = 1; o < kAttnGroups; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kAttnGroups));
+    const float w = (M == -__builtin_inff() || mb == -__builtin_inff()) ? 0.0f : __expf(mb - M);
+    cs.wgt[b] = w;
+    const float wl = w * lb;
+    float L = 0.0f;
+    for (int c = 0; c < groups; ++c) L += __shfl(wl, c, kAttnGroups);
+    if (b == 0) {
+      cs.l = L;
+      cs.lse = L > 0.0f ? M + logf(L) : -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  if (t < cnt) {
+    float X = 0.0f;
+#pragma unroll
+    for (int b = 0; b < kAttnGroups; ++b) {
+      const float w = cs.wgt[b];
+      X += w == 0.0f ? 0.0f : w * xv[b];
+    }
+    const float L = cs.l;
+    out_h[d] = L > 0.0f ? X / L : 0.0f;
+    if (lse_h && d == 0) *lse_h = cs.lse;
+  }
+}
+
 // Order a group's entries by their key (rank or position, distinct),
 // ascending: out_rows[i] = row of the i-th.  keys/rows[0..m) in LDS; all
 // threads call it; ends with a barrier.
