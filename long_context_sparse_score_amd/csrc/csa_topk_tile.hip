@@ -262,10 +262,12 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   uint8_t *const stage = &sh.ring[wave][1][0];
   const uint32_t stage_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage);
   if (wave < G && lane < 32) {
+    // the head rows' addresses are uniform: scalar bases, one lane offset
+    const uint32_t voff = 16u * (uint32_t)lane;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int h = 16 * wave + j < n_idx_heads ? 16 * wave + j : n_idx_heads - 1;
-      dma16(qh + (size_t)h * 128 + 4 * lane, stage_lds + kStageHead * j);
+      dma16s(reinterpret_cast<const uint8_t *>(qh + (size_t)h * 128), voff, stage_lds + kStageHead * j);
     }
   }
   dma4(wh + (lane < n_idx_heads ? lane : n_idx_heads - 1), stage_lds + kStageW);
