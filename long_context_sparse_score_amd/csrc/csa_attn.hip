@@ -37,7 +37,8 @@ struct RowsShared {
   uint32_t wcnt[kAttnWaves];
 };
 
-__global__ void __launch_bounds__(kAttnThreads) attn_rows_kernel(const AttnArgs a) {
+// (at least four waves per SIMD: two workgroups share a compute unit)
+__global__ void __launch_bounds__(kAttnThreads, 4) attn_rows_kernel(const AttnArgs a) {
   const int groups = 1 << a.groups_lg;
   const int sess = blockIdx.y, grp = blockIdx.x % groups, hg = blockIdx.x / groups;
   const AttnSession &S = a.s[sess];

@@ -51,7 +51,7 @@ namespace csa {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f_attn __attribute__((ext_vector_type(4)));
 
-typedef short v4s_attn __attribute__((ext_vector_type(4)));
+typedef short v8s_attn __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf_attn __attribute__((ext_vector_type(2)));
 
 constexpr int kKvDim = 512;
@@ -61,7 +61,7 @@ constexpr int kAttnGroupsLg = 5;
 constexpr int kAttnGroups = 1 << kAttnGroupsLg;  // row groups (at most)
 constexpr int kAttnHeadGroups = 4;  // 16 heads each
 constexpr int kAttnSlices = kAttnGroups * kAttnHeadGroups;  // workgroups per session
-constexpr int kAttnBatch = 16;      // rows per matrix-core batch
+constexpr int kAttnBatch = 32;      // rows per matrix-core batch
 static_assert(kAttnWaves * 64 == kKvDim, "one 64-dimension block per wave");
 
 // Row group of a selected row among 2^lg row groups (lg <= 5): the top lg
@@ -86,12 +86,12 @@ __device__ __forceinline__ size_t attn_q_index(int wave, int s, int t, int lane)
 // Packed rows staged in LDS, realigned: slot i holds its row's 583 bytes
 // from byte 0.
 constexpr int kRawStride = 592;  // bytes per slot: 148 dwords
-constexpr int kRawRows = 32;     // rows staged at once (two batches)
+constexpr int kRawRows = 32;     // rows staged at once (one batch)
 static_assert(kRawRows % kAttnBatch == 0, "batches do not straddle a staging round");
 
 struct AttnStage {
   uint32_t raw[kRawRows][kRawStride / 4];  // staged packed rows
-  float lgp[kAttnWaves][4][64];            // partial logit tiles [wave][v][lane]
+  float lgp[kAttnWaves][2][4][64];         // partial logit tiles [wave][tile][v][lane]
 };
 
 // x = t0 + t1 + t2 + r: three bf16 terms, each the round-to-nearest-even of
@@ -218,66 +218,85 @@ __device__ __forceinline__ int attn_slot(const int32_t *slotmap, int b0, int i, 
   return slotmap ? slotmap[b0 + i] : (b0 + i) % kRawRows;
 }
 
-// One batch: rows b0 .. b0 + 15 of the group's ordered rows, of which the
-// first `nvalid` (>= 1) exist and the rest are padding; row b0 + i is staged
-// in slot attn_slot(slotmap, b0, i, nvalid).  Updates this wave's running
-// softmax state and accumulators.  All kAttnThreads threads call it; it ends
-// with a barrier (the partial tiles and the staged rows are reused).
+// One batch: rows b0 .. b0 + 31 of the group's ordered rows, of which the
+// first `nvalid` (1 <= nvalid <= 32) exist and the rest are padding; row
+// b0 + i is staged in slot attn_slot(slotmap, b0, i, nvalid).  The logits are
+// two 16-row tiles (the second skipped when nvalid <= 16).  P V takes all 32
+// rows in one K = 32 product per 16-dimension tile: K index 8(l/16) + 4u + i
+// is row 16u + 4(l/16) + i, which is where lane l holds that row's logit of
+// head l%16.  Updates this wave's running softmax state and accumulators.
+// All kAttnThreads threads call it; it ends with a barrier (the partial
+// tiles and the staged rows are reused).
 __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, AttnStage &st, const int32_t *slotmap,
                                            int b0, int nvalid, float scale) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  // partial logits of the 16 rows x 16 heads over dimensions 64w .. +64
-  v4f_attn c = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
+  const bool two = nvalid > 16;  // uniform
+  // partial logits of the rows x 16 heads over dimensions 64w .. +64
+  v4f_attn c[2] = {v4f_attn{0.0f, 0.0f, 0.0f, 0.0f}, v4f_attn{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ks = 2 * wave + j;  // uniform
-    v8bf hi, lo;
-    attn_row_operand(st, attn_slot(slotmap, b0, lr, nvalid), ks, lr < nvalid, hi, lo);
 #pragma unroll
-    for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, q.b[j][t], c, 0, 0, 0);
-    if (ks >= kKvNope / 32) {
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      v8bf hi, lo;
+      attn_row_operand(st, attn_slot(slotmap, b0, 16 * u + lr, nvalid), ks, 16 * u + lr < nvalid, hi, lo);
 #pragma unroll
-      for (int t = 0; t < 3; ++t) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, q.b[j][t], c, 0, 0, 0);
+      for (int t = 0; t < 3; ++t) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, q.b[j][t], c[u], 0, 0, 0);
+      if (ks >= kKvNope / 32) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, q.b[j][t], c[u], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) st.lgp[wave][v][lane] = c[v];
-  __syncthreads();
-  // the full logits of rows 4(l/16) + v for head l%16, summed in a fixed order
-  float lg4[4];
+  for (int v = 0; v < 4; ++v) st.lgp[wave][0][v][lane] = c[0][v];
+  if (two) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    float p[kAttnWaves];
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) p[w] = st.lgp[w][v][lane];
-    const float sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    lg4[v] = 4 * lg + v < nvalid ? scale * sum : -__builtin_inff();
+    for (int v = 0; v < 4; ++v) st.lgp[wave][1][v][lane] = c[1][v];
   }
+  __syncthreads();
+  // the full logits of rows 16u + 4(l/16) + v for head l%16, summed in a
+  // fixed order
+  float lgt[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float sum = 0.0f;
+      if (u == 0 || two) {
+        float p[kAttnWaves];
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) p[w] = st.lgp[w][u][v][lane];
+        sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      }
+      lgt[u][v] = 16 * u + 4 * lg + v < nvalid ? scale * sum : -__builtin_inff();
+    }
   // online softmax of head l%16 over the batch's rows (held by the lanes of
   // that head in the four lane groups)
-  float mb = fmaxf(fmaxf(lg4[0], lg4[1]), fmaxf(lg4[2], lg4[3]));
+  float mb = fmaxf(fmaxf(fmaxf(lgt[0][0], lgt[0][1]), fmaxf(lgt[0][2], lgt[0][3])),
+                   fmaxf(fmaxf(lgt[1][0], lgt[1][1]), fmaxf(lgt[1][2], lgt[1][3])));
   mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
   mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
   const float m_new = fmaxf(S.m, mb);  // finite: the batch holds a row
   const float alpha = __expf(S.m - m_new);
-  float pv[4], ps = 0.0f;
+  float ps = 0.0f;
+  v8s_attn ph, pl;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    pv[v] = __expf(lg4[v] - m_new);
-    ps += pv[v];
-  }
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float pv = __expf(lgt[u][v] - m_new);
+      ps += pv;
+      const __bf16 b = (__bf16)pv;
+      ph[4 * u + v] = __builtin_bit_cast(short, b);
+      pl[4 * u + v] = bf16_bits(pv - (float)b);
+    }
   ps += __shfl_xor(ps, 16, 64);
   ps += __shfl_xor(ps, 32, 64);
   S.l = S.l * alpha + ps;
   S.m = m_new;
-  v4s_attn ph, pl;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const __bf16 b = (__bf16)pv[v];
-    ph[v] = __builtin_bit_cast(short, b);
-    pl[v] = bf16_bits(pv[v] - (float)b);
-  }
   // rescale: accumulator element v is head 4(l/16) + v, whose factor sits
   // in lane 4(l/16) + v
   float av[4];
@@ -288,45 +307,49 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
 #pragma unroll
     for (int v = 0; v < 4; ++v) S.acc[i][v] *= av[v];
   // acc += P V over this wave's 64 dimensions (4 tiles of 16)
-  const uint8_t *rb[4];
-  bool rv[4];
+  const v8bf PH = __builtin_bit_cast(v8bf, ph), PL = __builtin_bit_cast(v8bf, pl);
+  const uint8_t *rb[8];
+  bool rv[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rb[i] = reinterpret_cast<const uint8_t *>(&st.raw[attn_slot(slotmap, b0, 4 * lg + i, nvalid)][0]);
-    rv[i] = 4 * lg + i < nvalid;
+  for (int k = 0; k < 8; ++k) {
+    const int i = 16 * (k >> 2) + 4 * lg + (k & 3);
+    rb[k] = reinterpret_cast<const uint8_t *>(&st.raw[attn_slot(slotmap, b0, i, nvalid)][0]);
+    rv[k] = i < nvalid;
   }
   if (wave < kKvNope / 64) {  // E4M3 block `wave`: one scale per row
-    float sc[4];
+    float sc[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = ue8m0_scale(rb[i][kKvNope + 128 + wave]);
+    for (int k = 0; k < 8; ++k) sc[k] = ue8m0_scale(rb[k][kKvNope + 128 + wave]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int d = 64 * wave + 16 * t + lr;
-      v4s_attn vb;
+      v8s_attn vb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)rb[i][d], sc[i], 0);
-        vb[i] = bf16_bits(rv[i] ? f : 0.0f);
+      for (int k = 0; k < 8; ++k) {
+        const float f = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)rb[k][d], sc[k], 0);
+        vb[k] = bf16_bits(rv[k] ? f : 0.0f);
       }
-      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, S.acc[t], 0, 0, 0);
-      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, S.acc[t], 0, 0, 0);
+      const v8bf VB = __builtin_bit_cast(v8bf, vb);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PH, VB, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PL, VB, S.acc[t], 0, 0, 0);
     }
   } else {  // the RoPE values
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int d = 16 * t + lr;  // RoPE index
-      v4s_attn vh, vl;
+      v8s_attn vh, vl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int k = 0; k < 8; ++k) {
         short h, l;
-        f16_split(*reinterpret_cast<const uint16_t *>(rb[i] + kKvNope + 2 * d), h, l);
-        vh[i] = rv[i] ? h : (short)0;
-        vl[i] = rv[i] ? l : (short)0;
+        f16_split(*reinterpret_cast<const uint16_t *>(rb[k] + kKvNope + 2 * d), h, l);
+        vh[k] = rv[k] ? h : (short)0;
+        vl[k] = rv[k] ? l : (short)0;
       }
-      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vh, S.acc[t], 0, 0, 0);
-      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vh, S.acc[t], 0, 0, 0);
-      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, S.acc[t], 0, 0, 0);
-      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vl, S.acc[t], 0, 0, 0);
+      const v8bf VH = __builtin_bit_cast(v8bf, vh), VL = __builtin_bit_cast(v8bf, vl);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PH, VH, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PL, VH, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PH, VL, S.acc[t], 0, 0, 0);
+      S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PL, VL, S.acc[t], 0, 0, 0);
     }
   }
   __syncthreads();  // the partial tiles and staged rows are reused

@@ -89,8 +89,11 @@ struct SelShared {
   uint32_t ccnt, nfull, nmine, nloc;
   uint32_t bin, ca, cb;
 };
-static_assert(kEarlyStageOff + sizeof(AttnStage) <= offsetof(SelShared, u.s.mine) - offsetof(SelShared, u),
-              "the early stage ends before the group list");
+// The early stage's rows are copied in while the group list (mine) is
+// still read; its logit tiles are written only after that, and may overlap it.
+static_assert(kEarlyStageOff + offsetof(AttnStage, lgp) <= offsetof(SelShared, u.s.mine) - offsetof(SelShared, u),
+              "the early stage's rows end before the group list");
+static_assert(kEarlyStageOff + sizeof(AttnStage) <= sizeof(SelShared::u), "the early stage fits the union");
 
 // Lower bound G on the need-th largest of the keys that `visit` enumerates
 // (every thread visits its share, calling f(key) for each nonzero key): at
