@@ -89,8 +89,10 @@ constexpr int kRawStride = 592;  // bytes per slot: 148 dwords
 constexpr int kRawRows = 32;     // rows staged at once (one batch)
 static_assert(kRawRows % kAttnBatch == 0, "batches do not straddle a staging round");
 
+typedef uint32_t AttnRawRow[kRawStride / 4];  // one staging slot
+
 struct AttnStage {
-  uint32_t raw[kRawRows][kRawStride / 4];  // staged packed rows
+  AttnRawRow raw[kRawRows];                // staged packed rows
   float lgp[kAttnWaves][2][4][64];         // partial logit tiles [wave][tile][v][lane]
 };
 
@@ -183,10 +185,10 @@ __device__ __forceinline__ void f16_split(uint32_t h, short &hi, short &lo) {
 // slot `slot`: the lane's 8 values at dimensions 32 ks + 8(l/16) .. +8, as
 // bf16 (lo: the RoPE remainder; zero for E4M3 steps).  Zero for a padding
 // row.
-__device__ __forceinline__ void attn_row_operand(const AttnStage &st, int slot, int ks, bool valid, v8bf &hi,
+__device__ __forceinline__ void attn_row_operand(const AttnRawRow *raw, int slot, int ks, bool valid, v8bf &hi,
                                                  v8bf &lo) {
   const int lane = threadIdx.x & 63;
-  const uint8_t *rb = reinterpret_cast<const uint8_t *>(&st.raw[slot][0]);
+  const uint8_t *rb = reinterpret_cast<const uint8_t *>(&raw[slot][0]);
   if (ks < kKvNope / 32) {
     const uint2 c = *reinterpret_cast<const uint2 *>(rb + 32 * ks + 8 * (lane >> 4));
     const float sc = ue8m0_scale(rb[kKvNope + 128 + (ks >> 1)]);
@@ -227,9 +229,13 @@ __device__ __forceinline__ int attn_slot(const int32_t *slotmap, int b0, int i, 
 // head l%16.  Updates this wave's running softmax state and accumulators.
 // All kAttnThreads threads call it; it ends with a barrier (the partial
 // tiles and the staged rows are reused).
-__device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, AttnStage &st, const int32_t *slotmap,
-                                           int b0, int nvalid, float scale) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, AttnStage &st, const AttnRawRow *raw,
+                                           const int32_t *slotmap, int b0, int nvalid, float scale) {
+  // the lane offsets below are recomputed per batch rather than hoisted out
+  // of the caller's loop, where they would only hold registers
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const bool two = nvalid > 16;  // uniform
   // partial logits of the rows x 16 heads over dimensions 64w .. +64
@@ -241,7 +247,7 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
     for (int u = 0; u < 2; ++u) {
       if (u == 1 && !two) break;
       v8bf hi, lo;
-      attn_row_operand(st, attn_slot(slotmap, b0, 16 * u + lr, nvalid), ks, 16 * u + lr < nvalid, hi, lo);
+      attn_row_operand(raw, attn_slot(slotmap, b0, 16 * u + lr, nvalid), ks, 16 * u + lr < nvalid, hi, lo);
 #pragma unroll
       for (int t = 0; t < 3; ++t) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, q.b[j][t], c[u], 0, 0, 0);
       if (ks >= kKvNope / 32) {
@@ -313,7 +319,7 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int i = 16 * (k >> 2) + 4 * lg + (k & 3);
-    rb[k] = reinterpret_cast<const uint8_t *>(&st.raw[attn_slot(slotmap, b0, i, nvalid)][0]);
+    rb[k] = reinterpret_cast<const uint8_t *>(&raw[attn_slot(slotmap, b0, i, nvalid)][0]);
     rv[k] = i < nvalid;
   }
   if (wave < kKvNope / 64) {  // E4M3 block `wave`: one scale per row
@@ -375,32 +381,29 @@ __device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, int 
   }
 }
 
-// Staging of rows[0..m) (valid KV row indices, m <= kRawRows) into st.raw,
-// in two phases so that other work runs while the rows are in flight:
-// attn_stage_issue loads rows[i] (wave w takes i = first + w + 8u, u < U)
-// into registers, attn_stage_finish writes slot i realigned (the
-// row's 583 bytes from byte 0, 146 dwords).  Lane j builds dwords j, j + 64,
-// j + 128 of a row from the two aligned dwords that hold them; only dwords
-// holding a byte of the row are read, so nothing past the buffer's last
-// byte is touched.  The caller synchronizes before reading the slots.
+// Staging of rows[0..m) (valid KV row indices, m <= kRawRows) into a stage's
+// slots, in two phases so that other work runs while the rows are in flight:
+// attn_stage_issue loads rows[i] (wave w takes i = w + 8u, u < 4) into
+// registers, attn_stage_finish writes slot i realigned (the row's 583 bytes
+// from byte 0, 146 dwords).  Lane j loads aligned dwords j, j + 64, j + 128
+// of the row once; realigned dword j takes the next aligned dword from lane
+// j + 1 (from lane 0's next register for j = 63).  Only dwords holding a
+// byte of the row are read, so nothing past the buffer's last byte is
+// touched.  The caller synchronizes before reading the slots.
 constexpr int kRawDwords = (kKvRowBytes + 3) / 4;  // 146
-template <int U>  // rows per wave held at once
-struct AttnStageRegsT {
-  uint32_t lo[U][3], hi[U][3], sh[U];
+constexpr int kStageRowsPerWave = kRawRows / kAttnWaves;
+struct AttnStageRegs {
+  uint32_t d[kStageRowsPerWave][3], sh[kStageRowsPerWave];
 };
-using AttnStageRegs = AttnStageRegsT<kRawRows / kAttnWaves>;
 
-// Rows first + w + 8u (u < U) of rows[0..m), wave w.
-template <int U>
+// indices past m re-load row m - 1 (never written): no branch around the
+// loads, so they all stay in flight (m >= 1)
 __device__ __forceinline__ void attn_stage_issue(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
-                                                 AttnStageRegsT<U> &R, int first = 0) {
+                                                 AttnStageRegs &R) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (m <= 0) return;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    // indices past m re-load row m - 1 (never written): no branch around the
-    // loads, so they all stay in flight
-    const int i = first + wave + kAttnWaves * u;
+  for (int u = 0; u < kStageRowsPerWave; ++u) {
+    const int i = wave + kAttnWaves * u;
     const int32_t r = __builtin_amdgcn_readfirstlane(rows[i < m ? i : m - 1]);
     const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
     const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
@@ -410,24 +413,25 @@ __device__ __forceinline__ void attn_stage_issue(const uint8_t *__restrict__ kv_
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int j = lane + 64 * k;
-      R.lo[u][k] = a0[j < last ? j : last];
-      R.hi[u][k] = a0[j + 1 < last ? j + 1 : last];
+      R.d[u][k] = a0[j < last ? j : last];
     }
   }
 }
 
-template <int U>
-__device__ __forceinline__ void attn_stage_finish(const AttnStageRegsT<U> &R, int m, AttnStage &st, int first = 0) {
+__device__ __forceinline__ void attn_stage_finish(const AttnStageRegs &R, int m, AttnRawRow *raw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = first + wave + kAttnWaves * u;
-    if (i < m) {
+  for (int u = 0; u < kStageRowsPerWave; ++u) {
+    const int i = wave + kAttnWaves * u;
+    if (i < m) {  // uniform
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int j = lane + 64 * k;
-        const uint32_t w = (uint32_t)(((uint64_t)R.hi[u][k] << 32 | R.lo[u][k]) >> R.sh[u]);
-        if (j < kRawDwords) st.raw[i][j] = w;
+        const uint32_t up = (uint32_t)__shfl_down((int)R.d[u][k], 1, 64);
+        const uint32_t wrap = (uint32_t)__shfl((int)R.d[u][k < 2 ? k + 1 : 2], 0, 64);
+        const uint32_t hi = lane == 63 ? wrap : up;
+        const uint32_t w = (uint32_t)(((uint64_t)hi << 32 | R.d[u][k]) >> R.sh[u]);
+        if (j < kRawDwords) raw[i][j] = w;
       }
     }
   }
@@ -443,7 +447,7 @@ __device__ __forceinline__ void attn_stage_finish(const AttnStageRegsT<U> &R, in
 // the row starts at byte 0 (each wave reads all of a row's dwords before it
 // writes any).  The caller synchronizes again before reading the slots.
 __device__ __forceinline__ void attn_stage_dma_issue(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
-                                                     AttnStage &st) {
+                                                     AttnRawRow *raw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
@@ -452,20 +456,20 @@ __device__ __forceinline__ void attn_stage_dma_issue(const uint8_t *__restrict__
       const int32_t r = __builtin_amdgcn_readfirstlane(rows[i]);
       const uint8_t *rb = kv_rows + (size_t)(uint32_t)r * kKvRowBytes;
       const uint32_t mis = (uint32_t)(uintptr_t)rb & 3u;
-      const uint32_t *a0 = reinterpret_cast<const uint32_t *>(rb - mis);
+      const uint8_t *a0 = uniform_ptr(rb - mis);  // scalar base, lane offsets
       const int last = (int)(mis + kKvRowBytes - 1) >> 2;  // <= 146
-      const uint32_t slot = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&st.raw[i][0]);
+      const uint32_t slot = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&raw[i][0]);
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int j = lane + 64 * k;
-        if (j < kRawStride / 4) dma4(a0 + (j < last ? j : last), slot + 256 * k);
+        if (j < kRawStride / 4) dma4s(a0, 4u * (uint32_t)(j < last ? j : last), slot + 256 * k);
       }
     }
   }
 }
 
 __device__ __forceinline__ void attn_stage_dma_finish(const uint8_t *__restrict__ kv_rows, const int32_t *rows, int m,
-                                                      AttnStage &st) {
+                                                      AttnRawRow *raw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < kRawRows / kAttnWaves; ++u) {
@@ -477,13 +481,13 @@ __device__ __forceinline__ void attn_stage_dma_finish(const uint8_t *__restrict_
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int j = lane + 64 * k;
-        lo[k] = st.raw[i][j < kRawDwords ? j : 0];
-        hi[k] = st.raw[i][j < kRawDwords ? j + 1 : 0];
+        lo[k] = raw[i][j < kRawDwords ? j : 0];
+        hi[k] = raw[i][j < kRawDwords ? j + 1 : 0];
       }
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int j = lane + 64 * k;
-        if (j < kRawDwords) st.raw[i][j] = (uint32_t)(((uint64_t)hi[k] << 32 | lo[k]) >> sh);
+        if (j < kRawDwords) raw[i][j] = (uint32_t)(((uint64_t)hi[k] << 32 | lo[k]) >> sh);
       }
     }
   }
@@ -559,27 +563,26 @@ __device__ __forceinline__ void attn_order(const int32_t *keys, const int32_t *r
 }
 
 // Attention over a row group's rows (in order) for head group g -> the
-// partial of those heads.  Rows are staged kRawRows at a time, in two
-// halves.  All threads call it.
+// partial of those heads.  Rows are staged kRawRows at a time; the next
+// stage's loads are in flight while a batch is computed.  All threads call
+// it.
 __device__ __forceinline__ void attn_group_rows(const uint4 *qsplit, AttnStage &st, const int32_t *rows, int m,
                                                 const uint8_t *__restrict__ kv_rows, float scale, int n_heads, int g,
                                                 float *__restrict__ part, float *__restrict__ ml) {
+  static_assert(kAttnBatch == kRawRows, "one batch per stage");
   AttnQuery q;
   load_attn_query(q, qsplit, g);
   AttnState S;
   attn_init(S);
-  for (int b0 = 0; b0 < m; b0 += kAttnBatch) {
-    if (b0 % kRawRows == 0) {  // the previous batch ended with a barrier
-      const int cnt = m - b0 < kRawRows ? m - b0 : kRawRows;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {  // two rows per wave at a time: fewer live registers
-        AttnStageRegsT<kRawRows / kAttnWaves / 2> R;
-        attn_stage_issue(kv_rows, rows + b0, cnt, R, half * kRawRows / 2);
-        attn_stage_finish(R, cnt, st, half * kRawRows / 2);
-      }
-      __syncthreads();
-    }
-    attn_batch(q, S, st, nullptr, b0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
+  AttnStageRegs R;
+  if (m > 0) attn_stage_issue(kv_rows, rows, m < kRawRows ? m : kRawRows, R);
+  for (int b0 = 0; b0 < m; b0 += kRawRows) {
+    const int cnt = m - b0 < kRawRows ? m - b0 : kRawRows;
+    attn_stage_finish(R, cnt, st.raw);  // the previous batch ended with a barrier
+    __syncthreads();
+    const int nx = m - b0 - kRawRows;  // rows of the next stage
+    if (nx > 0) attn_stage_issue(kv_rows, rows + b0 + kRawRows, nx < kRawRows ? nx : kRawRows, R);
+    attn_batch(q, S, st, st.raw, nullptr, b0, cnt, scale);
   }
   attn_store(S, n_heads, g, part, ml);
 }
@@ -594,7 +597,7 @@ __device__ __forceinline__ void attn_staged_rows(const AttnQuery &q, AttnStage &
   AttnState S;
   attn_init(S);
   for (int b0 = 0; b0 < m; b0 += kAttnBatch)
-    attn_batch(q, S, st, slotmap, b0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
+    attn_batch(q, S, st, st.raw, slotmap, b0, m - b0 < kAttnBatch ? m - b0 : kAttnBatch, scale);
   attn_store(S, n_heads, g, part, ml);
 }
 

@@ -436,7 +436,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       AttnStage &est = *reinterpret_cast<AttnStage *>(reinterpret_cast<char *>(&sh.u) + kEarlyStageOff);
       if (tid < nm) sh.loc_row[tid] = (int32_t)key_row(sh.u.s.cand[sh.u.s.mine[tid]]);
       __syncthreads();
-      attn_stage_dma_issue(a.s[sess].kv_rows, sh.loc_row, nm, est);
+      attn_stage_dma_issue(a.s[sess].kv_rows, sh.loc_row, nm, est.raw);
       if (wave == 0) {  // slot i (candidate mine[i]) -> its position in the group's key order
         const uint64_t x = lane < nm ? sh.u.s.cand[sh.u.s.mine[lane]] : 0ull;
         const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
@@ -470,7 +470,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       }
       wait_vmcnt<0>();  // this wave's row copies have landed
       __syncthreads();
-      attn_stage_dma_finish(a.s[sess].kv_rows, sh.loc_row, nm, est);
+      attn_stage_dma_finish(a.s[sess].kv_rows, sh.loc_row, nm, est.raw);
       __syncthreads();
       attn_staged_rows(aq, est, sh.ordered, nm, a.softmax_scale, a.n_heads, hgroup,
                        a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)myslice * CSA_MAX_HEADS * kKvDim,

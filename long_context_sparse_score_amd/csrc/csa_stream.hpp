@@ -45,6 +45,11 @@ __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// 4 bytes per active lane from sbase + voff (sbase wave-uniform) to LDS
+// address lds + 4 * lane (M0 = lds).
+__device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Wait until at most N vector memory instructions are outstanding.
