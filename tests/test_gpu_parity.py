@@ -271,6 +271,26 @@ def test_sparse_attn_skips_invalid_entries(csa, orc):
     assert np.allclose(_np(lse), ref_lse, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("count", [33, 64, 65, 100, 512])
+def test_sparse_attn_crowded_row_group(csa, orc, count):
+    # every entry in one of the stand-alone attention's 32 row groups (the
+    # top five bits of row * 0x9E3779B1), so that one workgroup stages many
+    # 32-row rounds, the last one partial; plus the buffer's last row
+    n = 20000
+    s = gen.session(0, n_rows=n)
+    d = gu.to_dev(s)
+    rows = np.arange(n, dtype=np.uint64)
+    group = ((rows * np.uint64(0x9E3779B1)) & np.uint64(0xFFFFFFFF)) >> np.uint64(27)
+    g0 = np.nonzero(group == group[n - 1])[0]
+    assert len(g0) >= count
+    sel = np.random.default_rng(count).permutation(g0[g0 != n - 1])[:count - 1].astype(np.int32)
+    sel = np.concatenate([sel, [n - 1]]).astype(np.int32)
+    out, lse = csa.sparse_attn(d["kv_rows"], torch.from_numpy(sel).cuda(), len(sel), d["q_attn"], s["softmax_scale"])
+    ref, ref_lse = orc.attention(s["kv_rows"], sel, s["q_attn"], s["softmax_scale"])
+    gu.check_attention(_np(out), ref)
+    assert np.allclose(_np(lse), ref_lse, rtol=1e-5, atol=1e-5)
+
+
 def test_deterministic(csa):
     s = gen.session(1, n_rows=40000)
     a = _run_step(csa, [s], s["softmax_scale"])[0]
