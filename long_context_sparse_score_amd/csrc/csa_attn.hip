@@ -68,10 +68,10 @@ __global__ void __launch_bounds__(kAttnThreads, 4) attn_rows_kernel(const AttnAr
 
 // ---------------------------------------------------------------- combine
 
-constexpr int kCombineThreads = 128;  // a quarter of the dimensions per workgroup
+constexpr int kCombineThreads = 64;  // an eighth of the dimensions per workgroup
 constexpr int kCombineSplit = kKvDim / kCombineThreads;
 
-// Four workgroups per (head, session), one thread per dimension
+// Eight one-wave workgroups per (head, session), one thread per dimension
 // (attn_combine_head).
 __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const AttnArgs a) {
   const int sess = blockIdx.y, h = blockIdx.x / kCombineSplit;
