@@ -119,6 +119,10 @@ __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32
   mx = wave_reduce_u32(mx, 0u, umax);
   cnt = wave_reduce_u32(cnt, 0u, uadd);
   if (lane == 0) { sh.red_lo[wave] = mn; sh.red_hi[wave] = mx; sh.red_n[wave] = cnt; }
+  // the first pass's histogram is cleared under the same barrier (visit
+  // reads nothing of it); red_n is next written after the pass's atomics
+  // and their barrier, which every thread reaches only after reading it here
+  for (int i = tid; i < kSelBins; i += kSelThreads) sh.u.s.hist[i] = 0;
   __syncthreads();
   uint32_t omin = ~0u, omax = 0;
   uint32_t total = 0;
@@ -128,17 +132,18 @@ __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32
     omax = (uint32_t)sh.red_hi[w] > omax ? (uint32_t)sh.red_hi[w] : omax;
     total += sh.red_n[w];
   }
-  __syncthreads();
   uint64_t lo = (uint64_t)omin << 32, hi = ((uint64_t)omax << 32) | 0xFFFFFFFFull;
   if (total <= need) return 1ull;
   // (even with few keys, G = the smallest would make every tile "full")
   uint32_t above = 0;  // keys above the current range [lo, hi]
-  for (;;) {
+  for (bool first = true;; first = false) {
     const uint64_t span = hi - lo;
     const int hb = span ? 63 - __clzll((long long)span) : 0;
     const int shift = hb > 9 ? hb - 9 : 0;  // span >> shift < kSelBins (1024)
-    for (int i = tid; i < kSelBins; i += kSelThreads) sh.u.s.hist[i] = 0;
-    __syncthreads();
+    if (!first) {
+      for (int i = tid; i < kSelBins; i += kSelThreads) sh.u.s.hist[i] = 0;
+      __syncthreads();
+    }
     visit([&](uint64_t x) __attribute__((always_inline)) {
       if (x >= lo && x <= hi) atomicAdd(&sh.u.s.hist[(uint32_t)((x - lo) >> shift)], 1u);
     });
@@ -162,9 +167,11 @@ __device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32
     }
     __syncthreads();
     const uint32_t b = sh.bin, ca = sh.ca, cb = sh.cb;
-    __syncthreads();
     const uint64_t gb = lo + ((uint64_t)b << shift);
+    // (uniform; after the return nothing writes bin, ca, cb or the
+    // histogram before another barrier)
     if (above + ca + cb <= target || shift == 0) return gb;
+    __syncthreads();  // every thread has read bin, ca, cb
     above += ca;
     const uint64_t top = gb + ((1ull << shift) - 1);
     lo = gb;
