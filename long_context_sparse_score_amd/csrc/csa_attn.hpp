@@ -92,7 +92,7 @@ static_assert(kRawRows % kAttnBatch == 0, "batches do not straddle a staging rou
 typedef uint32_t AttnRawRow[kRawStride / 4];  // one staging slot
 
 struct AttnStage {
-  AttnRawRow raw[kRawRows];                // staged packed rows
+  alignas(16) AttnRawRow raw[kRawRows];    // staged packed rows
   float lgp[kAttnWaves][2][4][64];         // partial logit tiles [wave][tile][v][lane]
 };
 
@@ -157,7 +157,7 @@ __device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *qs, i
 }
 
 // Per-wave state of a workgroup: P V accumulator tiles (heads 4(l/16) + v of
-// the head group, dimensions 64w + 16i + l%16) and the running max / sum of
+// the head group, dimensions 64w + 4(l%16) + i) and the running max / sum of
 // head l%16 (the same in every lane of that head and in every wave).
 struct AttnState {
   v4f_attn acc[4];
@@ -169,6 +169,16 @@ __device__ __forceinline__ void attn_init(AttnState &S) {
   for (int i = 0; i < 4; ++i) S.acc[i] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
   S.m = -__builtin_inff();
   S.l = 0.0f;
+}
+
+// E4M3 byte t (0..3, a constant after unrolling) of w times sc.
+__device__ __forceinline__ float fp8_byte_scaled(uint32_t w, float sc, int t) {
+  switch (t) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 3);
+  }
 }
 
 __device__ __forceinline__ short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
@@ -312,7 +322,9 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) S.acc[i][v] *= av[v];
-  // acc += P V over this wave's 64 dimensions (4 tiles of 16)
+  // acc += P V over this wave's 64 dimensions: tile t holds dimensions
+  // 64w + 4n + t (n = l%16), so that a lane reads its four dimensions of a
+  // row with one LDS load
   const v8bf PH = __builtin_bit_cast(v8bf, ph), PL = __builtin_bit_cast(v8bf, pl);
   const uint8_t *rb[8];
   bool rv[8];
@@ -326,28 +338,32 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
     float sc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) sc[k] = ue8m0_scale(rb[k][kKvNope + 128 + wave]);
+    uint32_t c4[8];  // E4M3 codes of dimensions 64w + 4n .. +4
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c4[k] = *reinterpret_cast<const uint32_t *>(rb[k] + 64 * wave + 4 * lr);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int d = 64 * wave + 16 * t + lr;
       v8s_attn vb;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float f = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)rb[k][d], sc[k], 0);
+        const float f = fp8_byte_scaled(c4[k], sc[k], t);
         vb[k] = bf16_bits(rv[k] ? f : 0.0f);
       }
       const v8bf VB = __builtin_bit_cast(v8bf, vb);
       S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PH, VB, S.acc[t], 0, 0, 0);
       S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PL, VB, S.acc[t], 0, 0, 0);
     }
-  } else {  // the RoPE values
+  } else {  // the RoPE values, indices 4n .. +4
+    uint2 h4[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h4[k] = *reinterpret_cast<const uint2 *>(rb[k] + kKvNope + 8 * lr);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int d = 16 * t + lr;  // RoPE index
       v8s_attn vh, vl;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         short h, l;
-        f16_split(*reinterpret_cast<const uint16_t *>(rb[k] + kKvNope + 2 * d), h, l);
+        f16_split(((t < 2 ? h4[k].x : h4[k].y) >> (16 * (t & 1))) & 0xFFFFu, h, l);
         vh[k] = rv[k] ? h : (short)0;
         vl[k] = rv[k] ? l : (short)0;
       }
@@ -368,12 +384,12 @@ __device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, int 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = 16 * g + 4 * lg + v;
-      if (h < n_heads) part[(size_t)h * kKvDim + 64 * wave + 16 * t + lr] = S.acc[t][v];
-    }
+  for (int v = 0; v < 4; ++v) {  // dimensions 64w + 4 lr .. +4 of head 16g + 4 lg + v
+    const int h = 16 * g + 4 * lg + v;
+    if (h < n_heads)
+      *reinterpret_cast<float4 *>(&part[(size_t)h * kKvDim + 64 * wave + 4 * lr]) =
+          float4{S.acc[0][v], S.acc[1][v], S.acc[2][v], S.acc[3][v]};
+  }
   const int hh = 16 * g + lr;
   if (wave == 0 && lg == 0 && hh < n_heads) {
     ml[2 * hh] = S.m;
