@@ -94,6 +94,7 @@ typedef uint32_t AttnRawRow[kRawStride / 4];  // one staging slot
 struct AttnStage {
   alignas(16) AttnRawRow raw[kRawRows];    // staged packed rows
   float lgp[kAttnWaves][2][4][64];         // partial logit tiles [wave][tile][v][lane]
+  float lgf[2][4][64];                     // their sums [tile][v][lane]
 };
 
 // x = t0 + t1 + t2 + r: three bf16 terms, each the round-to-nearest-even of
@@ -273,20 +274,23 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
     for (int v = 0; v < 4; ++v) st.lgp[wave][1][v][lane] = c[1][v];
   }
   __syncthreads();
-  // the full logits of rows 16u + 4(l/16) + v for head l%16, summed in a
-  // fixed order
+  // the full logits of rows 16u + 4(l/16) + v for head l%16, summed over the
+  // waves in a fixed order: wave w sums entry (u, v) = (w / 4, w % 4) of
+  // every lane once, and every wave reads the sums
+  if (wave < 4 || two) {  // uniform
+    const int u = wave >> 2, v = wave & 3;
+    float p[kAttnWaves];
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) p[w] = st.lgp[w][u][v][lane];
+    st.lgf[u][v][lane] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  }
+  __syncthreads();
   float lgt[2][4];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float sum = 0.0f;
-      if (u == 0 || two) {
-        float p[kAttnWaves];
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) p[w] = st.lgp[w][u][v][lane];
-        sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      }
+      const float sum = u == 0 || two ? st.lgf[u][v][lane] : 0.0f;
       lgt[u][v] = 16 * u + 4 * lg + v < nvalid ? scale * sum : -__builtin_inff();
     }
   // online softmax of head l%16 over the batch's rows (held by the lanes of
