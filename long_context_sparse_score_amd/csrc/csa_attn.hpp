@@ -172,16 +172,6 @@ __device__ __forceinline__ void attn_init(AttnState &S) {
   S.l = 0.0f;
 }
 
-// E4M3 byte t (0..3, a constant after unrolling) of w times sc.
-__device__ __forceinline__ float fp8_byte_scaled(uint32_t w, float sc, int t) {
-  switch (t) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)w, sc, 3);
-  }
-}
-
 __device__ __forceinline__ short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 
 // fp16 bits -> (bf16 hi, bf16 lo) with hi + lo == the fp16 value exactly.
@@ -301,17 +291,13 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
   mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
   const float m_new = fmaxf(S.m, mb);  // finite: the batch holds a row
   const float alpha = __expf(S.m - m_new);
-  float ps = 0.0f;
-  v8s_attn ph, pl;
+  float ps = 0.0f, pw[8];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float pv = __expf(lgt[u][v] - m_new);
-      ps += pv;
-      const __bf16 b = (__bf16)pv;
-      ph[4 * u + v] = __builtin_bit_cast(short, b);
-      pl[4 * u + v] = bf16_bits(pv - (float)b);
+      pw[4 * u + v] = __expf(lgt[u][v] - m_new);
+      ps += pw[4 * u + v];
     }
   ps += __shfl_xor(ps, 16, 64);
   ps += __shfl_xor(ps, 32, 64);
@@ -327,37 +313,58 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
 #pragma unroll
     for (int v = 0; v < 4; ++v) S.acc[i][v] *= av[v];
   // acc += P V over this wave's 64 dimensions: tile t holds dimensions
-  // 64w + 4n + t (n = l%16), so that a lane reads its four dimensions of a
-  // row with one LDS load
-  const v8bf PH = __builtin_bit_cast(v8bf, ph), PL = __builtin_bit_cast(v8bf, pl);
+  // 64w + 4n + t (n = l%16), so that a lane reads its four values of a row
+  // with one LDS load.  The weights enter as two bf16 terms, hi + lo.
   const uint8_t *rb[8];
-  bool rv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int i = 16 * (k >> 2) + 4 * lg + (k & 3);
     rb[k] = reinterpret_cast<const uint8_t *>(&raw[attn_slot(slotmap, b0, i, nvalid)][0]);
-    rv[k] = i < nvalid;
   }
-  if (wave < kKvNope / 64) {  // E4M3 block `wave`: one scale per row
-    float sc[8];
+  // (padding rows, i >= nvalid, read slot 0 and carry weight 0)
+  auto split_weights = [&](const float (&x)[8], v8bf &hi, v8bf &lo) __attribute__((always_inline)) {
+    v8s_attn h, l;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) sc[k] = ue8m0_scale(rb[k][kKvNope + 128 + wave]);
+    for (int k = 0; k < 8; ++k) {
+      const __bf16 b = (__bf16)x[k];
+      h[k] = __builtin_bit_cast(short, b);
+      l[k] = bf16_bits(x[k] - (float)b);
+    }
+    hi = __builtin_bit_cast(v8bf, h);
+    lo = __builtin_bit_cast(v8bf, l);
+  };
+  v8bf PH, PL;
+  if (wave < kKvNope / 64) {  // E4M3 block `wave`: one power-of-two scale per row
+    // the row's scale moves onto its weight (exact: a power of two), so the
+    // codes enter unscaled, four rows' bytes per conversion
+    float pws[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pws[k] = pw[k] * ue8m0_scale(rb[k][kKvNope + 128 + wave]);
+    split_weights(pws, PH, PL);
     uint32_t c4[8];  // E4M3 codes of dimensions 64w + 4n .. +4
 #pragma unroll
     for (int k = 0; k < 8; ++k) c4[k] = *reinterpret_cast<const uint32_t *>(rb[k] + 64 * wave + 4 * lr);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      v8s_attn vb;
+      // bytes t of rows k, k + 1 (twice), then of rows k .. k + 3 in order
+      const uint32_t sel = (uint32_t)t | (uint32_t)(4 + t) << 8 | (uint32_t)t << 16 | (uint32_t)(4 + t) << 24;
+      uint32_t q[2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = fp8_byte_scaled(c4[k], sc[k], t);
-        vb[k] = bf16_bits(rv[k] ? f : 0.0f);
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t x = __builtin_amdgcn_perm(c4[4 * h + 1], c4[4 * h], sel);
+        const uint32_t y = __builtin_amdgcn_perm(c4[4 * h + 3], c4[4 * h + 2], sel);
+        q[h] = __builtin_amdgcn_perm(y, x, 0x05040100u);
       }
-      const v8bf VB = __builtin_bit_cast(v8bf, vb);
+      const v2bf_attn a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[0], 1.0f, false);
+      const v2bf_attn a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[0], 1.0f, true);
+      const v2bf_attn a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[1], 1.0f, false);
+      const v2bf_attn a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[1], 1.0f, true);
+      const v8bf VB = v8bf{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
       S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PH, VB, S.acc[t], 0, 0, 0);
       S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PL, VB, S.acc[t], 0, 0, 0);
     }
   } else {  // the RoPE values, indices 4n .. +4
+    split_weights(pw, PH, PL);
     uint2 h4[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) h4[k] = *reinterpret_cast<const uint2 *>(rb[k] + kKvNope + 8 * lr);
@@ -368,8 +375,8 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
       for (int k = 0; k < 8; ++k) {
         short h, l;
         f16_split(((t < 2 ? h4[k].x : h4[k].y) >> (16 * (t & 1))) & 0xFFFFu, h, l);
-        vh[k] = rv[k] ? h : (short)0;
-        vl[k] = rv[k] ? l : (short)0;
+        vh[k] = h;
+        vl[k] = l;
       }
       const v8bf VH = __builtin_bit_cast(v8bf, vh), VL = __builtin_bit_cast(v8bf, vl);
       S.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PH, VH, S.acc[t], 0, 0, 0);
