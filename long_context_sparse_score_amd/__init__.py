@@ -108,6 +108,27 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "
     return t.data_ptr() if t.numel() else None
 
 
+def _rows(t: torch.Tensor, width: int, name: str) -> int:
+    """A packed row buffer [n][width] of bytes; returns n.  Checked on the host
+    so that a mis-shaped buffer is refused before any launch."""
+    if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != width:
+        raise ValueError(f"{name}: expected a uint8 tensor of shape [n, {width}], got {t.dtype} {tuple(t.shape)}")
+    return int(t.shape[0])
+
+
+def _mat(t: torch.Tensor, cols: int, name: str, rows: int | None = None) -> int:
+    """A float32 matrix [rows][cols]; returns its row count."""
+    if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != cols or (rows is not None and t.shape[0] != rows):
+        want = f"[{rows if rows is not None else 'h'}, {cols}]"
+        raise ValueError(f"{name}: expected a float32 tensor of shape {want}, got {t.dtype} {tuple(t.shape)}")
+    return int(t.shape[0])
+
+
+def _vec(t: torch.Tensor, n: int, name: str, dtype=torch.float32) -> None:
+    if t.dtype != dtype or t.dim() != 1 or t.shape[0] != n:
+        raise ValueError(f"{name}: expected a {dtype} vector of length {n}, got {t.dtype} {tuple(t.shape)}")
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -127,19 +148,24 @@ def alloc_workspace(max_rows_per_session: int, n_sessions: int = 1, device="cuda
 
 def score(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, scores: torch.Tensor | None = None,
           ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    n = idx_rows.shape[0]
+    n = _rows(idx_rows, IDX_ROW_BYTES, "idx_rows")
+    h = _mat(q_idx, IDX_DIM, "q_idx")
+    _vec(w_idx, h, "w_idx")
     if scores is None:
         scores = torch.empty(n, dtype=torch.float32, device=idx_rows.device)
+    _vec(scores, n, "scores")
     if ws is None:
         ws = alloc_workspace(n, 1, idx_rows.device)
     _check(lib.csa_score(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(q_idx, torch.float32, "q_idx"),
-                         _ptr(w_idx, torch.float32, "w_idx"), w_idx.shape[0], _ptr(scores, torch.float32, "scores"),
+                         _ptr(w_idx, torch.float32, "w_idx"), h, _ptr(scores, torch.float32, "scores"),
                          _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_score")
     return scores
 
 
 def topk(scores: torch.Tensor, k: int = TOPK, ws: torch.Tensor | None = None, stream=None):
-    n = scores.shape[0]
+    if scores.dtype != torch.float32 or scores.dim() != 1:
+        raise ValueError(f"scores: expected a float32 vector, got {scores.dtype} {tuple(scores.shape)}")
+    n = int(scores.shape[0])
     if ws is None:
         ws = alloc_workspace(n, 1, scores.device)
     sel = torch.empty(k, dtype=torch.int32, device=scores.device)
@@ -151,13 +177,17 @@ def topk(scores: torch.Tensor, k: int = TOPK, ws: torch.Tensor | None = None, st
 
 def sparse_attn(kv_rows: torch.Tensor, sel_idx: torch.Tensor, n_sel: int, q_attn: torch.Tensor, softmax_scale: float,
                 ws: torch.Tensor | None = None, stream=None):
-    h = q_attn.shape[0]
+    n_rows = _rows(kv_rows, KV_ROW_BYTES, "kv_rows")
+    h = _mat(q_attn, KV_DIM, "q_attn")
+    if sel_idx.dtype != torch.int32 or sel_idx.dim() != 1 or not 0 <= n_sel <= min(TOPK, sel_idx.shape[0]):
+        raise ValueError(f"sel_idx: expected an int32 vector holding n_sel={n_sel} <= {TOPK} entries, "
+                         f"got {sel_idx.dtype} {tuple(sel_idx.shape)}")
     dev = q_attn.device
     if ws is None:
         ws = alloc_workspace(0, 1, dev)
     out = torch.empty((h, KV_DIM), dtype=torch.float32, device=dev)
     lse = torch.empty(h, dtype=torch.float32, device=dev)
-    _check(lib.csa_sparse_attn(_ptr(kv_rows, torch.uint8, "kv_rows"), kv_rows.shape[0], _ptr(sel_idx, torch.int32, "sel"),
+    _check(lib.csa_sparse_attn(_ptr(kv_rows, torch.uint8, "kv_rows"), n_rows, _ptr(sel_idx, torch.int32, "sel"),
                                n_sel, _ptr(q_attn, torch.float32, "q_attn"), h, softmax_scale, _ptr(out), _ptr(lse),
                                _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_sparse_attn")
     return out, lse
@@ -176,19 +206,22 @@ class DecodeStep:
         if not 1 <= len(sessions) <= MAX_SESSIONS:
             raise ValueError("1..64 sessions")
         self.sessions = list(sessions)
-        self.n_idx_heads = int(sessions[0]["w_idx"].shape[0])
-        self.n_heads = int(sessions[0]["q_attn"].shape[0])
+        self.n_idx_heads = _mat(sessions[0]["q_idx"], IDX_DIM, "q_idx")
+        self.n_heads = _mat(sessions[0]["q_attn"], KV_DIM, "q_attn")
+        if not (1 <= self.n_idx_heads <= MAX_HEADS and 1 <= self.n_heads <= MAX_HEADS):
+            raise ValueError("1..64 indexer and attention heads")
         self.softmax_scale = float(softmax_scale)
         dev = sessions[0]["q_attn"].device
-        max_rows = max(int(s["idx_rows"].shape[0]) for s in sessions)
+        max_rows = max(_rows(s["idx_rows"], IDX_ROW_BYTES, "idx_rows") for s in sessions)
         self.ws = alloc_workspace(max_rows, len(sessions), dev) if ws is None else ws
         arr = (Session * len(sessions))()
         for i, s in enumerate(self.sessions):
-            n = int(s["idx_rows"].shape[0])
-            if s["kv_rows"].shape[0] != n:
+            n = _rows(s["idx_rows"], IDX_ROW_BYTES, "idx_rows")
+            if _rows(s["kv_rows"], KV_ROW_BYTES, "kv_rows") != n:
                 raise ValueError("idx_rows and kv_rows disagree on n_rows")
-            if s["w_idx"].shape[0] != self.n_idx_heads or s["q_attn"].shape[0] != self.n_heads:
-                raise ValueError("all sessions need the same head counts")
+            _mat(s["q_idx"], IDX_DIM, "q_idx", self.n_idx_heads)
+            _vec(s["w_idx"], self.n_idx_heads, "w_idx")
+            _mat(s["q_attn"], KV_DIM, "q_attn", self.n_heads)
             s.setdefault("sel", torch.empty(TOPK, dtype=torch.int32, device=dev))
             s.setdefault("sel_score", torch.empty(TOPK, dtype=torch.float32, device=dev))
             s.setdefault("out", torch.empty((self.n_heads, KV_DIM), dtype=torch.float32, device=dev))
@@ -198,6 +231,10 @@ class DecodeStep:
                              _ptr(s["q_attn"], torch.float32, "q_attn"), _ptr(s["sel"], torch.int32, "sel"),
                              _ptr(s["sel_score"], torch.float32), _ptr(s["out"], torch.float32),
                              _ptr(s["lse"], torch.float32))
+            _vec(s["sel"], TOPK, "sel", torch.int32)
+            _vec(s["sel_score"], TOPK, "sel_score")
+            _mat(s["out"], KV_DIM, "out", self.n_heads)
+            _vec(s["lse"], self.n_heads, "lse")
         self._arr = arr
 
     def __call__(self, stream=None) -> None:
@@ -206,8 +243,8 @@ class DecodeStep:
                "csa_decode_step")
 
     def timed(self, events: Sequence["torch.cuda.Event"], stream=None) -> None:
-        """Same work as ``__call__``; records ``events[2s]`` / ``events[2s+1]``
-        around stage s (STAGES) on the stream."""
+        """Same work as ``__call__``; records ``events[2s]`` /
+        ``events[2s+1]`` around stage s (STAGES) on the stream."""
         if len(events) != 2 * len(STAGES):
             raise ValueError(f"need {2 * len(STAGES)} events")
         for e in events:

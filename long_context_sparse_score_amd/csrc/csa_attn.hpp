@@ -14,15 +14,23 @@
 // Logits l[h][j] = scale * q_h . kv_j and values use the decoded 512-value
 // row for both (DS4X page, "Packed cache ABI").  Every operand enters the
 // matrix cores exactly:
-//   * a decoded non-RoPE value is an E4M3 value times 2^(s-127): at most 4
-//     significant bits, one bf16 term (exact for magnitudes >= 2^-133),
-//     converted from the packed byte by gfx950's scaled fp8 conversion;
+//   * a non-RoPE value is an E4M3 code (at most 4 significant bits, exact in
+//     bf16) times its block's power of two 2^(s-127).  The codes enter
+//     unscaled, converted from the packed bytes by gfx950's fp8 conversion;
+//     the power of two is applied outside the products: to a wave's partial
+//     logits (one wave's K range is exactly one 64-value block, so the scale
+//     is one per row there), and to the softmax weights of P V relative to a
+//     running block exponent of the wave (below), so no decoded magnitude is
+//     cut off by bf16's range;
 //   * a RoPE value is FP16 (11 bits): hi = bf16(v), lo = v - hi, two terms;
 //   * the fp32 query is q0 + q1 + q2, q_t = bf16(q - q0 - ... - q_{t-1})
 //     (round to nearest even), residual below 2^-26 |q|; it is split once
 //     per call (by the score kernel or the query-split kernel);
-//   * a softmax weight p in [0, 1] is hi + lo (two bf16 terms, residual
-//     below 2^-17 p).
+//   * a softmax weight is hi + lo (two bf16 terms, residual below 2^-17 of
+//     it).  In the E4M3 waves the weight of row j is p_j 2^(s_j - E), E the
+//     largest block scale byte the wave has met so far: the accumulator is
+//     kept in units of 2^(E-127) (rescaled exactly when E grows) and
+//     multiplied by 2^(E-127) when the partial is written.
 // Products of bf16 values are exact in fp32; sums are fp32 in a fixed
 // order.  Everything a workgroup computes depends only on its rows and their
 // order, so the fused and the stand-alone paths give identical bits.
@@ -163,6 +171,7 @@ __device__ __forceinline__ void load_attn_query(AttnQuery &q, const uint4 *qs, i
 struct AttnState {
   v4f_attn acc[4];
   float m, l;
+  int e;  // E4M3 waves: the accumulator's block exponent (scale byte); 0 until a row is met
 };
 
 __device__ __forceinline__ void attn_init(AttnState &S) {
@@ -170,6 +179,7 @@ __device__ __forceinline__ void attn_init(AttnState &S) {
   for (int i = 0; i < 4; ++i) S.acc[i] = v4f_attn{0.0f, 0.0f, 0.0f, 0.0f};
   S.m = -__builtin_inff();
   S.l = 0.0f;
+  S.e = 0;
 }
 
 __device__ __forceinline__ short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
@@ -184,19 +194,19 @@ __device__ __forceinline__ void f16_split(uint32_t h, short &hi, short &lo) {
 
 // Logits A operand of K step ks (dimensions 32 ks .. +32) for the row in
 // slot `slot`: the lane's 8 values at dimensions 32 ks + 8(l/16) .. +8, as
-// bf16 (lo: the RoPE remainder; zero for E4M3 steps).  Zero for a padding
-// row.
+// bf16 (lo: the RoPE remainder; zero for E4M3 steps).  E4M3 values are the
+// unscaled codes (the block's power of two is applied to the products' sum
+// by the caller).  Zero for a padding row.
 __device__ __forceinline__ void attn_row_operand(const AttnRawRow *raw, int slot, int ks, bool valid, v8bf &hi,
                                                  v8bf &lo) {
   const int lane = threadIdx.x & 63;
   const uint8_t *rb = reinterpret_cast<const uint8_t *>(&raw[slot][0]);
   if (ks < kKvNope / 32) {
     const uint2 c = *reinterpret_cast<const uint2 *>(rb + 32 * ks + 8 * (lane >> 4));
-    const float sc = ue8m0_scale(rb[kKvNope + 128 + (ks >> 1)]);
-    const v2bf_attn p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false);
-    const v2bf_attn p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true);
-    const v2bf_attn p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false);
-    const v2bf_attn p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true);
+    const v2bf_attn p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+    const v2bf_attn p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+    const v2bf_attn p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+    const v2bf_attn p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
     hi = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     if (!valid) hi = v8bf{};
     lo = v8bf{};
@@ -254,6 +264,20 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
       if (ks >= kKvNope / 32) {
 #pragma unroll
         for (int t = 0; t < 3; ++t) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, q.b[j][t], c[u], 0, 0, 0);
+      }
+    }
+  }
+  if (wave < kKvNope / 64) {  // uniform: this wave's K range is block `wave` of every row
+    // c[u][v] is the sum for row 16u + 4(l/16) + v over unscaled codes: times
+    // the row's 2^(s-127) (one rounding at most, in the fp32 subnormal range)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * u + 4 * lg + v;
+        const uint8_t *rr = reinterpret_cast<const uint8_t *>(&raw[attn_slot(slotmap, b0, i, nvalid)][0]);
+        c[u][v] *= ue8m0_scale(rr[kKvNope + 128 + wave]);
       }
     }
   }
@@ -335,11 +359,29 @@ __device__ __forceinline__ void attn_batch(const AttnQuery &q, AttnState &S, Att
   };
   v8bf PH, PL;
   if (wave < kKvNope / 64) {  // E4M3 block `wave`: one power-of-two scale per row
-    // the row's scale moves onto its weight (exact: a power of two), so the
-    // codes enter unscaled, four rows' bytes per conversion
+    // the codes enter unscaled, four rows' bytes per conversion; row j's
+    // weight carries 2^(s_j - E), E the running block exponent (the largest
+    // scale byte of the rows met so far), and the accumulator counts in
+    // units of 2^(E-127): rescaled exactly (powers of two) when E grows
+    int sb[8], smax = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sb[k] = rb[k][kKvNope + 128 + wave];
+      const int i = 16 * (k >> 2) + 4 * lg + (k & 3);
+      smax = i < nvalid && sb[k] > smax ? sb[k] : smax;
+    }
+    smax = max(smax, __shfl_xor(smax, 16, 64));
+    smax = max(smax, __shfl_xor(smax, 32, 64));  // every row of the batch: uniform
+    if (smax > S.e) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S.acc[i][v] = ldexpf(S.acc[i][v], S.e - smax);
+      S.e = smax;
+    }
     float pws[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pws[k] = pw[k] * ue8m0_scale(rb[k][kKvNope + 128 + wave]);
+    for (int k = 0; k < 8; ++k) pws[k] = ldexpf(pw[k], sb[k] - S.e);
     split_weights(pws, PH, PL);
     uint32_t c4[8];  // E4M3 codes of dimensions 64w + 4n .. +4
 #pragma unroll
@@ -394,12 +436,15 @@ __device__ __forceinline__ void attn_store(const AttnState &S, int n_heads, int 
                                            float *__restrict__ ml) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
+  // E4M3 waves: from units of 2^(E-127) to values (exact unless the result
+  // is an fp32 subnormal)
+  const int ex = wave < kKvNope / 64 ? S.e - 127 : 0;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {  // dimensions 64w + 4 lr .. +4 of head 16g + 4 lg + v
     const int h = 16 * g + 4 * lg + v;
     if (h < n_heads)
       *reinterpret_cast<float4 *>(&part[(size_t)h * kKvDim + 64 * wave + 4 * lr]) =
-          float4{S.acc[0][v], S.acc[1][v], S.acc[2][v], S.acc[3][v]};
+          float4{ldexpf(S.acc[0][v], ex), ldexpf(S.acc[1][v], ex), ldexpf(S.acc[2][v], ex), ldexpf(S.acc[3][v], ex)};
   }
   const int hh = 16 * g + lr;
   if (wave == 0 && lg == 0 && hh < n_heads) {

@@ -1,5 +1,11 @@
-// csa_decode.hip -- row decoders exposed for bit-level testing of the
-// element decoding every other kernel uses (csa_device.hpp).
+// csa_decode.hip -- stand-alone row decoders (csa_dequant_idx /
+// csa_dequant_kv): the element formats decoded in software, element by
+// element (csa_device.hpp), into fp32 arrays.  The decode-step kernels do not
+// call these: the scorer feeds the packed codes and scale bytes to the
+// block-scaled matrix cores as they are stored, and the attention converts
+// E4M3 codes with gfx950's fp8 conversion and applies the block scales as
+// exact powers of two (csa_attn.hpp); that path is pinned bit for bit by the
+// single-row attention tests.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 

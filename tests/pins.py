@@ -285,4 +285,34 @@ def check_attention(o) -> None:
     assert np.all(out == 0) and np.all(np.isneginf(lse))
 
 
-ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention)
+def check_decode_step(o) -> None:
+    """The whole step against the pipeline built from the independent
+    references above (numpy score -> Python sort -> PyTorch attention), at a
+    history shorter than 512 rows, one longer, and an empty one, with indexer
+    and attention head counts that differ (so a swapped count or query
+    cannot pass)."""
+    rng = np.random.default_rng(17)
+    scale = float(np.float32(1 / math.sqrt(512)))
+    for n, h_idx, h in ((300, 3, 2), (700, 2, 3), (0, 2, 1)):
+        idx = random_idx_rows(n, 40 + n)
+        kv = random_kv_rows(n, 50 + n)
+        q = rng.standard_normal((h_idx, 128)).astype(np.float32)
+        w = rng.uniform(0, 1, h_idx).astype(np.float32)
+        qa = rng.standard_normal((h, 512)).astype(np.float32)
+        got = o.decode_step(idx, kv, q, w, qa, scale)
+        k_eff = min(512, n)
+        assert got["k_eff"] == k_eff
+        s = ref_score(idx, q, w)
+        sel = ref_topk(list(s), 512)
+        assert list(got["sel"][:k_eff]) == sel, f"decode step selection n={n}"
+        assert np.all(got["sel"][k_eff:] == -1) and np.all(np.isneginf(got["sel_score"][k_eff:]))
+        assert np.array_equal(got["sel_score"][:k_eff], s[sel]), "decode step selected scores"
+        if k_eff == 0:
+            assert np.all(got["out"] == 0) and np.all(np.isneginf(got["lse"])), "empty history"
+            continue
+        ref_o, ref_l = ref_attention(kv, np.array(sel), qa, scale)
+        assert np.max(np.abs(got["out"] - ref_o)) <= 1e-6 * np.max(np.abs(ref_o)), f"decode step attention n={n}"
+        assert np.allclose(got["lse"], ref_l, rtol=1e-6, atol=1e-6), "decode step lse"
+
+
+ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention, check_decode_step)

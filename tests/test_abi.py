@@ -100,3 +100,32 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
     sess[1] = csa.Session(fake, fake, 100, odd, fake, fake, fake, None, fake, None)
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
+
+
+def test_binding_rejects_misshaped_tensors_before_any_launch(csa):
+    import torch
+
+    rows = torch.zeros((10, 68), dtype=torch.uint8)
+    q = torch.zeros((8, 128), dtype=torch.float32)
+    w = torch.zeros(8, dtype=torch.float32)
+    kv = torch.zeros((10, 583), dtype=torch.uint8)
+    qa = torch.zeros((4, 512), dtype=torch.float32)
+    sel = torch.zeros(512, dtype=torch.int32)
+    bad_calls = [
+        lambda: csa.score(rows.view(-1), q, w),                   # flat row buffer
+        lambda: csa.score(rows[:, :64], q, w),                    # wrong row width
+        lambda: csa.score(rows, q[:, :64], w),                    # wrong query width
+        lambda: csa.score(rows, q, w[:7]),                        # weights vs heads
+        lambda: csa.score(rows, q.double(), w),                   # wrong dtype
+        lambda: csa.topk(torch.zeros((4, 4)), 8),                 # not a vector
+        lambda: csa.sparse_attn(kv.view(-1), sel, 4, qa, 0.1),    # flat KV buffer
+        lambda: csa.sparse_attn(kv, sel, 4, qa[:, :100], 0.1),    # wrong query width
+        lambda: csa.sparse_attn(kv, sel[:3], 4, qa, 0.1),         # fewer entries than n_sel
+        lambda: csa.sparse_attn(kv, sel.long(), 4, qa, 0.1),      # wrong index dtype
+        lambda: csa.DecodeStep([dict(idx_rows=rows, kv_rows=kv[:9], q_idx=q, w_idx=w, q_attn=qa)], 0.1),
+        lambda: csa.DecodeStep([dict(idx_rows=rows, kv_rows=kv, q_idx=q, w_idx=w[:3], q_attn=qa)], 0.1),
+        lambda: csa.DecodeStep([dict(idx_rows=rows, kv_rows=kv, q_idx=q, w_idx=w, q_attn=qa[:, :8])], 0.1),
+    ]
+    for i, call in enumerate(bad_calls):
+        with pytest.raises(ValueError):
+            call()

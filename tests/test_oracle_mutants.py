@@ -38,6 +38,13 @@ MUTANTS = [
     ("attn_lse_no_max", "lse[h] = (float)(m + log(z));", "lse[h] = (float)log(z);"),
     ("attn_no_normalise", "(float)(acc[e] / z)", "(float)(acc[e])"),
     ("attn_q_row", "const float *q = q_attn + (size_t)h * 512;", "const float *q = q_attn;"),
+    ("step_k_not_k_eff", "sel, (int)k_eff, q_attn, n_heads", "sel, k, q_attn, n_heads"),
+    ("step_heads_swapped", "csa_oracle_score(idx_rows, n_rows, q_idx, w_idx, n_idx_heads, scores);",
+     "csa_oracle_score(idx_rows, n_rows, q_idx, w_idx, n_heads, scores);"),
+    ("step_attends_first_rows", "int64_t k_eff = csa_oracle_topk(scores, n_rows, k, sel, sel_score);",
+     "int64_t k_eff = csa_oracle_topk(scores, n_rows, k, sel, sel_score);\n  for (int64_t i = 0; i < k_eff; ++i) sel[i] = (int32_t)i;"),
+    ("step_scale_dropped", "q_attn, n_heads, softmax_scale, out,\n                              lse);",
+     "q_attn, n_heads, 1.0, out,\n                              lse);"),
 ]
 
 
