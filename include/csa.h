@@ -154,6 +154,25 @@ int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx
                           float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
                           void *const *events);
 
+/* Bytes of the library's static per-device workspace (csa_decode_step_noalloc). */
+#define CSA_SCRATCH_BYTES (32u << 20)
+
+/* csa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static array of
+ * CSA_SCRATCH_BYTES in the library's device code: each GPU the library runs
+ * on holds its own copy from the module's load until the process ends.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine); the
+ * caller still owns every input and output.  Returns CSA_EWORKSPACE, with
+ * nothing enqueued, when csa_workspace_bytes(largest n_rows, n_sessions)
+ * exceeds CSA_SCRATCH_BYTES (1,048,576 rows in one session fit).  Results
+ * are bit-identical to csa_decode_step.  All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller; the array keeps the last call's
+ * contents, which no call reads before writing. */
+int csa_decode_step_noalloc(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                            float softmax_scale, void *hip_stream);
+
 /* Test entry points: decode packed rows to fp32, [n][128] and [n][512]
  * (exact products; overflow gives +-inf; a 0xFF scale or an E4M3 NaN code
  * gives NaN).  Used to check the kernels' decode bit for bit. */

@@ -27,6 +27,7 @@ ABI_VERSION = 1
 STAGES = ("score + tile heads", "select + attention", "merge")
 
 OK, EINVAL, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4
+SCRATCH_BYTES = 32 << 20  # CSA_SCRATCH_BYTES: the static workspace of csa_decode_step_noalloc
 
 
 class CsaError(RuntimeError):
@@ -72,6 +73,8 @@ def _load() -> ctypes.CDLL:
     L.csa_sparse_attn.argtypes = [vp, i64, vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
     L.csa_decode_step.restype = i32
     L.csa_decode_step.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, vp, sz, vp]
+    L.csa_decode_step_noalloc.restype = i32
+    L.csa_decode_step_noalloc.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, vp]
     L.csa_decode_step_timed.restype = i32
     L.csa_decode_step_timed.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)]
@@ -199,10 +202,13 @@ class DecodeStep:
     ``sessions`` is a sequence of dicts with device tensors ``idx_rows``,
     ``kv_rows``, ``q_idx``, ``w_idx``, ``q_attn``; outputs ``sel``,
     ``sel_score``, ``out``, ``lse`` are allocated here.  ``__call__`` enqueues
-    one decode step of every session on the current stream.
+    one decode step of every session on the current stream.  With
+    ``noalloc=True`` no workspace is allocated and ``__call__`` runs
+    csa_decode_step_noalloc (the library's static per-device workspace).
     """
 
-    def __init__(self, sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None):
+    def __init__(self, sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None,
+                 noalloc: bool = False):
         if not 1 <= len(sessions) <= MAX_SESSIONS:
             raise ValueError("1..64 sessions")
         self.sessions = list(sessions)
@@ -211,9 +217,13 @@ class DecodeStep:
         if not (1 <= self.n_idx_heads <= MAX_HEADS and 1 <= self.n_heads <= MAX_HEADS):
             raise ValueError("1..64 indexer and attention heads")
         self.softmax_scale = float(softmax_scale)
+        self.noalloc = bool(noalloc)
         dev = sessions[0]["q_attn"].device
         max_rows = max(_rows(s["idx_rows"], IDX_ROW_BYTES, "idx_rows") for s in sessions)
-        self.ws = alloc_workspace(max_rows, len(sessions), dev) if ws is None else ws
+        if self.noalloc:
+            self.ws = None
+        else:
+            self.ws = alloc_workspace(max_rows, len(sessions), dev) if ws is None else ws
         arr = (Session * len(sessions))()
         for i, s in enumerate(self.sessions):
             n = _rows(s["idx_rows"], IDX_ROW_BYTES, "idx_rows")
@@ -238,13 +248,19 @@ class DecodeStep:
         self._arr = arr
 
     def __call__(self, stream=None) -> None:
+        if self.noalloc:
+            _check(lib.csa_decode_step_noalloc(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads,
+                                               self.softmax_scale, _stream(stream)), "csa_decode_step_noalloc")
+            return
         _check(lib.csa_decode_step(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads, self.softmax_scale,
                                    _ptr(self.ws, torch.uint8, "ws"), self.ws.numel(), _stream(stream)),
                "csa_decode_step")
 
     def timed(self, events: Sequence["torch.cuda.Event"], stream=None) -> None:
-        """Same work as ``__call__``; records ``events[2s]`` /
+        """Same work as ``__call__`` (with a workspace); records ``events[2s]`` /
         ``events[2s+1]`` around stage s (STAGES) on the stream."""
+        if self.ws is None:
+            raise ValueError("timed steps need a workspace (noalloc=False)")
         if len(events) != 2 * len(STAGES):
             raise ValueError(f"need {2 * len(STAGES)} events")
         for e in events:

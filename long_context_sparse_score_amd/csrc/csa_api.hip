@@ -73,6 +73,14 @@ int choose_slices(int n_sessions) {
 
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
+// Workspace of csa_decode_step_noalloc: one array per device, held from the
+// module's load until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get the device
+// address that hipGetSymbolAddress returns for the current device, kept in
+// g_scratch_ptr (each device holds its own copy at its own address).
+__device__ __align__(256) uint8_t scratch[CSA_SCRATCH_BYTES];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return CSA_EDEVICE;
@@ -88,6 +96,19 @@ int check_device() {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EDEVICE; }
+
+// Device address of this device's `scratch`, looked up once per device (with
+// that device current); null on a HIP error.
+void *scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 bool rows_ok(int64_t n) { return n >= 0 && n <= CSA_MAX_ROWS; }
 bool heads_ok(int h) { return h >= 1 && h <= CSA_MAX_HEADS; }
@@ -341,6 +362,25 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream) {
   return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, ws_bytes, hip_stream,
                           nullptr);
+}
+
+int csa_decode_step_noalloc(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                            float softmax_scale, void *hip_stream) {
+  // the sizes are checked before the device is touched: a step whose
+  // workspace exceeds the static array is rejected with nothing enqueued
+  if (!sessions || n_sessions < 1 || n_sessions > CSA_MAX_SESSIONS) return CSA_EINVAL;
+  int64_t max_rows = 0;
+  for (int i = 0; i < n_sessions; ++i) {
+    if (!rows_ok(sessions[i].n_rows)) return CSA_EINVAL;
+    if (sessions[i].n_rows > max_rows) max_rows = sessions[i].n_rows;
+  }
+  if (make_layout(max_rows, n_sessions).total > (size_t)CSA_SCRATCH_BYTES) return CSA_EWORKSPACE;
+  int rc = check_device();
+  if (rc != CSA_OK) return rc;
+  void *ws = scratch_ptr();
+  if (ws == nullptr) return CSA_EDEVICE;
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, CSA_SCRATCH_BYTES,
+                          hip_stream, nullptr);
 }
 
 int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,

@@ -102,6 +102,22 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
 
 
+def test_noalloc_entry_point_rejects_oversized_steps_on_host(csa):
+    L = csa.lib
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the size check comes first
+    sess = (csa.Session * 16)()
+    for i in range(16):
+        sess[i] = csa.Session(fake, fake, 1 << 20, fake, fake, fake, fake, None, fake, None)
+    assert csa.workspace_bytes(1 << 20, 16) > csa.SCRATCH_BYTES >= csa.workspace_bytes(1 << 20, 1)
+    assert L.csa_decode_step_noalloc(sess, 16, 64, 64, 0.1, None) == csa.EWORKSPACE
+    assert L.csa_decode_step_noalloc(sess, 0, 64, 64, 0.1, None) == csa.EINVAL
+    assert L.csa_decode_step_noalloc(None, 1, 64, 64, 0.1, None) == csa.EINVAL
+    sess[0] = csa.Session(fake, fake, -5, fake, fake, fake, fake, None, fake, None)
+    assert L.csa_decode_step_noalloc(sess, 1, 64, 64, 0.1, None) == csa.EINVAL
+    text = open(HEADER).read()
+    assert "#define CSA_SCRATCH_BYTES (32u << 20)" in text and csa.SCRATCH_BYTES == 32 << 20
+
+
 def test_binding_rejects_misshaped_tensors_before_any_launch(csa):
     import torch
 
