@@ -96,15 +96,16 @@ size_t csa_workspace_bytes(int64_t max_rows_per_session, int n_sessions);
 /* Indexer score of every row (the legacy first stage; DS4X page, "What DS4X
  * changes": full F32 score array, then a separate exact top-512 pass):
  *   scores[j] = sum_h w_idx[h] * max(0, sum_i q_idx[h][i] * k_j[i]),
- * k_j the decoded row j.  Computed on the matrix cores from the packed row
- * itself (E2M1 codes and UE8M0 scales as a block-scaled fp4 operand); the
- * fp32 query enters as a sum of five fp6 terms (relative residual below
- * 2^-19 of each 32-value block's maximum), products are exact and sums are
- * fp32.  The operation order is fixed, so a row's score does not depend on
- * its position; -0 is stored as +0.  The fused csa_decode_step computes
- * bit-identical scores.  n_idx_heads in [1, 64]; n_rows in [0, CSA_MAX_ROWS];
- * idx_rows and q_idx must be 16-byte aligned (both are streamed in 16-byte
- * pieces; CSA_EINVAL otherwise); ws sized by csa_workspace_bytes(n_rows, 1). */
+ * k_j the decoded row j (each value an E2M1 code times its block's
+ * 2^(e-127), as fp32).  Computed in fp64 with i ascending inside a head and h
+ * ascending outside (products q * k are exact in fp64; w * max(0, d) is
+ * rounded, then added), rounded once to fp32, -0 stored as +0: the exact
+ * value the decode step's selection orders by.  n_idx_heads in [1, 64];
+ * n_rows in [0, CSA_MAX_ROWS]; idx_rows and q_idx must be 16-byte aligned
+ * (CSA_EINVAL otherwise); ws sized by csa_workspace_bytes(n_rows, 1).  The
+ * fp64 arithmetic bounds this call (about 0.2 ms per million rows at 64
+ * heads); the decode step scores exactly only the rows its filter cannot
+ * place (csa_score_bounds). */
 int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
               int n_idx_heads, float *scores, void *ws, size_t ws_bytes, void *hip_stream);
 
@@ -143,7 +144,7 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Stages of csa_decode_step, in launch order. */
-#define CSA_STAGES 3 /* 0 query split + score + tile heads, 1 select + attention partials, 2 merge */
+#define CSA_STAGES 3 /* 0 filter score + tile heads + exact rescoring of the candidates, 1 select + attention partials, 2 merge */
 
 /* csa_decode_step that also records events[2*s] right before and
  * events[2*s+1] right after the launches of stage s on hip_stream, so a
@@ -172,6 +173,16 @@ int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx
  * contents, which no call reads before writing. */
 int csa_decode_step_noalloc(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                             float softmax_scale, void *hip_stream);
+
+/* Test entry point: the decode step's matrix-core filter.  For every row,
+ * lower[j] <= scores[j] <= upper[j], scores as csa_score computes them: the
+ * filter scores the row with the query held to three fp6 terms per 32-value
+ * block on the block-scaled matrix cores and brackets the exact score by a
+ * rigorous bound from the query's residual and term magnitudes, the head
+ * weights and the row's four UE8M0 bytes (a byte >= 253 gives an infinite
+ * bracket).  Same arguments and rules as csa_score. */
+int csa_score_bounds(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
+                     int n_idx_heads, float *upper, float *lower, void *ws, size_t ws_bytes, void *hip_stream);
 
 /* Test entry points: decode packed rows to fp32, [n][128] and [n][512]
  * (exact products; overflow gives +-inf; a 0xFF scale or an E4M3 NaN code

@@ -24,7 +24,7 @@ TOPK = 512
 MAX_HEADS = 64
 MAX_SESSIONS = 64
 ABI_VERSION = 1
-STAGES = ("score + tile heads", "select + attention", "merge")
+STAGES = ("filter + tile heads + exact rescoring", "select + attention", "merge")
 
 OK, EINVAL, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4
 SCRATCH_BYTES = 32 << 20  # CSA_SCRATCH_BYTES: the static workspace of csa_decode_step_noalloc
@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     L.csa_workspace_bytes.argtypes = [i64, i32]
     L.csa_score.restype = i32
     L.csa_score.argtypes = [vp, i64, vp, vp, i32, vp, vp, sz, vp]
+    L.csa_score_bounds.restype = i32
+    L.csa_score_bounds.argtypes = [vp, i64, vp, vp, i32, vp, vp, vp, sz, vp]
     L.csa_topk.restype = i32
     L.csa_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
     L.csa_sparse_attn.restype = i32
@@ -163,6 +165,23 @@ def score(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, scor
                          _ptr(w_idx, torch.float32, "w_idx"), h, _ptr(scores, torch.float32, "scores"),
                          _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_score")
     return scores
+
+
+def score_bounds(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, ws: torch.Tensor | None = None,
+                 stream=None):
+    """The decode step's filter: (upper, lower) with lower <= score <= upper
+    for every row (csa_score_bounds)."""
+    n = _rows(idx_rows, IDX_ROW_BYTES, "idx_rows")
+    h = _mat(q_idx, IDX_DIM, "q_idx")
+    _vec(w_idx, h, "w_idx")
+    up = torch.empty(n, dtype=torch.float32, device=idx_rows.device)
+    lo = torch.empty(n, dtype=torch.float32, device=idx_rows.device)
+    if ws is None:
+        ws = alloc_workspace(n, 1, idx_rows.device)
+    _check(lib.csa_score_bounds(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(q_idx, torch.float32, "q_idx"),
+                                _ptr(w_idx, torch.float32, "w_idx"), h, _ptr(up), _ptr(lo),
+                                _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_score_bounds")
+    return up, lo
 
 
 def topk(scores: torch.Tensor, k: int = TOPK, ws: torch.Tensor | None = None, stream=None):

@@ -20,23 +20,31 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout for (max rows per session, sessions); sized for the
 // smallest tile so that it grows monotonically with max_rows:
-//   [attention query split][tile heads][scores][attention partials]
-//   [attention (m, l)]
+//   [attention query split][head keys][head lower-bound keys][tile next keys]
+//   [items][item counts][attention partials][attention (m, l)]
+// The items hold the exact keys of the rows that can reach the top-k: the
+// head slots plus, for the rare tiles whose other rows may also reach it,
+// every row of those tiles (at most every row of the session).
 struct Layout {
   int64_t tiles_cap;  // tiles per session at the smallest tile size
-  int64_t rows_cap;   // score slots per session
-  size_t attn_q_off, heads_off, scores_off, part_off, ml_off, total;
+  int64_t heads_cap;  // head slots per session
+  int64_t items_cap;  // items per session
+  size_t attn_q_off, hkey_off, hlow_off, hnext_off, items_off, count_off, part_off, ml_off, total;
 };
 
 Layout make_layout(int64_t max_rows, int n_sessions) {
   Layout L;
   L.tiles_cap = (max_rows + kMinTileRows - 1) / kMinTileRows;
-  L.rows_cap = (max_rows + 63) & ~(int64_t)63;
+  L.heads_cap = L.tiles_cap * kMaxTileHeads;
+  L.items_cap = L.heads_cap + ((max_rows + 63) & ~(int64_t)63);
   const size_t ns = (size_t)n_sessions;
   L.attn_q_off = 0;
-  L.heads_off = L.attn_q_off + align_up(ns * kAttnQBytes);
-  L.scores_off = L.heads_off + align_up(ns * (size_t)L.tiles_cap * kMaxTileHeads * sizeof(uint64_t));
-  L.part_off = L.scores_off + align_up(ns * (size_t)L.rows_cap * sizeof(float));
+  L.hkey_off = L.attn_q_off + align_up(ns * kAttnQBytes);
+  L.hlow_off = L.hkey_off + align_up(ns * (size_t)L.heads_cap * sizeof(uint64_t));
+  L.hnext_off = L.hlow_off + align_up(ns * (size_t)L.heads_cap * sizeof(uint64_t));
+  L.items_off = L.hnext_off + align_up(ns * (size_t)(L.tiles_cap > 0 ? L.tiles_cap : 1) * sizeof(uint64_t));
+  L.count_off = L.items_off + align_up(ns * (size_t)(L.items_cap > 0 ? L.items_cap : 1) * sizeof(uint64_t));
+  L.part_off = L.count_off + align_up(ns * sizeof(uint32_t));
   L.ml_off = L.part_off + align_up(ns * kAttnPartFloats * sizeof(float));
   L.total = L.ml_off + align_up(ns * kAttnMlFloats * sizeof(float));
   return L;
@@ -128,10 +136,12 @@ T *at(void *ws, size_t off) {
 
 void fill_job(TileJob &job, const Layout &L, void *ws, int n_sessions) {
   job.n_sessions = n_sessions;
-  job.attn_q = nullptr;
-  job.n_attn_heads = 0;
-  job.heads = at<uint64_t>(ws, L.heads_off);
-  job.heads_stride = L.tiles_cap * kMaxTileHeads;
+  job.hkey = at<uint64_t>(ws, L.hkey_off);
+  job.hlow = at<uint64_t>(ws, L.hlow_off);
+  job.hnext = at<uint64_t>(ws, L.hnext_off);
+  job.heads_stride = L.heads_cap;
+  job.tiles_stride = L.tiles_cap;
+  job.bnd_up = job.bnd_lo = nullptr;
   int64_t total = 0;
   for (int i = 0; i < n_sessions; ++i) total += job.n_rows[i];
   job.tile_rows = choose_tile_rows(total);
@@ -139,21 +149,56 @@ void fill_job(TileJob &job, const Layout &L, void *ws, int n_sessions) {
     job.hd[i] = heads_per_tile((job.n_rows[i] + job.tile_rows - 1) / job.tile_rows);
 }
 
-// The selection that follows a tile launch.
-void fill_select(SelectJob &sj, const TileJob &job, int k) {
+// Workgroups per session of the exact rescoring: about one per compute
+// unit in total.
+int refine_blocks(int n_sessions) {
+  const int b = 256 / n_sessions;
+  return b < 2 ? 2 : b;
+}
+
+// The exact rescoring that follows a tile launch.
+void fill_refine(RefineJob &rj, const TileJob &job, const Layout &L, void *ws, int k) {
+  rj.mode = job.mode == TileJob::kArray ? RefineJob::kArray : RefineJob::kDecode;
+  rj.n_sessions = job.n_sessions;
+  rj.n_idx_heads = job.n_idx_heads;
+  rj.tile_rows = job.tile_rows;
+  rj.k = k;
+  rj.blocks = refine_blocks(job.n_sessions);
+  rj.attn_q = nullptr;
+  rj.n_attn_heads = 0;
+  for (int i = 0; i < job.n_sessions; ++i) {
+    rj.q_attn[i] = nullptr;
+    rj.idx_rows[i] = job.idx_rows[i];
+    rj.q[i] = job.q[i];
+    rj.w[i] = job.w[i];
+    rj.scores[i] = const_cast<float *>(job.scores_in[i]);
+    rj.n_rows[i] = job.n_rows[i];
+    rj.hd[i] = job.hd[i];
+  }
+  rj.hkey = job.hkey;
+  rj.hlow = job.hlow;
+  rj.hnext = job.hnext;
+  rj.items = at<uint64_t>(ws, L.items_off);
+  rj.count = at<uint32_t>(ws, L.count_off);
+  rj.heads_stride = L.heads_cap;
+  rj.tiles_stride = L.tiles_cap;
+  rj.items_stride = L.items_cap;
+}
+
+// The selection that follows the rescoring.
+void fill_select(SelectJob &sj, const TileJob &job, const RefineJob &rj, int k) {
   sj.n_sessions = job.n_sessions;
-  sj.tile_rows = job.tile_rows;
   sj.k = k;
   sj.slices = choose_slices(job.n_sessions);
-  sj.array_scores = job.mode == TileJob::kArraySelect;
+  sj.array_scores = job.mode == TileJob::kArray;
   for (int i = 0; i < job.n_sessions; ++i) {
-    sj.scores[i] = sj.array_scores ? job.scores_in[i] : job.scores_out[i];
+    sj.scores[i] = job.scores_in[i];
     sj.n_rows[i] = job.n_rows[i];
-    sj.hd[i] = job.hd[i];
     sj.kv_rows[i] = nullptr;
   }
-  sj.heads = job.heads;
-  sj.heads_stride = job.heads_stride;
+  sj.items = rj.items;
+  sj.count = rj.count;
+  sj.items_stride = rj.items_stride;
   sj.attn_q = nullptr;
   sj.attn_part = nullptr;
   sj.attn_ml = nullptr;
@@ -206,20 +251,45 @@ int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const
   if (rc != CSA_OK) return rc;
   rc = check_device();
   if (rc != CSA_OK) return rc;
-  hipStream_t st = (hipStream_t)hip_stream;
+  if (n_rows == 0) return CSA_OK;
+  RefineJob rj{};
+  rj.mode = RefineJob::kAll;
+  rj.n_sessions = 1;
+  rj.n_idx_heads = n_idx_heads;
+  rj.tile_rows = kMinTileRows;
+  rj.k = CSA_TOPK;
+  rj.blocks = 1024;  // four workgroups per compute unit: the fp64 arithmetic bounds it
+  rj.idx_rows[0] = idx_rows;
+  rj.q[0] = q_idx;
+  rj.w[0] = w_idx;
+  rj.scores[0] = scores;
+  rj.n_rows[0] = n_rows;
+  rj.hd[0] = kMinTileHeads;
+  return status_of(launch_refine(rj, (hipStream_t)hip_stream));
+}
+
+int csa_score_bounds(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
+                     int n_idx_heads, float *upper, float *lower, void *ws, size_t ws_bytes, void *hip_stream) {
+  if (!rows_ok(n_rows) || !heads_ok(n_idx_heads) || !q_idx || !w_idx || !idx_aligned(q_idx)) return CSA_EINVAL;
+  if (n_rows > 0 && (!idx_rows || !upper || !lower || !idx_aligned(idx_rows))) return CSA_EINVAL;
+  Layout L;
+  int rc = check_ws(ws, ws_bytes, n_rows, 1, &L);
+  if (rc != CSA_OK) return rc;
+  rc = check_device();
+  if (rc != CSA_OK) return rc;
   TileJob job;
-  job.mode = TileJob::kScore;
+  job.mode = TileJob::kBounds;
   job.n_idx_heads = n_idx_heads;
   job.idx_rows[0] = idx_rows;
   job.scores_in[0] = nullptr;
-  job.scores_out[0] = scores;
   job.n_rows[0] = n_rows;
   job.q[0] = q_idx;
   job.w[0] = w_idx;
-  job.q_attn[0] = nullptr;
   fill_job(job, L, ws, 1);
+  job.bnd_up = upper;
+  job.bnd_lo = lower;
   if (n_rows == 0) return CSA_OK;
-  return status_of(launch_tiles(job, st));
+  return status_of(launch_tiles(job, (hipStream_t)hip_stream));
 }
 
 int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float *sel_score,
@@ -233,19 +303,21 @@ int csa_topk(const float *scores, int64_t n_rows, int k, int32_t *sel_idx, float
   if (rc != CSA_OK) return rc;
   hipStream_t st = (hipStream_t)hip_stream;
   TileJob job;
-  job.mode = TileJob::kArraySelect;
+  job.mode = TileJob::kArray;
   job.n_idx_heads = 1;
   job.idx_rows[0] = nullptr;
   job.scores_in[0] = scores;
-  job.scores_out[0] = nullptr;
   job.n_rows[0] = n_rows;
-  job.q[0] = job.w[0] = job.q_attn[0] = nullptr;
+  job.q[0] = job.w[0] = nullptr;
   fill_job(job, L, ws, 1);
+  RefineJob rj;
+  fill_refine(rj, job, L, ws, k);
   SelectJob sj;
-  fill_select(sj, job, k);
+  fill_select(sj, job, rj, k);
   sj.sel_idx[0] = sel_idx;
   sj.sel_score[0] = sel_score;
   hipError_t e = launch_tiles(job, st);
+  if (e == hipSuccess && n_rows > 0) e = launch_refine(rj, st);
   if (e == hipSuccess) e = launch_select(sj, st);
   return status_of(e);
 }
@@ -293,21 +365,18 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   hipStream_t st = (hipStream_t)hip_stream;
 
   TileJob job;
-  job.mode = TileJob::kScoreSelect;
+  job.mode = TileJob::kFilter;
   job.n_idx_heads = n_idx_heads;
   int32_t *sel[CSA_MAX_SESSIONS];
   float *sel_score[CSA_MAX_SESSIONS];
   AttnSession at_s[CSA_MAX_SESSIONS];
-  float *scores = at<float>(ws, L.scores_off);
   for (int i = 0; i < n_sessions; ++i) {
     const csa_session &s = sessions[i];
     job.idx_rows[i] = s.idx_rows;
     job.scores_in[i] = nullptr;
-    job.scores_out[i] = scores + (size_t)i * L.rows_cap;
     job.n_rows[i] = s.n_rows;
     job.q[i] = s.q_idx;
     job.w[i] = s.w_idx;
-    job.q_attn[i] = s.q_attn;
     sel[i] = s.sel_idx;
     sel_score[i] = s.sel_score;
     const int32_t n_sel = (int32_t)(s.n_rows < CSA_TOPK ? s.n_rows : CSA_TOPK);
@@ -315,11 +384,14 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   }
   fill_job(job, L, ws, n_sessions);
   uint4 *aq = at<uint4>(ws, L.attn_q_off);
-  job.attn_q = aq;  // split by the score kernel
-  job.n_attn_heads = n_heads;
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
+  RefineJob rj;
+  fill_refine(rj, job, L, ws, CSA_TOPK);
+  rj.attn_q = aq;  // the attention query is split by the rescoring's workgroups
+  rj.n_attn_heads = n_heads;
+  for (int i = 0; i < n_sessions; ++i) rj.q_attn[i] = sessions[i].q_attn;
   SelectJob sj;
-  fill_select(sj, job, CSA_TOPK);
+  fill_select(sj, job, rj, CSA_TOPK);
   // One session's selection workgroups also run its attention (one
   // workgroup per row group and head group).  With many sessions that grid
   // would take several rounds of the chip, so the selection runs alone and
@@ -341,11 +413,14 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     sj.sel_score[i] = sel_score[i];
     sj.kv_rows[i] = sessions[i].kv_rows;
   }
+  bool any_rows = false;
+  for (int i = 0; i < n_sessions; ++i) any_rows = any_rows || sessions[i].n_rows > 0;
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_tiles(job, st);
+  if (e == hipSuccess && any_rows) e = launch_refine(rj, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_select(sj, st);

@@ -32,41 +32,64 @@ inline int heads_per_tile(int64_t nt) {
   return hd;
 }
 
-// One launch of the score kernel.
+// One launch of the score kernel (csa_topk_tile.hip).
 struct TileJob {
-  enum Mode { kScore, kScoreSelect, kArraySelect } mode;
+  enum Mode { kFilter, kArray, kBounds } mode;  // score + heads; given scores + heads; score + brackets only
   int n_sessions;
   int n_idx_heads;
   int tile_rows;
   const uint8_t *idx_rows[CSA_MAX_SESSIONS];
-  const float *scores_in[CSA_MAX_SESSIONS];  // kArraySelect
-  float *scores_out[CSA_MAX_SESSIONS];       // kScore, kScoreSelect
+  const float *scores_in[CSA_MAX_SESSIONS];  // kArray
   int64_t n_rows[CSA_MAX_SESSIONS];
   int hd[CSA_MAX_SESSIONS];
   const float *q[CSA_MAX_SESSIONS];       // indexer query [n_idx_heads][128] (scoring modes)
   const float *w[CSA_MAX_SESSIONS];       // indexer head weights
-  const float *q_attn[CSA_MAX_SESSIONS];  // attention query [n_attn_heads][512] (when attn_q)
-  uint4 *attn_q;                          // attention query split, [session][kAttnQVecs], or null
+  uint64_t *hkey;   // [session][heads_stride]: head keys by upper bound, rank-major [hd][nt]
+  uint64_t *hlow;   // [session][heads_stride]: their lower-bound keys, same order
+  uint64_t *hnext;  // [session][tiles_stride]: per tile its (hd+1)-th key
+  int64_t heads_stride, tiles_stride;
+  float *bnd_up, *bnd_lo;  // kBounds: the brackets of every row (one session)
+};
+
+// One launch of the exact rescoring (csa_refine.hip).
+struct RefineJob {
+  enum Mode { kDecode, kArray, kAll } mode;  // candidates scored exactly; candidates from given scores; every row
+  int n_sessions;
+  int n_idx_heads;
+  int tile_rows;
+  int k;
+  int blocks;  // workgroups per session
+  const uint8_t *idx_rows[CSA_MAX_SESSIONS];
+  const float *q[CSA_MAX_SESSIONS];
+  const float *w[CSA_MAX_SESSIONS];
+  float *scores[CSA_MAX_SESSIONS];  // kArray: the given scores; kAll: the output
+  int64_t n_rows[CSA_MAX_SESSIONS];
+  int hd[CSA_MAX_SESSIONS];
+  const float *q_attn[CSA_MAX_SESSIONS];  // kDecode: the attention query [n_attn_heads][512]
+  uint4 *attn_q;                          // kDecode: its split, [session][kAttnQVecs] (null: none)
   int n_attn_heads;
-  uint64_t *heads;  // [session][heads_stride]: per tile its top-hd keys, sorted
-  int64_t heads_stride;
+  const uint64_t *hkey;  // rank-major heads (TileJob)
+  const uint64_t *hlow;
+  const uint64_t *hnext;
+  uint64_t *items;  // [session][items_stride]
+  uint32_t *count;  // [session]
+  int64_t heads_stride, tiles_stride, items_stride;
 };
 
 // One launch of the global selection (and, optionally, of the attention
-// attention of the selected rows).
+// of the selected rows).
 struct SelectJob {
   int n_sessions;
-  int tile_rows;
   int k;
   int slices;          // workgroups per session
   bool array_scores;   // sel_score from the score array (csa_topk) or the key
   const float *scores[CSA_MAX_SESSIONS];
   int64_t n_rows[CSA_MAX_SESSIONS];
-  int hd[CSA_MAX_SESSIONS];
   int32_t *sel_idx[CSA_MAX_SESSIONS];
   float *sel_score[CSA_MAX_SESSIONS];
-  const uint64_t *heads;
-  int64_t heads_stride;
+  const uint64_t *items;  // [session][items_stride]: exact keys of the rows that can reach the top-k
+  const uint32_t *count;  // [session]
+  int64_t items_stride;
   // attention partials of the selected rows (attn_part == nullptr: none);
   // then slices must equal kAttnSlices (row groups x head groups)
   const uint4 *attn_q;  // [session][attention query split]
@@ -96,6 +119,7 @@ hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStre
 hipError_t launch_attn_q_split(const float *const *q_attn, int n_sessions, int n_attn_heads, uint4 *attn_out,
                                hipStream_t st);
 hipError_t launch_tiles(const TileJob &job, hipStream_t st);
+hipError_t launch_refine(const RefineJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);
 // Attention partials of the rows sel_idx[0..n_sel) of every session, one
 // workgroup per group (csa_sparse_attn).

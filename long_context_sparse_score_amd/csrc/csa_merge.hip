@@ -1,24 +1,17 @@
-// csa_merge.hip -- the global exact top-k of a session from its tiles' heads
-// (DS4X page, "CSA score/top-512 fusion": merge the per-tile selections into
-// the model's exact top-512 with the same float order and lower-index tie
-// break as a separate top-k pass), and optionally the attention of
-// the selected rows.
+// csa_merge.hip -- the global exact top-k of a session (DS4X page, "CSA
+// score/top-512 fusion": the model's exact top-512 with the same float score
+// order and lower-index tie break as a separate top-k pass), and optionally
+// the attention of the selected rows.
 //
+// Input: the session's items (csa_refine.hip): exact keys of every row that
+// can reach the top-k (plus 0 = "no key" slots), count[session] of them.
 // Every workgroup of a session (grid.x = slices) runs the same selection:
-//   1. G: a lower bound on the 512th-largest head, found with one or two
-//      histogram passes over the heads: at least 512 heads are >= G, and at
-//      most kSelTarget are (or exactly 512).  Since every head is a key, at
-//      least 512 keys are >= G, so G also bounds the global 512th key, and
-//      the top-k (k <= 512) lies among the keys >= G.
-//   2. A tile is "full" when its hd-th (smallest) head is >= G: it may hold
-//      keys >= G that are not heads.  Any other tile holds no key >= G beyond
-//      its heads.  Candidates = heads >= G of tiles that are not full, plus
-//      every key >= G of the full tiles, read from the score array.  (Few
-//      heads per tile hold at least hd keys >= G, so at most kSelTarget / hd
-//      tiles are full.)
-//   3. If the candidates overflow the LDS buffer (many ties, crowded
-//      winners), the exact k_eff-th key among them replaces G.
-//   4. The candidates are ranked exactly (rank = number of larger
+//   1. G: a lower bound on the k_eff-th largest key, found with histogram
+//      passes (block_bound): at least k_eff keys are >= G, and at most
+//      kSelTarget are (or exactly k_eff); the top-k lies among the keys >= G.
+//   2. Candidates = keys >= G.  If they overflow the LDS buffer (many ties,
+//      crowded winners), the exact k_eff-th key among them replaces G.
+//   3. The candidates are ranked exactly (rank = number of larger
 //      candidates).  Workgroup b ranks the candidates whose row hashes to
 //      slice b and writes sel_idx[rank] / sel_score[rank] for ranks < k_eff.
 //      With attention, the slices are the kAttnGroups row groups and four
@@ -37,30 +30,27 @@ namespace csa {
 
 constexpr int kSelThreads = kAttnThreads;  // 512
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelKPT = 8;                            // heads per thread in registers
-constexpr int kSelRegHeads = kSelThreads * kSelKPT;  // 4096
-constexpr int kSelBins = 2 * kSelThreads;             // histogram bins per pass
+constexpr int kSelKPT = 8;                            // keys per thread in registers
+constexpr int kSelRegKeys = kSelThreads * kSelKPT;   // 4096
 constexpr int kSelCap = 4096;                         // candidates held in LDS
 constexpr int kSelTarget = 1024;                      // candidates at which G is good enough
-constexpr int kSelMaxFull = kSelTarget / kMinTileHeads;  // full tiles listed (each holds >= hd heads >= G)
 
 struct SelSessionArgs {
-  const float *scores;
+  const float *scores;  // csa_topk: the given scores (sel_score returns their values)
   int32_t *sel_idx;
   float *sel_score;
   const uint8_t *kv_rows;
   int64_t n_rows;
-  int hd;
 };
 
 struct SelArgs {
   SelSessionArgs s[CSA_MAX_SESSIONS];
-  const uint64_t *heads;
+  const uint64_t *items;  // [session][items_stride]
+  const uint32_t *count;  // [session]
   const uint4 *attn_q;
   float *attn_part;
   float *attn_ml;
-  int64_t heads_stride;
-  int tile_rows;
+  int64_t items_stride;
   int k;
   int n_heads;
   float softmax_scale;
@@ -77,17 +67,13 @@ struct SelShared {
   union {
     struct {
       uint64_t cand[kSelCap + 4 * 64];  // + over-read slack of the rank scan
-      uint32_t hist[kSelBins];
+      BoundShared<kSelWaves> bs;
       uint16_t mine[kSelCap];
     } s;
     AttnStage st;  // used after the ranks are written
   } u;
-  uint64_t red_lo[kSelWaves], red_hi[kSelWaves];
-  uint32_t red_n[kSelWaves];
-  uint32_t full_list[kSelMaxFull];
   int32_t loc_rank[CSA_TOPK + 16], loc_row[CSA_TOPK], ordered[CSA_TOPK];
-  uint32_t ccnt, nfull, nmine, nloc;
-  uint32_t bin, ca, cb;
+  uint32_t ccnt, nmine, nloc;
 };
 // The early stage's rows are copied in while the group list (mine) is
 // still read; its logit tiles are written only after that, and may overlap it.
@@ -95,98 +81,12 @@ static_assert(kEarlyStageOff + offsetof(AttnStage, lgp) <= offsetof(SelShared, u
               "the early stage's rows end before the group list");
 static_assert(kEarlyStageOff + sizeof(AttnStage) <= sizeof(SelShared::u), "the early stage fits the union");
 
-// Lower bound G on the need-th largest of the keys that `visit` enumerates
-// (every thread visits its share, calling f(key) for each nonzero key): at
-// least need keys are >= G, and at most max(target, need) are, unless the
-// finest bin already holds more.  Returns 1 (every key) when there are at
-// most need keys.  All threads call it.
-template <class Visit>
-__device__ __forceinline__ uint64_t sel_bound(Visit visit, uint32_t need, uint32_t target, SelShared &sh) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  auto umin = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
-  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
-  auto uadd = [](uint32_t a, uint32_t b) { return a + b; };
-  // range of the score parts (key >> 32), and the count
-  uint32_t mn = ~0u, mx = 0;
-  uint32_t cnt = 0;
-  visit([&](uint64_t x) __attribute__((always_inline)) {
-    const uint32_t o = (uint32_t)(x >> 32);
-    mn = o < mn ? o : mn;
-    mx = o > mx ? o : mx;
-    ++cnt;
-  });
-  mn = wave_reduce_u32(mn, ~0u, umin);
-  mx = wave_reduce_u32(mx, 0u, umax);
-  cnt = wave_reduce_u32(cnt, 0u, uadd);
-  if (lane == 0) { sh.red_lo[wave] = mn; sh.red_hi[wave] = mx; sh.red_n[wave] = cnt; }
-  // the first pass's histogram is cleared under the same barrier (visit
-  // reads nothing of it); red_n is next written after the pass's atomics
-  // and their barrier, which every thread reaches only after reading it here
-  for (int i = tid; i < kSelBins; i += kSelThreads) sh.u.s.hist[i] = 0;
-  __syncthreads();
-  uint32_t omin = ~0u, omax = 0;
-  uint32_t total = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    omin = (uint32_t)sh.red_lo[w] < omin ? (uint32_t)sh.red_lo[w] : omin;
-    omax = (uint32_t)sh.red_hi[w] > omax ? (uint32_t)sh.red_hi[w] : omax;
-    total += sh.red_n[w];
-  }
-  uint64_t lo = (uint64_t)omin << 32, hi = ((uint64_t)omax << 32) | 0xFFFFFFFFull;
-  if (total <= need) return 1ull;
-  // (even with few keys, G = the smallest would make every tile "full")
-  uint32_t above = 0;  // keys above the current range [lo, hi]
-  for (bool first = true;; first = false) {
-    const uint64_t span = hi - lo;
-    const int hb = span ? 63 - __clzll((long long)span) : 0;
-    const int shift = hb > 9 ? hb - 9 : 0;  // span >> shift < kSelBins (1024)
-    if (!first) {
-      for (int i = tid; i < kSelBins; i += kSelThreads) sh.u.s.hist[i] = 0;
-      __syncthreads();
-    }
-    visit([&](uint64_t x) __attribute__((always_inline)) {
-      if (x >= lo && x <= hi) atomicAdd(&sh.u.s.hist[(uint32_t)((x - lo) >> shift)], 1u);
-    });
-    __syncthreads();
-    const uint32_t need_here = need - above;
-    // thread t owns the upper bin kSelBins-1-2t and the lower bin
-    // kSelBins-2-2t, so "bins above" is a prefix over threads
-    const uint32_t bu = kSelBins - 1 - 2 * tid;
-    const uint32_t h1 = sh.u.s.hist[bu], h0 = sh.u.s.hist[bu - 1];
-    const uint32_t s = h0 + h1;
-    const uint32_t incl = wave_scan_u32(s, 0u, uadd);
-    if (lane == 63) sh.red_n[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += sh.red_n[w];
-    const uint32_t X = incl - s + before;  // keys in bins above bu
-    if (X < need_here && need_here <= X + h1) {
-      sh.bin = bu; sh.ca = X; sh.cb = h1;
-    } else if (X + h1 < need_here && need_here <= X + s) {
-      sh.bin = bu - 1; sh.ca = X + h1; sh.cb = h0;
-    }
-    __syncthreads();
-    const uint32_t b = sh.bin, ca = sh.ca, cb = sh.cb;
-    const uint64_t gb = lo + ((uint64_t)b << shift);
-    // (uniform; after the return nothing writes bin, ca, cb or the
-    // histogram before another barrier)
-    if (above + ca + cb <= target || shift == 0) return gb;
-    __syncthreads();  // every thread has read bin, ca, cb
-    above += ca;
-    const uint64_t top = gb + ((1ull << shift) - 1);
-    lo = gb;
-    hi = top < hi ? top : hi;
-  }
-}
-
 // Row of a key -> workgroup of the session that ranks it.
 __device__ __forceinline__ uint32_t row_slice(uint32_t row, int slices) {
   return (uint32_t)(((uint64_t)(row * 0x9E3779B1u) * (uint32_t)slices) >> 32);
 }
 
-// REG: every session's heads fit in registers (at most kSelRegHeads), chosen
-// on the host for the whole launch; otherwise they are re-read per pass.
-template <bool ATTN, bool REG>
+template <bool ATTN>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   const int sess = blockIdx.y;
   // fields used inside lambdas are copied first: a lambda taking the address
@@ -228,156 +128,61 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
     return;
   }
 
-  const int T = a.tile_rows;
-  const int hd = a.s[sess].hd;
-  const int lT = __builtin_ctz((unsigned)T), lhd = __builtin_ctz((unsigned)hd);  // both powers of two
-  const int64_t nt = (n + T - 1) >> lT;
-  const int64_t nh = nt * hd;
-  const uint64_t *heads = a.heads + (size_t)sess * a.heads_stride;
-  constexpr bool reg = REG;
-  if (tid == 0) { sh.ccnt = 0; sh.nfull = 0; sh.nmine = 0; sh.nloc = 0; }
+  const uint64_t *items = a.items + (size_t)sess * a.items_stride;
+  const int64_t ni = (int64_t)a.count[sess];
+  const bool reg = ni <= kSelRegKeys;  // uniform
+  if (tid == 0) { sh.ccnt = 0; sh.nmine = 0; sh.nloc = 0; }
 
-  // heads in registers: slot j of thread tid is head tid + 1024 j
+  // keys in registers: slot j of thread tid is item tid + 512 j
   uint64_t h[kSelKPT];
-  if constexpr (reg) {
+  if (reg) {
 #pragma unroll
     for (int j = 0; j < kSelKPT; ++j) {
       const int64_t i = tid + (int64_t)kSelThreads * j;
-      const uint64_t y = heads[i < nh ? i : nh - 1];  // clamped: no branch around the load
-      h[j] = i < nh ? y : 0ull;
+      const uint64_t y = items[i < ni ? i : (ni > 0 ? ni - 1 : 0)];  // clamped: no branch around the load
+      h[j] = i < ni ? y : 0ull;
     }
   }
-  // every head slot of this thread, in control flow uniform over the wave:
-  // f(ok, x), ok = "x is a head"
-  auto scan_heads = [&](auto f) __attribute__((always_inline)) {
-    if constexpr (reg) {
-#pragma unroll
-      for (int j = 0; j < kSelKPT; ++j) f(h[j] != 0, h[j]);
-    } else {
-      for (int64_t i0 = 0; i0 < nh; i0 += (int64_t)kSelThreads * 8) {
-        uint64_t y[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int64_t i = i0 + tid + (int64_t)kSelThreads * u;
-          const uint64_t z = heads[i < nh ? i : nh - 1];
-          y[u] = i < nh ? z : 0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) f(y[u] != 0, y[u]);
-      }
-    }
-  };
-  auto visit_heads = [&](auto f) __attribute__((always_inline)) {
-    scan_heads([&](bool ok, uint64_t x) __attribute__((always_inline)) {
-      if (ok) f(x);
-    });
-  };
-
-  // 1. the bound G
-  const uint64_t G = sel_bound(visit_heads, (uint32_t)kTopK, (uint32_t)kSelTarget, sh);
-
-  // 2. full tiles (hd-th head >= G) and the candidates
-  auto tile_is_full = [&](int64_t t) __attribute__((always_inline)) {
-    const uint64_t last = heads[t * hd + hd - 1];
-    return last != 0 && last >= G;
-  };
-  // REG: a tile's hd heads sit in hd consecutive lanes of one slot (hd
-  // divides 64), so the lane of its last head decides "full" for all of
-  // them with one ballot, and lists the tile
-  bool fullbit[kSelKPT];
-  if constexpr (reg) {
-    bool lists[kSelKPT];
-    uint64_t lm[kSelKPT];
-    uint32_t tot = 0;
-#pragma unroll
-    for (int j = 0; j < kSelKPT; ++j) {
-      const int i = tid + kSelThreads * j;  // < kSelRegHeads
-      lists[j] = i < nh && (i & (hd - 1)) == hd - 1 && h[j] != 0 && h[j] >= G;
-      lm[j] = __ballot(lists[j]);
-      fullbit[j] = ((lm[j] >> (lane | (hd - 1))) & 1ull) != 0;
-      tot += (uint32_t)__popcll(lm[j]);
-    }
-    if (tot != 0) {  // one LDS atomic per wave
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&sh.nfull, tot);
-      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
-#pragma unroll
-      for (int j = 0; j < kSelKPT; ++j) {
-        const uint32_t p = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(lm[j] >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)lm[j], 0u));
-        if (lists[j] && p < kSelMaxFull) sh.full_list[p] = (uint32_t)((tid + kSelThreads * j) >> lhd);
-        base += (uint32_t)__popcll(lm[j]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kSelKPT; ++j) fullbit[j] = false;
-    for (int64_t t = tid; t < nt; t += kSelThreads)
-      if (tile_is_full(t)) {
-        const uint32_t p = atomicAdd(&sh.nfull, 1u);
-        if (p < kSelMaxFull) sh.full_list[p] = (uint32_t)t;
-      }
-  }
-
-  // candidates >= lb, in batches of 8 slots per thread: fb(ok[8], x[8]) in
-  // control flow uniform over the wave.  Heads of tiles that are not full:
-  auto scan_head_cand = [&](uint64_t lb, auto fb) __attribute__((always_inline)) {
-    if constexpr (reg) {
-#pragma unroll
-      for (int j0 = 0; j0 < kSelKPT; j0 += 8) {
-        bool ok[8];
-        uint64_t x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          x[u] = h[j0 + u];
-          ok[u] = x[u] != 0 && x[u] >= lb && !fullbit[j0 + u];
-        }
-        fb(ok, x);
-      }
-    } else {
-      for (int64_t i0 = 0; i0 < nh; i0 += (int64_t)kSelThreads * 8) {
-        bool ok[8];
-        uint64_t x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int64_t i = i0 + tid + (int64_t)kSelThreads * u;
-          const uint64_t z = heads[i < nh ? i : nh - 1];
-          x[u] = i < nh ? z : 0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          // the tile of a head: keys carry the row, tiles are T rows
-          const int64_t t = x[u] != 0 ? (int64_t)(key_row(x[u]) >> lT) : 0;
-          ok[u] = x[u] != 0 && x[u] >= lb && !tile_is_full(t);
-        }
-        fb(ok, x);
-      }
-    }
-  };
-  // ... and every key of the full tiles (sh.full_list[0..nfull) complete)
-  auto scan_full_rows = [&](int nfull, uint64_t lb, auto fb) __attribute__((always_inline)) {
-    const int nfr = nfull << lT;  // at most kSelMaxFull * 4096
-    for (int i0 = 0; i0 < nfr; i0 += kSelThreads * 8) {
-      float v[8];
-      int64_t row[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + tid + kSelThreads * u;
-        row[u] = i < nfr ? ((int64_t)sh.full_list[i >> lT] << lT) + (i & (T - 1)) : n;
-        v[u] = scores[row[u] < n ? row[u] : n - 1];
-      }
+  // the candidates >= lb, in batches of 8 slots per thread: fb(ok[8], x[8])
+  // in control flow uniform over the wave
+  auto scan = [&](uint64_t lb, auto fb) __attribute__((always_inline)) {
+    if (reg) {
       bool ok[8];
       uint64_t x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        x[u] = ((uint64_t)score_ord(v[u]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row[u]);
-        ok[u] = row[u] < n && x[u] >= lb;
+        x[u] = h[u];
+        ok[u] = x[u] != 0 && x[u] >= lb;
       }
       fb(ok, x);
+    } else {
+      for (int64_t i0 = 0; i0 < ni; i0 += (int64_t)kSelThreads * 8) {
+        bool ok[8];
+        uint64_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i = i0 + tid + (int64_t)kSelThreads * u;
+          const uint64_t z = items[i < ni ? i : ni - 1];
+          x[u] = i < ni ? z : 0ull;
+          ok[u] = x[u] != 0 && x[u] >= lb;
+        }
+        fb(ok, x);
+      }
     }
   };
-  // one LDS atomic per wave and batch: the wave's selected slots take
-  // consecutive positions
+  auto visit_all = [&](auto f) __attribute__((always_inline)) {
+    scan(1ull, [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ok[u]) f(x[u]);
+    });
+  };
+
+  // 1. the bound G
+  const uint64_t G = block_bound<kSelWaves>(visit_all, (uint32_t)k_eff, (uint32_t)kSelTarget, sh.u.s.bs);
+
+  // 2. candidates: one LDS atomic per wave and batch, the wave's selected
+  // slots taking consecutive positions
   auto append = [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
     uint64_t m[8];
     uint32_t tot = 0;
@@ -398,35 +203,27 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       base += (uint32_t)__popcll(m[u]);
     }
   };
-  scan_head_cand(G, append);
-  __syncthreads();  // full tiles listed, head candidates appended
-  const int nfull = (int)(sh.nfull < kSelMaxFull ? sh.nfull : kSelMaxFull);
-  if (nfull > 0) {  // uniform
-    scan_full_rows(nfull, G, append);
-    __syncthreads();
-  }
+  scan(G, append);
+  __syncthreads();
   int C = (int)sh.ccnt;
   if (C > kSelCap) {
-    // 3. too many candidates: the exact k_eff-th key among them
+    // too many candidates: the exact k_eff-th key among them
     auto visit_cand = [&](auto f) __attribute__((always_inline)) {
-      auto each = [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
+      scan(G, [&](const bool (&ok)[8], const uint64_t (&x)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
           if (ok[u]) f(x[u]);
-      };
-      scan_head_cand(G, each);
-      scan_full_rows(nfull, G, each);
+      });
     };
-    const uint64_t thr = sel_bound(visit_cand, (uint32_t)k_eff, (uint32_t)k_eff, sh);
+    const uint64_t thr = block_bound<kSelWaves>(visit_cand, (uint32_t)k_eff, (uint32_t)k_eff, sh.u.s.bs);
     if (tid == 0) sh.ccnt = 0;
     __syncthreads();
-    scan_head_cand(thr, append);
-    scan_full_rows(nfull, thr, append);
+    scan(thr, append);
     __syncthreads();
     C = (int)sh.ccnt;
   }
 
-  // 4. rank this workgroup's candidates
+  // 3. rank this workgroup's candidates
   for (int i0 = 0; i0 < C; i0 += kSelThreads) {
     const int i = i0 + tid;
     if (i < C && row_slice(key_row(sh.u.s.cand[i]), nslice) == myslice) sh.u.s.mine[atomicAdd(&sh.nmine, 1u)] = (uint16_t)i;
@@ -526,7 +323,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   if constexpr (!ATTN) return;
   if (warm == 0x5A5A5A5Au && a.k < 0) sel_idx[0] = 0;  // never true (k >= 1): keeps the warming loads
 
-  // 5. attention over this workgroup's selected rows, in rank order
+  // 4. attention over this workgroup's selected rows, in rank order
   __syncthreads();
   const int nl = (int)sh.nloc;
   attn_order(sh.loc_rank, sh.loc_row, nl, sh.ordered);
@@ -539,28 +336,22 @@ hipError_t launch_select(const SelectJob &job, hipStream_t st) {
   SelArgs a;
   for (int i = 0; i < job.n_sessions; ++i)
     a.s[i] = SelSessionArgs{job.scores[i], job.sel_idx[i], job.sel_score[i],
-                            job.attn_part ? job.kv_rows[i] : nullptr, job.n_rows[i], job.hd[i]};
-  a.heads = job.heads;
+                            job.attn_part ? job.kv_rows[i] : nullptr, job.n_rows[i]};
+  a.items = job.items;
+  a.count = job.count;
+  a.items_stride = job.items_stride;
   a.attn_q = job.attn_q;
   a.attn_part = job.attn_part;
   a.attn_ml = job.attn_ml;
-  a.heads_stride = job.heads_stride;
-  a.tile_rows = job.tile_rows;
   a.k = job.k;
   a.n_heads = job.n_heads;
   a.softmax_scale = job.softmax_scale;
   a.array_scores = job.array_scores ? 1 : 0;
   const dim3 grid((unsigned)job.slices, (unsigned)job.n_sessions);
-  bool reg = true;
-  for (int i = 0; i < job.n_sessions; ++i)
-    reg = reg && ((job.n_rows[i] + job.tile_rows - 1) / job.tile_rows) * job.hd[i] <= kSelRegHeads;
-  if (job.attn_part) {
-    if (reg) select_kernel<true, true><<<grid, kSelThreads, 0, st>>>(a);
-    else select_kernel<true, false><<<grid, kSelThreads, 0, st>>>(a);
-  } else {
-    if (reg) select_kernel<false, true><<<grid, kSelThreads, 0, st>>>(a);
-    else select_kernel<false, false><<<grid, kSelThreads, 0, st>>>(a);
-  }
+  if (job.attn_part)
+    select_kernel<true><<<grid, kSelThreads, 0, st>>>(a);
+  else
+    select_kernel<false><<<grid, kSelThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,339 @@
+// csa_refine.hip -- exact scores of the rows that can still reach the top-k
+// (DS4X page, "CSA score/top-512 fusion": the fused selection keeps the same
+// float score order and lower-index tie break as a separate exact top-k).
+//
+// The score the selection orders by is the lightning-indexer score
+//     S_j = fl32( sum_h w_h * max(0, sum_i q_hi * k_ji) ),
+// evaluated in fp64 with i ascending inside each head and h ascending
+// outside (each product q_hi * k_ji of an fp32 query value and a decoded
+// fp32 row value is exact in fp64, so fma(q, k, d) = d + q * k; w_h *
+// max(0, d_h) is rounded, then added), rounded once to fp32, -0 stored as
+// +0.  Every row this kernel scores gets exactly that value.
+//
+// Inputs: per tile of the score kernel its hd heads (keys by upper bound
+// u_j, with lower-bound keys (l_j, row j)), rank-major (the best head of
+// every tile, then the second, ...), and its "next" key (the largest key of
+// its other rows).  Every workgroup of a session derives the same
+//   G = a lower bound on the k_eff-th largest lower-bound key over the first
+//       kRefBoundHeads heads (block_bound): at least k_eff rows have an exact
+//       key >= G, so the k_eff-th largest exact key is >= G (the best heads
+//       of all tiles hold nearly all of the top-k, so G stays close to it);
+//   full tiles = tiles whose next key is >= G: one of their other rows may
+//       reach the top-k, so every row of such a tile is scored;
+//   candidates = heads with key >= G outside full tiles.
+// A row outside both sets has an exact key at or below its upper-bound key,
+// which is below G, so it is not in the top-k.
+// Items (per session): the head slots (nh of them, in the heads' rank-major
+// order: a candidate's exact key, 0 = "no key" otherwise), followed by the
+// rows of the full tiles in tile order.  The selection kernel takes the top-k of the
+// items' keys.  Wave w of the launch's nw waves (per session) takes items w,
+// w + nw, ..., so the candidates spread over the whole chip.
+// Other modes: given scores (csa_topk: the key of the given score) and every
+// row (csa_score: the exact score of each row, written as fp32).
+// In the decode step the workgroups also split the attention query (its
+// three bf16 terms in the matrix-core operand order of csa_attn.hpp), a
+// share each, for the selection kernel that follows.
+#include "csa_attn.hpp"
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+#include "csa_select.hpp"
+
+namespace csa {
+
+constexpr int kRefThreads = 512;
+constexpr int kRefWaves = kRefThreads / 64;
+constexpr int kRefKPT = 2;                             // bound heads per thread in registers
+constexpr int kRefBoundHeads = kRefThreads * kRefKPT;  // 1024: the heads G is taken over
+constexpr int kQStride = 132;  // floats per query head in LDS: rows 528 B apart spread the lanes over banks
+constexpr int kRefMaxFull = 4096;  // full tiles listed per session (beyond: every row is an item)
+
+struct RefineSession {
+  const uint8_t *idx_rows;
+  const float *q, *w;  // indexer query [H][128] and head weights
+  float *scores;       // csa_topk: the given scores (read); csa_score: the output
+  const float *q_attn;  // decode step: the attention query [n_attn_heads][512]
+  int64_t n_rows;
+  int hd;
+};
+
+struct RefineArgs {
+  RefineSession s[CSA_MAX_SESSIONS];
+  const uint64_t *hkey;  // [session][heads_stride]: rank-major head keys (upper bounds)
+  const uint64_t *hlow;  // [session][heads_stride]: their lower-bound keys
+  const uint64_t *hnext;  // [session][tiles_stride]
+  uint64_t *items;       // [session][items_stride]
+  uint32_t *count;       // [session]: number of items
+  uint4 *attn_q;         // decode step: the attention query split [session][kAttnQVecs], or null
+  int64_t heads_stride, tiles_stride, items_stride;
+  int tile_rows;
+  int n_idx_heads, n_attn_heads;
+  int k;
+  int mode;  // RefineJob::Mode
+};
+static_assert(sizeof(RefineArgs) <= 4096, "kernel argument block");
+
+struct RefineShared {
+  float q[CSA_MAX_HEADS][kQStride];  // the fp32 indexer query
+  float w[CSA_MAX_HEADS];
+  double kv[kRefWaves][128];   // per wave: the decoded row being scored
+  double pv[kRefWaves][64];    // per wave: w_h * max(0, d_h) by head
+  BoundShared<kRefWaves> bs;
+  uint32_t full_tile[kRefMaxFull];
+  uint32_t wcnt[kRefWaves];
+  uint32_t nfull;
+  int all_rows;  // more full tiles than listed: every row is an item
+};
+
+// Wave-level ordering of LDS traffic between lanes (LDS accesses of one wave
+// complete in issue order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Lane l's bytes of a row: code byte l (values 2l, 2l + 1) and the scale byte
+// of its block.
+struct RowBytes {
+  uint32_t code, scale;
+};
+__device__ __forceinline__ RowBytes load_row_bytes(const uint8_t *__restrict__ idx_rows, int64_t row) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t *r = idx_rows + (size_t)row * kIdxRowBytes;
+  return RowBytes{r[lane], r[64 + (lane >> 4)]};
+}
+
+// The exact score S of a row (see the file comment) from its bytes, computed
+// by one wave: lane l decodes row values 2l and 2l + 1 exactly as fp32 (an
+// E2M1 value times 2^(e-127): exact, or +-inf on overflow, NaN for a 0xFF
+// scale), lane h < n_heads forms d_h in fp64 over i ascending, and lane 0
+// adds the heads' terms in order.  Returns S in every lane.
+__device__ __forceinline__ float exact_score(const RowBytes &rb, int n_heads, RefineShared &sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float sc = ue8m0_scale(rb.scale);
+  const float k0 = e2m1_value(rb.code & 15u) * sc, k1 = e2m1_value(rb.code >> 4) * sc;
+  sh.kv[wave][2 * lane] = (double)k0;
+  sh.kv[wave][2 * lane + 1] = (double)k1;
+  wave_lds_sync();
+  const int h = lane < n_heads ? lane : 0;
+  const float *qh = &sh.q[h][0];
+  double d = 0.0;
+#pragma unroll 4
+  for (int i = 0; i < 128; i += 4) {
+    const float4 q4 = *reinterpret_cast<const float4 *>(qh + i);
+    const double2 ka = *reinterpret_cast<const double2 *>(&sh.kv[wave][i]);
+    const double2 kb = *reinterpret_cast<const double2 *>(&sh.kv[wave][i + 2]);
+    d = __builtin_fma((double)q4.x, ka.x, d);
+    d = __builtin_fma((double)q4.y, ka.y, d);
+    d = __builtin_fma((double)q4.z, kb.x, d);
+    d = __builtin_fma((double)q4.w, kb.y, d);
+  }
+  const double relu = d > 0.0 ? d : 0.0;
+  sh.pv[wave][lane] = (double)sh.w[h] * relu;
+  wave_lds_sync();
+  double s = 0.0;
+  if (lane == 0) {
+    for (int hh = 0; hh < n_heads; hh += 2) {
+      const double2 p2 = *reinterpret_cast<const double2 *>(&sh.pv[wave][hh]);
+      s = s + p2.x;
+      if (hh + 1 < n_heads) s = s + p2.y;
+    }
+  }
+  float f = (float)s;
+  f = f == 0.0f ? 0.0f : f;
+  wave_lds_sync();  // kv and pv are reused by the wave's next row
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f)));
+}
+
+// Head items prefetched per wave (keys, then the rows' bytes) at the start,
+// so that their loads overlap the bound's computation.
+constexpr int kRefPrefetch = 2;
+
+__global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a) {
+  const int sess = blockIdx.y;
+  const RefineSession &S = a.s[sess];
+  const int64_t n = S.n_rows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int H = a.n_idx_heads;
+  const bool exact = a.mode != RefineJob::kArray;
+  __shared__ RefineShared sh;
+  const uint32_t nw = gridDim.x * kRefWaves;               // waves per session
+  const uint32_t gw = blockIdx.x * kRefWaves + (uint32_t)wave;  // this wave
+
+  if (exact) {  // the query and weights into LDS (padded rows): all loads in flight together
+    constexpr int kQPer = CSA_MAX_HEADS * 32 / kRefThreads;  // float4 per thread
+    float4 qv[kQPer];
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int t = tid + kRefThreads * u, h = t >> 5, c = t & 31;
+      qv[u] = h < H ? reinterpret_cast<const float4 *>(S.q + (size_t)h * 128)[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const float wv = tid < H ? S.w[tid] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int t = tid + kRefThreads * u;
+      *reinterpret_cast<float4 *>(&sh.q[t >> 5][4 * (t & 31)]) = qv[u];
+    }
+    if (tid < CSA_MAX_HEADS) sh.w[tid] = wv;
+  }
+  if (a.mode == RefineJob::kAll) {  // every row: its exact score
+    __syncthreads();
+    for (int64_t row = gw; row < n; row += nw) {
+      const float f = exact_score(load_row_bytes(S.idx_rows, row), H, sh);
+      if (lane == 0) S.scores[row] = f;
+    }
+    return;
+  }
+
+  const int T = a.tile_rows, hd = S.hd;
+  const int k_eff = (int)(n < a.k ? n : a.k);
+  const int64_t nt = (n + T - 1) / T;
+  const int64_t nh = nt * hd;
+  const uint64_t *hkey = a.hkey + (size_t)sess * a.heads_stride;
+  const uint64_t *hlow = a.hlow + (size_t)sess * a.heads_stride;
+  const uint64_t *hnext = a.hnext + (size_t)sess * a.tiles_stride;
+  uint64_t *items = a.items + (size_t)sess * a.items_stride;
+  if (k_eff == 0) {
+    if (blockIdx.x == 0 && tid == 0) a.count[sess] = 0;
+    return;
+  }
+  if (tid == 0) { sh.nfull = 0; sh.all_rows = 0; }
+
+  // this wave's first head items: their keys and (decode step) their rows'
+  // bytes, loaded now whether or not they turn out to be candidates
+  uint64_t px[kRefPrefetch];
+  RowBytes pb[kRefPrefetch] = {};
+#pragma unroll
+  for (int u = 0; u < kRefPrefetch; ++u) {
+    const int64_t i = gw + (int64_t)nw * u;
+    const uint64_t x = hkey[i < nh ? i : nh - 1];
+    px[u] = i < nh ? x : 0ull;
+  }
+  if (exact) {
+#pragma unroll
+    for (int u = 0; u < kRefPrefetch; ++u) pb[u] = load_row_bytes(S.idx_rows, px[u] != 0 ? key_row(px[u]) : 0);
+  }
+
+  // 1. G over the lower-bound keys of the first heads (a prefix of the
+  // rank-major order: every tile's best heads), two per thread
+  const int64_t nb = nh < kRefBoundHeads ? nh : kRefBoundHeads;
+  uint64_t lk[kRefKPT];
+#pragma unroll
+  for (int j = 0; j < kRefKPT; ++j) {
+    const int64_t i = tid + (int64_t)kRefThreads * j;
+    const uint64_t x = hlow[i < nb ? i : nb - 1];
+    lk[j] = i < nb ? x : 0ull;
+  }
+  auto visit_low = [&](auto f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kRefKPT; ++j)
+      if (lk[j] != 0) f(lk[j]);
+  };
+  const uint64_t G = block_bound<kRefWaves>(visit_low, (uint32_t)k_eff, (uint32_t)k_eff + 32u, sh.bs);
+
+  // 2. full tiles (next key >= G) in tile order: one pass of 512 tiles at a
+  // time, each wave's tiles placed after the earlier waves'
+  for (int64_t t0 = 0; t0 < nt; t0 += kRefThreads) {
+    const int64_t t = t0 + tid;
+    const uint64_t nx = t < nt ? hnext[t] : 0ull;
+    const bool full = nx != 0 && nx >= G;
+    const uint64_t m = __ballot(full);
+    if (lane == 0) sh.wcnt[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t before = sh.nfull, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kRefWaves; ++w) {
+      before += w < wave ? sh.wcnt[w] : 0u;
+      tot += sh.wcnt[w];
+    }
+    const uint32_t pos = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (full && pos < kRefMaxFull) sh.full_tile[pos] = (uint32_t)t;
+    __syncthreads();
+    if (tid == 0) sh.nfull += tot;
+    __syncthreads();
+  }
+  const uint32_t nfull_all = sh.nfull;
+  const bool all_rows = nfull_all > kRefMaxFull;  // uniform: then every row is an item
+  const int nfull = (int)(all_rows ? 0 : nfull_all);
+  // rows of the full tiles (the last tile of the session may be partial and,
+  // listed in tile order, is then the last one)
+  int64_t full_rows = 0;
+  if (nfull > 0) {
+    const int64_t tl = sh.full_tile[nfull - 1];
+    full_rows = (int64_t)(nfull - 1) * T + ((tl + 1) * T <= n ? T : n - tl * T);
+  }
+  const int64_t head_items = all_rows ? 0 : nh;
+  const int64_t n_items = all_rows ? n : head_items + full_rows;
+  if (blockIdx.x == 0 && tid == 0) a.count[sess] = (uint32_t)n_items;
+  if (a.attn_q) {  // this workgroup's share of the attention query split
+    const int per = (kAttnQTasks + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int t1 = ((int)blockIdx.x + 1) * per < kAttnQTasks ? ((int)blockIdx.x + 1) * per : kAttnQTasks;
+    for (int t = (int)blockIdx.x * per + tid; t < t1; t += kRefThreads)
+      attn_q_split_task(S.q_attn, a.n_attn_heads, a.attn_q + (size_t)sess * kAttnQVecs, t);
+  }
+  auto is_full = [&](int64_t t) __attribute__((always_inline)) {  // binary search of the sorted list
+    int lo = 0, hi = nfull;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)sh.full_tile[mid] < t) lo = mid + 1; else hi = mid;
+    }
+    return lo < nfull && (int64_t)sh.full_tile[lo] == t;
+  };
+
+  // 3. this wave's items (uniform over the wave): item i, with its head key
+  // and row bytes prefetched or not
+  auto item = [&](int64_t i, bool pre, uint64_t xp, const RowBytes &bp) __attribute__((always_inline)) {
+    int64_t row = -1;
+    bool have = false;  // the row's bytes are the prefetched ones
+    if (all_rows) {
+      row = i;
+    } else if (i < head_items) {
+      const uint64_t x = pre ? xp : hkey[i];  // rank i / nt of tile i % nt
+      if (x != 0 && x >= G && !is_full(i % nt)) row = key_row(x);
+      have = pre;
+    } else {
+      const int64_t r = i - head_items;
+      row = (int64_t)sh.full_tile[r / T] * T + r % T;
+    }
+    uint64_t key = 0;
+    if (row >= 0) {
+      const float f = exact ? exact_score(have ? bp : load_row_bytes(S.idx_rows, row), H, sh) : S.scores[row];
+      key = make_key(f, (uint32_t)row);
+    }
+    if (lane == 0) items[i] = key;
+  };
+#pragma unroll
+  for (int u = 0; u < kRefPrefetch; ++u) {
+    const int64_t i = gw + (int64_t)nw * u;
+    if (i < n_items) item(i, true, px[u], pb[u]);
+  }
+  for (int64_t i = gw + (int64_t)nw * kRefPrefetch; i < n_items; i += nw) item(i, false, 0ull, pb[0]);
+}
+
+hipError_t launch_refine(const RefineJob &job, hipStream_t st) {
+  RefineArgs a;
+  int64_t max_rows = 0;
+  for (int i = 0; i < job.n_sessions; ++i) {
+    a.s[i] = RefineSession{job.idx_rows[i], job.q[i], job.w[i], job.scores[i], job.q_attn[i], job.n_rows[i], job.hd[i]};
+    max_rows = job.n_rows[i] > max_rows ? job.n_rows[i] : max_rows;
+  }
+  a.hkey = job.hkey;
+  a.hlow = job.hlow;
+  a.hnext = job.hnext;
+  a.items = job.items;
+  a.count = job.count;
+  a.attn_q = job.attn_q;
+  a.n_attn_heads = job.n_attn_heads;
+  a.heads_stride = job.heads_stride;
+  a.tiles_stride = job.tiles_stride;
+  a.items_stride = job.items_stride;
+  a.tile_rows = job.tile_rows;
+  a.n_idx_heads = job.n_idx_heads;
+  a.k = job.k;
+  a.mode = (int)job.mode;
+  if (max_rows == 0 && job.mode == RefineJob::kAll) return hipSuccess;
+  refine_kernel<<<dim3((unsigned)job.blocks, (unsigned)job.n_sessions), kRefThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,6 +1,4 @@
-// csa_score.hpp -- the indexer score on gfx950 matrix cores, the single
-// definition shared by every kernel that scores rows (so unfused and fused
-// paths produce bit-identical scores).
+// csa_score.hpp -- the indexer score filter on gfx950 matrix cores.
 //
 // Score (lightning-indexer form adopted for the library; the DS4X page
 // describes the batch-one scorer only as a block-scaled MXFP4 matrix product
@@ -12,10 +10,13 @@
 // four UE8M0 bytes are the B block scales (one per 32 values, exactly the
 // row's block structure).  The fp32 query cannot be an MX operand, so it is
 // split into kTerms fp6 (E2M3) terms with their own E8M0 block scales,
-//     q = sum_t qt + r,   |r| <= 2^-19.9 * blockmax|q| per element,
+//     q = sum_t qt + r,   |r| <= max(2^-11.9 blockmax|q|, 2^-130) per element,
 // and the dot product is the fp32 accumulation of the kTerms exact-product
-// MFMAs.  Every product is exact; accumulation is fp32 inside the matrix
-// core.  Each lane splits its own fragment in registers (split_qfrag).
+// MFMAs.  This is a filter: the split also returns, per (head, block)
+// fragment, the L1 norms of the residual r and of the terms, from which the
+// tile kernel bounds each row's distance to the exact score rigorously; the
+// rows the bound cannot place are rescored exactly (csa_refine.hip).  Each
+// lane splits its own fragment in registers (split_qfrag).
 //
 // Lane layout of the 16x16x128 instruction (verified on MI355X): lane l holds
 // A row l%16 and B column l%16, for K elements [32*(l/16), 32*(l/16)+32),
@@ -35,7 +36,7 @@ namespace csa {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kTerms = 5;        // fp6 terms of the query split
+constexpr int kTerms = 3;        // fp6 terms of the query split
 constexpr int kMaxGroups = 4;    // 16-head groups (64 indexer heads)
 constexpr int kFmtFp6 = 2;       // MFMA operand format codes: E2M3
 constexpr int kFmtFp4 = 4;       // E2M1
@@ -47,6 +48,12 @@ struct QFrag {
   v8i a[G][kTerms];
   int scw[G][kScaleWords];  // byte t%4 of word t/4: E8M0 scale of term t
   float w[G][4];
+};
+
+// L1 norms of one lane's fragment after the split: rho = sum |r| (the
+// residual) and mag = sum over terms of |qt| plus rho (at least sum |q|).
+struct QFragNorms {
+  float rho, mag;
 };
 
 typedef float v16f_q __attribute__((ext_vector_type(16)));
@@ -61,8 +68,13 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 //   q_t = RNE_E2M3(r / 2^E_t) * 2^E_t,   r <- r - q_t   (exact in fp32),
 // for t < kTerms.  A term's rounding error is at most a quarter of its
 // scale (half the 0.5 spacing of E2M3's top binade), which the next term's
-// range 7.5 * 2^(E_t - 4) holds without saturating; after 5 terms
-// |r| <= 2^-2 * 2^(E_0 - 16) < 2^-19.9 * max|x|, since max|x| > 3.75 * 2^E_0.
+// range 7.5 * 2^(E_t - 4) holds without saturating, so no term saturates
+// and every subtraction is exact (both operands are multiples of the
+// finer of their spacings and the difference is below 2^(E_t - 2)); after
+// 3 terms |r| <= 2^-2 * 2^(E_0 - 8) < 2^-11.9 * max|x|, since max|x| >
+// 3.75 * 2^E_0 (below 2^-126 the scales stop at 2^-126 and |r| at 2^-130,
+// half the finest term spacing).  Returns the fragment's L1 norms (the
+// bound's inputs).
 // Heads past the query's heads carry a zero weight (load_qweights), so
 // their terms (split from a clamped head) add exact zeros to the score.
 // The conversions are gfx950's scaled fp6 instructions (round to nearest
@@ -70,7 +82,7 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 // two 16-value inputs (even, odd positions), so value i lands at bit 6i,
 // the MFMA operand order; the unpacking one returns the exact term values
 // for the residual.
-__device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float (&x)[32]) {
+__device__ __forceinline__ QFragNorms split_qfrag(QFrag<1> &q, const float (&x)[32]) {
   v16f_q re, ro;
   float amax = 0.0f;
 #pragma unroll
@@ -87,22 +99,26 @@ __device__ __forceinline__ void split_qfrag(QFrag<1> &q, const float (&x)[32]) {
   E0 = E0 < -126 ? -126 : (E0 > 127 ? 127 : E0);
 #pragma unroll
   for (int w = 0; w < kScaleWords; ++w) q.scw[0][w] = 0;
+  float mag = 0.0f;
 #pragma unroll
   for (int t = 0; t < kTerms; ++t) {
     const int E = E0 - 4 * t < -126 ? -126 : E0 - 4 * t;
     const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
     const v6u_q c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(re, ro, sc);
-    if (t + 1 < kTerms) {
-      const v32f_q d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
+    const v32f_q d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        re[i] -= d[2 * i];
-        ro[i] -= d[2 * i + 1];
-      }
+    for (int i = 0; i < 16; ++i) {
+      re[i] -= d[2 * i];
+      ro[i] -= d[2 * i + 1];
+      mag += fabsf(d[2 * i]) + fabsf(d[2 * i + 1]);
     }
     q.a[0][t] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4], (int)c[5], 0, 0};
     q.scw[0][t / 4] |= (E + 127) << (8 * (t % 4));
   }
+  float rho = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) rho += fabsf(re[i]) + fabsf(ro[i]);
+  return QFragNorms{rho, mag + rho};
 }
 
 // The weights of the heads whose results lane `lane` holds for group g:

@@ -252,4 +252,100 @@ __device__ uint64_t block_kth_largest_reg(const uint64_t (&x)[KPT], int nj, int 
   }
 }
 
+// Scratch of block_bound for a workgroup of NW waves.
+template <int NW>
+struct BoundShared {
+  static constexpr int kBins = 2 * NW * 64;  // two histogram bins per thread
+  uint32_t hist[kBins];
+  uint32_t red_lo[NW], red_hi[NW], red_n[NW];
+  uint32_t bin, ca, cb;
+};
+
+// Lower bound G on the need-th largest of the keys that `visit` enumerates
+// (every thread visits its share, calling f(key) for each nonzero key): at
+// least need keys are >= G, and at most max(target, need) are, unless the
+// finest bin already holds more.  Returns 1 (every key) when there are at
+// most need keys.  Histogram passes over the key range, 2 NW 64 bins each,
+// narrowing to the bin that holds the need-th key.  All threads call it.
+template <int NW, class Visit>
+__device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint32_t target, BoundShared<NW> &sh) {
+  constexpr int NT = NW * 64, kBins = BoundShared<NW>::kBins;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  auto umin = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  auto uadd = [](uint32_t a, uint32_t b) { return a + b; };
+  // range of the score parts (key >> 32), and the count
+  uint32_t mn = ~0u, mx = 0;
+  uint32_t cnt = 0;
+  visit([&](uint64_t x) __attribute__((always_inline)) {
+    const uint32_t o = (uint32_t)(x >> 32);
+    mn = o < mn ? o : mn;
+    mx = o > mx ? o : mx;
+    ++cnt;
+  });
+  mn = wave_reduce_u32(mn, ~0u, umin);
+  mx = wave_reduce_u32(mx, 0u, umax);
+  cnt = wave_reduce_u32(cnt, 0u, uadd);
+  if (lane == 0) { sh.red_lo[wave] = mn; sh.red_hi[wave] = mx; sh.red_n[wave] = cnt; }
+  // the first pass's histogram is cleared under the same barrier (visit
+  // reads nothing of it); red_n is next written after the pass's atomics
+  // and their barrier, which every thread reaches only after reading it here
+  for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0;
+  __syncthreads();
+  uint32_t omin = ~0u, omax = 0;
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    omin = sh.red_lo[w] < omin ? sh.red_lo[w] : omin;
+    omax = sh.red_hi[w] > omax ? sh.red_hi[w] : omax;
+    total += sh.red_n[w];
+  }
+  uint64_t lo = (uint64_t)omin << 32, hi = ((uint64_t)omax << 32) | 0xFFFFFFFFull;
+  if (total <= need) return 1ull;
+  uint32_t above = 0;  // keys above the current range [lo, hi]
+  for (bool first = true;; first = false) {
+    const uint64_t span = hi - lo;
+    const int hb = span ? 63 - __clzll((long long)span) : 0;
+    constexpr int kBinBits = kBins == 1024 ? 10 : (kBins == 512 ? 9 : 8);
+    static_assert((1 << kBinBits) == kBins, "power-of-two bins");
+    const int shift = hb > kBinBits - 1 ? hb - (kBinBits - 1) : 0;  // span >> shift < kBins
+    if (!first) {
+      for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0;
+      __syncthreads();
+    }
+    visit([&](uint64_t x) __attribute__((always_inline)) {
+      if (x >= lo && x <= hi) atomicAdd(&sh.hist[(uint32_t)((x - lo) >> shift)], 1u);
+    });
+    __syncthreads();
+    const uint32_t need_here = need - above;
+    // thread t owns the upper bin kBins-1-2t and the lower bin kBins-2-2t,
+    // so "bins above" is a prefix over threads
+    const uint32_t bu = kBins - 1 - 2 * tid;
+    const uint32_t h1 = sh.hist[bu], h0 = sh.hist[bu - 1];
+    const uint32_t s = h0 + h1;
+    const uint32_t incl = wave_scan_u32(s, 0u, uadd);
+    if (lane == 63) sh.red_n[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += sh.red_n[w];
+    const uint32_t X = incl - s + before;  // keys in bins above bu
+    if (X < need_here && need_here <= X + h1) {
+      sh.bin = bu; sh.ca = X; sh.cb = h1;
+    } else if (X + h1 < need_here && need_here <= X + s) {
+      sh.bin = bu - 1; sh.ca = X + h1; sh.cb = h0;
+    }
+    __syncthreads();
+    const uint32_t b = sh.bin, ca = sh.ca, cb = sh.cb;
+    const uint64_t gb = lo + ((uint64_t)b << shift);
+    // (uniform; after the return nothing writes bin, ca, cb or the
+    // histogram before another barrier)
+    if (above + ca + cb <= target || shift == 0) return gb;
+    __syncthreads();  // every thread has read bin, ca, cb
+    above += ca;
+    const uint64_t top = gb + ((1ull << shift) - 1);
+    lo = gb;
+    hi = top < hi ? top : hi;
+  }
+}
+
 }  // namespace csa

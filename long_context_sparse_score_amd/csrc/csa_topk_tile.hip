@@ -1,22 +1,34 @@
-// csa_topk_tile.hip -- fused score + per-tile heads (DS4X page, "CSA
+// csa_topk_tile.hip -- fused filter score + per-tile heads (DS4X page, "CSA
 // score/top-512 fusion": the scorer keeps exact local selections of sortable
-// (score, index) keys per tile of rows, so no separate pass over a score
-// array is needed to find the winners).
+// (score, index) keys per tile of rows, so no pass over a full score array is
+// needed to find the winners).
 //
 // tile_kernel (one workgroup per T-row tile of one session):
-//   1. scores the tile's rows on the matrix cores (csa_score.hpp) into LDS
-//      and writes them out (or reads a given score array);
-//   2. finds the tile's exact top-hd keys ("heads", hd in {8, 16, 32, 64}) and
-//      writes them sorted descending to heads[tile][hd] (0-padded).
-// Step 2 first bounds the hd-th key from below without sorting the tile:
-// every wave splits its 64 lanes into hd groups and takes the smallest group
-// maximum of the lanes' largest keys (score part), a value with at least hd
-// keys at or above it; the largest such bound over the waves is theta.  Only
-// keys >= theta can be heads: typically a few times hd of them, ranked
-// exactly against each other (an exact k-th selection replaces theta when
-// they overflow the candidate buffer).
-// The global selection over the heads is in csa_merge.hip.
+//   1. scores the tile's rows with the matrix-core filter (csa_score.hpp)
+//      and brackets each row's exact score, l_j <= S_j <= u_j (csa_bound.hpp),
+//      into LDS; the brackets' constants come from the query split of the
+//      same workgroup (with a given score array, csa_topk: l = u = S);
+//   2. finds the tile's top-(hd+1) keys by upper bound, key = (u_j, row j)
+//      (larger u first, lower row on ties; hd in {8, 16, 32, 64}), and writes
+//      the first hd ("heads", rank-major: rank r of tile t at r * nt + t, so
+//      the best heads of all tiles come first) with their lower-bound keys
+//      (l_j, row j), and the (hd+1)-th ("next": every other row of the tile
+//      has a key at or below it).  A row's bracket is kept as u (fp32) and
+//      beta rounded up to bf16; the heads' lower bounds are rebuilt from them
+//      (l = rounddown(u - 2 beta - ulp(u)) <= s~ - beta, since u <= s~ + beta
+//      + ulp(u); exactly l = u when beta = 0, as for given scores).
+// Nothing is written per row: the refine kernel (csa_refine.hip) takes the
+// heads that can reach the top-k and, for the rare tile whose "next" can,
+// every row of it, and scores them exactly.
+// Step 2 first bounds the (hd+1)-th key from below without sorting the tile:
+// every wave splits its 64 lanes into groups and takes the smallest group
+// maximum of the lanes' largest keys (score part), a value with at least
+// hd+1 keys at or above it; the largest such bound over the waves is theta.
+// Only keys >= theta can be among the top hd+1: typically a few times hd of
+// them, ranked exactly against each other (an exact k-th selection replaces
+// theta when they overflow the candidate buffer).
 #include "csa_attn.hpp"
+#include "csa_bound.hpp"
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "csa_score.hpp"
@@ -27,21 +39,22 @@ namespace csa {
 
 struct TileSession {
   const uint8_t *idx_rows;
-  float *scores;        // written (scoring modes) or read (array mode)
-  const float *q, *w;   // indexer query and head weights
-  const float *q_attn;  // attention query
+  const float *scores_in;  // array mode: the given scores
+  const float *q, *w;      // indexer query and head weights
   int64_t n_rows;
   int hd;
 };
 
 struct TileArgs {
   TileSession s[CSA_MAX_SESSIONS];
-  uint4 *attn_q;  // attention query split [session][kAttnQVecs], or null
-  uint64_t *heads;  // [session][heads_stride]
-  int64_t heads_stride;
+  uint64_t *hkey;    // [session][heads_stride]: head keys by upper bound, rank-major [hd][nt]
+  uint64_t *hlow;    // [session][heads_stride]: the heads' lower-bound keys, same order
+  uint64_t *hnext;   // [session][tiles_stride]: per tile its (hd+1)-th key, 0 if none
+  float *bnd_up, *bnd_lo;  // bounds mode: the brackets of every row (one session)
+  int64_t heads_stride, tiles_stride;
   int tile_rows;
-  int n_idx_heads, n_attn_heads;
-  int write_heads;  // scoring launches: also find and write the tile heads
+  int n_idx_heads;
+  int mode;  // TileJob::Mode
 };
 static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
 
@@ -68,22 +81,47 @@ struct TileShared {
     } h;  // step 2: the ring is drained by then
   };
   struct {
-    float score[kMaxTileRows];  // scores by tile position
+    union {
+      float score[kMaxTileRows];    // upper bounds u by tile position (from the streaming loop on)
+      double zpart[kMaxGroups][4];  // bound constants per head group and block (prologue only)
+    };
+    uint16_t beta[kMaxTileRows];    // the bracket half-widths, bf16 rounded up
   } a;
 };
 static_assert(sizeof(TileShared) <= 80 * 1024, "two workgroups per compute unit");
 
-// Step 2: the tile's scores in sh.a.score[0..rows) and, per thread, the
-// largest score part (score_ord) over its positions tid + 256 j -> the
-// tile's top-hd keys, sorted, at heads_out[0..hd).
+// x >= 0 (or +inf) rounded up to bf16 bits.
+__device__ __forceinline__ uint16_t bf16_round_up(double x) {
+  const uint32_t b = __float_as_uint(f32_round_up(x));
+  return (uint16_t)((b >> 16) + ((b & 0xFFFFu) != 0u ? 1u : 0u));
+}
+
+// The lower bound of a row from its upper bound u and bf16 half-width bits.
+__device__ __forceinline__ float row_lower(float u, uint16_t bb) {
+  const float beta = __uint_as_float((uint32_t)bb << 16);
+  if (beta == 0.0f) return u;  // exact (given scores)
+  if (!(fabsf(u) <= 3.40282347e38f) || !(beta <= 3.40282347e38f)) return -__builtin_inff();
+  // two ulps: one for u's rounding up, one covering the fp64 roundings here
+  const double ulp = (double)f32_next_up(fabsf(u)) - (double)fabsf(u);
+  return f32_round_down((double)u - 2.0 * (double)beta - 2.0 * ulp);
+}
+
+// Step 2: the tile's upper bounds in sh.a.score[0..rows) (half-widths in
+// sh.a.beta) and, per thread, the largest score part (score_ord) over its
+// positions tid + 256 j -> the tile's top-(hd+1) keys by upper bound: rank r
+// < hd to hkey_out[r * rstride] with its lower-bound key to
+// hlow_out[r * rstride], the (hd+1)-th to *next_out (0 if the tile has at
+// most hd rows; heads past the rows are 0).
 __device__ __forceinline__ void tile_heads(TileShared &sh, uint32_t o, int rows, int64_t row0, int hd,
-                                           uint64_t *__restrict__ heads_out) {
+                                           uint64_t *__restrict__ hkey_out, uint64_t *__restrict__ hlow_out,
+                                           int64_t rstride, uint64_t *__restrict__ next_out) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int want = hd + 1;  // heads and next
   auto key_at = [&](int i) __attribute__((always_inline)) {
     return make_key(sh.a.score[i], (uint32_t)(row0 + i));
   };
-  // the largest 24-bit prefix p with at least hd lane maxima at or above
-  // p << 8 (two bits per step): those hd keys are >= p << 40
+  // the largest 24-bit prefix p with at least `want` lane maxima at or above
+  // p << 8 (two bits per step): those keys are >= p << 40
   const uint32_t o24 = o >> 8;
   uint32_t p = 0;
 #pragma unroll
@@ -92,7 +130,7 @@ __device__ __forceinline__ void tile_heads(TileShared &sh, uint32_t o, int rows,
     const int n1 = __popcll(__ballot(o24 >= c1));
     const int n2 = __popcll(__ballot(o24 >= c2));
     const int n3 = __popcll(__ballot(o24 >= c3));
-    p = n3 >= hd ? c3 : (n2 >= hd ? c2 : (n1 >= hd ? c1 : p));
+    p = n3 >= want ? c3 : (n2 >= want ? c2 : (n1 >= want ? c1 : p));
   }
   if (lane == 0) sh.h.theta[wave] = (uint64_t)p << 40;
   if (tid == 0) sh.h.ccnt = 0;
@@ -144,8 +182,8 @@ __device__ __forceinline__ void tile_heads(TileShared &sh, uint32_t o, int rows,
   int C = (int)sh.h.ccnt;
   if (C > kTileCandCap) {
     // many keys tie with or crowd above the bound: select exactly instead
-    // (exactly hd keys are >= the hd-th largest)
-    const uint64_t thr = block_kth_largest<kTileWaves>(key_at, rows, hd, theta, sh.h.sc);
+    // (exactly `want` keys are >= the want-th largest)
+    const uint64_t thr = block_kth_largest<kTileWaves>(key_at, rows, want, theta, sh.h.sc);
     if (tid == 0) sh.h.ccnt = 0;
     __syncthreads();
     gather(thr, (uint32_t)kTileCandCap);
@@ -163,9 +201,19 @@ __device__ __forceinline__ void tile_heads(TileShared &sh, uint32_t o, int rows,
 #pragma unroll
       for (int u = 0; u < 16; ++u) r += (j0 + u < C && y[u] > key) ? 1 : 0;
     }
-    if (r < hd) heads_out[r] = key;
+    if (r < hd) {
+      const uint32_t i = key_row(key) - (uint32_t)row0;
+      hkey_out[r * rstride] = key;
+      hlow_out[r * rstride] = make_key(row_lower(sh.a.score[i], sh.a.beta[i]), key_row(key));
+    } else if (r == hd) {
+      *next_out = key;
+    }
   }
-  for (int r = C + tid; r < hd; r += kTileThreads) heads_out[r] = 0ull;
+  for (int r = C + tid; r < hd; r += kTileThreads) {
+    hkey_out[r * rstride] = 0ull;
+    hlow_out[r * rstride] = 0ull;
+  }
+  if (C <= hd && tid == 0) *next_out = 0ull;
 }
 
 // Rows [r0, r0 + 64) of a chunk that ends past the buffer: lane l copies
@@ -212,7 +260,9 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[
   }
 }
 
-// Score the tile's rows into sh.a.score[0..rows) (and out[0..rows)).
+// Score the tile's rows and bracket their exact scores: u into
+// sh.a.score[0..rows), the half-width into sh.a.beta (and, in the bounds
+// mode, u and l to bnd_up / bnd_lo).
 // Wave w owns chunks w, w + 4, w + 8, ... of the tile (64 rows each) and
 // scores them for every head group, so each row is read from LDS once and
 // the group parts of a row meet in the lane that holds it; the waves run
@@ -220,20 +270,22 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[
 // direct-to-LDS, kRingDepth - 1 chunks ahead, into the wave's own ring; a
 // chunk cut by the buffer end is copied with clamped per-lane loads.
 // Query terms: wave g brings the fp32 query of head group g (16 heads,
-// 8 KB) and all the weights direct-to-LDS into its ring slots 1 and 2 ahead
-// of its first chunk, so they arrive first and the split runs while the
-// chunk is in flight.  Each head's 512 bytes land at a 528-byte stride, so
+// 8 KB) and all the weights direct-to-LDS into its ring slots 2 and 3 ahead
+// of its first two chunks (slots 0 and 1), so they arrive first and the
+// split runs while the chunks are in flight.  Each head's 512 bytes land at a 528-byte stride, so
 // the split's reads spread over the LDS banks; each wave then writes its
 // group's terms over its own staging area (16-byte quad j of lane l at
-// 16 (64 j + l)), and after one barrier every wave reads every group's
-// terms.  The chunks after the first are issued once a second barrier has
-// released the slots.
+// 16 (64 j + l)) and its part of the bound constants, and after one barrier
+// every wave reads every group's terms and the constants.  The third chunk
+// is issued once a second barrier has released the slots (the loop issues
+// the rest, always in order).
 template <int G>
 __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
                                                int n_idx_heads, const uint8_t *__restrict__ idx_rows, int64_t row0,
-                                               int64_t n, int rows, float *__restrict__ out, TileShared &sh) {
+                                               int64_t n, int rows, TileShared &sh, float *__restrict__ bnd_up,
+                                               float *__restrict__ bnd_lo) {
   static_assert(G == 1 || G == 2 || G == 4, "head groups per workgroup");
-  static_assert(kRingDepth >= 3, "the query is staged in ring slots 1 and 2");
+  static_assert(kRingDepth == 4, "the query is staged in ring slots 2 and 3, chunks 0 and 1 go ahead");
   constexpr int kStageHead = 528, kStageW = 16 * kStageHead;
   static_assert(kStageW + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
   static_assert(kXchQuads * 64 * 16 <= kStageW, "the terms leave the weights alone");
@@ -259,7 +311,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   // staging: head 16 wave + j (clamped to the last one) at stage + 528 j,
   // one 512-byte load per head (the 16-byte pad spreads the split's reads
   // over the banks), the weights at stage + kStageW
-  uint8_t *const stage = &sh.ring[wave][1][0];
+  uint8_t *const stage = &sh.ring[wave][2][0];
   const uint32_t stage_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage);
   if (wave < G && lane < 32) {
     // the head rows' addresses are uniform: scalar bases, one lane offset
@@ -272,12 +324,19 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   }
   dma4(wh + (lane < n_idx_heads ? lane : n_idx_heads - 1), stage_lds + kStageW);
   if (nmy > 0) fill(0);
-  if (direct(0))
+  if (nmy > 1) fill(1);
+  // the query has landed once at most the two chunks' loads are outstanding
+  // (loads complete in issue order; a clamped copy waits for itself)
+  if (direct(0) && direct(1))
+    wait_vmcnt<2 * kChunkDma>();
+  else if (direct(0) || direct(1))
     wait_vmcnt<kChunkDma>();
   else
     wait_vmcnt<0>();
   QFrag<1> q[G];
+  FilterBound B;
   {
+    const float *wl = reinterpret_cast<const float *>(stage + kStageW);  // this wave's copy of the weights
     if (wave < G) {
       float x[32];
 #pragma unroll
@@ -290,10 +349,19 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
         x[4 * i + 3] = v.w;
       }
       QFrag<1> mine;
-      split_qfrag(mine, x);
+      const QFragNorms nm = split_qfrag(mine, x);
+      // this lane's part of the bound constants: |w_h| (rho + 2^-15 A) for its
+      // (head, block) fragment, summed over the group's 16 heads per block
+      // (lanes 16 b .. 16 b + 15 hold block b); fp64 so that no range is lost
+      const int h = 16 * wave + (lane & 15);
+      const double wa = h < n_idx_heads ? fabs((double)wl[h]) : 0.0;
+      double cz = wa * ((double)nm.rho + 0x1p-15 * (double)nm.mag);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) cz += __shfl_xor(cz, m, 64);
+      if ((lane & 15) == 0) sh.a.zpart[wave][lane >> 4] = cz;
       // the terms over the staging area (this wave's reads of it come first):
-      // the lane's 32 words (6 per term, then the packed scales) as eight
-      // 16-byte quads, quad j of lane l at stage + 16 (64 j + l)
+      // the lane's words (6 per term, then the packed scales) as 16-byte
+      // quads, quad j of lane l at stage + 16 (64 j + l)
       uint32_t w[kXchQuads * 4];
 #pragma unroll
       for (int t = 0; t < kTerms; ++t)
@@ -307,10 +375,22 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
 #pragma unroll
       for (int j = 0; j < kXchQuads; ++j) x16[64 * j] = uint4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
     }
+    // Z_abs from the weights (every wave, its own copy): 2^-117 sum_h |w_h|
+    double wsum = lane < n_idx_heads ? fabs((double)wl[lane]) : 0.0;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) wsum += __shfl_xor(wsum, m, 64);
     __syncthreads();
 #pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      double z = 0.0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) z += sh.a.zpart[g][b];
+      B.z[b] = z * (6.0 * (1.0 + 0x1p-10));
+    }
+    B.zabs = wsum * 0x1p-117;
+#pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4 *x16 = reinterpret_cast<const uint4 *>(&sh.ring[g][1][0]) + lane;
+      const uint4 *x16 = reinterpret_cast<const uint4 *>(&sh.ring[g][2][0]) + lane;
       uint32_t w[kXchQuads * 4];
 #pragma unroll
       for (int j = 0; j < kXchQuads; ++j) {
@@ -327,17 +407,14 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
 #pragma unroll
       for (int j = 0; j < kScaleWords; ++j) q[g].scw[0][j] = (int)w[6 * kTerms + j];
     }
-    // the weights (in slot 2, which the exchange leaves alone)
-    const float *wl = reinterpret_cast<const float *>(stage + kStageW);
+    // the weights (in slot 3, which the exchange leaves alone)
 #pragma unroll
     for (int g = 0; g < G; ++g) load_qweights(q[g], wl, n_idx_heads, g, lane);
     __syncthreads();  // every wave has read the terms and weights: the slots are free
-#pragma unroll
-    for (int t = 1; t <= kRingDepth - 2; ++t)
-      if (t < nmy) fill(t);
+    if (2 < nmy) fill(2);
   }
 
-  uint32_t omax = 0;  // largest score part of this thread's rows
+  uint32_t omax = 0;  // largest score part of this thread's upper bounds
   for (int s = 0; s < nmy; ++s) {
     int later = 0;
 #pragma unroll
@@ -363,14 +440,21 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
     }
     group_acc4(q[G - 1], c, acc);
-    // lane l: row l of the chunk, summed over every head
-    float v = rows_reduce4(acc);
+    // lane l: row l of the chunk, summed over every head, and its bracket
+    // from the row's four scale bytes
+    const float v = score_finish(rows_reduce4(acc), 0.0f);
+    const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + kIdxRowBytes * lane + 64);
     const int p = kChunkRows * chunk(s) + lane;
     if (p < rows) {
-      v = score_finish(v, 0.0f);
-      sh.a.score[p] = v;
-      out[p] = v;
-      const uint32_t so = score_ord(v);
+      float up, lo;
+      const double beta = row_bracket(v, sb, B, up, lo);
+      sh.a.score[p] = up;
+      sh.a.beta[p] = bf16_round_up(beta);
+      if (bnd_up) {
+        bnd_up[p] = up;
+        bnd_lo[p] = lo;
+      }
+      const uint32_t so = score_ord(up);
       omax = so > omax ? so : omax;
     }
   }
@@ -378,10 +462,9 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   return omax;
 }
 
-// ARRAY: the scores are given (csa_topk).  The scoring launches of csa_score
-// and of the decode step run the same code (the heads are a runtime choice),
-// so both produce the same bits: the scaled matrix-core accumulation may
-// round differently under a different instruction schedule.
+// Modes (TileJob::Mode): kFilter scores the rows (the decode step), kArray
+// takes given scores as exact (csa_topk: l = u = the score), kBounds scores
+// and writes every row's bracket (a test entry point; no heads).
 template <int G, bool ARRAY>
 __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a) {
   const int sess = blockIdx.y;
@@ -392,34 +475,17 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   if (row0 >= n) return;
   const int rows = (int)((n - row0) < T ? (n - row0) : T);
   __shared__ TileShared sh;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   uint32_t o = 0;  // largest score part of this thread's positions
   if constexpr (!ARRAY) {
-    uint4 *const aq = a.attn_q ? a.attn_q + (size_t)sess * kAttnQVecs : nullptr;
-    const float *const qa = S.q_attn;
-    const int n_attn_heads = a.n_attn_heads;
-    auto attn_split = [=]() __attribute__((always_inline)) {
-      if (aq) {
-        // this workgroup's share of the session's attention query split
-        // (read by the selection kernel that follows), spread over the
-        // first half of the tiles: they are dispatched first and finish
-        // while the second half still scores, so the split stays off the
-        // kernel's tail
-        const int nt = (int)((n + T - 1) / T);
-        const int nw = nt > 1 ? nt / 2 : 1;
-        const int per = (kAttnQTasks + nw - 1) / nw;
-        const int b = (int)blockIdx.x;
-        const int t1 = (b + 1) * per < kAttnQTasks ? (b + 1) * per : kAttnQTasks;
-        if (b < nw)
-          for (int t = b * per + tid; t < t1; t += kTileThreads) attn_q_split_task(qa, n_attn_heads, aq, t);
-      }
-    };
-    o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, S.scores + row0, sh);
-    attn_split();
-    if (!a.write_heads) return;
+    const bool bounds = a.mode == TileJob::kBounds;
+    o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, sh, bounds ? a.bnd_up + row0 : nullptr,
+                      bounds ? a.bnd_lo + row0 : nullptr);
+    if (bounds) return;
   } else {
-    // the given scores into LDS, four loads in flight per thread
-    const float *src = S.scores + row0;
+    // the given scores into LDS (exact: both bounds), four loads in flight
+    // per thread
+    const float *src = S.scores_in + row0;
     for (int j0 = 0; j0 < rows; j0 += 4 * kTileThreads) {
       float v[4];
 #pragma unroll
@@ -432,6 +498,7 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
         const int i = j0 + kTileThreads * u + tid;
         if (i < rows) {
           sh.a.score[i] = v[u];
+          sh.a.beta[i] = 0;
           const uint32_t so = score_ord(v[u]);
           o = so > o ? so : o;
         }
@@ -439,7 +506,11 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
     }
     __syncthreads();
   }
-  tile_heads(sh, o, rows, row0, S.hd, a.heads + (size_t)sess * a.heads_stride + (size_t)blockIdx.x * S.hd);
+  // rank-major heads of the session: rank r of tile t at r * nt + t
+  const int64_t nt = (n + T - 1) / T;
+  const size_t hb = (size_t)sess * a.heads_stride + (size_t)blockIdx.x;
+  tile_heads(sh, o, rows, row0, S.hd, a.hkey + hb, a.hlow + hb, nt,
+             a.hnext + (size_t)sess * a.tiles_stride + blockIdx.x);
 }
 
 // ---------------------------------------------------------------- launcher
@@ -459,31 +530,27 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   TileArgs a;
   int64_t max_rows = 0;
   for (int i = 0; i < job.n_sessions; ++i) {
-    float *scores = job.mode == TileJob::kArraySelect ? const_cast<float *>(job.scores_in[i]) : job.scores_out[i];
-    a.s[i] = TileSession{job.idx_rows[i], scores, job.q[i], job.w[i], job.q_attn[i], job.n_rows[i], job.hd[i]};
+    a.s[i] = TileSession{job.idx_rows[i], job.scores_in[i], job.q[i], job.w[i], job.n_rows[i], job.hd[i]};
     max_rows = job.n_rows[i] > max_rows ? job.n_rows[i] : max_rows;
   }
   if (max_rows == 0) return hipSuccess;
-  a.attn_q = job.mode == TileJob::kScoreSelect ? job.attn_q : nullptr;
   a.n_idx_heads = job.n_idx_heads;
-  a.n_attn_heads = job.n_attn_heads;
-  a.heads = job.heads;
+  a.hkey = job.hkey;
+  a.hlow = job.hlow;
+  a.hnext = job.hnext;
+  a.bnd_up = job.bnd_up;
+  a.bnd_lo = job.bnd_lo;
   a.heads_stride = job.heads_stride;
+  a.tiles_stride = job.tiles_stride;
   a.tile_rows = job.tile_rows;
+  a.mode = (int)job.mode;
   const int groups = (job.n_idx_heads + 15) / 16;
   dim3 grid((unsigned)((max_rows + job.tile_rows - 1) / job.tile_rows), (unsigned)job.n_sessions);
-  switch (job.mode) {
-    case TileJob::kScore:
-      a.write_heads = 0;
-      return launch_scoring(a, grid, groups, st);
-    case TileJob::kScoreSelect:
-      a.write_heads = 1;
-      return launch_scoring(a, grid, groups, st);
-    default:
-      a.write_heads = 1;
-      tile_kernel<1, true><<<grid, kTileThreads, 0, st>>>(a);
-      return hipGetLastError();
+  if (job.mode == TileJob::kArray) {
+    tile_kernel<1, true><<<grid, kTileThreads, 0, st>>>(a);
+    return hipGetLastError();
   }
+  return launch_scoring(a, grid, groups, st);
 }
 
 }  // namespace csa

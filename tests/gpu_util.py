@@ -37,6 +37,18 @@ def check_selection(gpu_sel: np.ndarray, ref_sel: np.ndarray, ref_scores_all: np
     return {"band": int(band.sum()), "swaps": len(diff) // 2}
 
 
+def check_selection_exact(gpu_sel: np.ndarray, gpu_score: np.ndarray, ref_sel: np.ndarray, ref_score: np.ndarray,
+                          k_eff: int) -> dict:
+    """The GPU's selection is the oracle's: the same rows in the same order
+    and the same scores bit for bit, -1 / -inf padded."""
+    assert np.array_equal(gpu_sel, ref_sel), (
+        f"selection differs at {int(np.sum(gpu_sel != ref_sel))} positions, first {np.nonzero(gpu_sel != ref_sel)[0][:5]}")
+    g, r = gpu_score[:k_eff].astype(np.float32), ref_score[:k_eff].astype(np.float32)
+    assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), "selected scores differ"
+    assert np.all(np.isneginf(gpu_score[k_eff:]))
+    return {"exact": True}
+
+
 def check_attention(gpu_out: np.ndarray, ref_out: np.ndarray) -> float:
     scale = float(np.max(np.abs(ref_out))) if ref_out.size else 0.0
     err = float(np.max(np.abs(gpu_out - ref_out))) if ref_out.size else 0.0

@@ -162,8 +162,8 @@ def test_decode_step_extreme_scale_bytes(csa, orc, sbyte):
     got = {k: got[k].cpu().numpy() for k in ("sel", "sel_score", "out", "lse")}
     ref_scores = orc.score(idx, s["q_idx"], s["w_idx"])
     assert np.all(np.isfinite(ref_scores))
-    ref_sel, _, _ = orc.topk(ref_scores, 512)
-    info = gu.check_selection(got["sel"], ref_sel, ref_scores, 512)
+    ref_sel, ref_sel_score, _ = orc.topk(ref_scores, 512)
+    info = gu.check_selection_exact(got["sel"], got["sel_score"], ref_sel, ref_sel_score, 512)
     att, lse = orc.attention(kv, got["sel"], s["q_attn"], s["softmax_scale"])
     assert np.max(np.abs(att)) > 0
     info["attn_rel_err"] = gu.check_attention(got["out"], att)
