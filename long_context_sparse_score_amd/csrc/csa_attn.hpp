@@ -118,20 +118,23 @@ __device__ __forceinline__ void split3_bf16(float x, __bf16 &t0, __bf16 &t1, __b
 // (n = n_heads; heads past n are zero): the three terms of
 //   q[16(w%4) + l%16][128(w/4) + 32s + 8(l/16) + i], i < 8,
 // for w = t / 256, s = (t / 64) % 4, l = t % 64, stored at
-// dst[attn_q_index(w, s, term, l)].
-__device__ __forceinline__ void attn_q_split_task(const float *__restrict__ qa, int n_heads, uint4 *__restrict__ dst,
-                                                  int t) {
+// dst[attn_q_index(w, s, term, l)].  attn_q_load reads the task's eight
+// values, attn_q_store splits and stores them (so a caller can issue the
+// loads early).
+__device__ __forceinline__ void attn_q_load(const float *__restrict__ qa, int n_heads, int t, float (&x)[8]) {
   const int lane = t % 64, s = (t / 64) % 4, wave = t / 256;
   const int h = 16 * (wave & 3) + (lane & 15);
   const int d0 = 128 * (wave >> 2) + 32 * s + 8 * (lane >> 4);
   const bool live = h < n_heads;
   const float *src = qa + (size_t)(live ? h : 0) * kKvDim + d0;
-  float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float v = src[i];
     x[i] = live ? v : 0.0f;
   }
+}
+__device__ __forceinline__ void attn_q_store(const float (&x)[8], uint4 *__restrict__ dst, int t) {
+  const int lane = t % 64, s = (t / 64) % 4, wave = t / 256;
   v8bf t0, t1, t2;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -144,6 +147,12 @@ __device__ __forceinline__ void attn_q_split_task(const float *__restrict__ qa, 
   dst[attn_q_index(wave, s, 0, lane)] = __builtin_bit_cast(uint4, t0);
   dst[attn_q_index(wave, s, 1, lane)] = __builtin_bit_cast(uint4, t1);
   dst[attn_q_index(wave, s, 2, lane)] = __builtin_bit_cast(uint4, t2);
+}
+__device__ __forceinline__ void attn_q_split_task(const float *__restrict__ qa, int n_heads, uint4 *__restrict__ dst,
+                                                  int t) {
+  float x[8];
+  attn_q_load(qa, n_heads, t, x);
+  attn_q_store(x, dst, t);
 }
 constexpr int kAttnQTasks = kAttnQVecs / 3;  // 4096
 

@@ -19,6 +19,18 @@ constexpr int kKvRowBytes = 583;
 constexpr int kKvNope = 448;
 constexpr int kTopK = 512;
 
+// Workgroup barrier that orders LDS accesses only: the fences are limited
+// to the local address space, so the barrier waits for the wave's LDS
+// operations (lgkmcnt) but leaves its global loads in flight, unlike
+// __syncthreads(), whose workgroup fence also waits for every outstanding
+// vector memory operation.  Not for direct-to-LDS loads (those are vector
+// memory operations) or for global memory shared between the waves.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // UE8M0 byte -> 2^(e-127) as fp32; e = 0 is the subnormal 2^-127, 0xFF NaN.
 __device__ __forceinline__ float ue8m0_scale(uint32_t e) {
   uint32_t bits = (e == 0u) ? 0x00400000u : ((e == 255u) ? 0x7FC00000u : (e << 23));

@@ -75,8 +75,7 @@ static_assert(sizeof(RefineArgs) <= 4096, "kernel argument block");
 struct RefineShared {
   float q[CSA_MAX_HEADS][kQStride];  // the fp32 indexer query
   float w[CSA_MAX_HEADS];
-  double kv[kRefWaves][128];   // per wave: the decoded row being scored
-  double pv[kRefWaves][64];    // per wave: w_h * max(0, d_h) by head
+  double kv[kRefWaves][2][128];  // per wave: the decoded rows being scored
   BoundShared<kRefWaves> bs;
   uint32_t full_tile[kRefMaxFull];
   uint32_t wcnt[kRefWaves];
@@ -103,46 +102,96 @@ __device__ __forceinline__ RowBytes load_row_bytes(const uint8_t *__restrict__ i
   return RowBytes{r[lane], r[64 + (lane >> 4)]};
 }
 
-// The exact score S of a row (see the file comment) from its bytes, computed
-// by one wave: lane l decodes row values 2l and 2l + 1 exactly as fp32 (an
-// E2M1 value times 2^(e-127): exact, or +-inf on overflow, NaN for a 0xFF
-// scale), lane h < n_heads forms d_h in fp64 over i ascending, and lane 0
-// adds the heads' terms in order.  Returns S in every lane.
-__device__ __forceinline__ float exact_score(const RowBytes &rb, int n_heads, RefineShared &sh) {
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The exact scores S of N <= 2 rows (see the file comment) from their bytes,
+// computed by one wave: lane l decodes row values 2l and 2l + 1 exactly as
+// fp32 (an E2M1 value times 2^(e-127): exact, or +-inf on overflow, NaN for
+// a 0xFF scale), lane h < n_heads forms d_h in fp64 over i ascending (the
+// rows' chains interleaved), and every lane adds the heads' terms in head
+// order, read lane by lane.  out[r] is S of row r in every lane.
+template <int N>
+__device__ __forceinline__ void exact_scores(const RowBytes (&rb)[N], int n_heads, RefineShared &sh, float (&out)[N]) {
+  static_assert(N == 1 || N == 2, "rows per call");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float sc = ue8m0_scale(rb.scale);
-  const float k0 = e2m1_value(rb.code & 15u) * sc, k1 = e2m1_value(rb.code >> 4) * sc;
-  sh.kv[wave][2 * lane] = (double)k0;
-  sh.kv[wave][2 * lane + 1] = (double)k1;
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    const float sc = ue8m0_scale(rb[r].scale);
+    const float k0 = e2m1_value(rb[r].code & 15u) * sc, k1 = e2m1_value(rb[r].code >> 4) * sc;
+    *reinterpret_cast<double2 *>(&sh.kv[wave][r][2 * lane]) = double2{(double)k0, (double)k1};
+  }
   wave_lds_sync();
   const int h = lane < n_heads ? lane : 0;
   const float *qh = &sh.q[h][0];
-  double d = 0.0;
+  double d[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) d[r] = 0.0;
 #pragma unroll 4
   for (int i = 0; i < 128; i += 4) {
     const float4 q4 = *reinterpret_cast<const float4 *>(qh + i);
-    const double2 ka = *reinterpret_cast<const double2 *>(&sh.kv[wave][i]);
-    const double2 kb = *reinterpret_cast<const double2 *>(&sh.kv[wave][i + 2]);
-    d = __builtin_fma((double)q4.x, ka.x, d);
-    d = __builtin_fma((double)q4.y, ka.y, d);
-    d = __builtin_fma((double)q4.z, kb.x, d);
-    d = __builtin_fma((double)q4.w, kb.y, d);
-  }
-  const double relu = d > 0.0 ? d : 0.0;
-  sh.pv[wave][lane] = (double)sh.w[h] * relu;
-  wave_lds_sync();
-  double s = 0.0;
-  if (lane == 0) {
-    for (int hh = 0; hh < n_heads; hh += 2) {
-      const double2 p2 = *reinterpret_cast<const double2 *>(&sh.pv[wave][hh]);
-      s = s + p2.x;
-      if (hh + 1 < n_heads) s = s + p2.y;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const double2 ka = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][i]);
+      const double2 kb = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][i + 2]);
+      d[r] = __builtin_fma((double)q4.x, ka.x, d[r]);
+      d[r] = __builtin_fma((double)q4.y, ka.y, d[r]);
+      d[r] = __builtin_fma((double)q4.z, kb.x, d[r]);
+      d[r] = __builtin_fma((double)q4.w, kb.y, d[r]);
     }
   }
-  float f = (float)s;
-  f = f == 0.0f ? 0.0f : f;
-  wave_lds_sync();  // kv and pv are reused by the wave's next row
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f)));
+  const double wh = (double)sh.w[h];
+  double p[N], acc[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    p[r] = wh * (d[r] > 0.0 ? d[r] : 0.0);
+    acc[r] = 0.0;
+  }
+#pragma unroll
+  for (int hh = 0; hh < CSA_MAX_HEADS; ++hh) {
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const double v = readlane_f64(p[r], hh);
+      acc[r] = hh < n_heads ? acc[r] + v : acc[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    const float f = (float)acc[r];
+    out[r] = f == 0.0f ? 0.0f : f;
+  }
+  wave_lds_sync();  // kv is reused by the wave's next rows
+}
+__device__ __forceinline__ float exact_score(const RowBytes &rb, int n_heads, RefineShared &sh) {
+  const RowBytes r1[1] = {rb};
+  float f[1];
+  exact_scores<1>(r1, n_heads, sh, f);
+  return f[0];
+}
+
+// The fp32 indexer query (padded rows) and weights into LDS, all loads in
+// flight together (no barrier here).
+__device__ __forceinline__ void load_query(const float *__restrict__ q, const float *__restrict__ w, int H,
+                                           RefineShared &sh) {
+  const int tid = threadIdx.x;
+  constexpr int kQPer = CSA_MAX_HEADS * 32 / kRefThreads;  // float4 per thread
+  float4 qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int t = tid + kRefThreads * u, h = t >> 5, c = t & 31;
+    qv[u] = h < H ? reinterpret_cast<const float4 *>(q + (size_t)h * 128)[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const float wv = tid < H ? w[tid] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int t = tid + kRefThreads * u;
+    *reinterpret_cast<float4 *>(&sh.q[t >> 5][4 * (t & 31)]) = qv[u];
+  }
+  if (tid < CSA_MAX_HEADS) sh.w[tid] = wv;
 }
 
 // Head items prefetched per wave (keys, then the rows' bytes) at the start,
@@ -160,24 +209,9 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   const uint32_t nw = gridDim.x * kRefWaves;               // waves per session
   const uint32_t gw = blockIdx.x * kRefWaves + (uint32_t)wave;  // this wave
 
-  if (exact) {  // the query and weights into LDS (padded rows): all loads in flight together
-    constexpr int kQPer = CSA_MAX_HEADS * 32 / kRefThreads;  // float4 per thread
-    float4 qv[kQPer];
-#pragma unroll
-    for (int u = 0; u < kQPer; ++u) {
-      const int t = tid + kRefThreads * u, h = t >> 5, c = t & 31;
-      qv[u] = h < H ? reinterpret_cast<const float4 *>(S.q + (size_t)h * 128)[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const float wv = tid < H ? S.w[tid] : 0.0f;
-#pragma unroll
-    for (int u = 0; u < kQPer; ++u) {
-      const int t = tid + kRefThreads * u;
-      *reinterpret_cast<float4 *>(&sh.q[t >> 5][4 * (t & 31)]) = qv[u];
-    }
-    if (tid < CSA_MAX_HEADS) sh.w[tid] = wv;
-  }
   if (a.mode == RefineJob::kAll) {  // every row: its exact score
-    __syncthreads();
+    load_query(S.q, S.w, H, sh);
+    lds_sync();
     for (int64_t row = gw; row < n; row += nw) {
       const float f = exact_score(load_row_bytes(S.idx_rows, row), H, sh);
       if (lane == 0) S.scores[row] = f;
@@ -199,22 +233,19 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   }
   if (tid == 0) { sh.nfull = 0; sh.all_rows = 0; }
 
-  // this wave's first head items: their keys and (decode step) their rows'
-  // bytes, loaded now whether or not they turn out to be candidates
+  // Loads, issued in the order their results are needed: this wave's first
+  // head items' keys and the bound's lower-bound keys, the query, the
+  // attention query values of this workgroup's first split tasks, then the
+  // head items' row bytes; everything after is synchronised through LDS only
+  // (lds_sync), so these stay in flight across the bound's barriers.
   uint64_t px[kRefPrefetch];
-  RowBytes pb[kRefPrefetch] = {};
 #pragma unroll
   for (int u = 0; u < kRefPrefetch; ++u) {
     const int64_t i = gw + (int64_t)nw * u;
     const uint64_t x = hkey[i < nh ? i : nh - 1];
     px[u] = i < nh ? x : 0ull;
   }
-  if (exact) {
-#pragma unroll
-    for (int u = 0; u < kRefPrefetch; ++u) pb[u] = load_row_bytes(S.idx_rows, px[u] != 0 ? key_row(px[u]) : 0);
-  }
-
-  // 1. G over the lower-bound keys of the first heads (a prefix of the
+  // G over the lower-bound keys of the first heads (a prefix of the
   // rank-major order: every tile's best heads), two per thread
   const int64_t nb = nh < kRefBoundHeads ? nh : kRefBoundHeads;
   uint64_t lk[kRefKPT];
@@ -224,6 +255,20 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
     const uint64_t x = hlow[i < nb ? i : nb - 1];
     lk[j] = i < nb ? x : 0ull;
   }
+  if (exact) load_query(S.q, S.w, H, sh);
+  // this workgroup's share of the attention query split (decode step)
+  const int qper = (kAttnQTasks + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int qt0 = (int)blockIdx.x * qper;
+  const int qt1 = qt0 + qper < kAttnQTasks ? qt0 + qper : kAttnQTasks;
+  float qx[8];
+  if (a.attn_q && qt0 + tid < qt1) attn_q_load(S.q_attn, a.n_attn_heads, qt0 + tid, qx);
+  RowBytes pb[kRefPrefetch] = {};
+  if (exact) {
+#pragma unroll
+    for (int u = 0; u < kRefPrefetch; ++u) pb[u] = load_row_bytes(S.idx_rows, px[u] != 0 ? key_row(px[u]) : 0);
+  }
+
+  // 1. the bound G
   auto visit_low = [&](auto f) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kRefKPT; ++j)
@@ -239,7 +284,7 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
     const bool full = nx != 0 && nx >= G;
     const uint64_t m = __ballot(full);
     if (lane == 0) sh.wcnt[wave] = (uint32_t)__popcll(m);
-    __syncthreads();
+    lds_sync();
     uint32_t before = sh.nfull, tot = 0;
 #pragma unroll
     for (int w = 0; w < kRefWaves; ++w) {
@@ -248,9 +293,9 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
     }
     const uint32_t pos = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     if (full && pos < kRefMaxFull) sh.full_tile[pos] = (uint32_t)t;
-    __syncthreads();
+    lds_sync();
     if (tid == 0) sh.nfull += tot;
-    __syncthreads();
+    lds_sync();
   }
   const uint32_t nfull_all = sh.nfull;
   const bool all_rows = nfull_all > kRefMaxFull;  // uniform: then every row is an item
@@ -265,12 +310,6 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   const int64_t head_items = all_rows ? 0 : nh;
   const int64_t n_items = all_rows ? n : head_items + full_rows;
   if (blockIdx.x == 0 && tid == 0) a.count[sess] = (uint32_t)n_items;
-  if (a.attn_q) {  // this workgroup's share of the attention query split
-    const int per = (kAttnQTasks + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int t1 = ((int)blockIdx.x + 1) * per < kAttnQTasks ? ((int)blockIdx.x + 1) * per : kAttnQTasks;
-    for (int t = (int)blockIdx.x * per + tid; t < t1; t += kRefThreads)
-      attn_q_split_task(S.q_attn, a.n_attn_heads, a.attn_q + (size_t)sess * kAttnQVecs, t);
-  }
   auto is_full = [&](int64_t t) __attribute__((always_inline)) {  // binary search of the sorted list
     int lo = 0, hi = nfull;
     while (lo < hi) {
@@ -280,34 +319,56 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
     return lo < nfull && (int64_t)sh.full_tile[lo] == t;
   };
 
-  // 3. this wave's items (uniform over the wave): item i, with its head key
-  // and row bytes prefetched or not
-  auto item = [&](int64_t i, bool pre, uint64_t xp, const RowBytes &bp) __attribute__((always_inline)) {
-    int64_t row = -1;
-    bool have = false;  // the row's bytes are the prefetched ones
-    if (all_rows) {
-      row = i;
-    } else if (i < head_items) {
+  // 3. this wave's items (uniform over the wave).  Item i's row, or -1 when
+  // it has no key; `pre` says whether its head key was prefetched (as xp),
+  // `have` comes back true when the row is the prefetched key's row.
+  auto item_row = [&](int64_t i, bool pre, uint64_t xp, bool &have) __attribute__((always_inline)) {
+    have = false;
+    if (all_rows) return i;
+    if (i < head_items) {
       const uint64_t x = pre ? xp : hkey[i];  // rank i / nt of tile i % nt
-      if (x != 0 && x >= G && !is_full(i % nt)) row = key_row(x);
       have = pre;
-    } else {
-      const int64_t r = i - head_items;
-      row = (int64_t)sh.full_tile[r / T] * T + r % T;
+      return (x != 0 && x >= G && !is_full(i % nt)) ? (int64_t)key_row(x) : (int64_t)-1;
     }
-    uint64_t key = 0;
-    if (row >= 0) {
-      const float f = exact ? exact_score(have ? bp : load_row_bytes(S.idx_rows, row), H, sh) : S.scores[row];
-      key = make_key(f, (uint32_t)row);
-    }
-    if (lane == 0) items[i] = key;
+    const int64_t r = i - head_items;
+    return (int64_t)sh.full_tile[r / T] * T + r % T;
   };
-#pragma unroll
-  for (int u = 0; u < kRefPrefetch; ++u) {
-    const int64_t i = gw + (int64_t)nw * u;
-    if (i < n_items) item(i, true, px[u], pb[u]);
+  auto score_of = [&](int64_t row, bool have, const RowBytes &bp) __attribute__((always_inline)) {
+    return exact ? exact_score(have ? bp : load_row_bytes(S.idx_rows, row), H, sh) : S.scores[row];
+  };
+  {  // the prefetched items: two rows to score are scored together
+    static_assert(kRefPrefetch == 2, "the prefetched items are scored as a pair");
+    const int64_t i0 = gw, i1 = gw + (int64_t)nw;
+    bool h0 = false, h1 = false;
+    const int64_t r0 = i0 < n_items ? item_row(i0, true, px[0], h0) : -1;
+    const int64_t r1 = i1 < n_items ? item_row(i1, true, px[1], h1) : -1;
+    uint64_t k0 = 0, k1 = 0;
+    if (exact && r0 >= 0 && r1 >= 0) {
+      const RowBytes rb[2] = {h0 ? pb[0] : load_row_bytes(S.idx_rows, r0), h1 ? pb[1] : load_row_bytes(S.idx_rows, r1)};
+      float f[2];
+      exact_scores<2>(rb, H, sh, f);
+      k0 = make_key(f[0], (uint32_t)r0);
+      k1 = make_key(f[1], (uint32_t)r1);
+    } else {
+      if (r0 >= 0) k0 = make_key(score_of(r0, h0, pb[0]), (uint32_t)r0);
+      if (r1 >= 0) k1 = make_key(score_of(r1, h1, pb[1]), (uint32_t)r1);
+    }
+    if (lane == 0) {
+      if (i0 < n_items) items[i0] = k0;
+      if (i1 < n_items) items[i1] = k1;
+    }
   }
-  for (int64_t i = gw + (int64_t)nw * kRefPrefetch; i < n_items; i += nw) item(i, false, 0ull, pb[0]);
+  for (int64_t i = gw + (int64_t)nw * kRefPrefetch; i < n_items; i += nw) {
+    bool have;
+    const int64_t row = item_row(i, false, 0ull, have);
+    const uint64_t key = row >= 0 ? make_key(score_of(row, false, pb[0]), (uint32_t)row) : 0ull;
+    if (lane == 0) items[i] = key;
+  }
+  if (a.attn_q) {  // the attention query split share
+    uint4 *dst = a.attn_q + (size_t)sess * kAttnQVecs;
+    if (qt0 + tid < qt1) attn_q_store(qx, dst, qt0 + tid);
+    for (int t = qt0 + tid + kRefThreads; t < qt1; t += kRefThreads) attn_q_split_task(S.q_attn, a.n_attn_heads, dst, t);
+  }
 }
 
 hipError_t launch_refine(const RefineJob &job, hipStream_t st) {

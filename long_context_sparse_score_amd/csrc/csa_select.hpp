@@ -5,7 +5,9 @@
 // means "no key".  block_kth_largest() is an MSB-first radix select that
 // starts at the highest bit in which the candidate keys differ, uses 8-bit
 // digits with one LDS histogram per wave, and stops as soon as the keys
-// sharing the current prefix are exactly the ones still needed.
+// sharing the current prefix are exactly the ones still needed.  The
+// helpers communicate through LDS only (lds_sync): global loads a caller
+// has in flight stay in flight across their barriers.
 #pragma once
 
 #include "csa_device.hpp"
@@ -122,7 +124,7 @@ __device__ uint64_t block_kth_largest(KeyFn key, int count, int k, uint64_t lb, 
     cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
   }
   if (lane == 0) { sc.wmax[wave] = kmax; sc.wmin[wave] = kmin; sc.wcnt[wave] = cnt; }
-  __syncthreads();
+  lds_sync();
   if (tid == 0) {
     uint64_t M = 0, m = ~0ull;
     uint32_t c = 0;
@@ -133,10 +135,10 @@ __device__ uint64_t block_kth_largest(KeyFn key, int count, int k, uint64_t lb, 
     }
     sc.r_max = M; sc.r_min = m; sc.r_cnt = c;
   }
-  __syncthreads();
+  lds_sync();
   const uint32_t total = sc.r_cnt;
   const uint64_t gmax = sc.r_max, gmin = sc.r_min;
-  __syncthreads();
+  lds_sync();
   if (total <= (uint32_t)k) return lb;
   int hi = 63 - __clzll((long long)(gmax ^ gmin));  // keys are distinct: gmax != gmin
   uint64_t prefix = (hi == 63) ? 0ull : (gmax & ~((2ull << hi) - 1));
@@ -146,30 +148,30 @@ __device__ uint64_t block_kth_largest(KeyFn key, int count, int k, uint64_t lb, 
     const int shift = hi - width + 1;
     const uint64_t pmask = (hi == 63) ? 0ull : ~((2ull << hi) - 1);
     for (int i = tid; i < NW * 256; i += NT) (&sc.hist[0][0])[i] = 0;
-    __syncthreads();
+    lds_sync();
     for (int i = tid; i < count; i += NT) {
       const uint64_t x = key(i);
       if (x >= lb && (x & pmask) == prefix) atomicAdd(&sc.hist[wave][(uint32_t)(x >> shift) & 255u], 1u);
     }
-    __syncthreads();
+    lds_sync();
     for (int b = tid; b < 256; b += NT) {
       uint32_t s = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += sc.hist[w][b];
       sc.hist[0][b] = s;
     }
-    __syncthreads();
+    lds_sync();
     if (wave == 0) {
       uint32_t above;
       const int d = find_digit_wave(sc.hist[0], need, &above);
       if (lane == 0) { sc.digit = d; sc.above = above; sc.bin = sc.hist[0][d]; }
     }
-    __syncthreads();
+    lds_sync();
     const int d = sc.digit;
     need -= sc.above;
     prefix |= (uint64_t)d << shift;
     const bool done = (sc.bin == need);
-    __syncthreads();
+    lds_sync();
     if (done) return prefix > lb ? prefix : lb;
     hi = shift - 1;
   }
@@ -201,7 +203,7 @@ __device__ uint64_t block_kth_largest_reg(const uint64_t (&x)[KPT], int nj, int 
     cnt += (uint32_t)__shfl_xor((int)cnt, m, 64);
   }
   if (lane == 0) { sc.wmax[wave] = kmax; sc.wmin[wave] = kmin; sc.wcnt[wave] = cnt; }
-  __syncthreads();
+  lds_sync();
   uint64_t gmax = 0, gmin = ~0ull;
   uint32_t total = 0;
 #pragma unroll
@@ -211,7 +213,7 @@ __device__ uint64_t block_kth_largest_reg(const uint64_t (&x)[KPT], int nj, int 
     total += sc.wcnt[w];
   }
   if (total <= (uint32_t)k) {
-    __syncthreads();
+    lds_sync();
     return lb;
   }
   int hi = 63 - __clzll((long long)(gmax ^ gmin));
@@ -222,31 +224,31 @@ __device__ uint64_t block_kth_largest_reg(const uint64_t (&x)[KPT], int nj, int 
     const int shift = hi - width + 1;
     const uint64_t pmask = (hi == 63) ? 0ull : ~((2ull << hi) - 1);
     for (int i = tid; i < NW * 256; i += NT) (&sc.hist[0][0])[i] = 0;
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       if (j < nj && x[j] >= lb && x[j] != 0 && (x[j] & pmask) == prefix)
         atomicAdd(&sc.hist[wave][(uint32_t)(x[j] >> shift) & 255u], 1u);
     }
-    __syncthreads();
+    lds_sync();
     for (int b = tid; b < 256; b += NT) {
       uint32_t s = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += sc.hist[w][b];
       sc.hist[0][b] = s;
     }
-    __syncthreads();
+    lds_sync();
     if (wave == 0) {
       uint32_t above;
       const int d = find_digit_wave(sc.hist[0], need, &above);
       if (lane == 0) { sc.digit = d; sc.above = above; sc.bin = sc.hist[0][d]; }
     }
-    __syncthreads();
+    lds_sync();
     const int d = sc.digit;
     need -= sc.above;
     prefix |= (uint64_t)d << shift;
     const bool done = (sc.bin == need);
-    __syncthreads();
+    lds_sync();
     if (done) return prefix > lb ? prefix : lb;
     hi = shift - 1;
   }
@@ -291,7 +293,7 @@ __device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint
   // reads nothing of it); red_n is next written after the pass's atomics
   // and their barrier, which every thread reaches only after reading it here
   for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0;
-  __syncthreads();
+  lds_sync();
   uint32_t omin = ~0u, omax = 0;
   uint32_t total = 0;
 #pragma unroll
@@ -311,12 +313,12 @@ __device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint
     const int shift = hb > kBinBits - 1 ? hb - (kBinBits - 1) : 0;  // span >> shift < kBins
     if (!first) {
       for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0;
-      __syncthreads();
+      lds_sync();
     }
     visit([&](uint64_t x) __attribute__((always_inline)) {
       if (x >= lo && x <= hi) atomicAdd(&sh.hist[(uint32_t)((x - lo) >> shift)], 1u);
     });
-    __syncthreads();
+    lds_sync();
     const uint32_t need_here = need - above;
     // thread t owns the upper bin kBins-1-2t and the lower bin kBins-2-2t,
     // so "bins above" is a prefix over threads
@@ -325,7 +327,7 @@ __device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint
     const uint32_t s = h0 + h1;
     const uint32_t incl = wave_scan_u32(s, 0u, uadd);
     if (lane == 63) sh.red_n[wave] = incl;
-    __syncthreads();
+    lds_sync();
     uint32_t before = 0;
     for (int w = 0; w < wave; ++w) before += sh.red_n[w];
     const uint32_t X = incl - s + before;  // keys in bins above bu
@@ -334,13 +336,13 @@ __device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint
     } else if (X + h1 < need_here && need_here <= X + s) {
       sh.bin = bu - 1; sh.ca = X + h1; sh.cb = h0;
     }
-    __syncthreads();
+    lds_sync();
     const uint32_t b = sh.bin, ca = sh.ca, cb = sh.cb;
     const uint64_t gb = lo + ((uint64_t)b << shift);
     // (uniform; after the return nothing writes bin, ca, cb or the
     // histogram before another barrier)
     if (above + ca + cb <= target || shift == 0) return gb;
-    __syncthreads();  // every thread has read bin, ca, cb
+    lds_sync();  // every thread has read bin, ca, cb
     above += ca;
     const uint64_t top = gb + ((1ull << shift) - 1);
     lo = gb;
