@@ -49,6 +49,7 @@ class Oracle:
         L.csa_oracle_topk.argtypes = [vp, i64, i32, vp, vp]
         L.csa_oracle_attention.restype = i32
         L.csa_oracle_attention.argtypes = [vp, i64, vp, i32, vp, i32, dbl, vp, vp]
+        L.csa_oracle_quantize_query.argtypes = [vp, i32, vp]
         L.csa_oracle_decode_step.restype = i32
         L.csa_oracle_decode_step.argtypes = [vp, vp, i64, vp, vp, i32, vp, i32, dbl, i32, vp, vp, vp, vp]
         self.L = L
@@ -78,6 +79,20 @@ class Oracle:
         out = np.empty((rows.shape[0], 512), dtype=np.float32)
         self.L.csa_oracle_decode_kv_rows(_p(rows), rows.shape[0], _p(out))
         return out
+
+    # -- MXFP4 query
+    def quantize_query(self, q) -> np.ndarray:
+        """The query [h][128] quantized to MXFP4, packed as indexer rows [h][68]."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        assert q.ndim == 2 and q.shape[1] == 128
+        rows = np.empty((q.shape[0], 68), dtype=np.uint8)
+        self.L.csa_oracle_quantize_query(_p(q), q.shape[0], _p(rows))
+        return rows
+
+    def quantized_query(self, q) -> np.ndarray:
+        """The MXFP4 query decoded back to fp32 (the query the quantized-query
+        scorer scores with)."""
+        return self.decode_idx(self.quantize_query(q))
 
     # -- score / select / attend
     def score(self, idx_rows, q_idx, w_idx) -> np.ndarray:

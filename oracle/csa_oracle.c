@@ -25,6 +25,16 @@
  *    fusion").  A full sort is used.
  *  - Attention: textbook softmax attention over the selected rows, with the
  *    decoded 512-value row used as both key and value, in double.
+ *  - MXFP4 query (the block-scaled scorer of DS4X README, "What DS4X
+ *    changes" and "Optimization details"): the pages never say how the fp32
+ *    query becomes an MXFP4 operand.  The reading adopted is the OCP MX v1.0
+ *    conversion of a 32-value block (its section 6.3): shared exponent
+ *    floor(log2(max |v|)) - 2, 2 being E2M1's largest exponent, held in UE8M0
+ *    (clamped to its range; an all-zero block gets byte 0); each element
+ *    v / 2^shared rounded to the nearest E2M1 value, ties to the even
+ *    significand, magnitudes past 6 saturating to 6, the sign kept.  The
+ *    quantized query is packed exactly like an indexer row, and the
+ *    quantized-query score is the score above with the decoded query.
  */
 #include "csa_oracle.h"
 
@@ -205,6 +215,49 @@ int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *
   }
   free(kv); free(logit); free(acc);
   return 0;
+}
+
+/* ---------------- MXFP4 query quantization ---------------- */
+
+/* The E2M1 code nearest to y: the magnitude closest to |y| among the eight
+ * E2M1 values (so anything past 6 goes to 6), a tie going to the code with
+ * an even significand bit; the sign bit copied from y. */
+static int e2m1_nearest(double y) {
+  double a = fabs(y);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    double d = fabs(a - csa_oracle_e2m1(c));
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return signbit(y) ? (best | 8) : best;
+}
+
+void csa_oracle_quantize_query(const float *q, int n_heads, uint8_t *rows) {
+  for (int h = 0; h < n_heads; ++h) {
+    uint8_t *r = rows + (int64_t)h * IDX_ROW;
+    int code[128];
+    for (int b = 0; b < 4; ++b) {
+      const float *v = q + (int64_t)h * 128 + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+      int shared = -127; /* the all-zero block */
+      if (amax > 0.0) {
+        int e;
+        frexp(amax, &e); /* amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+        shared = (e - 1) - 2;
+        if (shared < -127) shared = -127;
+        if (shared > 127) shared = 127;
+      }
+      r[64 + b] = (uint8_t)(shared + 127);
+      for (int i = 0; i < 32; ++i) code[32 * b + i] = e2m1_nearest(ldexp((double)v[i], -shared));
+    }
+    for (int i = 0; i < 64; ++i) r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));
+  }
 }
 
 /* ---------------- whole decode step ---------------- */

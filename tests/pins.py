@@ -10,6 +10,9 @@ Independent references used here:
     ``torch.float8_e8m0fnu`` and ``numpy.float16`` (little-endian '<f2');
   * the E2M1 value table of the OCP MX v1.0 specification (golden file);
   * numbers printed on the DS4X page, "Packed cache ABI" (golden file);
+  * hand-worked MXFP4 conversions of query blocks from the OCP MX v1.0
+    definition (golden file) and a brute-force nearest-value search over the
+    E2M1 table;
   * numpy float64 ``einsum`` for the score, Python ``sorted`` for the top-k,
     ``torch.nn.functional.scaled_dot_product_attention`` in float64 on the CPU
     for attention, plus closed-form special cases.
@@ -315,4 +318,87 @@ def check_decode_step(o) -> None:
         assert np.allclose(got["lse"], ref_l, rtol=1e-6, atol=1e-6), "decode step lse"
 
 
-ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention, check_decode_step)
+# ------------------------------------------------------- MXFP4 query quantizer
+
+def fp4_query_golden() -> list:
+    """Blocks of tests/golden/ocp_mx_fp4_query_blocks.txt: (name, scale byte,
+    32 fp32 values, 32 codes)."""
+    blocks, cur = [], None
+    with open(os.path.join(GOLDEN, "ocp_mx_fp4_query_blocks.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            t = line.split()
+            if t[0] == "block":
+                cur = [t[1], int(t[2]), np.zeros(32, np.float32), np.zeros(32, np.int64)]
+                blocks.append(cur)
+            else:
+                i = int(t[0])
+                v = float.fromhex(t[1]) if "x" in t[1] else float(t[1])
+                cur[2][i] = np.float32(v)
+                cur[3][i] = int(t[2])
+    return blocks
+
+
+def unpack_codes(rows: np.ndarray) -> np.ndarray:
+    rows = np.asarray(rows, dtype=np.uint8).reshape(-1, 68)
+    codes = np.empty((rows.shape[0], 128), dtype=np.int64)
+    codes[:, 0::2] = rows[:, :64] & 15
+    codes[:, 1::2] = rows[:, :64] >> 4
+    return codes
+
+
+def brute_force_fp4(v: np.ndarray):
+    """The conversion by exhaustive search: for each block the exponent
+    floor(log2 amax) (math.frexp) - 2 clamped to [-127, 127] (zero block:
+    -127), for each element the E2M1 table entry at the least distance from
+    v / 2^e, ties to the entry with an even code, sign from v's sign bit."""
+    v = np.asarray(v, dtype=np.float32).reshape(-1, 32).astype(np.float64)
+    table = e2m1_golden()[:8]
+    codes = np.zeros(v.shape, dtype=np.int64)
+    byte = np.zeros(v.shape[0], dtype=np.int64)
+    for b in range(v.shape[0]):
+        amax = float(np.max(np.abs(v[b])))
+        e = -127 if amax == 0.0 else min(max(math.frexp(amax)[1] - 1 - 2, -127), 127)
+        byte[b] = e + 127
+        y = np.abs(v[b]) * 2.0 ** (-e)
+        dist = np.abs(y[:, None] - table[None, :])           # [32][8]
+        best = dist.min(axis=1, keepdims=True)
+        cand = dist == best
+        even = cand & (np.arange(8)[None, :] % 2 == 0)
+        mag = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+        codes[b] = mag | np.where(np.signbit(v[b]), 8, 0)
+    return byte, codes
+
+
+def check_quantize_query(o) -> None:
+    # the hand-worked blocks, each placed at every block position of a head
+    gold = fp4_query_golden()
+    for pos in range(4):
+        q = np.zeros((len(gold), 128), np.float32)
+        for i, (_, _, vals, _) in enumerate(gold):
+            q[i, 32 * pos:32 * pos + 32] = vals
+        rows = o.quantize_query(q)
+        codes = unpack_codes(rows)
+        for i, (name, byte, _, want) in enumerate(gold):
+            assert rows[i, 64 + pos] == byte, (name, pos, rows[i, 64 + pos], byte)
+            assert np.array_equal(codes[i, 32 * pos:32 * pos + 32], want), (name, pos)
+            other = [b for b in range(4) if b != pos]
+            assert np.all(rows[i, 64 + np.array(other)] == 0), (name, pos)  # zero blocks: byte 0
+    # random blocks over many binades against the exhaustive search
+    rng = np.random.default_rng(11)
+    q = (rng.standard_normal((16, 128)) * 2.0 ** rng.integers(-40, 40, (16, 128))).astype(np.float32)
+    q[3] = (rng.integers(-16, 17, 128) * 0.25).astype(np.float32)  # many exact ties
+    q[4, :32] = 0.0
+    rows = o.quantize_query(q)
+    byte, codes = brute_force_fp4(q)
+    assert np.array_equal(rows[:, 64:68].reshape(-1), byte)
+    assert np.array_equal(unpack_codes(rows).reshape(-1, 32), codes)
+    # the decoded query is a fixed point of the conversion
+    qhat = o.decode_idx(rows)
+    assert np.array_equal(o.quantize_query(qhat), rows)
+
+
+ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention, check_decode_step,
+              check_quantize_query)

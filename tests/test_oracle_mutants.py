@@ -45,6 +45,16 @@ MUTANTS = [
      "int64_t k_eff = csa_oracle_topk(scores, n_rows, k, sel, sel_score);\n  for (int64_t i = 0; i < k_eff; ++i) sel[i] = (int32_t)i;"),
     ("step_scale_dropped", "q_attn, n_heads, softmax_scale, out,\n                              lse);",
      "q_attn, n_heads, 1.0, out,\n                              lse);"),
+    ("q4_scale_offset", "shared = (e - 1) - 2;", "shared = (e - 1) - 1;"),
+    ("q4_ceil_log2", "shared = (e - 1) - 2;", "shared = e - 2;"),
+    ("q4_tie_odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    ("q4_tie_to_lower", "(d == best_d && (c & 1) == 0)", "(0)"),
+    ("q4_sign_dropped", "return signbit(y) ? (best | 8) : best;", "return (y < 0.0) ? (best | 8) : best;"),
+    ("q4_no_clamp", "if (shared < -127) shared = -127;", ""),
+    ("q4_zero_block_byte", "int shared = -127; /* the all-zero block */", "int shared = 0; /* the all-zero block */"),
+    ("q4_nibble_order", "r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));",
+     "r[i] = (uint8_t)((code[2 * i] << 4) | code[2 * i + 1]);"),
+    ("q4_scale_slot", "r[64 + b] = (uint8_t)(shared + 127);", "r[64 + (b + 1) % 4] = (uint8_t)(shared + 127);"),
 ]
 
 
