@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the per-history-length figures of the other workloads")
     p.add_argument("--sweep-steps", type=int, default=20)
+    p.add_argument("--no-fit", action="store_true", help="skip the fixed + marginal cost fit over history lengths")
     return p.parse_args()
 
 
@@ -85,6 +86,17 @@ def measured_traffic(workload: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_calibration(mib: int):
     import torch
 
@@ -107,17 +119,23 @@ def algorithmic_bytes(n_rows: int, n_idx_heads: int, n_heads: int) -> dict:
     return {"score": score, "attention": attn, "step": score + attn}
 
 
-def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host):
-    """Cold / warm / per-stage timing of `steps` decode steps of workload wl."""
+def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host, query_format="fp32", sess_np=None,
+            n_rows=None):
+    """Cold / warm / per-stage timing of `steps` decode steps of workload wl
+    (or of the first n_rows rows of the given host sessions)."""
     t0 = time.time()
-    sess_np = [gen.session(wl.cid, s=i) for i in range(wl.n_sessions)]
+    if sess_np is None:
+        sess_np = [gen.session(wl.cid, s=i) for i in range(wl.n_sessions)]
     sess = []
     for s in sess_np:
-        sess.append({k: torch.from_numpy(s[k]).to(dev) for k in ("idx_rows", "kv_rows", "q_idx", "w_idx", "q_attn")})
+        d = {k: torch.from_numpy(s[k]).to(dev) for k in ("q_idx", "w_idx", "q_attn")}
+        for k in ("idx_rows", "kv_rows"):
+            d[k] = torch.from_numpy(s[k][:n_rows] if n_rows is not None else s[k]).to(dev)
+        sess.append(d)
     scale = sess_np[0]["softmax_scale"]
-    print(f"[bench] workload {wl.name}: {wl.n_sessions} x {wl.n_rows} rows, generated in {time.time() - t0:.1f}s",
-          file=sys.stderr, flush=True)
-    step = csa.DecodeStep(sess, scale)
+    print(f"[bench] workload {wl.name}: {len(sess)} x {sess[0]['idx_rows'].shape[0]} rows ({query_format} query), "
+          f"ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    step = csa.DecodeStep(sess, scale, query_format=query_format)
     stream = torch.cuda.current_stream()
 
     def do_flush():
@@ -169,9 +187,42 @@ def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host):
         "stage_ms": stage_ms,
         "score_ms": stage_ms[0],  # the score kernel's launch
     }
+    if keep_host:
+        r["filter"] = filter_diagnostics(sess[0], step.sessions[0], csa, np, torch, query_format)
     del step, sess
     torch.cuda.synchronize()
     return (sess_np if keep_host else None), r
+
+
+def filter_diagnostics(d, outs, csa, np, torch, query_format):
+    """How much the matrix-core filter leaves to the exact rescoring, on
+    session 0 (outside the timed steps, library calls only): the brackets'
+    relative half-widths, the band (rows whose upper bound reaches the exact
+    512th score: the fewest rows any exact rescoring must visit) and the
+    largest relative error of the step's selected scores against csa_score's
+    exact scores of the same rows."""
+    q = d["q_idx"]
+    if query_format == "mxfp4":
+        q = csa.dequant_idx(csa.quantize_query(q))
+    up, lo = csa.score_bounds(d["idx_rows"], d["q_idx"], d["w_idx"], query_format=query_format)
+    exact = csa.score(d["idx_rows"], q, d["w_idx"])
+    torch.cuda.synchronize()
+    up, lo, ex = up.cpu().numpy().astype(np.float64), lo.cpu().numpy().astype(np.float64), exact.cpu().numpy()
+    k_eff = min(512, ex.shape[0])
+    sel = outs["sel"].cpu().numpy()[:k_eff]
+    sel_score = outs["sel_score"].cpu().numpy()[:k_eff].astype(np.float64)
+    fin = np.isfinite(up) & np.isfinite(lo) & (ex != 0)
+    half = (up - lo)[fin] / 2.0 / np.abs(ex[fin].astype(np.float64))
+    T = float(np.sort(ex)[::-1][k_eff - 1]) if k_eff else float("inf")
+    ref = ex[sel].astype(np.float64)
+    err = np.abs(sel_score - ref) / np.maximum(np.abs(ref), 1e-30) if k_eff else np.zeros(1)
+    return {
+        "rows": int(ex.shape[0]),
+        "median_rel_bracket_halfwidth": float(np.median(half)) if half.size else 0.0,
+        "max_rel_bracket_halfwidth": float(np.max(half)) if half.size else 0.0,
+        "band_rows": int(np.sum(up >= T)),
+        "sel_score_max_rel_err": float(np.max(err)),
+    }
 
 
 def main():
@@ -198,6 +249,9 @@ def main():
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB: evicts the MALL and the L2s
 
     sess_np, r = measure(wl, a.steps, a.warmup, flush, dev, csa, gen, np, torch, keep_host=True)
+    # the MXFP4-quantized-query scorer on the same data
+    _, r_q4 = measure(wl, a.sweep_steps, 2, flush, dev, csa, gen, np, torch, keep_host=True, query_format="mxfp4",
+                      sess_np=sess_np)
     scale = sess_np[0]["softmax_scale"]
     ab = algorithmic_bytes(wl.n_rows, wl.n_idx_heads, wl.n_heads)
     ms = r["mean_ms"]
@@ -233,6 +287,14 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2),
         "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, r["stage_ms"])},
+        "filter": r["filter"],
+        "mxfp4_query": {
+            "cold_median_ms": round(r_q4["median_ms"], 5),
+            "warm_ms": round(r_q4["warm_ms"], 5),
+            "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, r_q4["stage_ms"])},
+            "score_kernel_hbm_frac": round(ab["score"] * wl.n_sessions / (r_q4["score_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+            "filter": r_q4["filter"],
+        },
         "roofline": {
             "kernel": "tile_kernel: query split + score + tile heads (all sessions, one launch)",
             "bound": "hbm",
@@ -245,6 +307,29 @@ def main():
             "algorithmic_bytes_per_launch": ab["score"] * wl.n_sessions,
         },
     }
+
+    if not a.no_fit and wl.n_sessions == 1:
+        # fixed + marginal cost: cold step time over history prefixes of
+        # 2^11 .. 2^20 rows of the same session, least squares ms = a + b MB
+        pts = []
+        for lg in range(11, 21):
+            n = 1 << lg
+            if n > wl.n_rows:
+                break
+            _, rf = measure(wl, a.sweep_steps, 2, flush, dev, csa, gen, np, torch, keep_host=False,
+                            sess_np=sess_np[:1], n_rows=n)
+            mb = algorithmic_bytes(n, wl.n_idx_heads, wl.n_heads)["step"] / 1e6
+            pts.append((n, mb, rf["median_ms"]))
+        x = np.array([p[1] for p in pts])
+        y = np.array([p[2] for p in pts])
+        b, a0 = np.polyfit(x, y, 1)
+        line["cost_fit"] = {
+            "model": "cold step ms = fixed_ms + ms_per_mb * algorithmic MB",
+            "fixed_ms": round(float(a0), 5),
+            "ms_per_mb": round(float(b), 7),
+            "marginal_gbs": round(1.0 / float(b), 1) if b > 0 else None,  # MB per ms = GB/s
+            "points": [{"rows": n, "mb": round(mb, 3), "ms": round(ms, 5)} for n, mb, ms in pts],
+        }
 
     if not a.no_sweep:
         # every history length of the workload set: cold step latency, the
@@ -287,6 +372,8 @@ def main():
             "value": round(per_session_ms * wl.n_sessions, 3),
             "unit": "ms",
             "cores": 1,
+            "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
             "kind": "oracle",
             "sample": f"{reps} decode steps of session 0 over its first {n} rows "
                       f"({dt:.2f} s measured), mean scaled by rows x sessions to the whole workload",

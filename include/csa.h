@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1u
+#define CSA_ABI_VERSION 2u
 
 /* Indexer row (DS4X page, "Packed cache ABI"): 128 E2M1 codes, two per byte,
  * element 2i in the low nibble (64 B), then 4 UE8M0 scales, scale b covering
@@ -51,6 +51,13 @@ extern "C" {
 #define CSA_KV_ROW_BYTES 583
 #define CSA_KV_DIM 512
 #define CSA_KV_NOPE 448
+/* Indexer query formats of the decode step.  CSA_QUERY_FP32 scores the fp32
+ * query as given.  CSA_QUERY_MXFP4 scores the query quantized to MXFP4
+ * (csa_quantize_query), the block-scaled MXFP4 scorer of the DS4X page ("What
+ * DS4X changes", "Optimization details"): every score is then that of the
+ * decoded quantized query, computed exactly as csa_score does. */
+#define CSA_QUERY_FP32 0
+#define CSA_QUERY_MXFP4 1
 /* Rows kept by the selection. */
 #define CSA_TOPK 512
 /* Limits checked by every entry point. */
@@ -143,8 +150,10 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
 int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream);
 
-/* Stages of csa_decode_step, in launch order. */
-#define CSA_STAGES 3 /* 0 filter score + tile heads + exact rescoring of the candidates, 1 select + attention partials, 2 merge */
+/* Stages of csa_decode_step, in launch order: 0 filter score + tile heads,
+ * 1 exact rescoring of the candidates, 2 selection + attention partials,
+ * 3 merge of the partials. */
+#define CSA_STAGES 4
 
 /* csa_decode_step that also records events[2*s] right before and
  * events[2*s+1] right after the launches of stage s on hip_stream, so a
@@ -154,6 +163,30 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
 int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                           float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
                           void *const *events);
+
+/* csa_decode_step with a choice of indexer query format (CSA_QUERY_FP32 or
+ * CSA_QUERY_MXFP4; any other value gives CSA_EINVAL) and optional stage
+ * events (NULL, or 2*CSA_STAGES events as for csa_decode_step_timed).  With
+ * CSA_QUERY_MXFP4 each session's q_idx is quantized as csa_quantize_query
+ * does, and the selection is the exact top-512 of csa_score over the decoded
+ * quantized query (csa_dequant_idx of csa_quantize_query's rows): selections
+ * and sel_score are bit-identical to csa_quantize_query -> csa_dequant_idx ->
+ * csa_score -> csa_topk(k = 512).  The attention is unchanged.  Other
+ * arguments and rules as csa_decode_step. */
+int csa_decode_step_ex(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                       float softmax_scale, int query_format, void *ws, size_t ws_bytes, void *hip_stream,
+                       void *const *events);
+
+/* MXFP4 quantization of an indexer query q_idx [n_idx_heads][128] (device,
+ * 16-byte aligned) into q_rows [n_idx_heads][68] (device, 4-byte aligned),
+ * packed like indexer rows.  The pages do not say how their MXFP4 scorer
+ * quantizes the query; this is the OCP MX v1.0 conversion of each 32-value
+ * block: the UE8M0 byte is floor(log2 max|v|) - 2 + 127, clamped at 0 (0 for
+ * an all-zero block), and each element is v / 2^(byte-127) rounded to the
+ * nearest E2M1 value, ties to the even code, magnitudes past 6 saturating
+ * to 6, sign kept (a negative value that rounds to zero gives -0).  Inputs
+ * must be finite.  n_idx_heads in [1, 64]. */
+int csa_quantize_query(const float *q_idx, int n_idx_heads, uint8_t *q_rows, void *hip_stream);
 
 /* Bytes of the library's static per-device workspace (csa_decode_step_noalloc). */
 #define CSA_SCRATCH_BYTES (32u << 20)
@@ -175,14 +208,17 @@ int csa_decode_step_noalloc(const csa_session *sessions, int n_sessions, int n_i
                             float softmax_scale, void *hip_stream);
 
 /* Test entry point: the decode step's matrix-core filter.  For every row,
- * lower[j] <= scores[j] <= upper[j], scores as csa_score computes them: the
- * filter scores the row with the query held to three fp6 terms per 32-value
- * block on the block-scaled matrix cores and brackets the exact score by a
- * rigorous bound from the query's residual and term magnitudes, the head
- * weights and the row's four UE8M0 bytes (a byte >= 253 gives an infinite
- * bracket).  Same arguments and rules as csa_score. */
+ * lower[j] <= scores[j] <= upper[j], scores as csa_score computes them (with
+ * CSA_QUERY_MXFP4: over the decoded quantized query).  The filter scores the
+ * row on the block-scaled matrix cores, with the query held to three fp6
+ * terms per 32-value block (CSA_QUERY_FP32) or as its one MXFP4 operand, and
+ * brackets the exact score by a rigorous bound from the query's residual and
+ * term magnitudes, the head weights and the row's four UE8M0 bytes (a byte
+ * >= 253 gives an infinite bracket).  Same arguments and rules as csa_score;
+ * query_format as for csa_decode_step_ex. */
 int csa_score_bounds(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
-                     int n_idx_heads, float *upper, float *lower, void *ws, size_t ws_bytes, void *hip_stream);
+                     int n_idx_heads, int query_format, float *upper, float *lower, void *ws, size_t ws_bytes,
+                     void *hip_stream);
 
 /* Test entry points: decode packed rows to fp32, [n][128] and [n][512]
  * (exact products; overflow gives +-inf; a 0xFF scale or an E4M3 NaN code

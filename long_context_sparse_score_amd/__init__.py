@@ -23,8 +23,9 @@ KV_DIM = 512
 TOPK = 512
 MAX_HEADS = 64
 MAX_SESSIONS = 64
-ABI_VERSION = 1
-STAGES = ("filter + tile heads + exact rescoring", "select + attention", "merge")
+ABI_VERSION = 2
+STAGES = ("filter score + tile heads", "exact rescoring", "select + attention", "merge")
+QUERY_FORMATS = {"fp32": 0, "mxfp4": 1}  # CSA_QUERY_FP32, CSA_QUERY_MXFP4
 
 OK, EINVAL, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4
 SCRATCH_BYTES = 32 << 20  # CSA_SCRATCH_BYTES: the static workspace of csa_decode_step_noalloc
@@ -68,7 +69,11 @@ def _load() -> ctypes.CDLL:
     L.csa_score.restype = i32
     L.csa_score.argtypes = [vp, i64, vp, vp, i32, vp, vp, sz, vp]
     L.csa_score_bounds.restype = i32
-    L.csa_score_bounds.argtypes = [vp, i64, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.csa_score_bounds.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.csa_quantize_query.restype = i32
+    L.csa_quantize_query.argtypes = [vp, i32, vp, vp]
+    L.csa_decode_step_ex.restype = i32
+    L.csa_decode_step_ex.argtypes = [ctypes.POINTER(Session), i32, i32, i32, f32, i32, vp, sz, vp, vp]
     L.csa_topk.restype = i32
     L.csa_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
     L.csa_sparse_attn.restype = i32
@@ -167,10 +172,18 @@ def score(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, scor
     return scores
 
 
+def _format(query_format: str) -> int:
+    if query_format not in QUERY_FORMATS:
+        raise ValueError(f"query_format: one of {sorted(QUERY_FORMATS)}, got {query_format!r}")
+    return QUERY_FORMATS[query_format]
+
+
 def score_bounds(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, ws: torch.Tensor | None = None,
-                 stream=None):
+                 stream=None, query_format: str = "fp32"):
     """The decode step's filter: (upper, lower) with lower <= score <= upper
-    for every row (csa_score_bounds)."""
+    for every row (csa_score_bounds; with query_format="mxfp4" the score of
+    the quantized query)."""
+    fmt = _format(query_format)
     n = _rows(idx_rows, IDX_ROW_BYTES, "idx_rows")
     h = _mat(q_idx, IDX_DIM, "q_idx")
     _vec(w_idx, h, "w_idx")
@@ -179,9 +192,19 @@ def score_bounds(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tenso
     if ws is None:
         ws = alloc_workspace(n, 1, idx_rows.device)
     _check(lib.csa_score_bounds(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(q_idx, torch.float32, "q_idx"),
-                                _ptr(w_idx, torch.float32, "w_idx"), h, _ptr(up), _ptr(lo),
+                                _ptr(w_idx, torch.float32, "w_idx"), h, fmt, _ptr(up), _ptr(lo),
                                 _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_score_bounds")
     return up, lo
+
+
+def quantize_query(q_idx: torch.Tensor, stream=None) -> torch.Tensor:
+    """The indexer query [h][128] quantized to MXFP4, packed as rows [h][68]
+    (csa_quantize_query)."""
+    h = _mat(q_idx, IDX_DIM, "q_idx")
+    rows = torch.empty((h, IDX_ROW_BYTES), dtype=torch.uint8, device=q_idx.device)
+    _check(lib.csa_quantize_query(_ptr(q_idx, torch.float32, "q_idx"), h, _ptr(rows, torch.uint8), _stream(stream)),
+           "csa_quantize_query")
+    return rows
 
 
 def topk(scores: torch.Tensor, k: int = TOPK, ws: torch.Tensor | None = None, stream=None):
@@ -224,10 +247,12 @@ class DecodeStep:
     one decode step of every session on the current stream.  With
     ``noalloc=True`` no workspace is allocated and ``__call__`` runs
     csa_decode_step_noalloc (the library's static per-device workspace).
+    ``query_format="mxfp4"`` scores the MXFP4-quantized indexer query
+    (csa_decode_step_ex).
     """
 
     def __init__(self, sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None,
-                 noalloc: bool = False):
+                 noalloc: bool = False, query_format: str = "fp32"):
         if not 1 <= len(sessions) <= MAX_SESSIONS:
             raise ValueError("1..64 sessions")
         self.sessions = list(sessions)
@@ -237,6 +262,9 @@ class DecodeStep:
             raise ValueError("1..64 indexer and attention heads")
         self.softmax_scale = float(softmax_scale)
         self.noalloc = bool(noalloc)
+        self.query_format = _format(query_format)
+        if self.noalloc and self.query_format != QUERY_FORMATS["fp32"]:
+            raise ValueError("the no-allocation entry point scores the fp32 query only")
         dev = sessions[0]["q_attn"].device
         max_rows = max(_rows(s["idx_rows"], IDX_ROW_BYTES, "idx_rows") for s in sessions)
         if self.noalloc:
@@ -271,6 +299,11 @@ class DecodeStep:
             _check(lib.csa_decode_step_noalloc(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads,
                                                self.softmax_scale, _stream(stream)), "csa_decode_step_noalloc")
             return
+        if self.query_format != QUERY_FORMATS["fp32"]:
+            _check(lib.csa_decode_step_ex(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads,
+                                          self.softmax_scale, self.query_format, _ptr(self.ws, torch.uint8, "ws"),
+                                          self.ws.numel(), _stream(stream), None), "csa_decode_step_ex")
+            return
         _check(lib.csa_decode_step(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads, self.softmax_scale,
                                    _ptr(self.ws, torch.uint8, "ws"), self.ws.numel(), _stream(stream)),
                "csa_decode_step")
@@ -286,14 +319,15 @@ class DecodeStep:
             if not e.cuda_event:  # torch creates the HIP event on its first record
                 e.record()
         handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
-        _check(lib.csa_decode_step_timed(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads,
-                                         self.softmax_scale, _ptr(self.ws, torch.uint8, "ws"), self.ws.numel(),
-                                         _stream(stream), handles), "csa_decode_step_timed")
+        _check(lib.csa_decode_step_ex(self._arr, len(self.sessions), self.n_idx_heads, self.n_heads,
+                                      self.softmax_scale, self.query_format, _ptr(self.ws, torch.uint8, "ws"),
+                                      self.ws.numel(), _stream(stream), handles), "csa_decode_step_ex")
 
 
-def decode_step(sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None, stream=None):
+def decode_step(sessions: Sequence[dict], softmax_scale: float, ws: torch.Tensor | None = None, stream=None,
+                query_format: str = "fp32"):
     """One decode step over ``sessions`` (see DecodeStep); returns the session dicts with outputs."""
-    step = DecodeStep(sessions, softmax_scale, ws)
+    step = DecodeStep(sessions, softmax_scale, ws, query_format=query_format)
     step(stream)
     return step.sessions
 

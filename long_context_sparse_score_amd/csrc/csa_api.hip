@@ -22,6 +22,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // smallest tile so that it grows monotonically with max_rows:
 //   [attention query split][head keys][head lower-bound keys][tile next keys]
 //   [items][item counts][attention partials][attention (m, l)]
+//   [quantized indexer query, fp32]
 // The items hold the exact keys of the rows that can reach the top-k: the
 // head slots plus, for the rare tiles whose other rows may also reach it,
 // every row of those tiles (at most every row of the session).
@@ -29,7 +30,7 @@ struct Layout {
   int64_t tiles_cap;  // tiles per session at the smallest tile size
   int64_t heads_cap;  // head slots per session
   int64_t items_cap;  // items per session
-  size_t attn_q_off, hkey_off, hlow_off, hnext_off, items_off, count_off, part_off, ml_off, total;
+  size_t attn_q_off, hkey_off, hlow_off, hnext_off, items_off, count_off, part_off, ml_off, qhat_off, total;
 };
 
 Layout make_layout(int64_t max_rows, int n_sessions) {
@@ -46,7 +47,8 @@ Layout make_layout(int64_t max_rows, int n_sessions) {
   L.count_off = L.items_off + align_up(ns * (size_t)(L.items_cap > 0 ? L.items_cap : 1) * sizeof(uint64_t));
   L.part_off = L.count_off + align_up(ns * sizeof(uint32_t));
   L.ml_off = L.part_off + align_up(ns * kAttnPartFloats * sizeof(float));
-  L.total = L.ml_off + align_up(ns * kAttnMlFloats * sizeof(float));
+  L.qhat_off = L.ml_off + align_up(ns * kAttnMlFloats * sizeof(float));
+  L.total = L.qhat_off + align_up(ns * (size_t)CSA_MAX_HEADS * 128 * sizeof(float));
   return L;
 }
 
@@ -119,6 +121,7 @@ void *scratch_ptr() {
 }
 
 bool rows_ok(int64_t n) { return n >= 0 && n <= CSA_MAX_ROWS; }
+bool format_ok(int f) { return f == CSA_QUERY_FP32 || f == CSA_QUERY_MXFP4; }
 bool heads_ok(int h) { return h >= 1 && h <= CSA_MAX_HEADS; }
 // The scorer streams indexer rows with 16-byte loads.
 bool idx_aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -142,6 +145,8 @@ void fill_job(TileJob &job, const Layout &L, void *ws, int n_sessions) {
   job.heads_stride = L.heads_cap;
   job.tiles_stride = L.tiles_cap;
   job.bnd_up = job.bnd_lo = nullptr;
+  job.query_format = kQueryFp32;
+  job.qhat = nullptr;
   int64_t total = 0;
   for (int i = 0; i < n_sessions; ++i) total += job.n_rows[i];
   job.tile_rows = choose_tile_rows(total);
@@ -269,8 +274,11 @@ int csa_score(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const
 }
 
 int csa_score_bounds(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
-                     int n_idx_heads, float *upper, float *lower, void *ws, size_t ws_bytes, void *hip_stream) {
-  if (!rows_ok(n_rows) || !heads_ok(n_idx_heads) || !q_idx || !w_idx || !idx_aligned(q_idx)) return CSA_EINVAL;
+                     int n_idx_heads, int query_format, float *upper, float *lower, void *ws, size_t ws_bytes,
+                     void *hip_stream) {
+  if (!rows_ok(n_rows) || !heads_ok(n_idx_heads) || !q_idx || !w_idx || !idx_aligned(q_idx) ||
+      !format_ok(query_format))
+    return CSA_EINVAL;
   if (n_rows > 0 && (!idx_rows || !upper || !lower || !idx_aligned(idx_rows))) return CSA_EINVAL;
   Layout L;
   int rc = check_ws(ws, ws_bytes, n_rows, 1, &L);
@@ -288,6 +296,7 @@ int csa_score_bounds(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx
   fill_job(job, L, ws, 1);
   job.bnd_up = upper;
   job.bnd_lo = lower;
+  job.query_format = query_format == CSA_QUERY_MXFP4 ? kQueryMxfp4 : kQueryFp32;
   if (n_rows == 0) return CSA_OK;
   return status_of(launch_tiles(job, (hipStream_t)hip_stream));
 }
@@ -344,10 +353,10 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
 }
 
 static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
-                            float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
+                            float softmax_scale, int query_format, void *ws, size_t ws_bytes, void *hip_stream,
                             void *const *events) {
   if (!sessions || n_sessions < 1 || n_sessions > CSA_MAX_SESSIONS || !heads_ok(n_idx_heads) ||
-      !heads_ok(n_heads))
+      !heads_ok(n_heads) || !format_ok(query_format))
     return CSA_EINVAL;
   int64_t max_rows = 0;
   for (int i = 0; i < n_sessions; ++i) {
@@ -387,6 +396,13 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   float *part = at<float>(ws, L.part_off), *ml = at<float>(ws, L.ml_off);
   RefineJob rj;
   fill_refine(rj, job, L, ws, CSA_TOPK);
+  if (query_format == CSA_QUERY_MXFP4) {
+    // the score kernel quantizes the query and keeps it (fp32) for the
+    // exact rescoring, which then scores with the quantized query
+    job.query_format = kQueryMxfp4;
+    job.qhat = at<float>(ws, L.qhat_off);
+    for (int i = 0; i < n_sessions; ++i) rj.q[i] = job.qhat + (size_t)i * CSA_MAX_HEADS * 128;
+  }
   rj.attn_q = aq;  // the attention query is split by the rescoring's workgroups
   rj.n_attn_heads = n_heads;
   for (int i = 0; i < n_sessions; ++i) rj.q_attn[i] = sessions[i].q_attn;
@@ -420,23 +436,43 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   };
   hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_tiles(job, st);
-  if (e == hipSuccess && any_rows) e = launch_refine(rj, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess && any_rows) e = launch_refine(rj, st);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = launch_select(sj, st);
   if (e == hipSuccess && !fused_attn)
     e = launch_attn_rows(at_s, n_sessions, n_heads, softmax_scale, aq, part, ml, groups_lg, st);
-  if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess) e = launch_attn_combine(at_s, n_sessions, n_heads, part, ml, groups_lg, st);
   if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(6);
+  if (e == hipSuccess) e = launch_attn_combine(at_s, n_sessions, n_heads, part, ml, groups_lg, st);
+  if (e == hipSuccess) e = mark(7);
   return status_of(e);
 }
 
 int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                     float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream) {
-  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, ws_bytes, hip_stream,
-                          nullptr);
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, CSA_QUERY_FP32, ws, ws_bytes,
+                          hip_stream, nullptr);
+}
+
+int csa_decode_step_ex(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
+                       float softmax_scale, int query_format, void *ws, size_t ws_bytes, void *hip_stream,
+                       void *const *events) {
+  if (events)
+    for (int i = 0; i < 2 * CSA_STAGES; ++i)
+      if (!events[i]) return CSA_EINVAL;
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, query_format, ws, ws_bytes,
+                          hip_stream, events);
+}
+
+int csa_quantize_query(const float *q_idx, int n_idx_heads, uint8_t *q_rows, void *hip_stream) {
+  if (!heads_ok(n_idx_heads) || !q_idx || !q_rows || !idx_aligned(q_idx) || ((uintptr_t)q_rows & 3u) != 0)
+    return CSA_EINVAL;
+  int rc = check_device();
+  if (rc != CSA_OK) return rc;
+  return status_of(launch_quantize_query(q_idx, n_idx_heads, q_rows, (hipStream_t)hip_stream));
 }
 
 int csa_decode_step_noalloc(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
@@ -454,8 +490,8 @@ int csa_decode_step_noalloc(const csa_session *sessions, int n_sessions, int n_i
   if (rc != CSA_OK) return rc;
   void *ws = scratch_ptr();
   if (ws == nullptr) return CSA_EDEVICE;
-  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, CSA_SCRATCH_BYTES,
-                          hip_stream, nullptr);
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, CSA_QUERY_FP32, ws,
+                          CSA_SCRATCH_BYTES, hip_stream, nullptr);
 }
 
 int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
@@ -464,8 +500,8 @@ int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx
   if (!events) return CSA_EINVAL;
   for (int i = 0; i < 2 * CSA_STAGES; ++i)
     if (!events[i]) return CSA_EINVAL;
-  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, ws, ws_bytes, hip_stream,
-                          events);
+  return decode_step_impl(sessions, n_sessions, n_idx_heads, n_heads, softmax_scale, CSA_QUERY_FP32, ws, ws_bytes,
+                          hip_stream, events);
 }
 
 }  // extern "C"

@@ -5,9 +5,11 @@
 // block-scaled matrix cores as they are stored, and the attention converts
 // E4M3 codes with gfx950's fp8 conversion and applies the block scales as
 // exact powers of two (csa_attn.hpp); that path is pinned bit for bit by the
-// single-row attention tests.
+// single-row attention tests.  csa_quantize_query's kernel is the
+// quantizer the score kernel runs on its query fragments (csa_score.hpp).
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
+#include "csa_score.hpp"
 
 namespace csa {
 
@@ -42,6 +44,36 @@ __global__ void __launch_bounds__(256) dequant_kv_kernel(const uint8_t *__restri
     }
     out[t] = v;
   }
+}
+
+// One thread per (head, 32-value block): the block quantized to MXFP4 and
+// stored as the codes and scale byte of a 68-byte row.
+__global__ void __launch_bounds__(256) quantize_query_kernel(const float *__restrict__ q, int n_heads,
+                                                             uint8_t *__restrict__ rows) {
+  const int t = threadIdx.x, h = t >> 2, b = t & 3;
+  if (h >= n_heads) return;
+  const float4 *src = reinterpret_cast<const float4 *>(q + (size_t)h * 128 + 32 * b);
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = src[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+  QFrag<1> f;
+  float deq[32];
+  quantize_qfrag_fp4(f, x, deq);
+  uint32_t *dst = reinterpret_cast<uint32_t *>(rows + (size_t)h * kIdxRowBytes + 16 * b);  // 4-byte aligned
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = (uint32_t)f.a[0][0][i];
+  rows[(size_t)h * kIdxRowBytes + 64 + b] = (uint8_t)f.scw[0][0];
+}
+
+hipError_t launch_quantize_query(const float *q, int n_heads, uint8_t *rows, hipStream_t st) {
+  quantize_query_kernel<<<1, 256, 0, st>>>(q, n_heads, rows);
+  return hipGetLastError();
 }
 
 static unsigned grid_for(int64_t total) {

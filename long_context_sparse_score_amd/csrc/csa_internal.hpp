@@ -49,6 +49,8 @@ struct TileJob {
   uint64_t *hnext;  // [session][tiles_stride]: per tile its (hd+1)-th key
   int64_t heads_stride, tiles_stride;
   float *bnd_up, *bnd_lo;  // kBounds: the brackets of every row (one session)
+  int query_format;        // kQueryFp32 or kQueryMxfp4 (csa_score.hpp)
+  float *qhat;             // kQueryMxfp4: the quantized query of every session, [session][64][128] (or null)
 };
 
 // One launch of the exact rescoring (csa_refine.hip).
@@ -114,6 +116,8 @@ struct AttnSession {
 
 hipError_t launch_dequant_idx(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
 hipError_t launch_dequant_kv(const uint8_t *rows, int64_t n, float *out, hipStream_t st);
+// MXFP4 quantization of an indexer query [n_heads][128] into rows [n_heads][68].
+hipError_t launch_quantize_query(const float *q, int n_heads, uint8_t *rows, hipStream_t st);
 // Attention query split of every session (csa_qsplit.hip): q_attn[i] ->
 // attn_out + i * kAttnQVecs.
 hipError_t launch_attn_q_split(const float *const *q_attn, int n_sessions, int n_attn_heads, uint4 *attn_out,

@@ -43,6 +43,17 @@ constexpr int kFmtFp4 = 4;       // E2M1
 
 constexpr int kScaleWords = (kTerms + 3) / 4;  // A scale bytes packed four per register
 
+// Query formats: kQueryFp32 scores the fp32 query through its kTerms fp6
+// terms; kQueryMxfp4 first quantizes it to MXFP4 (quantize_qfrag_fp4) and
+// scores the quantized query exactly as one fp4 operand.
+constexpr int kQueryFp32 = 0;
+constexpr int kQueryMxfp4 = 1;
+template <int QF>
+struct QueryFormat {
+  static constexpr int terms = QF == kQueryMxfp4 ? 1 : kTerms;
+  static constexpr int fmt = QF == kQueryMxfp4 ? kFmtFp4 : kFmtFp6;
+};
+
 template <int G>
 struct QFrag {
   v8i a[G][kTerms];
@@ -121,6 +132,55 @@ __device__ __forceinline__ QFragNorms split_qfrag(QFrag<1> &q, const float (&x)[
   return QFragNorms{rho, mag + rho};
 }
 
+// E2M1 code of y (the rounding of an MXFP4 conversion): the magnitude code
+// of the E2M1 value nearest to |y|, ties to the even code (0 | 0.5 -> 0,
+// 0.5 | 1 -> 1, 1 | 1.5 -> 1, 1.5 | 2 -> 2, 2 | 3 -> 2, 3 | 4 -> 4, 4 | 6 -> 4),
+// past 6 saturating to 6 (code 7), with y's sign bit as bit 3.
+__device__ __forceinline__ uint32_t e2m1_round(float y) {
+  const float a = fabsf(y);
+  uint32_t c = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) + (a >= 1.75f ? 1u : 0u) +
+               (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) + (a > 5.0f ? 1u : 0u);
+  return c | ((__float_as_uint(y) >> 31) << 3);
+}
+
+// This lane's query fragment (the same 32 values as split_qfrag's) quantized
+// to MXFP4 by the OCP MX v1.0 conversion: the block's UE8M0 byte is
+// floor(log2 max|x|) - 2 + 127, clamped at 0 (fp32 exponent field minus 2;
+// an all-zero block gets 0), and element i is e2m1_round(x_i / 2^(byte-127))
+// (the division is an exact power-of-two multiply except where the quotient
+// is far below 0.25 and rounds to a signed zero either way).  The codes are
+// the single fp4 A operand (value i at bit 4i) and its scale byte; deq gets
+// the quantized values (exact in fp32) and the norms are rho = 0 (the
+// quantized query is scored exactly) and mag = sum |deq|.
+__device__ __forceinline__ QFragNorms quantize_qfrag_fp4(QFrag<1> &q, const float (&x)[32], float (&deq)[32]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const uint32_t ef = __float_as_uint(amax) >> 23;  // amax >= 0: the exponent field
+  const uint32_t byte = ef >= 2u ? ef - 2u : 0u;
+  // 2^(127 - byte) and 2^(byte - 127) as fp32: byte <= 252, so both are
+  // normal except 2^-127 for byte 0, the subnormal 0x00400000
+  const float inv = __uint_as_float((254u - byte) << 23);
+  const float sc = byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  float mag = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = e2m1_round(x[i] * inv);
+    w[i / 8] |= c << (4 * (i % 8));
+    const float v = e2m1_value(c) * sc;
+    deq[i] = v;
+    mag += fabsf(v);
+  }
+#pragma unroll
+  for (int t = 0; t < kTerms; ++t) q.a[0][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  q.a[0][0] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kScaleWords; ++j) q.scw[0][j] = 0;
+  q.scw[0][0] = (int)byte;
+  return QFragNorms{0.0f, mag};
+}
+
 // The weights of the heads whose results lane `lane` holds for group g:
 // heads 16 g + 4(l/16) + v, v < 4 (0 past n_heads).
 __device__ __forceinline__ void load_qweights(QFrag<1> &q, const float *wh, int n_heads, int g, int lane) {
@@ -145,29 +205,30 @@ __device__ __forceinline__ v8i as_b(const RowOperand &o) {
 // group g) x (row operand s).  Issued term-major so that NS*G independent
 // accumulation chains are in flight; the op_sel immediate picks term t's
 // scale byte out of its packed register.
-template <int G, int NS, int T>
+template <int G, int NS, int T, int FA>
 __device__ __forceinline__ void mfma_term(const QFrag<G> &q, const v8i (&b)[NS], const int (&sb)[NS],
                                           v4f (&c)[NS][G]) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
     for (int r = 0; r < NS; ++r)
-      c[r][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[g][T], b[r], c[r][g], kFmtFp6, kFmtFp4, T % 4,
+      c[r][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[g][T], b[r], c[r][g], FA, kFmtFp4, T % 4,
                                                                   q.scw[g][T / 4], 0, sb[r]);
   }
 }
 
-template <int G, int NS, int... Ts>
+template <int G, int NS, int FA, int... Ts>
 __device__ __forceinline__ void mfma_terms(const QFrag<G> &q, const v8i (&b)[NS], const int (&sb)[NS],
                                            v4f (&c)[NS][G], std::integer_sequence<int, Ts...>) {
-  (mfma_term<G, NS, Ts>(q, b, sb, c), ...);
+  (mfma_term<G, NS, Ts, FA>(q, b, sb, c), ...);
 }
 
-// The kTerms matrix-core products of NS row operands with one 16-head
-// group's query: c[r] = sum over terms t, in order, of (term t) x (operand r),
-// each operand r being this lane's 16 code bytes of row l%16 and its scale
-// byte.  Lane l receives heads 4(l/16) + v, v < 4, of row l%16.
-template <int NS>
+// The matrix-core products of NS row operands with one 16-head group's
+// query (kTerms fp6 terms, or the one fp4 operand of the quantized query):
+// c[r] = sum over terms t, in order, of (term t) x (operand r), each operand
+// r being this lane's 16 code bytes of row l%16 and its scale byte.  Lane l
+// receives heads 4(l/16) + v, v < 4, of row l%16.
+template <int NS, int QF = kQueryFp32>
 __device__ __forceinline__ void group_dots(const QFrag<1> &q, const RowOperand (&ops)[NS], v4f (&c)[NS][1]) {
   v8i b[NS];
   int sb[NS];
@@ -177,7 +238,7 @@ __device__ __forceinline__ void group_dots(const QFrag<1> &q, const RowOperand (
     sb[r] = ops[r].sb;
     c[r][0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  mfma_terms<1, NS>(q, b, sb, c, std::make_integer_sequence<int, kTerms>{});
+  mfma_terms<1, NS, QueryFormat<QF>::fmt>(q, b, sb, c, std::make_integer_sequence<int, QueryFormat<QF>::terms>{});
 }
 
 // One head group's contribution to the score partials of four operands (64

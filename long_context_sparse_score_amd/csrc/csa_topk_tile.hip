@@ -51,6 +51,7 @@ struct TileArgs {
   uint64_t *hlow;    // [session][heads_stride]: the heads' lower-bound keys, same order
   uint64_t *hnext;   // [session][tiles_stride]: per tile its (hd+1)-th key, 0 if none
   float *bnd_up, *bnd_lo;  // bounds mode: the brackets of every row (one session)
+  float *qhat;             // quantized query: [session][64][128] fp32 copy for the rescoring, or null
   int64_t heads_stride, tiles_stride;
   int tile_rows;
   int n_idx_heads;
@@ -279,11 +280,11 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[
 // every wave reads every group's terms and the constants.  The third chunk
 // is issued once a second barrier has released the slots (the loop issues
 // the rest, always in order).
-template <int G>
+template <int G, int QF>
 __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
                                                int n_idx_heads, const uint8_t *__restrict__ idx_rows, int64_t row0,
                                                int64_t n, int rows, TileShared &sh, float *__restrict__ bnd_up,
-                                               float *__restrict__ bnd_lo) {
+                                               float *__restrict__ bnd_lo, float *__restrict__ qhat) {
   static_assert(G == 1 || G == 2 || G == 4, "head groups per workgroup");
   static_assert(kRingDepth == 4, "the query is staged in ring slots 2 and 3, chunks 0 and 1 go ahead");
   constexpr int kStageHead = 528, kStageW = 16 * kStageHead;
@@ -349,7 +350,21 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
         x[4 * i + 3] = v.w;
       }
       QFrag<1> mine;
-      const QFragNorms nm = split_qfrag(mine, x);
+      QFragNorms nm;
+      if constexpr (QF == kQueryMxfp4) {
+        float deq[32];
+        nm = quantize_qfrag_fp4(mine, x, deq);
+        // one workgroup of the session keeps the quantized query (fp32) for
+        // the exact rescoring
+        const int hq = 16 * wave + (lane & 15);
+        if (qhat && hq < n_idx_heads) {
+          float4 *dst = reinterpret_cast<float4 *>(qhat + (size_t)hq * 128 + 32 * (lane >> 4));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dst[i] = float4{deq[4 * i], deq[4 * i + 1], deq[4 * i + 2], deq[4 * i + 3]};
+        }
+      } else {
+        nm = split_qfrag(mine, x);
+      }
       // this lane's part of the bound constants: |w_h| (rho + 2^-15 A) for its
       // (head, block) fragment, summed over the group's 16 heads per block
       // (lanes 16 b .. 16 b + 15 hold block b); fp64 so that no range is lost
@@ -431,10 +446,10 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     load_ops(base, ops);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f c[4][1], cn[4][1];
-    group_dots<4>(q[0], ops, c);
+    group_dots<4, QF>(q[0], ops, c);
 #pragma unroll
     for (int g = 1; g < G; ++g) {
-      group_dots<4>(q[g], ops, cn);
+      group_dots<4, QF>(q[g], ops, cn);
       group_acc4(q[g - 1], c, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
@@ -465,7 +480,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
 // Modes (TileJob::Mode): kFilter scores the rows (the decode step), kArray
 // takes given scores as exact (csa_topk: l = u = the score), kBounds scores
 // and writes every row's bracket (a test entry point; no heads).
-template <int G, bool ARRAY>
+template <int G, bool ARRAY, int QF>
 __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a) {
   const int sess = blockIdx.y;
   const TileSession &S = a.s[sess];
@@ -479,8 +494,9 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   uint32_t o = 0;  // largest score part of this thread's positions
   if constexpr (!ARRAY) {
     const bool bounds = a.mode == TileJob::kBounds;
-    o = score_tile<G>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, sh, bounds ? a.bnd_up + row0 : nullptr,
-                      bounds ? a.bnd_lo + row0 : nullptr);
+    float *qhat = (QF == kQueryMxfp4 && a.qhat && blockIdx.x == 0) ? a.qhat + (size_t)sess * CSA_MAX_HEADS * 128 : nullptr;
+    o = score_tile<G, QF>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, sh, bounds ? a.bnd_up + row0 : nullptr,
+                          bounds ? a.bnd_lo + row0 : nullptr, qhat);
     if (bounds) return;
   } else {
     // the given scores into LDS (exact: both bounds), four loads in flight
@@ -515,14 +531,22 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
 
 // ---------------------------------------------------------------- launcher
 
-static hipError_t launch_scoring(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
+template <int QF>
+static void launch_scoring_q(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
   // three groups run as four: the query split holds zero terms and weights
   // for heads past n_idx_heads, which add exact zeros
   switch (groups) {
-    case 1: tile_kernel<1, false><<<grid, kTileThreads, 0, st>>>(a); break;
-    case 2: tile_kernel<2, false><<<grid, kTileThreads, 0, st>>>(a); break;
-    default: tile_kernel<4, false><<<grid, kTileThreads, 0, st>>>(a); break;
+    case 1: tile_kernel<1, false, QF><<<grid, kTileThreads, 0, st>>>(a); break;
+    case 2: tile_kernel<2, false, QF><<<grid, kTileThreads, 0, st>>>(a); break;
+    default: tile_kernel<4, false, QF><<<grid, kTileThreads, 0, st>>>(a); break;
   }
+}
+
+static hipError_t launch_scoring(const TileArgs &a, dim3 grid, int groups, int qfmt, hipStream_t st) {
+  if (qfmt == kQueryMxfp4)
+    launch_scoring_q<kQueryMxfp4>(a, grid, groups, st);
+  else
+    launch_scoring_q<kQueryFp32>(a, grid, groups, st);
   return hipGetLastError();
 }
 
@@ -540,6 +564,7 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   a.hnext = job.hnext;
   a.bnd_up = job.bnd_up;
   a.bnd_lo = job.bnd_lo;
+  a.qhat = job.qhat;
   a.heads_stride = job.heads_stride;
   a.tiles_stride = job.tiles_stride;
   a.tile_rows = job.tile_rows;
@@ -547,10 +572,10 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   const int groups = (job.n_idx_heads + 15) / 16;
   dim3 grid((unsigned)((max_rows + job.tile_rows - 1) / job.tile_rows), (unsigned)job.n_sessions);
   if (job.mode == TileJob::kArray) {
-    tile_kernel<1, true><<<grid, kTileThreads, 0, st>>>(a);
+    tile_kernel<1, true, kQueryFp32><<<grid, kTileThreads, 0, st>>>(a);
     return hipGetLastError();
   }
-  return launch_scoring(a, grid, groups, st);
+  return launch_scoring(a, grid, groups, job.query_format, st);
 }
 
 }  // namespace csa

@@ -46,11 +46,14 @@ def test_every_declared_symbol_is_exported(csa):
 
 def test_constants_match_header(csa):
     text = open(HEADER).read()
-    consts = dict(re.findall(r"#define (CSA_[A-Z_]+) (\d+)u?\b", text))
+    consts = dict(re.findall(r"#define (CSA_[A-Z_0-9]+) (\d+)u?\b", text))
     assert int(consts["CSA_IDX_ROW_BYTES"]) == csa.IDX_ROW_BYTES == 68
     assert int(consts["CSA_KV_ROW_BYTES"]) == csa.KV_ROW_BYTES == 583
     assert int(consts["CSA_TOPK"]) == csa.TOPK == 512
     assert int(consts["CSA_ABI_VERSION"]) == csa.lib.csa_abi_version() == csa.ABI_VERSION
+    assert int(consts["CSA_STAGES"]) == len(csa.STAGES)
+    assert int(consts["CSA_QUERY_FP32"]) == csa.QUERY_FORMATS["fp32"]
+    assert int(consts["CSA_QUERY_MXFP4"]) == csa.QUERY_FORMATS["mxfp4"]
 
 
 def test_strerror_and_workspace(csa):
@@ -100,6 +103,20 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
     sess[1] = csa.Session(fake, fake, 100, odd, fake, fake, fake, None, fake, None)
     assert L.csa_decode_step(sess, 2, 8, 64, 0.1, fake, 1 << 30, None) == csa.EINVAL
+    # the query-format entry points: unknown formats, bad queries, missing events
+    for i in range(2):
+        sess[i] = csa.Session(fake, fake, 100, fake, fake, fake, fake, None, fake, None)
+    for fmt in (-1, 2, 7):
+        assert L.csa_decode_step_ex(sess, 2, 8, 64, 0.1, fmt, fake, 1 << 30, None, None) == csa.EINVAL
+        assert L.csa_score_bounds(fake, 10, fake, fake, 8, fmt, fake, fake, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_decode_step_ex(sess, 2, 8, 64, 0.1, 1, fake, 64, None, None) == csa.EWORKSPACE
+    no_events = (ctypes.c_void_p * 8)()
+    assert L.csa_decode_step_ex(sess, 2, 8, 64, 0.1, 1, fake, 1 << 30, None, no_events) == csa.EINVAL
+    assert L.csa_quantize_query(fake, 0, fake, None) == csa.EINVAL
+    assert L.csa_quantize_query(fake, 65, fake, None) == csa.EINVAL
+    assert L.csa_quantize_query(odd, 8, fake, None) == csa.EINVAL
+    assert L.csa_quantize_query(fake, 8, ctypes.c_void_p(4096 + 2), None) == csa.EINVAL
+    assert L.csa_quantize_query(None, 8, fake, None) == csa.EINVAL
 
 
 def test_noalloc_entry_point_rejects_oversized_steps_on_host(csa):
