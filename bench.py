@@ -45,6 +45,11 @@ def parse():
                    help="skip the per-history-length figures of the other workloads")
     p.add_argument("--sweep-steps", type=int, default=20)
     p.add_argument("--no-fit", action="store_true", help="skip the fixed + marginal cost fit over history lengths")
+    p.add_argument("--steps-only", action="store_true",
+                   help="run decode steps only (no MXFP4-query leg, no filter diagnostics, no fit, no sweep, no CPU "
+                        "baseline): for kernel traces and counters")
+    p.add_argument("--query-format", default="fp32", choices=("fp32", "mxfp4"),
+                   help="indexer query format of the headline steps")
     return p.parse_args()
 
 
@@ -122,7 +127,9 @@ def algorithmic_bytes(n_rows: int, n_idx_heads: int, n_heads: int) -> dict:
 def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host, query_format="fp32", sess_np=None,
             n_rows=None):
     """Cold / warm / per-stage timing of `steps` decode steps of workload wl
-    (or of the first n_rows rows of the given host sessions)."""
+    (or of the first n_rows rows of the given host sessions); returns the
+    host sessions and the timings (with keep_host, also the filter
+    diagnostics of session 0)."""
     t0 = time.time()
     if sess_np is None:
         sess_np = [gen.session(wl.cid, s=i) for i in range(wl.n_sessions)]
@@ -191,7 +198,7 @@ def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host, query
         r["filter"] = filter_diagnostics(sess[0], step.sessions[0], csa, np, torch, query_format)
     del step, sess
     torch.cuda.synchronize()
-    return (sess_np if keep_host else None), r
+    return sess_np, r
 
 
 def filter_diagnostics(d, outs, csa, np, torch, query_format):
@@ -236,6 +243,9 @@ def main():
         copy_calibration(a.copy_calibration)
         return
 
+    if a.steps_only:
+        a.no_fit = a.no_sweep = a.no_cpu_baseline = True
+
     import numpy as np
     import torch
 
@@ -248,10 +258,12 @@ def main():
     torch.cuda.set_device(dev)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB: evicts the MALL and the L2s
 
-    sess_np, r = measure(wl, a.steps, a.warmup, flush, dev, csa, gen, np, torch, keep_host=True)
-    # the MXFP4-quantized-query scorer on the same data
-    _, r_q4 = measure(wl, a.sweep_steps, 2, flush, dev, csa, gen, np, torch, keep_host=True, query_format="mxfp4",
-                      sess_np=sess_np)
+    sess_np, r = measure(wl, a.steps, a.warmup, flush, dev, csa, gen, np, torch, keep_host=not a.steps_only,
+                         query_format=a.query_format)
+    r_q4 = None
+    if not a.steps_only:  # the MXFP4-quantized-query scorer on the same data
+        _, r_q4 = measure(wl, a.sweep_steps, 2, flush, dev, csa, gen, np, torch, keep_host=True, query_format="mxfp4",
+                          sess_np=sess_np)
     scale = sess_np[0]["softmax_scale"]
     ab = algorithmic_bytes(wl.n_rows, wl.n_idx_heads, wl.n_heads)
     ms = r["mean_ms"]
@@ -277,6 +289,7 @@ def main():
             "indexer_heads": wl.n_idx_heads,
             "attention_heads": wl.n_heads,
             "topk": 512,
+            "indexer_query": a.query_format,
             "cache": "cold: MALL and L2 flushed before each step, outside its events",
         },
         "median_ms": round(r["median_ms"], 5),
@@ -287,14 +300,6 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2),
         "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, r["stage_ms"])},
-        "filter": r["filter"],
-        "mxfp4_query": {
-            "cold_median_ms": round(r_q4["median_ms"], 5),
-            "warm_ms": round(r_q4["warm_ms"], 5),
-            "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, r_q4["stage_ms"])},
-            "score_kernel_hbm_frac": round(ab["score"] * wl.n_sessions / (r_q4["score_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-            "filter": r_q4["filter"],
-        },
         "roofline": {
             "kernel": "tile_kernel: query split + score + tile heads (all sessions, one launch)",
             "bound": "hbm",
@@ -308,6 +313,16 @@ def main():
         },
     }
 
+    if "filter" in r:
+        line["filter"] = r["filter"]
+    if r_q4 is not None:
+        line["mxfp4_query"] = {
+            "cold_median_ms": round(r_q4["median_ms"], 5),
+            "warm_ms": round(r_q4["warm_ms"], 5),
+            "stage_ms": {name: round(t, 5) for name, t in zip(csa.STAGES, r_q4["stage_ms"])},
+            "score_kernel_hbm_frac": round(ab["score"] * wl.n_sessions / (r_q4["score_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+            "filter": r_q4["filter"],
+        }
     if not a.no_fit and wl.n_sessions == 1:
         # fixed + marginal cost: cold step time over history prefixes of
         # 2^11 .. 2^20 rows of the same session, least squares ms = a + b MB

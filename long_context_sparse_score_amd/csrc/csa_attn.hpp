@@ -119,27 +119,28 @@ __device__ __forceinline__ void split3_bf16(float x, __bf16 &t0, __bf16 &t1, __b
 //   q[16(w%4) + l%16][128(w/4) + 32s + 8(l/16) + i], i < 8,
 // for w = t / 256, s = (t / 64) % 4, l = t % 64, stored at
 // dst[attn_q_index(w, s, term, l)].  attn_q_load reads the task's eight
-// values, attn_q_store splits and stores them (so a caller can issue the
-// loads early).
+// values (a head past n_heads reads head 0), attn_q_store zeroes those of a
+// head past n_heads, splits and stores them: a caller can issue the loads
+// early and consume them late.
+__device__ __forceinline__ bool attn_q_live(int n_heads, int t) {
+  return 16 * ((t / 256) & 3) + ((t % 64) & 15) < n_heads;
+}
 __device__ __forceinline__ void attn_q_load(const float *__restrict__ qa, int n_heads, int t, float (&x)[8]) {
   const int lane = t % 64, s = (t / 64) % 4, wave = t / 256;
   const int h = 16 * (wave & 3) + (lane & 15);
   const int d0 = 128 * (wave >> 2) + 32 * s + 8 * (lane >> 4);
-  const bool live = h < n_heads;
-  const float *src = qa + (size_t)(live ? h : 0) * kKvDim + d0;
+  const float *src = qa + (size_t)(h < n_heads ? h : 0) * kKvDim + d0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = src[i];
-    x[i] = live ? v : 0.0f;
-  }
+  for (int i = 0; i < 8; ++i) x[i] = src[i];
 }
-__device__ __forceinline__ void attn_q_store(const float (&x)[8], uint4 *__restrict__ dst, int t) {
+__device__ __forceinline__ void attn_q_store(const float (&x)[8], int n_heads, uint4 *__restrict__ dst, int t) {
   const int lane = t % 64, s = (t / 64) % 4, wave = t / 256;
+  const bool live = attn_q_live(n_heads, t);
   v8bf t0, t1, t2;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __bf16 a0, a1, a2;
-    split3_bf16(x[i], a0, a1, a2);
+    split3_bf16(live ? x[i] : 0.0f, a0, a1, a2);
     t0[i] = a0;
     t1[i] = a1;
     t2[i] = a2;
@@ -152,7 +153,7 @@ __device__ __forceinline__ void attn_q_split_task(const float *__restrict__ qa, 
                                                   int t) {
   float x[8];
   attn_q_load(qa, n_heads, t, x);
-  attn_q_store(x, dst, t);
+  attn_q_store(x, n_heads, dst, t);
 }
 constexpr int kAttnQTasks = kAttnQVecs / 3;  // 4096
 

@@ -75,7 +75,8 @@ static_assert(sizeof(RefineArgs) <= 4096, "kernel argument block");
 struct RefineShared {
   float q[CSA_MAX_HEADS][kQStride];  // the fp32 indexer query
   float w[CSA_MAX_HEADS];
-  double kv[kRefWaves][2][128];  // per wave: the decoded rows being scored
+  double kv[kRefWaves][2][128];  // per wave: the decoded rows being scored (exact fp32 values, as fp64)
+  double pv[kRefWaves][2][64];   // per wave: their heads' terms w_h max(0, d_h)
   BoundShared<kRefWaves> bs;
   uint32_t full_tile[kRefMaxFull];
   uint32_t wcnt[kRefWaves];
@@ -102,6 +103,12 @@ __device__ __forceinline__ RowBytes load_row_bytes(const uint8_t *__restrict__ i
   return RowBytes{r[lane], r[64 + (lane >> 4)]};
 }
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int64_t readlane_i64(int64_t x, int l) { return (int64_t)readlane_u64((uint64_t)x, l); }
 __device__ __forceinline__ double readlane_f64(double x, int l) {
   const uint64_t b = __builtin_bit_cast(uint64_t, x);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
@@ -112,9 +119,15 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
 // The exact scores S of N <= 2 rows (see the file comment) from their bytes,
 // computed by one wave: lane l decodes row values 2l and 2l + 1 exactly as
 // fp32 (an E2M1 value times 2^(e-127): exact, or +-inf on overflow, NaN for
-// a 0xFF scale), lane h < n_heads forms d_h in fp64 over i ascending (the
-// rows' chains interleaved), and every lane adds the heads' terms in head
-// order, read lane by lane.  out[r] is S of row r in every lane.
+// a 0xFF scale) and stores them as fp64 in LDS; lane h forms d_h in fp64
+// over i ascending from its fp32 query row in LDS and the row values (one
+// read serves every lane), the rows' chains interleaved and each step's
+// operands read a step ahead so the reads overlap the arithmetic.  The
+// heads' terms w_h max(0, d_h) (exactly +0 for lanes past n_heads) go to LDS
+// and every lane adds all 64 in head order, sixteen reads at a time: a +0
+// term leaves the sum unchanged (the sum starts at +0 and cannot become -0),
+// so this is the reference's sum over the n_heads heads.
+// out[r] is S of row r in every lane.
 template <int N>
 __device__ __forceinline__ void exact_scores(const RowBytes (&rb)[N], int n_heads, RefineShared &sh, float (&out)[N]) {
   static_assert(N == 1 || N == 2, "rows per call");
@@ -126,45 +139,68 @@ __device__ __forceinline__ void exact_scores(const RowBytes (&rb)[N], int n_head
     *reinterpret_cast<double2 *>(&sh.kv[wave][r][2 * lane]) = double2{(double)k0, (double)k1};
   }
   wave_lds_sync();
-  const int h = lane < n_heads ? lane : 0;
-  const float *qh = &sh.q[h][0];
+  const bool head = lane < n_heads;
+  const float *qh = &sh.q[head ? lane : 0][0];
   double d[N];
-#pragma unroll
-  for (int r = 0; r < N; ++r) d[r] = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < 128; i += 4) {
-    const float4 q4 = *reinterpret_cast<const float4 *>(qh + i);
-#pragma unroll
-    for (int r = 0; r < N; ++r) {
-      const double2 ka = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][i]);
-      const double2 kb = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][i + 2]);
-      d[r] = __builtin_fma((double)q4.x, ka.x, d[r]);
-      d[r] = __builtin_fma((double)q4.y, ka.y, d[r]);
-      d[r] = __builtin_fma((double)q4.z, kb.x, d[r]);
-      d[r] = __builtin_fma((double)q4.w, kb.y, d[r]);
-    }
-  }
-  const double wh = (double)sh.w[h];
-  double p[N], acc[N];
+  float4 qn = *reinterpret_cast<const float4 *>(qh);
+  double2 kn0[N], kn1[N];
 #pragma unroll
   for (int r = 0; r < N; ++r) {
-    p[r] = wh * (d[r] > 0.0 ? d[r] : 0.0);
-    acc[r] = 0.0;
+    d[r] = 0.0;
+    kn0[r] = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][0]);
+    kn1[r] = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][2]);
   }
-#pragma unroll
-  for (int hh = 0; hh < CSA_MAX_HEADS; ++hh) {
+#pragma unroll 4
+  for (int i = 0; i < 128; i += 4) {
+    const float4 qc = qn;
+    double2 kc0[N], kc1[N];
 #pragma unroll
     for (int r = 0; r < N; ++r) {
-      const double v = readlane_f64(p[r], hh);
-      acc[r] = hh < n_heads ? acc[r] + v : acc[r];
+      kc0[r] = kn0[r];
+      kc1[r] = kn1[r];
     }
+    const int in = i + 4 < 128 ? i + 4 : i;  // the last step re-reads its own operands
+    qn = *reinterpret_cast<const float4 *>(qh + in);
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      kn0[r] = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][in]);
+      kn1[r] = *reinterpret_cast<const double2 *>(&sh.kv[wave][r][in + 2]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's arithmetic
+    const double q0 = qc.x, q1 = qc.y, q2 = qc.z, q3 = qc.w;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      d[r] = __builtin_fma(q0, kc0[r].x, d[r]);
+      d[r] = __builtin_fma(q1, kc0[r].y, d[r]);
+      d[r] = __builtin_fma(q2, kc1[r].x, d[r]);
+      d[r] = __builtin_fma(q3, kc1[r].y, d[r]);
+    }
+  }
+  const double wh = (double)sh.w[head ? lane : 0];
+#pragma unroll
+  for (int r = 0; r < N; ++r) sh.pv[wave][r][lane] = head ? wh * (d[r] > 0.0 ? d[r] : 0.0) : 0.0;
+  wave_lds_sync();
+  double acc[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) acc[r] = 0.0;
+#pragma unroll 1
+  for (int c = 0; c < CSA_MAX_HEADS; c += 16) {
+    double2 v[N][8];
+#pragma unroll
+    for (int r = 0; r < N; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[r][j] = *reinterpret_cast<const double2 *>(&sh.pv[wave][r][c + 2 * j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < N; ++r) acc[r] = (acc[r] + v[r][j].x) + v[r][j].y;
   }
 #pragma unroll
   for (int r = 0; r < N; ++r) {
     const float f = (float)acc[r];
     out[r] = f == 0.0f ? 0.0f : f;
   }
-  wave_lds_sync();  // kv is reused by the wave's next rows
+  wave_lds_sync();  // kv and pv are reused by the wave's next rows
 }
 __device__ __forceinline__ float exact_score(const RowBytes &rb, int n_heads, RefineShared &sh) {
   const RowBytes r1[1] = {rb};
@@ -179,37 +215,42 @@ __device__ __forceinline__ void load_query(const float *__restrict__ q, const fl
                                            RefineShared &sh) {
   const int tid = threadIdx.x;
   constexpr int kQPer = CSA_MAX_HEADS * 32 / kRefThreads;  // float4 per thread
+  // every load is issued (heads past H read the last head, in this
+  // workgroup's own lines) and its value zeroed after: no branch, so no
+  // early wait for loads issued before
   float4 qv[kQPer];
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
     const int t = tid + kRefThreads * u, h = t >> 5, c = t & 31;
-    qv[u] = h < H ? reinterpret_cast<const float4 *>(q + (size_t)h * 128)[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    qv[u] = reinterpret_cast<const float4 *>(q + (size_t)(h < H ? h : H - 1) * 128)[c];
   }
-  const float wv = tid < H ? w[tid] : 0.0f;
+  const float wl = w[tid < H ? tid : H - 1];
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
     const int t = tid + kRefThreads * u;
-    *reinterpret_cast<float4 *>(&sh.q[t >> 5][4 * (t & 31)]) = qv[u];
+    *reinterpret_cast<float4 *>(&sh.q[t >> 5][4 * (t & 31)]) = (t >> 5) < H ? qv[u] : float4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  if (tid < CSA_MAX_HEADS) sh.w[tid] = wv;
+  if (tid < CSA_MAX_HEADS) sh.w[tid] = tid < H ? wl : 0.0f;
 }
 
-// Head items prefetched per wave (keys, then the rows' bytes) at the start,
-// so that their loads overlap the bound's computation.
+// Rows whose bytes each wave prefetches at the start, before the bound is
+// known (the rows of its first two head items' keys), so that the usual one
+// or two candidates per wave need no load after the bound.
 constexpr int kRefPrefetch = 2;
 
+template <bool EXACT>  // EXACT: rows scored exactly (decode step, csa_score); else given scores (csa_topk)
 __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a) {
   const int sess = blockIdx.y;
   const RefineSession &S = a.s[sess];
   const int64_t n = S.n_rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int H = a.n_idx_heads;
-  const bool exact = a.mode != RefineJob::kArray;
+  constexpr bool exact = EXACT;
   __shared__ RefineShared sh;
   const uint32_t nw = gridDim.x * kRefWaves;               // waves per session
   const uint32_t gw = blockIdx.x * kRefWaves + (uint32_t)wave;  // this wave
 
-  if (a.mode == RefineJob::kAll) {  // every row: its exact score
+  if (EXACT && a.mode == RefineJob::kAll) {  // every row: its exact score
     load_query(S.q, S.w, H, sh);
     lds_sync();
     for (int64_t row = gw; row < n; row += nw) {
@@ -238,37 +279,46 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   // attention query values of this workgroup's first split tasks, then the
   // head items' row bytes; everything after is synchronised through LDS only
   // (lds_sync), so these stay in flight across the bound's barriers.
-  uint64_t px[kRefPrefetch];
-#pragma unroll
-  for (int u = 0; u < kRefPrefetch; ++u) {
-    const int64_t i = gw + (int64_t)nw * u;
-    const uint64_t x = hkey[i < nh ? i : nh - 1];
-    px[u] = i < nh ? x : 0ull;
-  }
+  // (lane u: head item gw + nw u, the first of this wave's rounds)
+  // (a lane past the heads reads its wave's first head: no line is read by
+  // every wave)
+  // The values are masked where they are used, not here: a select right
+  // after a load would wait for it before the next loads are issued.
+  const int64_t i_first = gw + (int64_t)nw * lane;
+  const uint64_t xk_raw = hkey[i_first < nh ? i_first : (gw < nh ? gw : nh - 1)];
   // G over the lower-bound keys of the first heads (a prefix of the
   // rank-major order: every tile's best heads), two per thread
   const int64_t nb = nh < kRefBoundHeads ? nh : kRefBoundHeads;
-  uint64_t lk[kRefKPT];
+  uint64_t lk_raw[kRefKPT];
 #pragma unroll
   for (int j = 0; j < kRefKPT; ++j) {
     const int64_t i = tid + (int64_t)kRefThreads * j;
-    const uint64_t x = hlow[i < nb ? i : nb - 1];
-    lk[j] = i < nb ? x : 0ull;
+    lk_raw[j] = hlow[i < nb ? i : nb - 1];
   }
-  if (exact) load_query(S.q, S.w, H, sh);
-  // this workgroup's share of the attention query split (decode step)
+  if constexpr (EXACT) load_query(S.q, S.w, H, sh);
+  // this workgroup's share of the attention query split (decode step):
+  // threads past the share read its first task (no branch around the loads)
   const int qper = (kAttnQTasks + (int)gridDim.x - 1) / (int)gridDim.x;
   const int qt0 = (int)blockIdx.x * qper;
   const int qt1 = qt0 + qper < kAttnQTasks ? qt0 + qper : kAttnQTasks;
   float qx[8];
-  if (a.attn_q && qt0 + tid < qt1) attn_q_load(S.q_attn, a.n_attn_heads, qt0 + tid, qx);
+  if (a.attn_q) attn_q_load(S.q_attn, a.n_attn_heads, qt0 + tid < qt1 ? qt0 + tid : qt0, qx);
+  // the rows of lanes 0 and 1's keys (speculatively: candidates or not)
+  const uint64_t xk = i_first < nh ? xk_raw : 0ull;
   RowBytes pb[kRefPrefetch] = {};
-  if (exact) {
+  if constexpr (EXACT) {
+    const int64_t fallback = (int64_t)(gw % (uint64_t)n);  // a row of its own for a wave without keys
 #pragma unroll
-    for (int u = 0; u < kRefPrefetch; ++u) pb[u] = load_row_bytes(S.idx_rows, px[u] != 0 ? key_row(px[u]) : 0);
+    for (int u = 0; u < kRefPrefetch; ++u) {
+      const uint64_t x = readlane_u64(xk, u);
+      pb[u] = load_row_bytes(S.idx_rows, x != 0 ? (int64_t)key_row(x) : fallback);
+    }
   }
 
   // 1. the bound G
+  uint64_t lk[kRefKPT];
+#pragma unroll
+  for (int j = 0; j < kRefKPT; ++j) lk[j] = tid + (int64_t)kRefThreads * j < nb ? lk_raw[j] : 0ull;
   auto visit_low = [&](auto f) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kRefKPT; ++j)
@@ -319,54 +369,74 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
     return lo < nfull && (int64_t)sh.full_tile[lo] == t;
   };
 
-  // 3. this wave's items (uniform over the wave).  Item i's row, or -1 when
-  // it has no key; `pre` says whether its head key was prefetched (as xp),
-  // `have` comes back true when the row is the prefetched key's row.
-  auto item_row = [&](int64_t i, bool pre, uint64_t xp, bool &have) __attribute__((always_inline)) {
-    have = false;
-    if (all_rows) return i;
-    if (i < head_items) {
-      const uint64_t x = pre ? xp : hkey[i];  // rank i / nt of tile i % nt
-      have = pre;
-      return (x != 0 && x >= G && !is_full(i % nt)) ? (int64_t)key_row(x) : (int64_t)-1;
+  // 3. this wave's items, 64 per round (lane u of round r: item gw + nw
+  // (64 r + u)): each lane finds its item's row (-1: no key, stored as 0);
+  // the wave then scores the candidates two at a time in lane order, the
+  // next pair's row bytes loading while the current pair is scored.
+  for (int64_t r0 = 0;; r0 += 64) {
+    const int64_t i = gw + (int64_t)nw * (r0 + lane);
+    const bool live = i < n_items;
+    if (__ballot(live) == 0) break;  // uniform
+    int64_t row = -1;
+    if (live) {
+      if (all_rows) {
+        row = i;
+      } else if (i < head_items) {
+        const uint64_t x = r0 == 0 ? xk : hkey[i];  // rank i / nt of tile i % nt
+        if (x != 0 && x >= G && !is_full(i % nt)) row = (int64_t)key_row(x);
+      } else {
+        const int64_t r = i - head_items;
+        row = (int64_t)sh.full_tile[r / T] * T + r % T;
+      }
     }
-    const int64_t r = i - head_items;
-    return (int64_t)sh.full_tile[r / T] * T + r % T;
-  };
-  auto score_of = [&](int64_t row, bool have, const RowBytes &bp) __attribute__((always_inline)) {
-    return exact ? exact_score(have ? bp : load_row_bytes(S.idx_rows, row), H, sh) : S.scores[row];
-  };
-  {  // the prefetched items: two rows to score are scored together
-    static_assert(kRefPrefetch == 2, "the prefetched items are scored as a pair");
-    const int64_t i0 = gw, i1 = gw + (int64_t)nw;
-    bool h0 = false, h1 = false;
-    const int64_t r0 = i0 < n_items ? item_row(i0, true, px[0], h0) : -1;
-    const int64_t r1 = i1 < n_items ? item_row(i1, true, px[1], h1) : -1;
-    uint64_t k0 = 0, k1 = 0;
-    if (exact && r0 >= 0 && r1 >= 0) {
-      const RowBytes rb[2] = {h0 ? pb[0] : load_row_bytes(S.idx_rows, r0), h1 ? pb[1] : load_row_bytes(S.idx_rows, r1)};
-      float f[2];
-      exact_scores<2>(rb, H, sh, f);
-      k0 = make_key(f[0], (uint32_t)r0);
-      k1 = make_key(f[1], (uint32_t)r1);
-    } else {
-      if (r0 >= 0) k0 = make_key(score_of(r0, h0, pb[0]), (uint32_t)r0);
-      if (r1 >= 0) k1 = make_key(score_of(r1, h1, pb[1]), (uint32_t)r1);
+    if (live && row < 0) items[i] = 0ull;
+    if constexpr (!EXACT) {  // given scores: every candidate lane at once
+      if (row >= 0) items[i] = make_key(S.scores[row], (uint32_t)row);
+      continue;
     }
-    if (lane == 0) {
-      if (i0 < n_items) items[i0] = k0;
-      if (i1 < n_items) items[i1] = k1;
+    uint64_t m = __ballot(row >= 0);
+    // the rows' bytes: the prefetched ones for lanes 0 and 1 of the first
+    // round of head items (their rows are their prefetched keys' rows)
+    const bool pre_ok = r0 == 0 && !all_rows;
+    // (constant indices into pb: a dynamic index would place it in memory)
+    static_assert(kRefPrefetch == 2, "lanes 0 and 1");
+    auto bytes_of = [&](int l, int64_t rr) __attribute__((always_inline)) {
+      const bool pre = pre_ok && l < kRefPrefetch && gw + (int64_t)nw * l < head_items;
+      if (pre) return l == 0 ? pb[0] : pb[1];
+      return load_row_bytes(S.idx_rows, rr);
+    };
+    auto next_pair = [&](int &la, int &lb) __attribute__((always_inline)) {
+      la = m ? __builtin_ctzll(m) : -1;
+      if (la >= 0) m &= m - 1;
+      lb = m ? __builtin_ctzll(m) : -1;
+      if (lb >= 0) m &= m - 1;
+    };
+    int la, lb;
+    next_pair(la, lb);
+    int64_t ra = la >= 0 ? readlane_i64(row, la) : -1, rb = lb >= 0 ? readlane_i64(row, lb) : -1;
+    RowBytes ba = la >= 0 ? bytes_of(la, ra) : RowBytes{}, bb = lb >= 0 ? bytes_of(lb, rb) : RowBytes{};
+    while (la >= 0) {  // uniform
+      int lc, ld;
+      next_pair(lc, ld);
+      const int64_t rc = lc >= 0 ? readlane_i64(row, lc) : -1, rd = ld >= 0 ? readlane_i64(row, ld) : -1;
+      const RowBytes bc = lc >= 0 ? load_row_bytes(S.idx_rows, rc) : RowBytes{};
+      const RowBytes bd = ld >= 0 ? load_row_bytes(S.idx_rows, rd) : RowBytes{};
+      if (lb >= 0) {
+        const RowBytes rbs[2] = {ba, bb};
+        float f[2];
+        exact_scores<2>(rbs, H, sh, f);
+        if (lane == la) items[i] = make_key(f[0], (uint32_t)ra);
+        if (lane == lb) items[i] = make_key(f[1], (uint32_t)rb);
+      } else {
+        const float f = exact_score(ba, H, sh);
+        if (lane == la) items[i] = make_key(f, (uint32_t)ra);
+      }
+      la = lc; lb = ld; ra = rc; rb = rd; ba = bc; bb = bd;
     }
-  }
-  for (int64_t i = gw + (int64_t)nw * kRefPrefetch; i < n_items; i += nw) {
-    bool have;
-    const int64_t row = item_row(i, false, 0ull, have);
-    const uint64_t key = row >= 0 ? make_key(score_of(row, false, pb[0]), (uint32_t)row) : 0ull;
-    if (lane == 0) items[i] = key;
   }
   if (a.attn_q) {  // the attention query split share
     uint4 *dst = a.attn_q + (size_t)sess * kAttnQVecs;
-    if (qt0 + tid < qt1) attn_q_store(qx, dst, qt0 + tid);
+    if (qt0 + tid < qt1) attn_q_store(qx, a.n_attn_heads, dst, qt0 + tid);
     for (int t = qt0 + tid + kRefThreads; t < qt1; t += kRefThreads) attn_q_split_task(S.q_attn, a.n_attn_heads, dst, t);
   }
 }
@@ -393,7 +463,11 @@ hipError_t launch_refine(const RefineJob &job, hipStream_t st) {
   a.k = job.k;
   a.mode = (int)job.mode;
   if (max_rows == 0 && job.mode == RefineJob::kAll) return hipSuccess;
-  refine_kernel<<<dim3((unsigned)job.blocks, (unsigned)job.n_sessions), kRefThreads, 0, st>>>(a);
+  const dim3 grid((unsigned)job.blocks, (unsigned)job.n_sessions);
+  if (job.mode == RefineJob::kArray)
+    refine_kernel<false><<<grid, kRefThreads, 0, st>>>(a);
+  else
+    refine_kernel<true><<<grid, kRefThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
