@@ -56,8 +56,8 @@ def parse():
 # Kernel sources whose HBM counters profiles/ records; the recorded figures
 # are used only while these files are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_kernel_frontier-1m-rows_hbm_counters.txt")
-TRAFFIC_SOURCES = ["csa_topk_tile.hip", "csa_score.hpp", "csa_select.hpp", "csa_stream.hpp", "csa_device.hpp", "csa_attn.hpp",
-                   "csa_internal.hpp"]
+TRAFFIC_SOURCES = ["csa_topk_tile.hip", "csa_score.hpp", "csa_bound.hpp", "csa_select.hpp", "csa_stream.hpp",
+                   "csa_device.hpp", "csa_attn.hpp", "csa_internal.hpp"]
 
 
 def kernel_source_hash() -> str:
