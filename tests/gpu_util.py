@@ -1,40 +1,24 @@
 """Helpers of the GPU parity tests: device copies of generated sessions and
 the acceptance rules of the decode step.
 
-Acceptance (scores are fp32 on the GPU, fp64-rounded-once in the oracle):
-  * selection: with T the oracle's k-th score and B = {j : |s_j - T| <=
-    1e-6 |T|}, the GPU's selection and the oracle's agree outside B, and the
-    GPU selects exactly k_eff distinct valid rows;
+Acceptance:
+  * selection: the GPU's selection is the oracle's, row for row and in the
+    same order, and sel_score holds the oracle's scores bit for bit (the
+    candidates are rescored exactly in the reference's fp64 arithmetic);
   * attention: max |out_gpu - out_ref| <= 1e-3 max |out_ref|, where out_ref is
-    the oracle's attention over the GPU's own selection.
+    the oracle's attention over the GPU's own selection (lse within 1e-5).
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-SEL_BAND = 1e-6
 ATTN_TOL = 1e-3
 KEYS = ("idx_rows", "kv_rows", "q_idx", "w_idx", "q_attn")
 
 
 def to_dev(s: dict, dev="cuda") -> dict:
     return {k: torch.from_numpy(np.ascontiguousarray(s[k])).to(dev) for k in KEYS}
-
-
-def check_selection(gpu_sel: np.ndarray, ref_sel: np.ndarray, ref_scores_all: np.ndarray, k_eff: int) -> dict:
-    """Set equality outside the band around the oracle's k-th score."""
-    g = [int(x) for x in gpu_sel[:k_eff]]
-    assert all(x == -1 for x in gpu_sel[k_eff:]), "padding must be -1"
-    assert len(set(g)) == k_eff and all(0 <= x < len(ref_scores_all) for x in g), "k_eff distinct valid rows"
-    if k_eff == 0:
-        return {"band": 0, "swaps": 0}
-    T = float(ref_scores_all[ref_sel[k_eff - 1]])
-    band = np.abs(ref_scores_all.astype(np.float64) - T) <= SEL_BAND * abs(T)
-    diff = set(g) ^ set(int(x) for x in ref_sel[:k_eff])
-    outside = sorted(j for j in diff if not band[j])
-    assert not outside, f"selection differs outside the band at rows {outside[:10]}"
-    return {"band": int(band.sum()), "swaps": len(diff) // 2}
 
 
 def check_selection_exact(gpu_sel: np.ndarray, gpu_score: np.ndarray, ref_sel: np.ndarray, ref_score: np.ndarray,

@@ -43,8 +43,8 @@ def test_noalloc_matches_workspace_entry_point(csa, orc, sizes):
             assert a[k].tobytes() == b[k].tobytes(), f"n={n}: {k} differs"
         if n <= 5_000:  # and against the oracle, to the usual bar
             ref_scores = orc.score(s["idx_rows"], s["q_idx"], s["w_idx"])
-            ref_sel, _, _ = orc.topk(ref_scores, 512)
-            gu.check_selection(a["sel"], ref_sel, ref_scores, min(512, n))
+            ref_sel, ref_sel_score, _ = orc.topk(ref_scores, 512)
+            gu.check_selection_exact(a["sel"], a["sel_score"], ref_sel, ref_sel_score, min(512, n))
             att, _ = orc.attention(s["kv_rows"], a["sel"][:min(512, n)], s["q_attn"], s["softmax_scale"])
             gu.check_attention(a["out"], att)
 
