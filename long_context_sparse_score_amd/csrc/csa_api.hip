@@ -403,6 +403,14 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     job.qhat = at<float>(ws, L.qhat_off);
     for (int i = 0; i < n_sessions; ++i) rj.q[i] = job.qhat + (size_t)i * CSA_MAX_HEADS * 128;
   }
+  // Short histories (at most two rows per rescoring wave in every session):
+  // every row is scored exactly by the rescoring kernel and the score kernel
+  // is skipped; the selection then takes the top-k of all rows' exact keys.
+  // (The fp32 query only: the MXFP4 query is quantized by the score kernel.)
+  bool exact_all = query_format == CSA_QUERY_FP32;
+  for (int i = 0; i < n_sessions; ++i)
+    exact_all = exact_all && sessions[i].n_rows <= (int64_t)2 * rj.blocks * kRefineWaves;
+  if (exact_all) rj.mode = RefineJob::kKeysAll;
   rj.attn_q = aq;  // the attention query is split by the rescoring's workgroups
   rj.n_attn_heads = n_heads;
   for (int i = 0; i < n_sessions; ++i) rj.q_attn[i] = sessions[i].q_attn;
@@ -435,7 +443,7 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
     return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_tiles(job, st);
+  if (e == hipSuccess && !exact_all) e = launch_tiles(job, st);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess && any_rows) e = launch_refine(rj, st);

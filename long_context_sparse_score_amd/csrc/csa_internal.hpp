@@ -53,9 +53,15 @@ struct TileJob {
   float *qhat;             // kQueryMxfp4: the quantized query of every session, [session][64][128] (or null)
 };
 
+// Waves per workgroup of the exact rescoring.
+constexpr int kRefineWaves = 8;
+
 // One launch of the exact rescoring (csa_refine.hip).
 struct RefineJob {
-  enum Mode { kDecode, kArray, kAll } mode;  // candidates scored exactly; candidates from given scores; every row
+  // kDecode: the filter's candidates scored exactly; kArray: candidates from
+  // given scores; kAll: every row's exact score (csa_score); kKeysAll: every
+  // row's exact key as an item (the decode step of short histories)
+  enum Mode { kDecode, kArray, kAll, kKeysAll } mode;
   int n_sessions;
   int n_idx_heads;
   int tile_rows;

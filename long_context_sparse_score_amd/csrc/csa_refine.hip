@@ -42,6 +42,7 @@ namespace csa {
 
 constexpr int kRefThreads = 512;
 constexpr int kRefWaves = kRefThreads / 64;
+static_assert(kRefWaves == kRefineWaves, "the host's view of the workgroup");
 constexpr int kRefKPT = 2;                             // bound heads per thread in registers
 constexpr int kRefBoundHeads = kRefThreads * kRefKPT;  // 1024: the heads G is taken over
 constexpr int kQStride = 132;  // floats per query head in LDS: rows 528 B apart spread the lanes over banks
@@ -250,12 +251,42 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   const uint32_t nw = gridDim.x * kRefWaves;               // waves per session
   const uint32_t gw = blockIdx.x * kRefWaves + (uint32_t)wave;  // this wave
 
-  if (EXACT && a.mode == RefineJob::kAll) {  // every row: its exact score
+  if (EXACT && (a.mode == RefineJob::kAll || a.mode == RefineJob::kKeysAll)) {
+    // every row: its exact score (csa_score) or its exact key as an item (a
+    // short history's decode step: the filter would cost more than it
+    // saves), rows gw + 2 nw t and gw + 2 nw t + nw scored as a pair
+    const bool keys = a.mode == RefineJob::kKeysAll;
+    uint64_t *items = a.items + (size_t)sess * a.items_stride;
+    if (keys && blockIdx.x == 0 && tid == 0) a.count[sess] = (uint32_t)n;
     load_query(S.q, S.w, H, sh);
     lds_sync();
-    for (int64_t row = gw; row < n; row += nw) {
-      const float f = exact_score(load_row_bytes(S.idx_rows, row), H, sh);
-      if (lane == 0) S.scores[row] = f;
+    for (int64_t r0 = gw; r0 < n; r0 += 2 * (int64_t)nw) {
+      const int64_t r1 = r0 + nw;
+      const RowBytes b0 = load_row_bytes(S.idx_rows, r0);
+      const RowBytes b1 = load_row_bytes(S.idx_rows, r1 < n ? r1 : r0);
+      float f[2];
+      if (r1 < n) {
+        const RowBytes rbs[2] = {b0, b1};
+        exact_scores<2>(rbs, H, sh, f);
+      } else {
+        f[0] = exact_score(b0, H, sh);
+        f[1] = 0.0f;
+      }
+      if (lane == 0) {
+        if (keys) {
+          items[r0] = make_key(f[0], (uint32_t)r0);
+          if (r1 < n) items[r1] = make_key(f[1], (uint32_t)r1);
+        } else {
+          S.scores[r0] = f[0];
+          if (r1 < n) S.scores[r1] = f[1];
+        }
+      }
+    }
+    if (keys && a.attn_q) {  // this workgroup's share of the attention query split
+      const int per = (kAttnQTasks + (int)gridDim.x - 1) / (int)gridDim.x;
+      const int t1 = ((int)blockIdx.x + 1) * per < kAttnQTasks ? ((int)blockIdx.x + 1) * per : kAttnQTasks;
+      for (int t = (int)blockIdx.x * per + tid; t < t1; t += kRefThreads)
+        attn_q_split_task(S.q_attn, a.n_attn_heads, a.attn_q + (size_t)sess * kAttnQVecs, t);
     }
     return;
   }
@@ -462,7 +493,7 @@ hipError_t launch_refine(const RefineJob &job, hipStream_t st) {
   a.n_idx_heads = job.n_idx_heads;
   a.k = job.k;
   a.mode = (int)job.mode;
-  if (max_rows == 0 && job.mode == RefineJob::kAll) return hipSuccess;
+  if (max_rows == 0 && (job.mode == RefineJob::kAll || job.mode == RefineJob::kKeysAll)) return hipSuccess;
   const dim3 grid((unsigned)job.blocks, (unsigned)job.n_sessions);
   if (job.mode == RefineJob::kArray)
     refine_kernel<false><<<grid, kRefThreads, 0, st>>>(a);
