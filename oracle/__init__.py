@@ -50,6 +50,8 @@ class Oracle:
         L.csa_oracle_attention.restype = i32
         L.csa_oracle_attention.argtypes = [vp, i64, vp, i32, vp, i32, dbl, vp, vp]
         L.csa_oracle_quantize_query.argtypes = [vp, i32, vp]
+        L.csa_oracle_dense_attention.restype = i32
+        L.csa_oracle_dense_attention.argtypes = [vp, i64, vp, i32, dbl, vp, vp]
         L.csa_oracle_decode_step.restype = i32
         L.csa_oracle_decode_step.argtypes = [vp, vp, i64, vp, vp, i32, vp, i32, dbl, i32, vp, vp, vp, vp]
         self.L = L
@@ -126,6 +128,20 @@ class Oracle:
                                          float(softmax_scale), _p(out), _p(lse))
         if rc != 0:
             raise ValueError(f"oracle attention failed ({rc})")
+        return out, lse
+
+    def dense_attention(self, kv_rows, q_attn, softmax_scale: float):
+        """Softmax attention over every row."""
+        kv_rows = _rows(kv_rows, 583)
+        q_attn = np.ascontiguousarray(q_attn, dtype=np.float32)
+        h = q_attn.shape[0]
+        assert q_attn.shape == (h, 512)
+        out = np.empty((h, 512), dtype=np.float32)
+        lse = np.empty(h, dtype=np.float32)
+        rc = self.L.csa_oracle_dense_attention(_p(kv_rows), kv_rows.shape[0], _p(q_attn), h, float(softmax_scale),
+                                               _p(out), _p(lse))
+        if rc != 0:
+            raise ValueError(f"oracle dense attention failed ({rc})")
         return out, lse
 
     def decode_step(self, idx_rows, kv_rows, q_idx, w_idx, q_attn, softmax_scale: float, k: int = 512):

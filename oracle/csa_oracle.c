@@ -25,6 +25,10 @@
  *    fusion").  A full sort is used.
  *  - Attention: textbook softmax attention over the selected rows, with the
  *    decoded 512-value row used as both key and value, in double.
+ *  - Dense attention (the HCA layers of DS4X README, "What DS4X changes" and
+ *    "Optimization details": exact score-split attention over every
+ *    compressed row, no row ceiling): the same textbook softmax attention
+ *    over all n rows, each row used once, in row order.
  *  - MXFP4 query (the block-scaled scorer of DS4X README, "What DS4X
  *    changes" and "Optimization details"): the pages never say how the fp32
  *    query becomes an MXFP4 operand.  The reading adopted is the OCP MX v1.0
@@ -215,6 +219,18 @@ int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *
   }
   free(kv); free(logit); free(acc);
   return 0;
+}
+
+/* ---------------- dense attention ---------------- */
+
+int csa_oracle_dense_attention(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads,
+                               double softmax_scale, float *out, float *lse) {
+  int32_t *all = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+  if (!all) return -1;
+  for (int64_t j = 0; j < n_rows; ++j) all[j] = (int32_t)j;
+  int rc = csa_oracle_attention(kv_rows, n_rows, all, (int)n_rows, q_attn, n_heads, softmax_scale, out, lse);
+  free(all);
+  return rc;
 }
 
 /* ---------------- MXFP4 query quantization ---------------- */

@@ -21,6 +21,9 @@ int64_t csa_oracle_topk(const float *scores, int64_t n, int k, int32_t *sel, flo
 int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel, int n_sel,
                          const float *q_attn, int n_heads, double softmax_scale, float *out,
                          float *lse);
+/* Softmax attention over every row (each row once, in row order). */
+int csa_oracle_dense_attention(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads,
+                               double softmax_scale, float *out, float *lse);
 /* The indexer query [n_heads][128] quantized to MXFP4 rows [n_heads][68]. */
 void csa_oracle_quantize_query(const float *q, int n_heads, uint8_t *rows);
 int csa_oracle_decode_step(const uint8_t *idx_rows, const uint8_t *kv_rows, int64_t n_rows,

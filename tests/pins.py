@@ -288,6 +288,31 @@ def check_attention(o) -> None:
     assert np.all(out == 0) and np.all(np.isneginf(lse))
 
 
+def check_dense_attention(o) -> None:
+    """Attention over every row against float64 scaled_dot_product_attention
+    over the library-decoded rows, and closed forms: one row gives that row,
+    q = 0 gives the mean of all rows with lse = log n, no row gives 0 and
+    -inf."""
+    rng = np.random.default_rng(13)
+    rows = random_kv_rows(300, 6)
+    scale = float(np.float32(1 / math.sqrt(512)))
+    for n, h in ((1, 1), (2, 3), (33, 2), (300, 4)):
+        q = rng.standard_normal((h, 512)).astype(np.float32)
+        out, lse = o.dense_attention(rows[:n], q, scale)
+        ref_o, ref_l = ref_attention(rows[:n], np.arange(n), q, scale)
+        assert np.max(np.abs(out - ref_o)) <= 1e-6 * max(1e-30, np.max(np.abs(ref_o))), f"dense n={n}"
+        assert np.allclose(lse, ref_l, rtol=1e-6, atol=1e-6), "dense lse"
+    kv = ref_decode_kv(rows)
+    out, _ = o.dense_attention(rows[5:6], rng.standard_normal((2, 512)).astype(np.float32), scale)
+    assert np.array_equal(out[0], kv[5]) and np.array_equal(out[1], kv[5]), "dense n=1"
+    out, lse = o.dense_attention(rows[:77], np.zeros((1, 512), np.float32), scale)
+    mean = kv[:77].astype(np.float64).mean(axis=0)
+    assert np.max(np.abs(out[0] - mean)) <= 1e-6 * np.max(np.abs(mean)), "dense q=0 mean"
+    assert abs(lse[0] - math.log(77)) < 1e-6, "dense q=0 lse"
+    out, lse = o.dense_attention(rows[:0], np.ones((2, 512), np.float32), scale)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
 def check_decode_step(o) -> None:
     """The whole step against the pipeline built from the independent
     references above (numpy score -> Python sort -> PyTorch attention), at a
@@ -401,4 +426,4 @@ def check_quantize_query(o) -> None:
 
 
 ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention, check_decode_step,
-              check_quantize_query)
+              check_quantize_query, check_dense_attention)

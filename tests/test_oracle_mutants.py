@@ -45,6 +45,10 @@ MUTANTS = [
      "int64_t k_eff = csa_oracle_topk(scores, n_rows, k, sel, sel_score);\n  for (int64_t i = 0; i < k_eff; ++i) sel[i] = (int32_t)i;"),
     ("step_scale_dropped", "q_attn, n_heads, softmax_scale, out,\n                              lse);",
      "q_attn, n_heads, 1.0, out,\n                              lse);"),
+    ("dense_skips_last_row", "csa_oracle_attention(kv_rows, n_rows, all, (int)n_rows,",
+     "csa_oracle_attention(kv_rows, n_rows, all, (int)n_rows - (n_rows > 1),"),
+    ("dense_row_offset", "for (int64_t j = 0; j < n_rows; ++j) all[j] = (int32_t)j;",
+     "for (int64_t j = 0; j < n_rows; ++j) all[j] = (int32_t)(j / 2);"),
     ("q4_scale_offset", "shared = (e - 1) - 2;", "shared = (e - 1) - 1;"),
     ("q4_ceil_log2", "shared = (e - 1) - 2;", "shared = e - 2;"),
     ("q4_tie_odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
