@@ -201,6 +201,34 @@ def measure(wl, steps, warmup, flush, dev, csa, gen, np, torch, keep_host, query
     return sess_np, r
 
 
+def measure_dense(n_rows, steps, flush, dev, csa, gen, np, torch):
+    """Cold time of csa_dense_attn over n_rows KV rows (64 heads): the HCA
+    layers' dense attention.  Rows and query from the 1M-row workload's
+    generator (prefix), cold as the decode step."""
+    s = gen.session(3, n_rows=n_rows)
+    kv = torch.from_numpy(s["kv_rows"]).to(dev)
+    q = torch.from_numpy(s["q_attn"]).to(dev)
+    ws = torch.empty(int(csa.lib.csa_dense_workspace_bytes(n_rows)), dtype=torch.uint8, device=dev)
+    out = torch.empty((q.shape[0], 512), dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[0], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        flush.sum()
+        csa.dense_attn(kv, q, s["softmax_scale"], ws=ws, out=out, lse=lse)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        flush.sum()
+        e0.record(stream)
+        csa.dense_attn(kv, q, s["softmax_scale"], ws=ws, out=out, lse=lse)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = [e0.elapsed_time(e1) for e0, e1 in ev]
+    alg = 583 * n_rows + 4 * 512 * 64 * 2 + 4 * 64
+    med = statistics.median(t)
+    return {"rows": n_rows, "heads": int(q.shape[0]), "cold_median_ms": round(med, 5),
+            "algorithmic_bytes": alg, "hbm_gbs": round(alg / (med * 1e-3) / 1e9, 2)}
+
+
 def filter_diagnostics(d, outs, csa, np, torch, query_format):
     """How much the matrix-core filter leaves to the exact rescoring, on
     session 0 (outside the timed steps, library calls only): the brackets'
@@ -315,6 +343,8 @@ def main():
 
     if "filter" in r:
         line["filter"] = r["filter"]
+    if not a.steps_only:  # dense attention of a ratio-128 (HCA) layer at a 1M-token context
+        line["dense_attention"] = measure_dense(8194, a.sweep_steps, flush, dev, csa, gen, np, torch)
     if r_q4 is not None:
         line["mxfp4_query"] = {
             "cold_median_ms": round(r_q4["median_ms"], 5),

@@ -140,6 +140,28 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
                     const float *q_attn, int n_heads, float softmax_scale, float *out, float *lse,
                     void *ws, size_t ws_bytes, void *hip_stream);
 
+/* Rows accepted by csa_dense_attn. */
+#define CSA_DENSE_MAX_ROWS (((int64_t)1) << 17)
+
+/* Workspace bytes of csa_dense_attn over n_rows rows (0 if n_rows is out of
+ * range). */
+size_t csa_dense_workspace_bytes(int64_t n_rows);
+
+/* Dense softmax attention over every KV row (the HCA layers of the DS4X page,
+ * "What DS4X changes" and "Optimization details": exact score-split attention
+ * over all compressed rows, with no row ceiling; at a 1M-token context a
+ * ratio-128 layer holds 8,194 rows):
+ *   l[h][j] = softmax_scale * q_attn[h] . kv[j]   for every row j < n_rows,
+ *   out[h]  = sum_j softmax(l[h])[j] * kv[j],   lse[h] = log(sum_j exp(l[h][j])),
+ * kv[j] the decoded 512-value row (csa_sparse_attn's operands and
+ * arithmetic).  The rows are split into at most 256 contiguous groups of a
+ * multiple of 32 rows whose partials are merged in group order.  n_rows in
+ * [0, CSA_DENSE_MAX_ROWS] (n_rows = 0 gives out = 0 and lse = -inf); n_heads
+ * in [1, 64]; lse may be NULL; ws sized by csa_dense_workspace_bytes(n_rows),
+ * 256-byte aligned. */
+int csa_dense_attn(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads, float softmax_scale,
+                   float *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
+
 /* One CSA decode step for each of n_sessions independent sessions: score
  * every indexer row, select the exact top-512 (csa_topk order) and attend
  * over the selected KV rows (csa_sparse_attn).  Selections and outputs are

@@ -70,6 +70,10 @@ def _load() -> ctypes.CDLL:
     L.csa_score.argtypes = [vp, i64, vp, vp, i32, vp, vp, sz, vp]
     L.csa_score_bounds.restype = i32
     L.csa_score_bounds.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.csa_dense_workspace_bytes.restype = sz
+    L.csa_dense_workspace_bytes.argtypes = [i64]
+    L.csa_dense_attn.restype = i32
+    L.csa_dense_attn.argtypes = [vp, i64, vp, i32, f32, vp, vp, vp, sz, vp]
     L.csa_quantize_query.restype = i32
     L.csa_quantize_query.argtypes = [vp, i32, vp, vp]
     L.csa_decode_step_ex.restype = i32
@@ -235,6 +239,31 @@ def sparse_attn(kv_rows: torch.Tensor, sel_idx: torch.Tensor, n_sel: int, q_attn
     _check(lib.csa_sparse_attn(_ptr(kv_rows, torch.uint8, "kv_rows"), n_rows, _ptr(sel_idx, torch.int32, "sel"),
                                n_sel, _ptr(q_attn, torch.float32, "q_attn"), h, softmax_scale, _ptr(out), _ptr(lse),
                                _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_sparse_attn")
+    return out, lse
+
+
+DENSE_MAX_ROWS = 1 << 17  # CSA_DENSE_MAX_ROWS
+
+
+def dense_attn(kv_rows: torch.Tensor, q_attn: torch.Tensor, softmax_scale: float, ws: torch.Tensor | None = None,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """Softmax attention over every KV row (csa_dense_attn)."""
+    n = _rows(kv_rows, KV_ROW_BYTES, "kv_rows")
+    if n > DENSE_MAX_ROWS:
+        raise ValueError(f"kv_rows: at most {DENSE_MAX_ROWS} rows, got {n}")
+    h = _mat(q_attn, KV_DIM, "q_attn")
+    dev = q_attn.device
+    if ws is None:
+        ws = torch.empty(int(lib.csa_dense_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((h, KV_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(h, dtype=torch.float32, device=dev)
+    _mat(out, KV_DIM, "out", h)
+    _vec(lse, h, "lse")
+    _check(lib.csa_dense_attn(_ptr(kv_rows, torch.uint8, "kv_rows"), n, _ptr(q_attn, torch.float32, "q_attn"), h,
+                              softmax_scale, _ptr(out, torch.float32), _ptr(lse, torch.float32),
+                              _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_dense_attn")
     return out, lse
 
 

@@ -352,6 +352,43 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   return status_of(e);
 }
 
+// Workspace of csa_dense_attn: [attention query split][group partials][group (m, l)].
+struct DenseLayout {
+  size_t q_off, part_off, ml_off, total;
+};
+DenseLayout make_dense_layout(int64_t n_rows) {
+  int per = 0, groups = 0;
+  dense_grouping(n_rows, &per, &groups);
+  DenseLayout L;
+  L.q_off = 0;
+  L.part_off = align_up(kAttnQBytes);
+  L.ml_off = L.part_off + align_up((size_t)groups * CSA_MAX_HEADS * kKvDim * sizeof(float));
+  L.total = L.ml_off + align_up((size_t)(groups > 0 ? groups : 1) * CSA_MAX_HEADS * 2 * sizeof(float));
+  return L;
+}
+
+size_t csa_dense_workspace_bytes(int64_t n_rows) {
+  if (n_rows < 0 || n_rows > CSA_DENSE_MAX_ROWS) return 0;
+  return make_dense_layout(n_rows).total;
+}
+
+int csa_dense_attn(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads, float softmax_scale,
+                   float *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream) {
+  if (n_rows < 0 || n_rows > CSA_DENSE_MAX_ROWS || !heads_ok(n_heads) || !q_attn || !out) return CSA_EINVAL;
+  if (n_rows > 0 && !kv_rows) return CSA_EINVAL;
+  const DenseLayout L = make_dense_layout(n_rows);
+  if (ws == nullptr || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < L.total) return CSA_EWORKSPACE;
+  int rc = check_device();
+  if (rc != CSA_OK) return rc;
+  hipStream_t st = (hipStream_t)hip_stream;
+  uint4 *aq = at<uint4>(ws, L.q_off);
+  hipError_t e = launch_attn_q_split(&q_attn, 1, n_heads, aq, st);
+  if (e == hipSuccess)
+    e = launch_dense_attn(kv_rows, n_rows, aq, n_heads, softmax_scale, at<float>(ws, L.part_off), at<float>(ws, L.ml_off),
+                          out, lse, st);
+  return status_of(e);
+}
+
 static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                             float softmax_scale, int query_format, void *ws, size_t ws_bytes, void *hip_stream,
                             void *const *events) {

@@ -128,6 +128,18 @@ hipError_t launch_quantize_query(const float *q, int n_heads, uint8_t *rows, hip
 // attn_out + i * kAttnQVecs.
 hipError_t launch_attn_q_split(const float *const *q_attn, int n_sessions, int n_attn_heads, uint4 *attn_out,
                                hipStream_t st);
+// Dense attention (csa_dense_attn): at most kDenseMaxGroups groups of a
+// multiple of 32 rows (at most 512), as few rows per group as that allows.
+constexpr int kDenseMaxGroups = 256;
+inline void dense_grouping(int64_t n_rows, int *rows_per_group, int *groups) {
+  const int64_t per = 32 * ((n_rows + 32 * kDenseMaxGroups - 1) / (32 * kDenseMaxGroups));
+  *rows_per_group = (int)(per > 32 ? per : 32);
+  *groups = (int)((n_rows + *rows_per_group - 1) / *rows_per_group);
+}
+// Partials and the merge of a dense attention (csa_attn.hip); qsplit holds
+// the attention query split (launch_attn_q_split).
+hipError_t launch_dense_attn(const uint8_t *kv_rows, int64_t n_rows, const uint4 *qsplit, int n_heads, float scale,
+                             float *part, float *ml, float *out, float *lse, hipStream_t st);
 hipError_t launch_tiles(const TileJob &job, hipStream_t st);
 hipError_t launch_refine(const RefineJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);

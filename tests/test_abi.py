@@ -112,6 +112,13 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_decode_step_ex(sess, 2, 8, 64, 0.1, 1, fake, 64, None, None) == csa.EWORKSPACE
     no_events = (ctypes.c_void_p * 8)()
     assert L.csa_decode_step_ex(sess, 2, 8, 64, 0.1, 1, fake, 1 << 30, None, no_events) == csa.EINVAL
+    assert L.csa_dense_attn(fake, -1, fake, 8, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_dense_attn(fake, (1 << 17) + 1, fake, 8, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_dense_attn(fake, 100, fake, 0, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_dense_attn(None, 100, fake, 8, 0.1, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_dense_attn(fake, 100, fake, 8, 0.1, fake, None, fake, 64, None) == csa.EWORKSPACE
+    assert L.csa_dense_attn(fake, 100, fake, 8, 0.1, fake, None, ctypes.c_void_p(4096 + 8), 1 << 30, None) == csa.EWORKSPACE
+    assert csa.lib.csa_dense_workspace_bytes(8194) > csa.lib.csa_dense_workspace_bytes(100) > 0
     assert L.csa_quantize_query(fake, 0, fake, None) == csa.EINVAL
     assert L.csa_quantize_query(fake, 65, fake, None) == csa.EINVAL
     assert L.csa_quantize_query(odd, 8, fake, None) == csa.EINVAL
