@@ -50,6 +50,9 @@ class Oracle:
         L.csa_oracle_attention.restype = i32
         L.csa_oracle_attention.argtypes = [vp, i64, vp, i32, vp, i32, dbl, vp, vp]
         L.csa_oracle_quantize_query.argtypes = [vp, i32, vp]
+        L.csa_oracle_pack_kv_rows.argtypes = [vp, i64, vp]
+        L.csa_oracle_pack_idx_rows.argtypes = [vp, i64, vp]
+        L.csa_oracle_lse_merge.argtypes = [vp, vp, vp, vp, i32, vp, vp]
         L.csa_oracle_dense_attention.restype = i32
         L.csa_oracle_dense_attention.argtypes = [vp, i64, vp, i32, dbl, vp, vp]
         L.csa_oracle_decode_step.restype = i32
@@ -128,6 +131,30 @@ class Oracle:
                                          float(softmax_scale), _p(out), _p(lse))
         if rc != 0:
             raise ValueError(f"oracle attention failed ({rc})")
+        return out, lse
+
+    def pack_kv(self, v) -> np.ndarray:
+        """Rows of 512 values packed into 583-byte KV rows."""
+        v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1, 512)
+        rows = np.empty((v.shape[0], 583), dtype=np.uint8)
+        self.L.csa_oracle_pack_kv_rows(_p(v), v.shape[0], _p(rows))
+        return rows
+
+    def pack_idx(self, v) -> np.ndarray:
+        """Rows of 128 values packed into 68-byte indexer rows."""
+        v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1, 128)
+        rows = np.empty((v.shape[0], 68), dtype=np.uint8)
+        self.L.csa_oracle_pack_idx_rows(_p(v), v.shape[0], _p(rows))
+        return rows
+
+    def lse_merge(self, out_a, lse_a, out_b, lse_b):
+        """The merge of two attention results over disjoint rows."""
+        out_a, out_b = (np.ascontiguousarray(x, dtype=np.float32) for x in (out_a, out_b))
+        lse_a, lse_b = (np.ascontiguousarray(x, dtype=np.float32) for x in (lse_a, lse_b))
+        h = lse_a.shape[0]
+        out = np.empty((h, 512), dtype=np.float32)
+        lse = np.empty(h, dtype=np.float32)
+        self.L.csa_oracle_lse_merge(_p(out_a), _p(lse_a), _p(out_b), _p(lse_b), h, _p(out), _p(lse))
         return out, lse
 
     def dense_attention(self, kv_rows, q_attn, softmax_scale: float):

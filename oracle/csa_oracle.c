@@ -29,6 +29,19 @@
  *    "Optimization details": exact score-split attention over every
  *    compressed row, no row ceiling): the same textbook softmax attention
  *    over all n rows, each row used once, in row order.
+ *  - Packing new rows (the pack path of DS4X README, "Packed cache ABI": new
+ *    compressed and raw-ring rows are written in the 583/68-byte formats):
+ *    the pages name the formats but not the conversion.  The reading adopted
+ *    is the OCP MX v1.0 block conversion: byte = floor(log2 amax) - emax + 127
+ *    (emax 8 for E4M3, 2 for E2M1), clamped to [0, 254], 127 for an all-zero
+ *    block; each element v / 2^(byte-127) rounded to the nearest element
+ *    value, ties to the even significand, saturating (448 for E4M3, 6 for
+ *    E2M1); a value that rounds to zero is stored as +0.  The RoPE values are
+ *    IEEE binary16, round to nearest even (overflow gives infinity).
+ *  - Merging two attention results over disjoint row sets (the sliding-window
+ *    raw ring and the compressed rows share one softmax): out = (e^{a-M}
+ *    out_a + e^{b-M} out_b) / (e^{a-M} + e^{b-M}), lse = M + log(e^{a-M} +
+ *    e^{b-M}), M = max(a, b), a and b the two log-sum-exps, in double.
  *  - MXFP4 query (the block-scaled scorer of DS4X README, "What DS4X
  *    changes" and "Optimization details"): the pages never say how the fp32
  *    query becomes an MXFP4 operand.  The reading adopted is the OCP MX v1.0
@@ -273,6 +286,134 @@ void csa_oracle_quantize_query(const float *q, int n_heads, uint8_t *rows) {
       for (int i = 0; i < 32; ++i) code[32 * b + i] = e2m1_nearest(ldexp((double)v[i], -shared));
     }
     for (int i = 0; i < 64; ++i) r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));
+  }
+}
+
+/* ---------------- packing new rows ---------------- */
+
+/* The element value nearest to |y| among the non-negative values of a
+ * format (codes 0..ncodes-1 ascending, value(c) from `val`), a tie going to
+ * the code with an even significand bit; values past the largest give the
+ * largest (saturation). */
+static int nearest_code(double y, int ncodes, double (*val)(int)) {
+  double a = fabs(y);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c < ncodes; ++c) {
+    double v = val(c);
+    if (isnan(v)) continue;
+    double d = fabs(a - v);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
+/* OCP MX shared-exponent byte of a block with largest magnitude amax. */
+static int pack_scale_byte(double amax, int emax_elem) {
+  if (amax == 0.0) return 127;
+  int e;
+  frexp(amax, &e); /* floor(log2 amax) = e - 1 */
+  int b = (e - 1) - emax_elem + 127;
+  return b < 0 ? 0 : (b > 254 ? 254 : b);
+}
+
+/* IEEE binary16 bits of x, round to nearest even: the nearest of the 63,488
+ * finite non-negative binary16 values (ties to even), infinity at or beyond
+ * 65520 (the midpoint past the largest finite value). */
+static int f16_bits_of(double x) {
+  int s = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a >= 65520.0) return s | 0x7C00;
+  /* candidate neighbours: the binary16 values at the same exponent */
+  int best = 0;
+  double best_d = INFINITY;
+  int e;
+  frexp(a, &e);
+  int lo = 0, hi = 0x7BFF;
+  if (a > 0.0) {
+    int ee = (e - 1) + 15; /* biased exponent of a, before rounding */
+    if (ee < 1) ee = 0;
+    lo = ee > 0 ? ((ee - 1) << 10) : 0;
+    hi = (ee + 1) << 10;
+    if (hi > 0x7BFF) hi = 0x7BFF;
+  } else {
+    hi = 0;
+  }
+  for (int c = lo; c <= hi; ++c) {
+    double v = csa_oracle_f16(c);
+    double d = fabs(a - v);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return s | best; /* the sign is kept, -0 included (IEEE) */
+}
+
+void csa_oracle_pack_kv_rows(const float *v, int64_t n, uint8_t *rows) {
+  for (int64_t j = 0; j < n; ++j) {
+    const float *x = v + j * 512;
+    uint8_t *r = rows + j * KV_ROW;
+    for (int b = 0; b < 7; ++b) {
+      double amax = 0.0;
+      for (int i = 0; i < 64; ++i)
+        if (fabs((double)x[64 * b + i]) > amax) amax = fabs((double)x[64 * b + i]);
+      int sb = pack_scale_byte(amax, 8);
+      r[576 + b] = (uint8_t)sb;
+      for (int i = 0; i < 64; ++i) {
+        double y = ldexp((double)x[64 * b + i], 127 - sb);
+        int c = nearest_code(y, 127, csa_oracle_e4m3); /* codes 0..126: 0 .. 448 */
+        r[64 * b + i] = (uint8_t)((c != 0 && signbit(y)) ? (c | 0x80) : c);
+      }
+    }
+    for (int t = 0; t < 64; ++t) {
+      int h = f16_bits_of((double)x[448 + t]);
+      r[448 + 2 * t] = (uint8_t)(h & 0xFF);
+      r[448 + 2 * t + 1] = (uint8_t)(h >> 8);
+    }
+  }
+}
+
+void csa_oracle_pack_idx_rows(const float *v, int64_t n, uint8_t *rows) {
+  for (int64_t j = 0; j < n; ++j) {
+    const float *x = v + j * 128;
+    uint8_t *r = rows + j * IDX_ROW;
+    int code[128];
+    for (int b = 0; b < 4; ++b) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs((double)x[32 * b + i]) > amax) amax = fabs((double)x[32 * b + i]);
+      int sb = pack_scale_byte(amax, 2);
+      r[64 + b] = (uint8_t)sb;
+      for (int i = 0; i < 32; ++i) {
+        double y = ldexp((double)x[32 * b + i], 127 - sb);
+        int c = nearest_code(y, 8, csa_oracle_e2m1);
+        code[32 * b + i] = (c != 0 && signbit(y)) ? (c | 8) : c;
+      }
+    }
+    for (int i = 0; i < 64; ++i) r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));
+  }
+}
+
+/* ---------------- merging two attention results ---------------- */
+
+void csa_oracle_lse_merge(const float *out_a, const float *lse_a, const float *out_b, const float *lse_b,
+                          int n_heads, float *out, float *lse) {
+  for (int h = 0; h < n_heads; ++h) {
+    double a = lse_a[h], b = lse_b[h];
+    double M = a > b ? a : b;
+    if (M == -INFINITY) { /* neither side has a row */
+      for (int e = 0; e < 512; ++e) out[h * 512 + e] = 0.0f;
+      lse[h] = -INFINITY;
+      continue;
+    }
+    double wa = exp(a - M), wb = exp(b - M);
+    for (int e = 0; e < 512; ++e)
+      out[h * 512 + e] = (float)((wa * out_a[h * 512 + e] + wb * out_b[h * 512 + e]) / (wa + wb));
+    lse[h] = (float)(M + log(wa + wb));
   }
 }
 

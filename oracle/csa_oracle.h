@@ -24,6 +24,14 @@ int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *
 /* Softmax attention over every row (each row once, in row order). */
 int csa_oracle_dense_attention(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads,
                                double softmax_scale, float *out, float *lse);
+/* New rows packed into the 583-byte KV format ([n][512] values) and the
+ * 68-byte indexer format ([n][128] values). */
+void csa_oracle_pack_kv_rows(const float *v, int64_t n, uint8_t *rows);
+void csa_oracle_pack_idx_rows(const float *v, int64_t n, uint8_t *rows);
+/* The merge of two attention results over disjoint rows ([n_heads][512] and
+ * [n_heads] each). */
+void csa_oracle_lse_merge(const float *out_a, const float *lse_a, const float *out_b, const float *lse_b,
+                          int n_heads, float *out, float *lse);
 /* The indexer query [n_heads][128] quantized to MXFP4 rows [n_heads][68]. */
 void csa_oracle_quantize_query(const float *q, int n_heads, uint8_t *rows);
 int csa_oracle_decode_step(const uint8_t *idx_rows, const uint8_t *kv_rows, int64_t n_rows,

@@ -425,5 +425,99 @@ def check_quantize_query(o) -> None:
     assert np.array_equal(o.quantize_query(qhat), rows)
 
 
+# ------------------------------------------------ packing new rows, the merge
+
+def lib_e4m3_code(y: np.ndarray) -> np.ndarray:
+    """E4M3 codes of |y| <= 464 by torch's float8_e4m3fn conversion (round to
+    nearest even)."""
+    t = torch.as_tensor(np.asarray(y, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().astype(np.int64)
+
+
+def check_pack(o) -> None:
+    rng = np.random.default_rng(21)
+    n = 24
+    v = (rng.standard_normal((n, 512)) * 2.0 ** rng.integers(-30, 30, (n, 1))).astype(np.float32)
+    v[1, :64] = 0.0                                                     # a zero block
+    v[2, 64:128] = (rng.integers(-15, 16, 64) * 0.0625).astype(np.float32)  # exact E4M3 ties at scale 2^-? blocks
+    v[3, 448:] = (rng.standard_normal(64) * 1e-6).astype(np.float32)    # binary16 subnormals
+    v[4, 448:] = (rng.standard_normal(64) * 3e4).astype(np.float32)     # binary16 overflow to infinity
+    v[5, 448:] = np.array([65504.0, 65519.0, 65520.0, -65520.0, 2.0 ** -25, 3 * 2.0 ** -26] * 10 + [0.0, -0.0, 1.0, -1.0],
+                          np.float32)
+    rows = o.pack_kv(v)
+    # RoPE part: numpy's IEEE binary16 conversion, bit for bit
+    with np.errstate(over="ignore"):
+        f16 = v[:, 448:].astype("<f2")
+    assert np.array_equal(rows[:, 448:576], f16.view(np.uint8).reshape(n, 128)), "f16"
+    # non-RoPE blocks: the scale byte by frexp, the codes by torch's E4M3
+    for j in range(n):
+        for b in range(7):
+            x = v[j, 64 * b:64 * b + 64].astype(np.float64)
+            amax = float(np.max(np.abs(x)))
+            byte = 127 if amax == 0.0 else min(max(math.frexp(amax)[1] - 1 - 8 + 127, 0), 254)
+            assert rows[j, 576 + b] == byte, ("e4m3 scale", j, b)
+            y = x * 2.0 ** (127 - byte)
+            want = lib_e4m3_code(np.clip(y, -448.0, 448.0))     # beyond 448: saturation
+            want = np.where((want & 0x7F) == 0, 0, want)         # zeros stored as +0
+            assert np.array_equal(rows[j, 64 * b:64 * b + 64].astype(np.int64), want), ("e4m3", j, b)
+    # hand-worked E4M3 cases at scale byte 127 (block maximum in [256, 512))
+    x = np.zeros((1, 512), np.float32)
+    x[0, :9] = [480.0, 464.0, 1.0625, 1.1875, 0.0009765625, -0.00146484375, 300.0, -0.0009, -0.0029296875]
+    r = o.pack_kv(x)
+    assert r[0, 576] == 127
+    # 480 and 464 saturate to 448 (0x7E); 1.0625 ties to 1.0 (0x38), 1.1875
+    # to 1.25 (0x3A); 2^-10 ties between 0 and 2^-9 -> +0; -0.75 * 2^-9 ->
+    # -2^-9 (0x81); 300 -> 288 = 2^8 * 1.125 (0x79); -0.0009 = -0.46 * 2^-9 ->
+    # +0; -1.5 * 2^-9 ties between 2^-9 and 2^-8 -> -2^-8 (0x82)
+    assert list(r[0, :9]) == [0x7E, 0x7E, 0x38, 0x3A, 0x00, 0x81, 0x79, 0x00, 0x82], list(r[0, :9])
+    # the indexer format: exhaustive nearest-value search (zero block 127,
+    # zeros as +0), and the generator's encoder (an independent
+    # implementation of the same rule) on random rows
+    vi = (rng.standard_normal((12, 128)) * 2.0 ** rng.integers(-40, 40, (12, 128))).astype(np.float32)
+    vi[3, :32] = 0.0
+    vi[4] = (rng.integers(-16, 17, 128) * 0.25).astype(np.float32)
+    ri = o.pack_idx(vi)
+    byte, codes = brute_force_fp4(vi)
+    zero = np.max(np.abs(vi.reshape(-1, 32)), axis=1) == 0
+    byte = np.where(zero, 127, byte)
+    codes = np.where((codes & 7) == 0, 0, codes)
+    assert np.array_equal(ri[:, 64:68].reshape(-1), byte), "idx scale"
+    assert np.array_equal(unpack_codes(ri).reshape(-1, 32), codes), "idx codes"
+    import gen as _gen
+    g = _gen.lib()
+    for j in range(4):
+        gk = np.empty(583, np.uint8)
+        g.csa_gen_pack_kv_row(np.ascontiguousarray(v[j]).ctypes.data, gk.ctypes.data)
+        assert np.array_equal(gk, rows[j]), ("generator kv", j)
+        gi = np.empty(68, np.uint8)
+        g.csa_gen_pack_idx_row(np.ascontiguousarray(vi[j]).ctypes.data, gi.ctypes.data)
+        assert np.array_equal(gi, ri[j]), ("generator idx", j)
+
+
+def check_lse_merge(o) -> None:
+    """Attention over two disjoint row sets merged equals attention over their
+    union (an identity of the softmax); an empty side leaves the other."""
+    rng = np.random.default_rng(23)
+    rows = random_kv_rows(90, 8)
+    scale = float(np.float32(1 / math.sqrt(512)))
+    q = rng.standard_normal((5, 512)).astype(np.float32)
+    sa = rng.permutation(90)
+    A, B = sa[:50].astype(np.int32), sa[50:].astype(np.int32)
+    oa, la = o.attention(rows, A, q, scale)
+    ob, lb = o.attention(rows, B, q, scale)
+    om, lm = o.lse_merge(oa, la, ob, lb)
+    ref_o, ref_l = ref_attention(rows, np.concatenate([A, B]), q, scale)
+    assert np.max(np.abs(om - ref_o)) <= 2e-6 * np.max(np.abs(ref_o)), "merge out"
+    assert np.allclose(lm, ref_l, rtol=1e-6, atol=1e-6), "merge lse"
+    # swapping the sides gives the same result
+    om2, lm2 = o.lse_merge(ob, lb, oa, la)
+    assert np.max(np.abs(om2 - om)) <= 1e-6 * np.max(np.abs(om)) and np.allclose(lm2, lm, rtol=1e-7, atol=1e-7)
+    empty_o, empty_l = o.attention(rows, np.zeros(0, np.int32), q, scale)
+    om, lm = o.lse_merge(oa, la, empty_o, empty_l)
+    assert np.array_equal(om, oa) and np.array_equal(lm, la), "empty side"
+    om, lm = o.lse_merge(empty_o, empty_l, empty_o, empty_l)
+    assert np.all(om == 0) and np.all(np.isneginf(lm)), "both empty"
+
+
 ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention, check_decode_step,
-              check_quantize_query, check_dense_attention)
+              check_quantize_query, check_dense_attention, check_pack, check_lse_merge)

@@ -49,15 +49,35 @@ MUTANTS = [
      "csa_oracle_attention(kv_rows, n_rows, all, (int)n_rows - (n_rows > 1),"),
     ("dense_row_offset", "for (int64_t j = 0; j < n_rows; ++j) all[j] = (int32_t)j;",
      "for (int64_t j = 0; j < n_rows; ++j) all[j] = (int32_t)(j / 2);"),
+    ("pack_e4m3_emax", "int sb = pack_scale_byte(amax, 8);", "int sb = pack_scale_byte(amax, 7);"),
+    ("pack_e2m1_emax", "int sb = pack_scale_byte(amax, 2);", "int sb = pack_scale_byte(amax, 3);"),
+    ("pack_tie_odd", "if (isnan(v)) continue;\n    double d = fabs(a - v);\n    if (d < best_d || (d == best_d && (c & 1) == 0))",
+     "if (isnan(v)) continue;\n    double d = fabs(a - v);\n    if (d < best_d || (d == best_d && (c & 1) == 1))"),
+    ("pack_f16_tie_odd", "double v = csa_oracle_f16(c);\n    double d = fabs(a - v);\n    if (d < best_d || (d == best_d && (c & 1) == 0))",
+     "double v = csa_oracle_f16(c);\n    double d = fabs(a - v);\n    if (d < best_d || (d == best_d && (c & 1) == 1))"),
+    ("pack_negative_zero", "r[64 * b + i] = (uint8_t)((c != 0 && signbit(y)) ? (c | 0x80) : c);",
+     "r[64 * b + i] = (uint8_t)(signbit(y) ? (c | 0x80) : c);"),
+    ("pack_zero_block_byte", "if (amax == 0.0) return 127;\n  int e;\n  frexp(amax, &e); /* floor(log2 amax) = e - 1 */\n  int b =",
+     "if (amax == 0.0) return 0;\n  int e;\n  frexp(amax, &e); /* floor(log2 amax) = e - 1 */\n  int b ="),
+    ("pack_f16_overflow", "if (a >= 65520.0) return s | 0x7C00;", "if (a >= 65536.0) return s | 0x7C00;"),
+    ("pack_f16_sign", "  return s | best; /* the sign is kept, -0 included (IEEE) */", "  return best;"),
+    ("pack_rope_bytes", "r[448 + 2 * t] = (uint8_t)(h & 0xFF);\n      r[448 + 2 * t + 1] = (uint8_t)(h >> 8);",
+     "r[448 + 2 * t] = (uint8_t)(h >> 8);\n      r[448 + 2 * t + 1] = (uint8_t)(h & 0xFF);"),
+    ("merge_weights_swapped", "(wa * out_a[h * 512 + e] + wb * out_b[h * 512 + e])", "(wb * out_a[h * 512 + e] + wa * out_b[h * 512 + e])"),
+    ("merge_lse_no_max", "lse[h] = (float)(M + log(wa + wb));", "lse[h] = (float)log(wa + wb);"),
     ("q4_scale_offset", "shared = (e - 1) - 2;", "shared = (e - 1) - 1;"),
     ("q4_ceil_log2", "shared = (e - 1) - 2;", "shared = e - 2;"),
-    ("q4_tie_odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
-    ("q4_tie_to_lower", "(d == best_d && (c & 1) == 0)", "(0)"),
+    ("q4_tie_odd", "double d = fabs(a - csa_oracle_e2m1(c));\n    if (d < best_d || (d == best_d && (c & 1) == 0))",
+     "double d = fabs(a - csa_oracle_e2m1(c));\n    if (d < best_d || (d == best_d && (c & 1) == 1))"),
+    ("q4_tie_to_lower", "double d = fabs(a - csa_oracle_e2m1(c));\n    if (d < best_d || (d == best_d && (c & 1) == 0))",
+     "double d = fabs(a - csa_oracle_e2m1(c));\n    if (d < best_d || (0))"),
     ("q4_sign_dropped", "return signbit(y) ? (best | 8) : best;", "return (y < 0.0) ? (best | 8) : best;"),
     ("q4_no_clamp", "if (shared < -127) shared = -127;", ""),
     ("q4_zero_block_byte", "int shared = -127; /* the all-zero block */", "int shared = 0; /* the all-zero block */"),
-    ("q4_nibble_order", "r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));",
-     "r[i] = (uint8_t)((code[2 * i] << 4) | code[2 * i + 1]);"),
+    ("q4_nibble_order", "-shared));\n    }\n    for (int i = 0; i < 64; ++i) r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));",
+     "-shared));\n    }\n    for (int i = 0; i < 64; ++i) r[i] = (uint8_t)((code[2 * i] << 4) | code[2 * i + 1]);"),
+    ("pack_idx_nibble_order", "(c | 8) : c;\n      }\n    }\n    for (int i = 0; i < 64; ++i) r[i] = (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));",
+     "(c | 8) : c;\n      }\n    }\n    for (int i = 0; i < 64; ++i) r[i] = (uint8_t)((code[2 * i] << 4) | code[2 * i + 1]);"),
     ("q4_scale_slot", "r[64 + b] = (uint8_t)(shared + 127);", "r[64 + (b + 1) % 4] = (uint8_t)(shared + 127);"),
 ]
 
