@@ -229,6 +229,46 @@ def measure_dense(n_rows, steps, flush, dev, csa, gen, np, torch):
             "algorithmic_bytes": alg, "hbm_gbs": round(alg / (med * 1e-3) / 1e9, 2)}
 
 
+def measure_layer_parts(steps, flush, dev, csa, gen, np, torch):
+    """Cold times of the rest of a decode layer around the CSA step: the
+    append of one new row (its 583-byte KV row and 68-byte indexer row), the
+    dense attention over a 256-row raw sliding-window ring, and the merge of
+    the two attention results."""
+    s = gen.session(2, n_rows=256)
+    ring = torch.from_numpy(s["kv_rows"]).to(dev)
+    q = torch.from_numpy(s["q_attn"]).to(dev)
+    g = torch.Generator().manual_seed(7)
+    kv_new = torch.randn((1, 512), generator=g).to(dev)
+    idx_new = torch.randn((1, 128), generator=g).to(dev)
+    kv_slot = torch.empty((1, 583), dtype=torch.uint8, device=dev)
+    idx_slot = torch.empty((1, 68), dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(csa.lib.csa_dense_workspace_bytes(256)), dtype=torch.uint8, device=dev)
+    o_r = torch.empty((64, 512), dtype=torch.float32, device=dev)
+    l_r = torch.empty(64, dtype=torch.float32, device=dev)
+    o_c, l_c = torch.randn((64, 512), device=dev), torch.randn(64, device=dev)
+    stream = torch.cuda.current_stream()
+    parts = {
+        "append_one_row_us": lambda: csa.pack_rows(kv_new, idx_new, kv_rows=kv_slot, idx_rows=idx_slot),
+        "ring_attention_256_rows_us": lambda: csa.dense_attn(ring, q, s["softmax_scale"], ws=ws, out=o_r, lse=l_r),
+        "lse_merge_us": lambda: csa.lse_merge(o_c, l_c, o_r, l_r),
+    }
+    res = {}
+    for name, fn in parts.items():
+        for _ in range(3):
+            fn()
+        t = []
+        for _ in range(steps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3)
+        res[name] = round(statistics.median(t), 2)
+    return res
+
+
 def filter_diagnostics(d, outs, csa, np, torch, query_format):
     """How much the matrix-core filter leaves to the exact rescoring, on
     session 0 (outside the timed steps, library calls only): the brackets'
@@ -345,6 +385,7 @@ def main():
         line["filter"] = r["filter"]
     if not a.steps_only:  # dense attention of a ratio-128 (HCA) layer at a 1M-token context
         line["dense_attention"] = measure_dense(8194, a.sweep_steps, flush, dev, csa, gen, np, torch)
+        line["layer_parts"] = measure_layer_parts(a.sweep_steps, flush, dev, csa, gen, np, torch)
     if r_q4 is not None:
         line["mxfp4_query"] = {
             "cold_median_ms": round(r_q4["median_ms"], 5),

@@ -162,6 +162,35 @@ size_t csa_dense_workspace_bytes(int64_t n_rows);
 int csa_dense_attn(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads, float softmax_scale,
                    float *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
 
+/* New rows in the packed formats (DS4X page, "Packed cache ABI": new
+ * compressed rows and raw sliding-window ring rows are stored as 583-byte KV
+ * rows, compressed indexer keys as 68-byte rows).  Row j of kv_vals
+ * ([n_rows][512] fp32: 448 non-RoPE values, then 64 RoPE values) is written
+ * to kv_rows + 583 j, row j of idx_vals ([n_rows][128]) to idx_rows + 68 j;
+ * either value array may be NULL (that output is not written), not both.
+ * The pages name the formats but not the conversion; this is the OCP MX v1.0
+ * block conversion: per block the UE8M0 byte is floor(log2 max|v|) - emax +
+ * 127 (emax 8 for E4M3 over 64 values, 2 for E2M1 over 32) clamped to
+ * [0, 254], 127 for an all-zero block; each element v / 2^(byte-127) rounds
+ * to the nearest element value, ties to the even significand, saturating at
+ * 448 / 6, a value rounding to zero stored as +0; RoPE values become IEEE
+ * binary16 (round to nearest even, overflow to infinity).  Inputs must be
+ * finite.  kv_vals 4-byte and idx_vals 8-byte aligned; n_rows in
+ * [0, CSA_MAX_ROWS]. */
+int csa_pack_rows(const float *kv_vals, const float *idx_vals, int64_t n_rows, uint8_t *kv_rows, uint8_t *idx_rows,
+                  void *hip_stream);
+
+/* Merge of two attention results over disjoint row sets into the attention
+ * over their union (the sliding-window raw ring and the selected compressed
+ * rows in one softmax): with a = lse_a[h], b = lse_b[h], M = max(a, b),
+ *   out[h] = (e^{a-M} out_a[h] + e^{b-M} out_b[h]) / (e^{a-M} + e^{b-M}),
+ *   lse[h] = M + log(e^{a-M} + e^{b-M});
+ * a side with lse = -inf (no row) weighs nothing; both -inf give out = 0 and
+ * lse = -inf.  All arrays [n_heads][512] / [n_heads], n_heads in [1, 64];
+ * out may be out_a or out_b (in place), lse must not be lse_a or lse_b. */
+int csa_lse_merge(const float *out_a, const float *lse_a, const float *out_b, const float *lse_b, int n_heads,
+                  float *out, float *lse, void *hip_stream);
+
 /* One CSA decode step for each of n_sessions independent sessions: score
  * every indexer row, select the exact top-512 (csa_topk order) and attend
  * over the selected KV rows (csa_sparse_attn).  Selections and outputs are

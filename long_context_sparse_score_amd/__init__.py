@@ -74,6 +74,10 @@ def _load() -> ctypes.CDLL:
     L.csa_dense_workspace_bytes.argtypes = [i64]
     L.csa_dense_attn.restype = i32
     L.csa_dense_attn.argtypes = [vp, i64, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.csa_pack_rows.restype = i32
+    L.csa_pack_rows.argtypes = [vp, vp, i64, vp, vp, vp]
+    L.csa_lse_merge.restype = i32
+    L.csa_lse_merge.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
     L.csa_quantize_query.restype = i32
     L.csa_quantize_query.argtypes = [vp, i32, vp, vp]
     L.csa_decode_step_ex.restype = i32
@@ -264,6 +268,51 @@ def dense_attn(kv_rows: torch.Tensor, q_attn: torch.Tensor, softmax_scale: float
     _check(lib.csa_dense_attn(_ptr(kv_rows, torch.uint8, "kv_rows"), n, _ptr(q_attn, torch.float32, "q_attn"), h,
                               softmax_scale, _ptr(out, torch.float32), _ptr(lse, torch.float32),
                               _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_dense_attn")
+    return out, lse
+
+
+def pack_rows(kv_vals: torch.Tensor | None = None, idx_vals: torch.Tensor | None = None, kv_rows=None, idx_rows=None,
+              stream=None):
+    """New rows in the packed formats (csa_pack_rows): kv_vals [n][512] ->
+    583-byte rows, idx_vals [n][128] -> 68-byte rows.  Returns (kv_rows,
+    idx_rows) (None where no values were given)."""
+    if kv_vals is None and idx_vals is None:
+        raise ValueError("pack_rows: kv_vals or idx_vals")
+    n = None
+    if kv_vals is not None:
+        n = _mat(kv_vals, KV_DIM, "kv_vals")
+        if kv_rows is None:
+            kv_rows = torch.empty((n, KV_ROW_BYTES), dtype=torch.uint8, device=kv_vals.device)
+        if _rows(kv_rows, KV_ROW_BYTES, "kv_rows") < n:
+            raise ValueError("kv_rows: fewer rows than kv_vals")
+    if idx_vals is not None:
+        ni = _mat(idx_vals, IDX_DIM, "idx_vals")
+        if n is not None and ni != n:
+            raise ValueError("kv_vals and idx_vals disagree on the row count")
+        n = ni
+        if idx_rows is None:
+            idx_rows = torch.empty((n, IDX_ROW_BYTES), dtype=torch.uint8, device=idx_vals.device)
+        if _rows(idx_rows, IDX_ROW_BYTES, "idx_rows") < n:
+            raise ValueError("idx_rows: fewer rows than idx_vals")
+    if n == 0:
+        return kv_rows, idx_rows
+    _check(lib.csa_pack_rows(_ptr(kv_vals, torch.float32, "kv_vals"), _ptr(idx_vals, torch.float32, "idx_vals"), n,
+                             _ptr(kv_rows, torch.uint8, "kv_rows"), _ptr(idx_rows, torch.uint8, "idx_rows"),
+                             _stream(stream)), "csa_pack_rows")
+    return kv_rows, idx_rows
+
+
+def lse_merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: torch.Tensor, stream=None):
+    """The attention over the union of two disjoint row sets from their two
+    results (csa_lse_merge)."""
+    h = _mat(out_a, KV_DIM, "out_a")
+    _mat(out_b, KV_DIM, "out_b", h)
+    _vec(lse_a, h, "lse_a")
+    _vec(lse_b, h, "lse_b")
+    out = torch.empty_like(out_a)
+    lse = torch.empty_like(lse_a)
+    _check(lib.csa_lse_merge(_ptr(out_a, torch.float32), _ptr(lse_a, torch.float32), _ptr(out_b, torch.float32),
+                             _ptr(lse_b, torch.float32), h, _ptr(out), _ptr(lse), _stream(stream)), "csa_lse_merge")
     return out, lse
 
 

@@ -352,6 +352,25 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   return status_of(e);
 }
 
+int csa_pack_rows(const float *kv_vals, const float *idx_vals, int64_t n_rows, uint8_t *kv_rows, uint8_t *idx_rows,
+                  void *hip_stream) {
+  if (!rows_ok(n_rows) || (!kv_vals && !idx_vals)) return CSA_EINVAL;
+  if (kv_vals && (!kv_rows || ((uintptr_t)kv_vals & 3u) != 0)) return CSA_EINVAL;
+  if (idx_vals && (!idx_rows || ((uintptr_t)idx_vals & 7u) != 0)) return CSA_EINVAL;
+  int rc = check_device();
+  if (rc != CSA_OK) return rc;
+  return status_of(launch_pack(kv_vals, idx_vals, n_rows, kv_rows, idx_rows, (hipStream_t)hip_stream));
+}
+
+int csa_lse_merge(const float *out_a, const float *lse_a, const float *out_b, const float *lse_b, int n_heads,
+                  float *out, float *lse, void *hip_stream) {
+  if (!heads_ok(n_heads) || !out_a || !lse_a || !out_b || !lse_b || !out || !lse) return CSA_EINVAL;
+  if (lse == lse_a || lse == lse_b) return CSA_EINVAL;
+  int rc = check_device();
+  if (rc != CSA_OK) return rc;
+  return status_of(launch_lse_merge(out_a, lse_a, out_b, lse_b, n_heads, out, lse, (hipStream_t)hip_stream));
+}
+
 // Workspace of csa_dense_attn: [attention query split][group partials][group (m, l)].
 struct DenseLayout {
   size_t q_off, part_off, ml_off, total;

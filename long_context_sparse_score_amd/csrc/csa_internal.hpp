@@ -140,6 +140,13 @@ inline void dense_grouping(int64_t n_rows, int *rows_per_group, int *groups) {
 // the attention query split (launch_attn_q_split).
 hipError_t launch_dense_attn(const uint8_t *kv_rows, int64_t n_rows, const uint4 *qsplit, int n_heads, float scale,
                              float *part, float *ml, float *out, float *lse, hipStream_t st);
+// New rows packed into the 583/68-byte formats (csa_pack.hip); either
+// value array may be null.
+hipError_t launch_pack(const float *kv_vals, const float *idx_vals, int64_t n, uint8_t *kv_rows, uint8_t *idx_rows,
+                       hipStream_t st);
+// The merge of two attention results over disjoint rows (csa_pack.hip).
+hipError_t launch_lse_merge(const float *out_a, const float *lse_a, const float *out_b, const float *lse_b,
+                            int n_heads, float *out, float *lse, hipStream_t st);
 hipError_t launch_tiles(const TileJob &job, hipStream_t st);
 hipError_t launch_refine(const RefineJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);

@@ -119,6 +119,14 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_dense_attn(fake, 100, fake, 8, 0.1, fake, None, fake, 64, None) == csa.EWORKSPACE
     assert L.csa_dense_attn(fake, 100, fake, 8, 0.1, fake, None, ctypes.c_void_p(4096 + 8), 1 << 30, None) == csa.EWORKSPACE
     assert csa.lib.csa_dense_workspace_bytes(8194) > csa.lib.csa_dense_workspace_bytes(100) > 0
+    assert L.csa_pack_rows(None, None, 10, fake, fake, None) == csa.EINVAL
+    assert L.csa_pack_rows(fake, None, 10, None, fake, None) == csa.EINVAL
+    assert L.csa_pack_rows(None, fake, 10, fake, None, None) == csa.EINVAL
+    assert L.csa_pack_rows(None, ctypes.c_void_p(4096 + 4), 10, fake, fake, None) == csa.EINVAL
+    assert L.csa_pack_rows(fake, None, -1, fake, fake, None) == csa.EINVAL
+    assert L.csa_lse_merge(fake, fake, fake, fake, 0, fake, ctypes.c_void_p(8192), None) == csa.EINVAL
+    assert L.csa_lse_merge(fake, fake, fake, ctypes.c_void_p(8192), 8, fake, fake, None) == csa.EINVAL  # lse aliases lse_a
+    assert L.csa_lse_merge(fake, None, fake, fake, 8, fake, ctypes.c_void_p(8192), None) == csa.EINVAL
     assert L.csa_quantize_query(fake, 0, fake, None) == csa.EINVAL
     assert L.csa_quantize_query(fake, 65, fake, None) == csa.EINVAL
     assert L.csa_quantize_query(odd, 8, fake, None) == csa.EINVAL
