@@ -162,6 +162,21 @@ size_t csa_dense_workspace_bytes(int64_t n_rows);
 int csa_dense_attn(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads, float softmax_scale,
                    float *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
 
+/* Multi-token score and exact top-k over one history (DS4X page, "Packed
+ * prefill implementation": batch score/top-k for several query tokens, as in
+ * prefill and speculative verification): for every token t < n_tokens, the
+ * exact top-k of csa_score over idx_rows with query q_idx + t*n_idx_heads*128
+ * and weights w_idx + t*n_idx_heads (csa_topk order), written to
+ * sel_idx + t*k and, if sel_score is not NULL, sel_score + t*k.  Each
+ * token's selection is bit-identical to csa_score -> csa_topk for that
+ * token; the tokens' score passes run tile by tile side by side so a tile's
+ * rows are read from HBM once for all of them.  n_tokens in [1, 64],
+ * n_idx_heads in [1, 64], k in [1, 512]; idx_rows and q_idx 16-byte aligned;
+ * ws sized by csa_workspace_bytes(n_rows, n_tokens). */
+int csa_score_topk_multi(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
+                         int n_tokens, int n_idx_heads, int k, int32_t *sel_idx, float *sel_score, void *ws,
+                         size_t ws_bytes, void *hip_stream);
+
 /* New rows in the packed formats (DS4X page, "Packed cache ABI": new
  * compressed rows and raw sliding-window ring rows are stored as 583-byte KV
  * rows, compressed indexer keys as 68-byte rows).  Row j of kv_vals

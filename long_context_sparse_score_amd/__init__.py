@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
     L.csa_dense_workspace_bytes.argtypes = [i64]
     L.csa_dense_attn.restype = i32
     L.csa_dense_attn.argtypes = [vp, i64, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.csa_score_topk_multi.restype = i32
+    L.csa_score_topk_multi.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.csa_pack_rows.restype = i32
     L.csa_pack_rows.argtypes = [vp, vp, i64, vp, vp, vp]
     L.csa_lse_merge.restype = i32
@@ -269,6 +271,26 @@ def dense_attn(kv_rows: torch.Tensor, q_attn: torch.Tensor, softmax_scale: float
                               softmax_scale, _ptr(out, torch.float32), _ptr(lse, torch.float32),
                               _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_dense_attn")
     return out, lse
+
+
+def score_topk_multi(idx_rows: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor, k: int = TOPK,
+                     ws: torch.Tensor | None = None, stream=None):
+    """Exact top-k of every token's scores over one history
+    (csa_score_topk_multi): q_idx [T][H][128], w_idx [T][H] -> (sel [T][k],
+    sel_score [T][k])."""
+    n = _rows(idx_rows, IDX_ROW_BYTES, "idx_rows")
+    if q_idx.dim() != 3 or q_idx.shape[2] != IDX_DIM or w_idx.dim() != 2 or tuple(w_idx.shape) != tuple(q_idx.shape[:2]):
+        raise ValueError(f"q_idx [T][H][128] and w_idx [T][H] expected, got {tuple(q_idx.shape)} {tuple(w_idx.shape)}")
+    T, H = int(q_idx.shape[0]), int(q_idx.shape[1])
+    dev = idx_rows.device
+    if ws is None:
+        ws = alloc_workspace(n, T, dev)
+    sel = torch.empty((T, k), dtype=torch.int32, device=dev)
+    sel_score = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib.csa_score_topk_multi(_ptr(idx_rows, torch.uint8, "idx_rows"), n, _ptr(q_idx, torch.float32, "q_idx"),
+                                    _ptr(w_idx, torch.float32, "w_idx"), T, H, k, _ptr(sel), _ptr(sel_score),
+                                    _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "csa_score_topk_multi")
+    return sel, sel_score
 
 
 def pack_rows(kv_vals: torch.Tensor | None = None, idx_vals: torch.Tensor | None = None, kv_rows=None, idx_rows=None,

@@ -352,6 +352,49 @@ int csa_sparse_attn(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel_i
   return status_of(e);
 }
 
+int csa_score_topk_multi(const uint8_t *idx_rows, int64_t n_rows, const float *q_idx, const float *w_idx,
+                         int n_tokens, int n_idx_heads, int k, int32_t *sel_idx, float *sel_score, void *ws,
+                         size_t ws_bytes, void *hip_stream) {
+  if (!rows_ok(n_rows) || n_tokens < 1 || n_tokens > CSA_MAX_SESSIONS || !heads_ok(n_idx_heads) || k < 1 ||
+      k > CSA_TOPK || !q_idx || !w_idx || !sel_idx || !idx_aligned(q_idx))
+    return CSA_EINVAL;
+  if (n_rows > 0 && (!idx_rows || !idx_aligned(idx_rows))) return CSA_EINVAL;
+  Layout L;
+  int rc = check_ws(ws, ws_bytes, n_rows, n_tokens, &L);
+  if (rc != CSA_OK) return rc;
+  rc = check_device();
+  if (rc != CSA_OK) return rc;
+  hipStream_t st = (hipStream_t)hip_stream;
+  // each token is a session over the same rows (the score kernel runs their
+  // tiles side by side), selecting without attention
+  TileJob job;
+  job.mode = TileJob::kFilter;
+  job.n_idx_heads = n_idx_heads;
+  for (int t = 0; t < n_tokens; ++t) {
+    job.idx_rows[t] = idx_rows;
+    job.scores_in[t] = nullptr;
+    job.n_rows[t] = n_rows;
+    job.q[t] = q_idx + (size_t)t * n_idx_heads * CSA_IDX_DIM;
+    job.w[t] = w_idx + (size_t)t * n_idx_heads;
+  }
+  fill_job(job, L, ws, n_tokens);
+  RefineJob rj;
+  fill_refine(rj, job, L, ws, k);
+  const bool exact_all = n_rows <= (int64_t)2 * rj.blocks * kRefineWaves;
+  if (exact_all) rj.mode = RefineJob::kKeysAll;
+  SelectJob sj;
+  fill_select(sj, job, rj, k);
+  for (int t = 0; t < n_tokens; ++t) {
+    sj.sel_idx[t] = sel_idx + (size_t)t * k;
+    sj.sel_score[t] = sel_score ? sel_score + (size_t)t * k : nullptr;
+  }
+  hipError_t e = hipSuccess;
+  if (!exact_all) e = launch_tiles(job, st);
+  if (e == hipSuccess && n_rows > 0) e = launch_refine(rj, st);
+  if (e == hipSuccess) e = launch_select(sj, st);
+  return status_of(e);
+}
+
 int csa_pack_rows(const float *kv_vals, const float *idx_vals, int64_t n_rows, uint8_t *kv_rows, uint8_t *idx_rows,
                   void *hip_stream) {
   if (!rows_ok(n_rows) || (!kv_vals && !idx_vals)) return CSA_EINVAL;

@@ -56,6 +56,9 @@ struct TileArgs {
   int tile_rows;
   int n_idx_heads;
   int mode;  // TileJob::Mode
+  int shared_rows;  // > 0: every session scores the same rows; the grid is
+                    // one-dimensional, tile-major (the sessions of a tile run
+                    // side by side and share its rows in the L2)
 };
 static_assert(sizeof(TileArgs) <= 4096, "kernel argument block");
 
@@ -482,11 +485,12 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
 // and writes every row's bracket (a test entry point; no heads).
 template <int G, bool ARRAY, int QF>
 __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a) {
-  const int sess = blockIdx.y;
+  const int sess = a.shared_rows ? (int)(blockIdx.x % (unsigned)a.shared_rows) : (int)blockIdx.y;
+  const int tile = a.shared_rows ? (int)(blockIdx.x / (unsigned)a.shared_rows) : (int)blockIdx.x;
   const TileSession &S = a.s[sess];
   const int64_t n = S.n_rows;
   const int T = a.tile_rows;
-  const int64_t row0 = (int64_t)blockIdx.x * T;
+  const int64_t row0 = (int64_t)tile * T;
   if (row0 >= n) return;
   const int rows = (int)((n - row0) < T ? (n - row0) : T);
   __shared__ TileShared sh;
@@ -494,7 +498,7 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   uint32_t o = 0;  // largest score part of this thread's positions
   if constexpr (!ARRAY) {
     const bool bounds = a.mode == TileJob::kBounds;
-    float *qhat = (QF == kQueryMxfp4 && a.qhat && blockIdx.x == 0) ? a.qhat + (size_t)sess * CSA_MAX_HEADS * 128 : nullptr;
+    float *qhat = (QF == kQueryMxfp4 && a.qhat && tile == 0) ? a.qhat + (size_t)sess * CSA_MAX_HEADS * 128 : nullptr;
     o = score_tile<G, QF>(S.q, S.w, a.n_idx_heads, S.idx_rows, row0, n, rows, sh, bounds ? a.bnd_up + row0 : nullptr,
                           bounds ? a.bnd_lo + row0 : nullptr, qhat);
     if (bounds) return;
@@ -524,9 +528,9 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
   }
   // rank-major heads of the session: rank r of tile t at r * nt + t
   const int64_t nt = (n + T - 1) / T;
-  const size_t hb = (size_t)sess * a.heads_stride + (size_t)blockIdx.x;
+  const size_t hb = (size_t)sess * a.heads_stride + (size_t)tile;
   tile_heads(sh, o, rows, row0, S.hd, a.hkey + hb, a.hlow + hb, nt,
-             a.hnext + (size_t)sess * a.tiles_stride + blockIdx.x);
+             a.hnext + (size_t)sess * a.tiles_stride + tile);
 }
 
 // ---------------------------------------------------------------- launcher
@@ -569,8 +573,14 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   a.tiles_stride = job.tiles_stride;
   a.tile_rows = job.tile_rows;
   a.mode = (int)job.mode;
+  // sessions over the same rows (multi-token scoring): a tile-major grid
+  bool shared = job.n_sessions > 1;
+  for (int i = 1; i < job.n_sessions; ++i)
+    shared = shared && job.idx_rows[i] == job.idx_rows[0] && job.n_rows[i] == job.n_rows[0];
+  a.shared_rows = shared ? job.n_sessions : 0;
   const int groups = (job.n_idx_heads + 15) / 16;
-  dim3 grid((unsigned)((max_rows + job.tile_rows - 1) / job.tile_rows), (unsigned)job.n_sessions);
+  const unsigned nt = (unsigned)((max_rows + job.tile_rows - 1) / job.tile_rows);
+  dim3 grid = shared ? dim3(nt * (unsigned)job.n_sessions, 1u) : dim3(nt, (unsigned)job.n_sessions);
   if (job.mode == TileJob::kArray) {
     tile_kernel<1, true, kQueryFp32><<<grid, kTileThreads, 0, st>>>(a);
     return hipGetLastError();

@@ -50,6 +50,8 @@ class Oracle:
         L.csa_oracle_attention.restype = i32
         L.csa_oracle_attention.argtypes = [vp, i64, vp, i32, vp, i32, dbl, vp, vp]
         L.csa_oracle_quantize_query.argtypes = [vp, i32, vp]
+        L.csa_oracle_score_topk_multi.restype = i32
+        L.csa_oracle_score_topk_multi.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
         L.csa_oracle_pack_kv_rows.argtypes = [vp, i64, vp]
         L.csa_oracle_pack_idx_rows.argtypes = [vp, i64, vp]
         L.csa_oracle_lse_merge.argtypes = [vp, vp, vp, vp, i32, vp, vp]
@@ -132,6 +134,22 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle attention failed ({rc})")
         return out, lse
+
+    def score_topk_multi(self, idx_rows, q_idx, w_idx, k: int = 512):
+        """Each token's exact top-k over the same rows: q_idx [T][H][128],
+        w_idx [T][H] -> (sel [T][k], sel_score [T][k])."""
+        idx_rows = _rows(idx_rows, 68)
+        q_idx = np.ascontiguousarray(q_idx, dtype=np.float32)
+        w_idx = np.ascontiguousarray(w_idx, dtype=np.float32)
+        T, H = w_idx.shape
+        assert q_idx.shape == (T, H, 128)
+        sel = np.empty((T, k), dtype=np.int32)
+        sel_score = np.empty((T, k), dtype=np.float32)
+        rc = self.L.csa_oracle_score_topk_multi(_p(idx_rows), idx_rows.shape[0], _p(q_idx), _p(w_idx), T, H, k,
+                                                _p(sel), _p(sel_score))
+        if rc != 0:
+            raise MemoryError("oracle multi-token top-k")
+        return sel, sel_score
 
     def pack_kv(self, v) -> np.ndarray:
         """Rows of 512 values packed into 583-byte KV rows."""

@@ -25,6 +25,9 @@
  *    fusion").  A full sort is used.
  *  - Attention: textbook softmax attention over the selected rows, with the
  *    decoded 512-value row used as both key and value, in double.
+ *  - Multi-token score/top-k (DS4X README, "Packed prefill implementation":
+ *    batch score/top-k): for each token its own score over the same rows and
+ *    its own exact top-k, token after token.
  *  - Dense attention (the HCA layers of DS4X README, "What DS4X changes" and
  *    "Optimization details": exact score-split attention over every
  *    compressed row, no row ceiling): the same textbook softmax attention
@@ -231,6 +234,24 @@ int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *
     if (lse) lse[h] = (float)(m + log(z));
   }
   free(kv); free(logit); free(acc);
+  return 0;
+}
+
+/* ---------------- multi-token score/top-k ---------------- */
+
+int csa_oracle_score_topk_multi(const uint8_t *idx_rows, int64_t n, const float *q_idx, const float *w_idx,
+                                int n_tokens, int n_idx_heads, int k, int32_t *sel, float *sel_score) {
+  float *scores = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  if (!scores) return -1;
+  for (int t = 0; t < n_tokens; ++t) {
+    csa_oracle_score(idx_rows, n, q_idx + (size_t)t * n_idx_heads * 128, w_idx + (size_t)t * n_idx_heads,
+                     n_idx_heads, scores);
+    if (csa_oracle_topk(scores, n, k, sel + (size_t)t * k, sel_score ? sel_score + (size_t)t * k : NULL) < 0) {
+      free(scores);
+      return -1;
+    }
+  }
+  free(scores);
   return 0;
 }
 

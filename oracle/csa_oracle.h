@@ -21,6 +21,11 @@ int64_t csa_oracle_topk(const float *scores, int64_t n, int k, int32_t *sel, flo
 int csa_oracle_attention(const uint8_t *kv_rows, int64_t n_rows, const int32_t *sel, int n_sel,
                          const float *q_attn, int n_heads, double softmax_scale, float *out,
                          float *lse);
+/* For each of n_tokens queries ([n_tokens][n_idx_heads][128], weights
+ * [n_tokens][n_idx_heads]) its exact top-k over the same rows
+ * (sel, sel_score: [n_tokens][k]). */
+int csa_oracle_score_topk_multi(const uint8_t *idx_rows, int64_t n, const float *q_idx, const float *w_idx,
+                                int n_tokens, int n_idx_heads, int k, int32_t *sel, float *sel_score);
 /* Softmax attention over every row (each row once, in row order). */
 int csa_oracle_dense_attention(const uint8_t *kv_rows, int64_t n_rows, const float *q_attn, int n_heads,
                                double softmax_scale, float *out, float *lse);

@@ -519,5 +519,21 @@ def check_lse_merge(o) -> None:
     assert np.all(om == 0) and np.all(np.isneginf(lm)), "both empty"
 
 
+def check_score_topk_multi(o) -> None:
+    """Each token's selection against float64 einsum scores and Python's
+    sorted, over one shared history."""
+    rng = np.random.default_rng(29)
+    rows = random_idx_rows(700, 12)
+    T, H, k = 3, 5, 40
+    q = rng.standard_normal((T, H, 128)).astype(np.float32)
+    w = rng.uniform(-1, 1, (T, H)).astype(np.float32)
+    sel, sel_score = o.score_topk_multi(rows, q, w, k)
+    for t in range(T):
+        s = ref_score(rows, q[t], w[t])
+        want = [j for _, j in sorted((-float(s[j]), j) for j in range(len(s)))][:k]
+        assert list(sel[t]) == want, f"token {t}"
+        assert np.array_equal(sel_score[t], s[want].astype(np.float32)), f"token {t} scores"
+
+
 ALL_CHECKS = (check_tables, check_decode, check_score, check_topk, check_attention, check_decode_step,
-              check_quantize_query, check_dense_attention, check_pack, check_lse_merge)
+              check_quantize_query, check_dense_attention, check_pack, check_lse_merge, check_score_topk_multi)

@@ -119,6 +119,13 @@ def test_invalid_arguments_rejected_on_host(csa):
     assert L.csa_dense_attn(fake, 100, fake, 8, 0.1, fake, None, fake, 64, None) == csa.EWORKSPACE
     assert L.csa_dense_attn(fake, 100, fake, 8, 0.1, fake, None, ctypes.c_void_p(4096 + 8), 1 << 30, None) == csa.EWORKSPACE
     assert csa.lib.csa_dense_workspace_bytes(8194) > csa.lib.csa_dense_workspace_bytes(100) > 0
+    assert L.csa_score_topk_multi(fake, 10, fake, fake, 0, 8, 512, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score_topk_multi(fake, 10, fake, fake, 65, 8, 512, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score_topk_multi(fake, 10, fake, fake, 4, 8, 513, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score_topk_multi(fake, 10, fake, fake, 4, 8, 0, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score_topk_multi(odd, 10, fake, fake, 4, 8, 512, fake, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score_topk_multi(fake, 10, fake, fake, 4, 8, 512, None, None, fake, 1 << 30, None) == csa.EINVAL
+    assert L.csa_score_topk_multi(fake, 10, fake, fake, 4, 8, 512, fake, None, fake, 64, None) == csa.EWORKSPACE
     assert L.csa_pack_rows(None, None, 10, fake, fake, None) == csa.EINVAL
     assert L.csa_pack_rows(fake, None, 10, None, fake, None) == csa.EINVAL
     assert L.csa_pack_rows(None, fake, 10, fake, None, None) == csa.EINVAL

@@ -65,6 +65,10 @@ MUTANTS = [
      "r[448 + 2 * t] = (uint8_t)(h >> 8);\n      r[448 + 2 * t + 1] = (uint8_t)(h & 0xFF);"),
     ("merge_weights_swapped", "(wa * out_a[h * 512 + e] + wb * out_b[h * 512 + e])", "(wb * out_a[h * 512 + e] + wa * out_b[h * 512 + e])"),
     ("merge_lse_no_max", "lse[h] = (float)(M + log(wa + wb));", "lse[h] = (float)log(wa + wb);"),
+    ("multi_token_query_stride", "q_idx + (size_t)t * n_idx_heads * 128, w_idx + (size_t)t * n_idx_heads,",
+     "q_idx + (size_t)t * 128, w_idx + (size_t)t * n_idx_heads,"),
+    ("multi_token_output_order", "sel + (size_t)t * k, sel_score ? sel_score + (size_t)t * k : NULL",
+     "sel + (size_t)(n_tokens - 1 - t) * k, sel_score ? sel_score + (size_t)(n_tokens - 1 - t) * k : NULL"),
     ("q4_scale_offset", "shared = (e - 1) - 2;", "shared = (e - 1) - 1;"),
     ("q4_ceil_log2", "shared = (e - 1) - 2;", "shared = e - 2;"),
     ("q4_tie_odd", "double d = fabs(a - csa_oracle_e2m1(c));\n    if (d < best_d || (d == best_d && (c & 1) == 0))",
