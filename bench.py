@@ -269,6 +269,34 @@ def measure_layer_parts(steps, flush, dev, csa, gen, np, torch):
     return res
 
 
+def measure_multi_token(n_tokens, steps, flush, dev, csa, gen, np, torch):
+    """Cold time of csa_score_topk_multi: n_tokens queries over the 1M-row
+    history, each with its exact top-512."""
+    s = gen.session(3)
+    rows = torch.from_numpy(s["idx_rows"]).to(dev)
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn((n_tokens, 64, 128), generator=g).to(dev)
+    w = torch.rand((n_tokens, 64), generator=g).to(dev)
+    ws = csa.alloc_workspace(rows.shape[0], n_tokens, dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        flush.sum()
+        csa.score_topk_multi(rows, q, w, ws=ws)
+    t = []
+    for _ in range(steps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        csa.score_topk_multi(rows, q, w, ws=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    med = statistics.median(t)
+    return {"tokens": n_tokens, "rows": int(rows.shape[0]), "cold_median_ms": round(med, 5),
+            "ms_per_token": round(med / n_tokens, 5),
+            "indexer_gbs_once": round(68 * rows.shape[0] / (med * 1e-3) / 1e9, 1)}
+
+
 def filter_diagnostics(d, outs, csa, np, torch, query_format):
     """How much the matrix-core filter leaves to the exact rescoring, on
     session 0 (outside the timed steps, library calls only): the brackets'
@@ -386,6 +414,7 @@ def main():
     if not a.steps_only:  # dense attention of a ratio-128 (HCA) layer at a 1M-token context
         line["dense_attention"] = measure_dense(8194, a.sweep_steps, flush, dev, csa, gen, np, torch)
         line["layer_parts"] = measure_layer_parts(a.sweep_steps, flush, dev, csa, gen, np, torch)
+        line["multi_token_topk"] = [measure_multi_token(t, a.sweep_steps, flush, dev, csa, gen, np, torch) for t in (1, 4)]
     if r_q4 is not None:
         line["mxfp4_query"] = {
             "cold_median_ms": round(r_q4["median_ms"], 5),
