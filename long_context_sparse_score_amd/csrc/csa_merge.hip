@@ -130,19 +130,20 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
 
   const uint64_t *items = a.items + (size_t)sess * a.items_stride;
   const int64_t ni = (int64_t)a.count[sess];
+  // keys in registers: slot j of thread tid is item tid + 512 j.  The first
+  // kSelRegKeys slots of the session's item array are read without waiting
+  // for the count (the loads stay inside the array; slots past the count
+  // hold stale keys and are masked once it has arrived)
+  uint64_t h[kSelKPT];
+#pragma unroll
+  for (int j = 0; j < kSelKPT; ++j) {
+    const int64_t i = tid + (int64_t)kSelThreads * j;
+    h[j] = items[i < a.items_stride ? i : a.items_stride - 1];
+  }
   const bool reg = ni <= kSelRegKeys;  // uniform
   if (tid == 0) { sh.ccnt = 0; sh.nmine = 0; sh.nloc = 0; }
-
-  // keys in registers: slot j of thread tid is item tid + 512 j
-  uint64_t h[kSelKPT];
-  if (reg) {
 #pragma unroll
-    for (int j = 0; j < kSelKPT; ++j) {
-      const int64_t i = tid + (int64_t)kSelThreads * j;
-      const uint64_t y = items[i < ni ? i : (ni > 0 ? ni - 1 : 0)];  // clamped: no branch around the load
-      h[j] = i < ni ? y : 0ull;
-    }
-  }
+  for (int j = 0; j < kSelKPT; ++j) h[j] = tid + (int64_t)kSelThreads * j < ni ? h[j] : 0ull;
   // the candidates >= lb, in batches of 8 slots per thread: fb(ok[8], x[8])
   // in control flow uniform over the wave
   auto scan = [&](uint64_t lb, auto fb) __attribute__((always_inline)) {

@@ -319,6 +319,8 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   const uint64_t xk_raw = hkey[i_first < nh ? i_first : (gw < nh ? gw : nh - 1)];
   // G over the lower-bound keys of the first heads (a prefix of the
   // rank-major order: every tile's best heads), two per thread
+  // the first 512 tiles' next keys (the full-tile test after the bound)
+  const uint64_t nx_first = hnext[tid < nt ? tid : nt - 1];
   const int64_t nb = nh < kRefBoundHeads ? nh : kRefBoundHeads;
   uint64_t lk_raw[kRefKPT];
 #pragma unroll
@@ -361,7 +363,7 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(const RefineArgs a)
   // time, each wave's tiles placed after the earlier waves'
   for (int64_t t0 = 0; t0 < nt; t0 += kRefThreads) {
     const int64_t t = t0 + tid;
-    const uint64_t nx = t < nt ? hnext[t] : 0ull;
+    const uint64_t nx = t >= nt ? 0ull : (t0 == 0 ? nx_first : hnext[t]);
     const bool full = nx != 0 && nx >= G;
     const uint64_t m = __ballot(full);
     if (lane == 0) sh.wcnt[wave] = (uint32_t)__popcll(m);
