@@ -220,6 +220,35 @@ __device__ __forceinline__ void tile_heads(TileShared &sh, uint32_t o, int rows,
   if (C <= hd && tid == 0) *next_out = 0ull;
 }
 
+// Sums of fp64 values over lanes on the DPP network (the 32-bit halves move
+// separately; lanes without a source add +0).  row_sum_f64: inclusive scan
+// within each 16-lane row (lane 15 of a row ends with its sum);
+// wave_sum_f64: the whole wave's sum in every lane.  Summation order is
+// immaterial to the callers (bound constants with a rounding margin).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v += dpp_f64<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xF>(v);  // row_shr:8
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = row_sum_f64(v);
+  v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Rows [r0, r0 + 64) of a chunk that ends past the buffer: lane l copies
 // row min(r0 + l, n - 1) to dst + 68 l with ordinary loads (the compiler
 // waits for them before the LDS stores; rows past n are scored and dropped).
@@ -374,9 +403,8 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       const int h = 16 * wave + (lane & 15);
       const double wa = h < n_idx_heads ? fabs((double)wl[h]) : 0.0;
       double cz = wa * ((double)nm.rho + 0x1p-15 * (double)nm.mag);
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) cz += __shfl_xor(cz, m, 64);
-      if ((lane & 15) == 0) sh.a.zpart[wave][lane >> 4] = cz;
+      cz = row_sum_f64(cz);  // lane 15 of each 16-lane row: the row's sum
+      if ((lane & 15) == 15) sh.a.zpart[wave][lane >> 4] = cz;
       // the terms over the staging area (this wave's reads of it come first):
       // the lane's words (6 per term, then the packed scales) as 16-byte
       // quads, quad j of lane l at stage + 16 (64 j + l)
@@ -395,8 +423,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     }
     // Z_abs from the weights (every wave, its own copy): 2^-117 sum_h |w_h|
     double wsum = lane < n_idx_heads ? fabs((double)wl[lane]) : 0.0;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) wsum += __shfl_xor(wsum, m, 64);
+    wsum = wave_sum_f64(wsum);
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
