@@ -21,10 +21,29 @@
 //     final fp32 rounding of the exact score add 21 more roundings;
 //   * the fp64 evaluation of the reference adds below 2^-44 relative;
 // 412 * 2^-24 < 2^-15 covers all the relative terms; (1 + 2^-10) covers the
-// rounding of Z's own evaluation.  A block byte of 253 or more can decode
-// to an fp32 infinity: such a row gets an infinite bracket, as does a row
-// whose filter score is not finite.  The bracket is then rounded outward to
-// fp32: u = roundup(s~ + beta), l = rounddown(s~ - beta).
+// rounding of Z's own evaluation (fp64, once per query).  A block byte of 253
+// or more can decode to an fp32 infinity: such a row gets an infinite
+// bracket, as does a row whose filter score is not finite.
+//
+// Per row the bracket is evaluated in fp32 and widened so that no rounding
+// can cut into it (every step rounds to nearest):
+//   * zf_b, zfabs: Z_b, Z_abs rounded up to fp32 (once per query);
+//   * t_b = ldexp(zf_b, s_jb - 127) is exact unless it falls below 2^-126
+//     (then off by at most 2^-150) and +inf on overflow;
+//   * the four additions of the five nonnegative terms lose at most a
+//     factor (1 - 2^-24)^4, so sum >= (beta_j - 2^-148)(1 - 2^-24)^4;
+//   * beta' = fma(sum, 1 + 2^-20, 2^-139) >= beta_j + 2^-140, since
+//     (1 + 2^-20)(1 - 2^-24)^5 > 1 and 2^-139 (1 - 2^-24) > 2^-140 + 2^-148;
+//   * u0 = s~ + beta' is off by at most half an ulp of u0, and
+//     u = fma(|u0|, 2^-23, u0) lies at least one ulp above u0 when u0 is
+//     normal (|u0| 2^-23 is at least that ulp, and the next fp32 value away
+//     from u0 in that direction is then at or below the exact result);
+//     when u0 is below 2^-126 the half ulp (2^-150) is inside the 2^-140
+//     slack of beta'.  So u >= s~ + beta_j >= S_j; likewise
+//     l = fma(|l0|, -2^-23, l0) <= S_j with l0 = s~ - beta'.
+//   * In the other direction u <= s~ + beta' + 6 ulp(u), which the lower
+//     bound rebuilt from u and beta' (row_lower in the tile kernel) allows
+//     for.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,6 +54,12 @@ namespace csa {
 struct FilterBound {
   double z[4];  // Z_b (including the factor 6 (1 + 2^-10))
   double zabs;  // Z_abs
+};
+
+// The per-row constants in fp32, rounded up.
+struct FilterBoundF {
+  float z[4];
+  float zabs;
 };
 
 // The next fp32 value above / below f (f not NaN).
@@ -56,34 +81,33 @@ __device__ __forceinline__ float f32_round_down(double x) {
   return (double)f > x ? f32_next_down(f) : f;
 }
 
-// 2^(e - 127) as fp64 for a scale byte e <= 252 (always a normal fp64).
-__device__ __forceinline__ double pow2_ue8m0(uint32_t e) {
-  return __longlong_as_double((long long)((uint64_t)(e + 896u) << 52));
+__device__ __forceinline__ FilterBoundF bound_f32(const FilterBound &B) {
+  FilterBoundF F;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) F.z[b] = f32_round_up(B.z[b]);
+  F.zabs = f32_round_up(B.zabs);
+  return F;
 }
 
-// Bracket [lo, up] of the exact score of a row with filter score st and
-// block scale bytes sb (byte b = block b); returns its half-width beta (with
-// the outward margins; +inf for an infinite bracket).
-__device__ __forceinline__ double row_bracket(float st, uint32_t sb, const FilterBound &B, float &up, float &lo) {
-  bool inf = !(fabsf(st) <= 3.40282347e38f);
-  double beta = B.zabs;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint32_t e = (sb >> (8 * b)) & 255u;
-    inf = inf || e >= 253u;
-    beta += B.z[b] * pow2_ue8m0(e < 253u ? e : 0u);
+// Bracket of the exact score of a row with filter score st and block scale
+// bytes sb (byte b = block b): returns its half-width beta' (+inf for an
+// infinite bracket) and the upper bound u; with LOWER also the lower bound
+// l.  All fp32 (the margins above).
+template <bool LOWER>
+__device__ __forceinline__ float row_bracket(float st, uint32_t sb, const FilterBoundF &F, float &up, float &lo) {
+  const uint32_t e0 = sb & 255u, e1 = (sb >> 8) & 255u, e2 = (sb >> 16) & 255u, e3 = sb >> 24;
+  const bool inf = !(fabsf(st) <= 3.40282347e38f) || e0 > 252u || e1 > 252u || e2 > 252u || e3 > 252u;
+  const float t0 = __builtin_ldexpf(F.z[0], (int)e0 - 127), t1 = __builtin_ldexpf(F.z[1], (int)e1 - 127);
+  const float t2 = __builtin_ldexpf(F.z[2], (int)e2 - 127), t3 = __builtin_ldexpf(F.z[3], (int)e3 - 127);
+  const float sum = ((t0 + t1) + (t2 + t3)) + F.zabs;
+  const float beta = __builtin_fmaf(sum, 1.0f + 0x1p-20f, 0x1p-139f);
+  const float u0 = st + beta;
+  up = inf ? __builtin_inff() : __builtin_fmaf(fabsf(u0), 0x1p-23f, u0);
+  if constexpr (LOWER) {
+    const float l0 = st - beta;
+    lo = inf ? -__builtin_inff() : __builtin_fmaf(fabsf(l0), -0x1p-23f, l0);
   }
-  if (inf) {
-    up = __builtin_inff();
-    lo = -__builtin_inff();
-    return __builtin_inf();
-  }
-  // outward margin for the fp64 evaluation of beta and of st +- beta
-  const double s = (double)st;
-  beta = beta * (1.0 + 0x1p-30) + fabs(s) * 0x1p-50;
-  up = f32_round_up(s + beta);
-  lo = f32_round_down(s - beta);
-  return beta;
+  return inf ? __builtin_inff() : beta;
 }
 
 }  // namespace csa

@@ -59,6 +59,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until this wave's LDS loads and stores have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // A wave-uniform pointer moved to scalar registers (readfirstlane works on
 // 32 bits: each half separately).
 __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {

@@ -15,8 +15,7 @@
 //      (l_j, row j), and the (hd+1)-th ("next": every other row of the tile
 //      has a key at or below it).  A row's bracket is kept as u (fp32) and
 //      beta rounded up to bf16; the heads' lower bounds are rebuilt from them
-//      (l = rounddown(u - 2 beta - ulp(u)) <= s~ - beta, since u <= s~ + beta
-//      + ulp(u); exactly l = u when beta = 0, as for given scores).
+//      (row_lower; exactly l = u when beta = 0, as for given scores).
 // Nothing is written per row: the refine kernel (csa_refine.hip) takes the
 // heads that can reach the top-k and, for the rare tile whose "next" can,
 // every row of it, and scores them exactly.
@@ -86,8 +85,11 @@ struct TileShared {
   };
   struct {
     union {
-      float score[kMaxTileRows];    // upper bounds u by tile position (from the streaming loop on)
-      double zpart[kMaxGroups][4];  // bound constants per head group and block (prologue only)
+      float score[kMaxTileRows];  // upper bounds u by tile position (from the streaming loop on)
+      struct {
+        double zpart[kMaxGroups][4];  // bound constants per head group and block
+        uint4 xq[kMaxGroups][64];     // the last quad of each group's exchanged terms
+      } pro;                          // prologue only
     };
     uint16_t beta[kMaxTileRows];    // the bracket half-widths, bf16 rounded up
   } a;
@@ -95,19 +97,21 @@ struct TileShared {
 static_assert(sizeof(TileShared) <= 80 * 1024, "two workgroups per compute unit");
 
 // x >= 0 (or +inf) rounded up to bf16 bits.
-__device__ __forceinline__ uint16_t bf16_round_up(double x) {
-  const uint32_t b = __float_as_uint(f32_round_up(x));
+__device__ __forceinline__ uint16_t bf16_round_up(float x) {
+  const uint32_t b = __float_as_uint(x);
   return (uint16_t)((b >> 16) + ((b & 0xFFFFu) != 0u ? 1u : 0u));
 }
 
-// The lower bound of a row from its upper bound u and bf16 half-width bits.
+// The lower bound of a row from its upper bound u and bf16 half-width bits:
+// u lies at most 6 ulp(u) above s~ + beta (csa_bound.hpp), so
+// l = rounddown(u - 2 beta - 8 ulp(u)) <= s~ - beta; l = u when beta = 0
+// (given scores, exact).
 __device__ __forceinline__ float row_lower(float u, uint16_t bb) {
   const float beta = __uint_as_float((uint32_t)bb << 16);
   if (beta == 0.0f) return u;  // exact (given scores)
   if (!(fabsf(u) <= 3.40282347e38f) || !(beta <= 3.40282347e38f)) return -__builtin_inff();
-  // two ulps: one for u's rounding up, one covering the fp64 roundings here
   const double ulp = (double)f32_next_up(fabsf(u)) - (double)fabsf(u);
-  return f32_round_down((double)u - 2.0 * (double)beta - 2.0 * ulp);
+  return f32_round_down((double)u - 2.0 * (double)beta - 8.0 * ulp);
 }
 
 // Step 2: the tile's upper bounds in sh.a.score[0..rows) (half-widths in
@@ -305,13 +309,16 @@ __device__ __forceinline__ void load_ops(const uint8_t *base, RowOperand (&ops)[
 // Query terms: wave g brings the fp32 query of head group g (16 heads,
 // 8 KB) and all the weights direct-to-LDS into its ring slots 2 and 3 ahead
 // of its first two chunks (slots 0 and 1), so they arrive first and the
-// split runs while the chunks are in flight.  Each head's 512 bytes land at a 528-byte stride, so
-// the split's reads spread over the LDS banks; each wave then writes its
-// group's terms over its own staging area (16-byte quad j of lane l at
-// 16 (64 j + l)) and its part of the bound constants, and after one barrier
-// every wave reads every group's terms and the constants.  The third chunk
-// is issued once a second barrier has released the slots (the loop issues
-// the rest, always in order).
+// split runs while the chunks are in flight.  Each head's 512 bytes land at
+// a 528-byte stride, so the split's reads spread over the LDS banks.  Once
+// the wave holds its query values, slot 2 is free and the wave issues its
+// third chunk there (a wave without a query group issues it with the first
+// two).  Each wave then writes its group's terms as 16-byte quads (quad
+// j < 4 of lane l at 16 (64 j + l) in its slot 3, below the weights; the
+// last quad in LDS outside the ring) and its part of the bound constants;
+// after one barrier every wave reads every group's terms and the constants,
+// and after a second the loop may refill slot 3 (the loop issues the rest,
+// always in order).
 template <int G, int QF>
 __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, const float *__restrict__ wh,
                                                int n_idx_heads, const uint8_t *__restrict__ idx_rows, int64_t row0,
@@ -321,7 +328,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   static_assert(kRingDepth == 4, "the query is staged in ring slots 2 and 3, chunks 0 and 1 go ahead");
   constexpr int kStageHead = 528, kStageW = 16 * kStageHead;
   static_assert(kStageW + 256 <= 2 * kChunkBytes, "group query + weights fit two ring slots");
-  static_assert(kXchQuads * 64 * 16 <= kStageW, "the terms leave the weights alone");
+  static_assert(kXchQuads == 5 && 4 * 64 * 16 == kStageW - kChunkBytes, "four quads in slot 3 below the weights, one outside");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: chunk bookkeeping stays scalar
   const int nch = (rows + kChunkRows - 1) / kChunkRows;
@@ -358,17 +365,21 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   dma4(wh + (lane < n_idx_heads ? lane : n_idx_heads - 1), stage_lds + kStageW);
   if (nmy > 0) fill(0);
   if (nmy > 1) fill(1);
-  // the query has landed once at most the two chunks' loads are outstanding
-  // (loads complete in issue order; a clamped copy waits for itself)
-  if (direct(0) && direct(1))
-    wait_vmcnt<2 * kChunkDma>();
-  else if (direct(0) || direct(1))
-    wait_vmcnt<kChunkDma>();
-  else
-    wait_vmcnt<0>();
+  const bool early2 = wave >= G;  // uniform: no query staged in slot 2
+  if (early2 && nmy > 2) fill(2);
+  // the query and weights have landed once at most the chunks issued after
+  // them are outstanding (loads complete in issue order; direct chunks are
+  // a prefix of the wave's chunks, and a clamped copy waits for itself)
+  switch ((direct(0) ? 1 : 0) + (direct(1) ? 1 : 0) + (early2 && direct(2) ? 1 : 0)) {
+    case 3: wait_vmcnt<3 * kChunkDma>(); break;
+    case 2: wait_vmcnt<2 * kChunkDma>(); break;
+    case 1: wait_vmcnt<kChunkDma>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
   QFrag<1> q[G];
-  FilterBound B;
+  FilterBoundF F;
   {
+    FilterBound B;
     const float *wl = reinterpret_cast<const float *>(stage + kStageW);  // this wave's copy of the weights
     if (wave < G) {
       float x[32];
@@ -397,6 +408,9 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       } else {
         nm = split_qfrag(mine, x);
       }
+      // the query values are in registers: slot 2 takes the third chunk
+      wait_lgkmcnt0();
+      if (nmy > 2) fill(2);
       // this lane's part of the bound constants: |w_h| (rho + 2^-15 A) for its
       // (head, block) fragment, summed over the group's 16 heads per block
       // (lanes 16 b .. 16 b + 15 hold block b); fp64 so that no range is lost
@@ -404,10 +418,9 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       const double wa = h < n_idx_heads ? fabs((double)wl[h]) : 0.0;
       double cz = wa * ((double)nm.rho + 0x1p-15 * (double)nm.mag);
       cz = row_sum_f64(cz);  // lane 15 of each 16-lane row: the row's sum
-      if ((lane & 15) == 15) sh.a.zpart[wave][lane >> 4] = cz;
-      // the terms over the staging area (this wave's reads of it come first):
-      // the lane's words (6 per term, then the packed scales) as 16-byte
-      // quads, quad j of lane l at stage + 16 (64 j + l)
+      if ((lane & 15) == 15) sh.a.pro.zpart[wave][lane >> 4] = cz;
+      // the terms (this wave's reads of its staged query come first): the
+      // lane's words (6 per term, then the packed scales) as 16-byte quads
       uint32_t w[kXchQuads * 4];
 #pragma unroll
       for (int t = 0; t < kTerms; ++t)
@@ -417,9 +430,10 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       for (int j = 0; j < kScaleWords; ++j) w[6 * kTerms + j] = (uint32_t)mine.scw[0][j];
 #pragma unroll
       for (int j = 6 * kTerms + kScaleWords; j < kXchQuads * 4; ++j) w[j] = 0u;
-      uint4 *x16 = reinterpret_cast<uint4 *>(stage) + lane;
+      uint4 *x16 = reinterpret_cast<uint4 *>(&sh.ring[wave][3][0]) + lane;
 #pragma unroll
-      for (int j = 0; j < kXchQuads; ++j) x16[64 * j] = uint4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+      for (int j = 0; j < 4; ++j) x16[64 * j] = uint4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+      sh.a.pro.xq[wave][lane] = uint4{w[16], w[17], w[18], w[19]};
     }
     // Z_abs from the weights (every wave, its own copy): 2^-117 sum_h |w_h|
     double wsum = lane < n_idx_heads ? fabs((double)wl[lane]) : 0.0;
@@ -429,17 +443,18 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     for (int b = 0; b < 4; ++b) {
       double z = 0.0;
 #pragma unroll
-      for (int g = 0; g < G; ++g) z += sh.a.zpart[g][b];
+      for (int g = 0; g < G; ++g) z += sh.a.pro.zpart[g][b];
       B.z[b] = z * (6.0 * (1.0 + 0x1p-10));
     }
     B.zabs = wsum * 0x1p-117;
+    F = bound_f32(B);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4 *x16 = reinterpret_cast<const uint4 *>(&sh.ring[g][2][0]) + lane;
+      const uint4 *x16 = reinterpret_cast<const uint4 *>(&sh.ring[g][3][0]) + lane;
       uint32_t w[kXchQuads * 4];
 #pragma unroll
       for (int j = 0; j < kXchQuads; ++j) {
-        const uint4 v = x16[64 * j];
+        const uint4 v = j < 4 ? x16[64 * j] : sh.a.pro.xq[g][lane];
         w[4 * j] = v.x;
         w[4 * j + 1] = v.y;
         w[4 * j + 2] = v.z;
@@ -455,8 +470,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     // the weights (in slot 3, which the exchange leaves alone)
 #pragma unroll
     for (int g = 0; g < G; ++g) load_qweights(q[g], wl, n_idx_heads, g, lane);
-    __syncthreads();  // every wave has read the terms and weights: the slots are free
-    if (2 < nmy) fill(2);
+    __syncthreads();  // every wave has read the terms and weights: slot 3 is free
   }
 
   uint32_t omax = 0;  // largest score part of this thread's upper bounds
@@ -485,20 +499,24 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
     }
     group_acc4(q[G - 1], c, acc);
-    // lane l: row l of the chunk, summed over every head, and its bracket
-    // from the row's four scale bytes
-    const float v = score_finish(rows_reduce4(acc), 0.0f);
+    // lane l: row l of the chunk, summed over every head (the sign of a zero
+    // is immaterial to the bracket), and its bracket from the row's four
+    // scale bytes
+    const float v = rows_reduce4(acc);
     const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + kIdxRowBytes * lane + 64);
     const int p = kChunkRows * chunk(s) + lane;
     if (p < rows) {
       float up, lo;
-      const double beta = row_bracket(v, sb, B, up, lo);
-      sh.a.score[p] = up;
-      sh.a.beta[p] = bf16_round_up(beta);
-      if (bnd_up) {
+      float beta;
+      if (bnd_up) {  // uniform (the bounds mode)
+        beta = row_bracket<true>(v, sb, F, up, lo);
         bnd_up[p] = up;
         bnd_lo[p] = lo;
+      } else {
+        beta = row_bracket<false>(v, sb, F, up, lo);
       }
+      sh.a.score[p] = up;
+      sh.a.beta[p] = bf16_round_up(beta);
       const uint32_t so = score_ord(up);
       omax = so > omax ? so : omax;
     }
