@@ -8,8 +8,9 @@
 // s_jb the row's UE8M0 byte of block b, with per-query constants
 //     Z_b   = 6 (1 + 2^-10) sum_h |w_h| (rho_hb + 2^-15 A_hb),
 //     Z_abs = 2^-117 sum_h |w_h|,
-// where rho_hb and A_hb are the L1 norms over block b of head h of the query
-// residual and of the terms plus residual (QFragNorms).  Why this holds:
+// where rho_hb is the L1 norm over block b of head h of the query residual
+// and A_hb an upper bound on the L1 norm of the terms plus the residual
+// (QFragNorms).  Why this holds:
 //   * |k_ji| <= 6 * 2^(s_jb - 127) (E2M1's largest magnitude is 6), so the
 //     residual contributes at most sum_h |w_h| sum_b rho_hb 6 2^(s_jb-127)
 //     (the ReLU is 1-Lipschitz);

@@ -61,10 +61,12 @@ struct QFrag {
   float w[G][4];
 };
 
-// L1 norms of one lane's fragment after the split: rho = sum |r| (the
-// residual) and mag = sum over terms of |qt| plus rho (at least sum |q|).
+// Norms of one lane's fragment after the split: rho = sum |r| (the
+// residual's L1 norm) and mag, an upper bound on the L1 norm of the terms
+// plus rho (fp64: no overflow for any finite query).
 struct QFragNorms {
-  float rho, mag;
+  float rho;
+  double mag;
 };
 
 typedef float v16f_q __attribute__((ext_vector_type(16)));
@@ -84,8 +86,10 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 // finer of their spacings and the difference is below 2^(E_t - 2)); after
 // 3 terms |r| <= 2^-2 * 2^(E_0 - 8) < 2^-11.9 * max|x|, since max|x| >
 // 3.75 * 2^E_0 (below 2^-126 the scales stop at 2^-126 and |r| at 2^-130,
-// half the finest term spacing).  Returns the fragment's L1 norms (the
-// bound's inputs).
+// half the finest term spacing).  Returns the bound's inputs: rho = the
+// residual's L1 norm, and mag >= sum_t |q_t| + |r| summed over the block,
+// from |q_t| <= |r_{t-1}| + |r_t| (r_{-1} = x) and |r_t| <= 2^(E_t - 2):
+// mag = sum |x| + sum_t 32 * 2 * 2^(E_t - 2) = sum |x| + sum_t 2^(E_t + 4).
 // Heads past the query's heads carry a zero weight (load_qweights), so
 // their terms (split from a clamped head) add exact zeros to the score.
 // The conversions are gfx950's scaled fp6 instructions (round to nearest
@@ -95,12 +99,13 @@ typedef unsigned v6u_q __attribute__((ext_vector_type(6)));
 // for the residual.
 __device__ __forceinline__ QFragNorms split_qfrag(QFrag<1> &q, const float (&x)[32]) {
   v16f_q re, ro;
-  float amax = 0.0f;
+  float amax = 0.0f, sumx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     re[i] = x[2 * i];
     ro[i] = x[2 * i + 1];
     amax = fmaxf(amax, fmaxf(fabsf(re[i]), fabsf(ro[i])));
+    sumx += fabsf(re[i]) + fabsf(ro[i]);
   }
   // amax = m 2^e, m in [1, 2): amax / 2^(e-2) = 4m is in [4, 8), above 7.5
   // when m > 1.875; a zero block keeps scale 2^0 (its codes are zero)
@@ -110,7 +115,7 @@ __device__ __forceinline__ QFragNorms split_qfrag(QFrag<1> &q, const float (&x)[
   E0 = E0 < -126 ? -126 : (E0 > 127 ? 127 : E0);
 #pragma unroll
   for (int w = 0; w < kScaleWords; ++w) q.scw[0][w] = 0;
-  float mag = 0.0f;
+  double mag = (double)sumx;
 #pragma unroll
   for (int t = 0; t < kTerms; ++t) {
     const int E = E0 - 4 * t < -126 ? -126 : E0 - 4 * t;
@@ -121,15 +126,15 @@ __device__ __forceinline__ QFragNorms split_qfrag(QFrag<1> &q, const float (&x)[
     for (int i = 0; i < 16; ++i) {
       re[i] -= d[2 * i];
       ro[i] -= d[2 * i + 1];
-      mag += fabsf(d[2 * i]) + fabsf(d[2 * i + 1]);
     }
+    mag += __longlong_as_double((long long)((uint64_t)(E + 4 + 1023) << 52));  // 2^(E + 4), E >= -126
     q.a[0][t] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4], (int)c[5], 0, 0};
     q.scw[0][t / 4] |= (E + 127) << (8 * (t % 4));
   }
   float rho = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) rho += fabsf(re[i]) + fabsf(ro[i]);
-  return QFragNorms{rho, mag + rho};
+  return QFragNorms{rho, mag};
 }
 
 // E2M1 code of y (the rounding of an MXFP4 conversion): the magnitude code
@@ -152,25 +157,55 @@ __device__ __forceinline__ uint32_t e2m1_round(float y) {
 // the single fp4 A operand (value i at bit 4i) and its scale byte; deq gets
 // the quantized values (exact in fp32) and the norms are rho = 0 (the
 // quantized query is scored exactly) and mag = sum |deq|.
+// With a normal scale (byte >= 1) the conversions are gfx950's scaled fp4
+// instructions (two values per instruction, the first in the low nibble;
+// round to nearest even, saturating at 6, the sign of a zero kept), and the
+// decoded values come back from the scaled fp4 -> fp32 conversion; a block
+// whose scale is the subnormal 2^-127 takes e2m1_round.
+typedef float v2f_q __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ QFragNorms quantize_qfrag_fp4(QFrag<1> &q, const float (&x)[32], float (&deq)[32]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
   const uint32_t ef = __float_as_uint(amax) >> 23;  // amax >= 0: the exponent field
   const uint32_t byte = ef >= 2u ? ef - 2u : 0u;
-  // 2^(127 - byte) and 2^(byte - 127) as fp32: byte <= 252, so both are
-  // normal except 2^-127 for byte 0, the subnormal 0x00400000
-  const float inv = __uint_as_float((254u - byte) << 23);
-  const float sc = byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   float mag = 0.0f;
+  if (byte != 0u) {
+    const float sc = __uint_as_float(byte << 23);  // 2^(byte - 127), normal
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t c = e2m1_round(x[i] * inv);
-    w[i / 8] |= c << (4 * (i % 8));
-    const float v = e2m1_value(c) * sc;
-    deq[i] = v;
-    mag += fabsf(v);
+    for (int j = 0; j < 4; ++j) {
+      const float *xj = &x[8 * j];
+      uint32_t ww = 0u;
+      ww = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ww, xj[0], xj[1], sc, 0);
+      ww = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ww, xj[2], xj[3], sc, 1);
+      ww = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ww, xj[4], xj[5], sc, 2);
+      ww = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ww, xj[6], xj[7], sc, 3);
+      w[j] = ww;
+      const v2f_q d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww, sc, 0);
+      const v2f_q d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww, sc, 1);
+      const v2f_q d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww, sc, 2);
+      const v2f_q d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww, sc, 3);
+      const v2f_q dd[4] = {d0, d1, d2, d3};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        deq[8 * j + 2 * k] = dd[k][0];
+        deq[8 * j + 2 * k + 1] = dd[k][1];
+        mag += fabsf(dd[k][0]) + fabsf(dd[k][1]);
+      }
+    }
+  } else {
+    // 2^127 and 2^-127 (the subnormal 0x00400000) as fp32
+    const float inv = __uint_as_float(254u << 23);
+    const float sc = __uint_as_float(0x00400000u);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t c = e2m1_round(x[i] * inv);
+      w[i / 8] |= c << (4 * (i % 8));
+      const float v = e2m1_value(c) * sc;
+      deq[i] = v;
+      mag += fabsf(v);
+    }
   }
 #pragma unroll
   for (int t = 0; t < kTerms; ++t) q.a[0][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -178,7 +213,7 @@ __device__ __forceinline__ QFragNorms quantize_qfrag_fp4(QFrag<1> &q, const floa
 #pragma unroll
   for (int j = 0; j < kScaleWords; ++j) q.scw[0][j] = 0;
   q.scw[0][0] = (int)byte;
-  return QFragNorms{0.0f, mag};
+  return QFragNorms{0.0f, (double)mag};
 }
 
 // The weights of the heads whose results lane `lane` holds for group g:

@@ -416,7 +416,7 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
       // (lanes 16 b .. 16 b + 15 hold block b); fp64 so that no range is lost
       const int h = 16 * wave + (lane & 15);
       const double wa = h < n_idx_heads ? fabs((double)wl[h]) : 0.0;
-      double cz = wa * ((double)nm.rho + 0x1p-15 * (double)nm.mag);
+      double cz = wa == 0.0 ? 0.0 : wa * ((double)nm.rho + 0x1p-15 * nm.mag);
       cz = row_sum_f64(cz);  // lane 15 of each 16-lane row: the row's sum
       if ((lane & 15) == 15) sh.a.pro.zpart[wave][lane >> 4] = cz;
       // the terms (this wave's reads of its staged query come first): the

@@ -6,13 +6,17 @@ The decode step scores rows with the query held to three fp6 (E2M3) terms per
     beta_j = sum_b Z_b 2^(s_jb - 127) + Z_abs,
     Z_b = 6 (1 + 2^-10) sum_h |w_h| (rho_hb + 2^-15 A_hb),  Z_abs = 2^-117 sum_h |w_h|,
 
-rho_hb = L1 norm of the query residual of head h in block b, A_hb = L1 norm of
-the terms plus rho_hb (csa_bound.hpp).  Here the split is emulated in numpy
+rho_hb = L1 norm of the query residual of head h in block b, A_hb = an upper
+bound on the L1 norm of the terms plus rho_hb: the kernel takes
+A_hb = sum |q| + sum_t 2^(E_t + 4) over the block's term exponents E_t
+(csa_score.hpp, csa_bound.hpp).  Here the split is emulated in numpy
 (the same exponent rule, round-to-nearest-even onto the E2M3 grid) and the
 bound is checked against exact arithmetic on adversarial queries:
 
   * the split is exact: q = t0 + t1 + t2 + r, and |r| <= max(2^-11.9 max|q|,
     2^-130) per block (the floor: term scales stop at 2^-126);
+  * the kernel's closed-form A_hb is at least the exact L1 norm of the terms
+    plus the residual;
   * the filter's score with exact sums, s~ = sum_h w_h max(0, (t0+t1+t2)_h . k),
     lies within the residual part of beta of the exact score, and the oracle's
     fp32 score lies within beta of s~;
@@ -52,11 +56,14 @@ def split_block(x: np.ndarray, terms: int = 3):
     E0 = min(max(E0, -126), 127)
     r = x.astype(np.float64)
     out = []
+    exps = []
     for t in range(terms):
         E = max(E0 - 4 * t, -126)
         qt = e2m3_rne(r / 2.0**E) * 2.0**E
         out.append(qt)
+        exps.append(E)
         r = r - qt
+    split_block.exps = exps
     return out, r
 
 
@@ -95,7 +102,11 @@ def bound_constants(q: np.ndarray, w: np.ndarray):
             # finest term spacing (scales clamp at 2^-126: subnormal blocks)
             assert np.max(np.abs(r)) <= max(2.0**-11.9 * amax, 2.0**-130)
             rho[hh, b] = np.sum(np.abs(r))
-            mag[hh, b] = sum(np.sum(np.abs(t)) for t in terms) + rho[hh, b]
+            exact_mag = sum(np.sum(np.abs(t)) for t in terms) + rho[hh, b]
+            # the kernel's closed form, an upper bound on that norm
+            mag[hh, b] = np.sum(np.abs(q[hh, 32 * b:32 * b + 32].astype(np.float64))) + sum(
+                2.0 ** (E + 4) for E in split_block.exps)
+            assert mag[hh, b] >= exact_mag
             qt_sum[hh, 32 * b:32 * b + 32] = t_sum
     wa = np.abs(w.astype(np.float64))
     z_res = 6.0 * (wa[:, None] * rho).sum(axis=0)                      # residual part, per block
