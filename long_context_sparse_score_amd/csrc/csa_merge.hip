@@ -283,17 +283,6 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       return;
     }
   }
-  // warm the L2 with the KV rows of this workgroup's candidates (a superset
-  // of the rows it will attend over) while the ranks are computed
-  uint32_t warm = 0;
-  if constexpr (ATTN) {
-    const uint8_t *kv = a.s[sess].kv_rows;
-    for (int t = tid; t < nm * 6; t += kSelThreads) {
-      const uint32_t row = key_row(sh.u.s.cand[sh.u.s.mine[t / 6]]);
-      const int off = 128 * (t % 6) < kKvRowBytes - 1 ? 128 * (t % 6) : kKvRowBytes - 1;
-      warm ^= kv[(size_t)row * kKvRowBytes + off];
-    }
-  }
   for (int m = wave; m < nm; m += kSelWaves) {
     const uint64_t x = sh.u.s.cand[sh.u.s.mine[m]];
     uint32_t r = 0;
@@ -322,7 +311,6 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
     }
   }
   if constexpr (!ATTN) return;
-  if (warm == 0x5A5A5A5Au && a.k < 0) sel_idx[0] = 0;  // never true (k >= 1): keeps the warming loads
 
   // 4. attention over this workgroup's selected rows, in rank order
   __syncthreads();
