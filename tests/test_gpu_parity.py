@@ -264,6 +264,38 @@ def test_fused_equals_unfused(csa, n_rows):
     assert np.array_equal(_np(sel), gu.topk_keys_host(_np(scores), 512))
 
 
+@pytest.mark.parametrize("pattern", ["one_stretch", "ascending", "descending", "clustered", "two_rows"])
+def test_decode_step_adversarial_layouts(csa, orc, pattern):
+    """The decode step (filter, tile heads, rescoring, selection) on score
+    layouts built from the rows themselves: a row's scale bytes set its
+    scores' magnitude, so the winners can be packed into one stretch of
+    rows (whole tiles are then "full" and rescored row by row), sit at the
+    end or the start, form clusters, or tie massively (two distinct rows).
+    The selection must still be exactly the oracle's."""
+    n = 60000
+    s = gen.session(1, n_rows=n, seed_=91)
+    idx = s["idx_rows"]
+    r = np.arange(n)
+    if pattern == "one_stretch":  # 700 consecutive rows eight times larger
+        idx[:, 64:68] = 120
+        idx[30000:30700, 64:68] = 123
+    elif pattern == "ascending":  # every winner among the last rows
+        idx[:, 64:68] = (110 + (20 * r) // n)[:, None]
+    elif pattern == "descending":
+        idx[:, 64:68] = (130 - (20 * r) // n)[:, None]
+    elif pattern == "clustered":  # eight clusters of 90 rows
+        idx[:, 64:68] = 118
+        for c in range(8):
+            idx[5000 + 7000 * c:5090 + 7000 * c, 64:68] = 121
+    else:  # two distinct rows alternating: ties decided by the row index
+        a, b = idx[3].copy(), idx[4].copy()
+        idx[0::2] = a
+        idx[1::2] = b
+    print(f"adversarial layout {pattern}: n_rows={n}", flush=True)
+    got = _run_step(csa, [s], s["softmax_scale"])[0]
+    _check_session(orc, s, got)
+
+
 def test_zero_cache_selects_first_rows(csa, orc):
     s = gen.session(1, n_rows=20000)
     s["idx_rows"] = np.zeros_like(s["idx_rows"])
