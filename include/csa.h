@@ -223,9 +223,11 @@ int csa_decode_step(const csa_session *sessions, int n_sessions, int n_idx_heads
 
 /* csa_decode_step that also records events[2*s] right before and
  * events[2*s+1] right after the launches of stage s on hip_stream, so a
- * caller can time each stage with hipEventElapsedTime.  `events` is a HOST
- * array of 2*CSA_STAGES hipEvent_t (as void*) created by the caller; the
- * work done is exactly that of csa_decode_step. */
+ * caller can time each stage with hipEventElapsedTime; stage 0's score
+ * kernel records its two events at its own start and end (an extended HIP
+ * launch), so they time the kernel rather than the queue around it.
+ * `events` is a HOST array of 2*CSA_STAGES hipEvent_t (as void*) created by
+ * the caller; the work done is exactly that of csa_decode_step. */
 int csa_decode_step_timed(const csa_session *sessions, int n_sessions, int n_idx_heads, int n_heads,
                           float softmax_scale, void *ws, size_t ws_bytes, void *hip_stream,
                           void *const *events);

@@ -541,9 +541,14 @@ static int decode_step_impl(const csa_session *sessions, int n_sessions, int n_i
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
   };
-  hipError_t e = mark(0);
-  if (e == hipSuccess && !exact_all) e = launch_tiles(job, st);
-  if (e == hipSuccess) e = mark(1);
+  // the score kernel records stage 0's events at its own start and end
+  hipError_t e = hipSuccess;
+  if (exact_all) {
+    e = mark(0);
+    if (e == hipSuccess) e = mark(1);
+  } else {
+    e = launch_tiles(job, st, events ? (hipEvent_t)events[0] : nullptr, events ? (hipEvent_t)events[1] : nullptr);
+  }
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess && any_rows) e = launch_refine(rj, st);
   if (e == hipSuccess) e = mark(3);

@@ -147,7 +147,11 @@ hipError_t launch_pack(const float *kv_vals, const float *idx_vals, int64_t n, u
 // The merge of two attention results over disjoint rows (csa_pack.hip).
 hipError_t launch_lse_merge(const float *out_a, const float *lse_a, const float *out_b, const float *lse_b,
                             int n_heads, float *out, float *lse, hipStream_t st);
-hipError_t launch_tiles(const TileJob &job, hipStream_t st);
+// With ev_start and ev_end (both or neither) the scoring launch records them
+// at its own start and end (hipExtLaunchKernelGGL), so they time the kernel
+// itself rather than the queue around it.
+hipError_t launch_tiles(const TileJob &job, hipStream_t st, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_end = nullptr);
 hipError_t launch_refine(const RefineJob &job, hipStream_t st);
 hipError_t launch_select(const SelectJob &job, hipStream_t st);
 // Attention partials of the rows sel_idx[0..n_sel) of every session, one

@@ -26,6 +26,8 @@
 // Only keys >= theta can be among the top hd+1: typically a few times hd of
 // them, ranked exactly against each other (an exact k-th selection replaces
 // theta when they overflow the candidate buffer).
+#include <hip/hip_ext.h>
+
 #include "csa_attn.hpp"
 #include "csa_bound.hpp"
 #include "csa_device.hpp"
@@ -580,33 +582,47 @@ __global__ void __launch_bounds__(kTileThreads, 2) tile_kernel(const TileArgs a)
 
 // ---------------------------------------------------------------- launcher
 
+template <int G, int QF>
+static void launch_scoring_g(const TileArgs &a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (e0)
+    hipExtLaunchKernelGGL(tile_kernel<G, false, QF>, grid, dim3(kTileThreads), 0, st, e0, e1, 0, a);
+  else
+    tile_kernel<G, false, QF><<<grid, kTileThreads, 0, st>>>(a);
+}
+
 template <int QF>
-static void launch_scoring_q(const TileArgs &a, dim3 grid, int groups, hipStream_t st) {
+static void launch_scoring_q(const TileArgs &a, dim3 grid, int groups, hipStream_t st, hipEvent_t e0,
+                             hipEvent_t e1) {
   // three groups run as four: the query split holds zero terms and weights
   // for heads past n_idx_heads, which add exact zeros
   switch (groups) {
-    case 1: tile_kernel<1, false, QF><<<grid, kTileThreads, 0, st>>>(a); break;
-    case 2: tile_kernel<2, false, QF><<<grid, kTileThreads, 0, st>>>(a); break;
-    default: tile_kernel<4, false, QF><<<grid, kTileThreads, 0, st>>>(a); break;
+    case 1: launch_scoring_g<1, QF>(a, grid, st, e0, e1); break;
+    case 2: launch_scoring_g<2, QF>(a, grid, st, e0, e1); break;
+    default: launch_scoring_g<4, QF>(a, grid, st, e0, e1); break;
   }
 }
 
-static hipError_t launch_scoring(const TileArgs &a, dim3 grid, int groups, int qfmt, hipStream_t st) {
+static hipError_t launch_scoring(const TileArgs &a, dim3 grid, int groups, int qfmt, hipStream_t st,
+                                 hipEvent_t e0, hipEvent_t e1) {
   if (qfmt == kQueryMxfp4)
-    launch_scoring_q<kQueryMxfp4>(a, grid, groups, st);
+    launch_scoring_q<kQueryMxfp4>(a, grid, groups, st, e0, e1);
   else
-    launch_scoring_q<kQueryFp32>(a, grid, groups, st);
+    launch_scoring_q<kQueryFp32>(a, grid, groups, st, e0, e1);
   return hipGetLastError();
 }
 
-hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
+hipError_t launch_tiles(const TileJob &job, hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_end) {
   TileArgs a;
   int64_t max_rows = 0;
   for (int i = 0; i < job.n_sessions; ++i) {
     a.s[i] = TileSession{job.idx_rows[i], job.scores_in[i], job.q[i], job.w[i], job.n_rows[i], job.hd[i]};
     max_rows = job.n_rows[i] > max_rows ? job.n_rows[i] : max_rows;
   }
-  if (max_rows == 0) return hipSuccess;
+  if (max_rows == 0) {  // nothing to score: the events mark the empty stage
+    hipError_t e = ev_start ? hipEventRecord(ev_start, st) : hipSuccess;
+    if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, st);
+    return e;
+  }
   a.n_idx_heads = job.n_idx_heads;
   a.hkey = job.hkey;
   a.hlow = job.hlow;
@@ -627,10 +643,13 @@ hipError_t launch_tiles(const TileJob &job, hipStream_t st) {
   const unsigned nt = (unsigned)((max_rows + job.tile_rows - 1) / job.tile_rows);
   dim3 grid = shared ? dim3(nt * (unsigned)job.n_sessions, 1u) : dim3(nt, (unsigned)job.n_sessions);
   if (job.mode == TileJob::kArray) {
-    tile_kernel<1, true, kQueryFp32><<<grid, kTileThreads, 0, st>>>(a);
+    if (ev_start)
+      hipExtLaunchKernelGGL(tile_kernel<1, true, kQueryFp32>, grid, dim3(kTileThreads), 0, st, ev_start, ev_end, 0, a);
+    else
+      tile_kernel<1, true, kQueryFp32><<<grid, kTileThreads, 0, st>>>(a);
     return hipGetLastError();
   }
-  return launch_scoring(a, grid, groups, job.query_format, st);
+  return launch_scoring(a, grid, groups, job.query_format, st, ev_start, ev_end);
 }
 
 }  // namespace csa
