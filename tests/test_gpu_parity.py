@@ -346,6 +346,31 @@ def test_sparse_attn_crowded_row_group(csa, orc, count):
     assert np.allclose(_np(lse), ref_lse, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("n_rows,fmt", [(20000, "fp32"), (20000, "mxfp4"), (300, "fp32")])
+def test_decode_step_timed_matches_untimed(csa, n_rows, fmt):
+    """The timed decode step (stage events) does exactly the untimed step's
+    work: identical outputs.  Every stage's event pair completes; stage 0's
+    pair, recorded by the score kernel's launch at the kernel's own start
+    and end, spans a positive time whenever the kernel runs (a short fp32
+    history skips it, and its pair is then recorded back to back)."""
+    s = gen.session(1, n_rows=n_rows)
+    d = gu.to_dev(s)
+    ref = csa.decode_step([dict(d)], s["softmax_scale"], query_format=fmt)[0]
+    ref = {k: ref[k].clone() for k in ("sel", "sel_score", "out", "lse")}
+    step = csa.DecodeStep([dict(d)], s["softmax_scale"], query_format=fmt)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(csa.STAGES))]
+    step.timed(evs)
+    torch.cuda.synchronize()
+    got = step.sessions[0]
+    for k, v in ref.items():
+        assert torch.equal(got[k], v), k
+    ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(csa.STAGES))]
+    print(f"stage ms {ms}")
+    assert all(m >= 0.0 for m in ms)
+    if n_rows > 4096 or fmt == "mxfp4":
+        assert ms[0] > 0.0
+
+
 def test_deterministic(csa):
     s = gen.session(1, n_rows=40000)
     a = _run_step(csa, [s], s["softmax_scale"])[0]
