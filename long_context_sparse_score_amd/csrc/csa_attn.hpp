@@ -628,22 +628,6 @@ __device__ __forceinline__ void attn_combine_head(const float *ml, const float *
   }
 }
 
-// Order a group's entries by their key (rank or position, distinct),
-// ascending: out_rows[i] = row of the i-th.  keys/rows[0..m) in LDS; all
-// threads call it; ends with a barrier.
-__device__ __forceinline__ void attn_order(const int32_t *keys, const int32_t *rows, int m, int32_t *out_rows) {
-  for (int i = threadIdx.x; i < m; i += kAttnThreads) {
-    const int32_t k = keys[i];
-    int r = 0;
-    for (int j0 = 0; j0 < m; j0 += 16) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) r += (j0 + u < m && keys[j0 + u] < k) ? 1 : 0;
-    }
-    out_rows[r] = rows[i];
-  }
-  __syncthreads();
-}
-
 // Attention over a row group's rows (in order) for head group g -> the
 // partial of those heads.  Rows are staged kRawRows at a time; the next
 // stage's loads are in flight while a batch is computed.  All threads call

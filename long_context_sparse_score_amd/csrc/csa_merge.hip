@@ -72,7 +72,7 @@ struct SelShared {
     } s;
     AttnStage st;  // used after the ranks are written
   } u;
-  int32_t loc_rank[CSA_TOPK + 16], loc_row[CSA_TOPK], ordered[CSA_TOPK];
+  int32_t loc_row[CSA_TOPK], ordered[CSA_TOPK];
   uint32_t ccnt, nmine, nloc;
 };
 // The early stage's rows are copied in while the group list (mine) is
@@ -283,31 +283,55 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       return;
     }
   }
-  for (int m = wave; m < nm; m += kSelWaves) {
-    const uint64_t x = sh.u.s.cand[sh.u.s.mine[m]];
-    uint32_t r = 0;
+  // wave w ranks group entries w, w + 8, ... two per pass over the
+  // candidates.  With attention, a selected entry's position in the
+  // group's key order is the number of group entries with a larger key
+  // (every such entry has a smaller rank, so it is selected too): the
+  // selected rows land in ordered[0..nl) in rank order directly.
+  for (int m0 = wave; m0 < nm; m0 += 2 * kSelWaves) {
+    const int m1 = m0 + kSelWaves;
+    const bool two = m1 < nm;  // uniform
+    const uint64_t x0 = sh.u.s.cand[sh.u.s.mine[m0]];
+    const uint64_t x1 = two ? sh.u.s.cand[sh.u.s.mine[m1]] : x0;
+    uint32_t r0 = 0, r1 = 0;
     for (int j0 = 0; j0 < C; j0 += 4 * 64) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = j0 + 64 * u + lane;
         const uint64_t y = sh.u.s.cand[j];
-        r += (uint32_t)__popcll(__ballot(j < C && y > x));
+        r0 += (uint32_t)__popcll(__ballot(j < C && y > x0));
+        r1 += (uint32_t)__popcll(__ballot(j < C && y > x1));
       }
     }
-    if (lane == 0 && r < (uint32_t)k_eff) {
-      const uint32_t row = key_row(x);
-      if (writer) {
-        sel_idx[r] = (int32_t)row;
-        if (sel_score) {
-          if constexpr (ATTN)  // the fused path: the key holds the score
-            sel_score[r] = key_score(x);
-          else
-            sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+    uint32_t p0 = 0, p1 = 0;  // positions in the group's key order
+    if constexpr (ATTN) {
+      for (int j0 = 0; j0 < nm; j0 += 64) {
+        const int j = j0 + lane;
+        const uint64_t y = j < nm ? sh.u.s.cand[sh.u.s.mine[j]] : 0ull;
+        p0 += (uint32_t)__popcll(__ballot(y > x0));
+        p1 += (uint32_t)__popcll(__ballot(y > x1));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint64_t x = t == 0 ? x0 : x1;
+      const uint32_t r = t == 0 ? r0 : r1;
+      if (lane == 0 && (t == 0 || two) && r < (uint32_t)k_eff) {
+        const uint32_t row = key_row(x);
+        if (writer) {
+          sel_idx[r] = (int32_t)row;
+          if (sel_score) {
+            if constexpr (ATTN)  // the fused path: the key holds the score
+              sel_score[r] = key_score(x);
+            else
+              sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+          }
+        }
+        if constexpr (ATTN) {
+          sh.ordered[t == 0 ? p0 : p1] = (int32_t)row;
+          atomicAdd(&sh.nloc, 1u);
         }
       }
-      const uint32_t p = atomicAdd(&sh.nloc, 1u);
-      sh.loc_rank[p] = (int32_t)r;
-      sh.loc_row[p] = (int32_t)row;
     }
   }
   if constexpr (!ATTN) return;
@@ -315,7 +339,6 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   // 4. attention over this workgroup's selected rows, in rank order
   __syncthreads();
   const int nl = (int)sh.nloc;
-  attn_order(sh.loc_rank, sh.loc_row, nl, sh.ordered);
   attn_group_rows(a.attn_q + (size_t)sess * kAttnQVecs, sh.u.st, sh.ordered, nl, a.s[sess].kv_rows, a.softmax_scale, a.n_heads,
                   hgroup, a.attn_part + (size_t)sess * kAttnPartFloats + (size_t)myslice * CSA_MAX_HEADS * kKvDim,
                   a.attn_ml + (size_t)sess * kAttnMlFloats + (size_t)myslice * CSA_MAX_HEADS * 2);
