@@ -19,6 +19,9 @@
 //      row group's candidates, the first writes the selection, and each runs
 //      the attention of those rows in rank order for its heads and writes
 //      their partial (csa_attn.hpp; the same partials as csa_sparse_attn's).
+//      A selected candidate's place in that order is the number of the row
+//      group's candidates with a larger key (each of them is selected too),
+//      found while ranking, so no sort follows.
 // Selection keys are (ord32(score) << 32) | (2^32 - 1 - row): distinct,
 // larger = better; 0 means "no key".
 #include "csa_attn.hpp"
