@@ -9,6 +9,8 @@
 //   1. G: a lower bound on the k_eff-th largest key, found with histogram
 //      passes (block_bound): at least k_eff keys are >= G, and at most
 //      kSelTarget are (or exactly k_eff); the top-k lies among the keys >= G.
+//      With at most kSelRankAll keys G admits them all (ranking that many
+//      costs less than the passes).
 //   2. Candidates = keys >= G.  If they overflow the LDS buffer (many ties,
 //      crowded winners), the exact k_eff-th key among them replaces G.
 //   3. The candidates are ranked exactly (rank = number of larger
@@ -37,6 +39,8 @@ constexpr int kSelKPT = 8;                            // keys per thread in regi
 constexpr int kSelRegKeys = kSelThreads * kSelKPT;   // 4096
 constexpr int kSelCap = 4096;                         // candidates held in LDS
 constexpr int kSelTarget = 1024;                      // candidates at which G is good enough
+constexpr int kSelRankAll = 1024;  // at most this many keys: all are ranked (no bound passes)
+static_assert(kSelRankAll <= kSelCap, "the candidates fit the LDS buffer");
 
 struct SelSessionArgs {
   const float *scores;  // csa_topk: the given scores (sel_score returns their values)
@@ -183,7 +187,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
   };
 
   // 1. the bound G
-  const uint64_t G = block_bound<kSelWaves>(visit_all, (uint32_t)k_eff, (uint32_t)kSelTarget, sh.u.s.bs);
+  const uint64_t G =
+      block_bound<kSelWaves>(visit_all, (uint32_t)k_eff, (uint32_t)kSelTarget, sh.u.s.bs, (uint32_t)kSelRankAll);
 
   // 2. candidates: one LDS atomic per wave and batch, the wave's selected
   // slots taking consecutive positions

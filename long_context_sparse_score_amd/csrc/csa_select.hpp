@@ -267,10 +267,13 @@ struct BoundShared {
 // (every thread visits its share, calling f(key) for each nonzero key): at
 // least need keys are >= G, and at most max(target, need) are, unless the
 // finest bin already holds more.  Returns 1 (every key) when there are at
-// most need keys.  Histogram passes over the key range, 2 NW 64 bins each,
-// narrowing to the bin that holds the need-th key.  All threads call it.
+// most max(need, all_upto) keys (a caller that handles that many keys as
+// cheaply as it narrows them skips the passes).  Histogram passes over the
+// key range, 2 NW 64 bins each, narrowing to the bin that holds the need-th
+// key.  All threads call it.
 template <int NW, class Visit>
-__device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint32_t target, BoundShared<NW> &sh) {
+__device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint32_t target, BoundShared<NW> &sh,
+                                                uint32_t all_upto = 0) {
   constexpr int NT = NW * 64, kBins = BoundShared<NW>::kBins;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   auto umin = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
@@ -303,7 +306,7 @@ __device__ __forceinline__ uint64_t block_bound(Visit visit, uint32_t need, uint
     total += sh.red_n[w];
   }
   uint64_t lo = (uint64_t)omin << 32, hi = ((uint64_t)omax << 32) | 0xFFFFFFFFull;
-  if (total <= need) return 1ull;
+  if (total <= need || total <= all_upto) return 1ull;
   uint32_t above = 0;  // keys above the current range [lo, hi]
   for (bool first = true;; first = false) {
     const uint64_t span = hi - lo;
