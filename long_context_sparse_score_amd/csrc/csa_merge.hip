@@ -291,52 +291,55 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const SelArgs a) {
       return;
     }
   }
-  // wave w ranks group entries w, w + 8, ... two per pass over the
-  // candidates.  With attention, a selected entry's position in the
-  // group's key order is the number of group entries with a larger key
-  // (every such entry has a smaller rank, so it is selected too): the
-  // selected rows land in ordered[0..nl) in rank order directly.
-  for (int m0 = wave; m0 < nm; m0 += 2 * kSelWaves) {
-    const int m1 = m0 + kSelWaves;
-    const bool two = m1 < nm;  // uniform
-    const uint64_t x0 = sh.u.s.cand[sh.u.s.mine[m0]];
-    const uint64_t x1 = two ? sh.u.s.cand[sh.u.s.mine[m1]] : x0;
-    uint32_t r0 = 0, r1 = 0;
+  // wave w ranks group entries w, w + 8, w + 16, ... up to four per pass
+  // over the candidates (the entries of one pass are uniform over the
+  // wave).  With attention, a selected entry's position in the group's key
+  // order is the number of group entries with a larger key (every such
+  // entry has a smaller rank, so it is selected too): the selected rows land
+  // in ordered[0..nl) in rank order directly.
+  constexpr int kRankPer = 4;
+  for (int m0 = wave; m0 < nm; m0 += kRankPer * kSelWaves) {
+    uint64_t x[kRankPer];
+    bool has[kRankPer];
+#pragma unroll
+    for (int t = 0; t < kRankPer; ++t) {
+      const int m = m0 + kSelWaves * t;
+      has[t] = m < nm;  // uniform
+      x[t] = has[t] ? sh.u.s.cand[sh.u.s.mine[m]] : ~0ull;  // (all ones: no candidate is larger)
+    }
+    uint32_t r[kRankPer] = {}, pos[kRankPer] = {};
     for (int j0 = 0; j0 < C; j0 += 4 * 64) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = j0 + 64 * u + lane;
         const uint64_t y = sh.u.s.cand[j];
-        r0 += (uint32_t)__popcll(__ballot(j < C && y > x0));
-        r1 += (uint32_t)__popcll(__ballot(j < C && y > x1));
+#pragma unroll
+        for (int t = 0; t < kRankPer; ++t) r[t] += (uint32_t)__popcll(__ballot(j < C && y > x[t]));
       }
     }
-    uint32_t p0 = 0, p1 = 0;  // positions in the group's key order
-    if constexpr (ATTN) {
+    if constexpr (ATTN) {  // positions in the group's key order
       for (int j0 = 0; j0 < nm; j0 += 64) {
         const int j = j0 + lane;
         const uint64_t y = j < nm ? sh.u.s.cand[sh.u.s.mine[j]] : 0ull;
-        p0 += (uint32_t)__popcll(__ballot(y > x0));
-        p1 += (uint32_t)__popcll(__ballot(y > x1));
+#pragma unroll
+        for (int t = 0; t < kRankPer; ++t) pos[t] += (uint32_t)__popcll(__ballot(y > x[t]));
       }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint64_t x = t == 0 ? x0 : x1;
-      const uint32_t r = t == 0 ? r0 : r1;
-      if (lane == 0 && (t == 0 || two) && r < (uint32_t)k_eff) {
-        const uint32_t row = key_row(x);
+    for (int t = 0; t < kRankPer; ++t) {
+      if (lane == 0 && has[t] && r[t] < (uint32_t)k_eff) {
+        const uint32_t row = key_row(x[t]);
         if (writer) {
-          sel_idx[r] = (int32_t)row;
+          sel_idx[r[t]] = (int32_t)row;
           if (sel_score) {
             if constexpr (ATTN)  // the fused path: the key holds the score
-              sel_score[r] = key_score(x);
+              sel_score[r[t]] = key_score(x[t]);
             else
-              sel_score[r] = a.array_scores ? scores[row] : key_score(x);
+              sel_score[r[t]] = a.array_scores ? scores[row] : key_score(x[t]);
           }
         }
         if constexpr (ATTN) {
-          sh.ordered[t == 0 ? p0 : p1] = (int32_t)row;
+          sh.ordered[pos[t]] = (int32_t)row;
           atomicAdd(&sh.nloc, 1u);
         }
       }
