@@ -1,8 +1,9 @@
-// csa_qsplit.hip -- the attention query split for csa_sparse_attn: three
-// bf16 terms per value in the matrix-core operand order of csa_attn.hpp
-// (attn_q_split_task).  The decode step does the same split inside the score
-// kernel, and the indexer query is split in registers by every score wave
-// (csa_score.hpp), so this launch serves the stand-alone attention only.
+// csa_qsplit.hip -- the attention query split for csa_sparse_attn and
+// csa_dense_attn: three bf16 terms per value in the matrix-core operand order
+// of csa_attn.hpp (attn_q_split_task).  The decode step does the same split
+// inside the exact rescoring kernel (a share per workgroup), and the indexer
+// query is split in registers by the score kernel's waves (csa_score.hpp), so
+// this launch serves the stand-alone attention only.
 #include "csa_attn.hpp"
 #include "csa_internal.hpp"
 
