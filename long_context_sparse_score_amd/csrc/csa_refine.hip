@@ -125,9 +125,10 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
 // read serves every lane), the rows' chains interleaved and each step's
 // operands read a step ahead so the reads overlap the arithmetic.  The
 // heads' terms w_h max(0, d_h) (exactly +0 for lanes past n_heads) go to LDS
-// and every lane adds all 64 in head order, sixteen reads at a time: a +0
-// term leaves the sum unchanged (the sum starts at +0 and cannot become -0),
-// so this is the reference's sum over the n_heads heads.
+// and every lane adds them in head order, sixteen reads at a time, up to
+// n_heads rounded up to 16: a +0 term leaves the sum unchanged (the sum
+// starts at +0 and cannot become -0), so this is the reference's sum over
+// the n_heads heads.
 // out[r] is S of row r in every lane.
 template <int N>
 __device__ __forceinline__ void exact_scores(const RowBytes (&rb)[N], int n_heads, RefineShared &sh, float (&out)[N]) {
@@ -185,7 +186,7 @@ __device__ __forceinline__ void exact_scores(const RowBytes (&rb)[N], int n_head
 #pragma unroll
   for (int r = 0; r < N; ++r) acc[r] = 0.0;
 #pragma unroll 1
-  for (int c = 0; c < CSA_MAX_HEADS; c += 16) {
+  for (int c = 0; c < n_heads; c += 16) {  // (the +0 terms past n_heads are skipped)
     double2 v[N][8];
 #pragma unroll
     for (int r = 0; r < N; ++r)
