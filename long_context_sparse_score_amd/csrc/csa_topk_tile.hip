@@ -476,6 +476,39 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
   }
 
   uint32_t omax = 0;  // largest score part of this thread's upper bounds
+  // With the fp32 query (three products per group and row block) a chunk's
+  // last group of products, its partial sums over the other groups, its
+  // scale bytes and this lane's tile position are carried into the next
+  // step: the last group's epilogue, the row sums and the bracket run behind
+  // the next chunk's first products (the same arithmetic in the same order).
+  // The MXFP4 query (one product) finishes each chunk in its own step.
+  constexpr bool kCarry = QF == kQueryFp32;
+  float accp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f cp[4][1];
+  uint32_t sbp = 0;
+  int pp = 0;
+  auto finish = [&]() __attribute__((always_inline)) {
+    group_acc4(q[G - 1], cp, accp);
+    // lane l: row l of the chunk, summed over every head (the sign of a zero
+    // is immaterial to the bracket), and its bracket from the row's four
+    // scale bytes
+    const float v = rows_reduce4(accp);
+    if (pp < rows) {
+      float up, lo;
+      float beta;
+      if (bnd_up) {  // uniform (the bounds mode)
+        beta = row_bracket<true>(v, sbp, F, up, lo);
+        bnd_up[pp] = up;
+        bnd_lo[pp] = lo;
+      } else {
+        beta = row_bracket<false>(v, sbp, F, up, lo);
+      }
+      sh.a.score[pp] = up;
+      sh.a.beta[pp] = bf16_round_up(beta);
+      const uint32_t so = score_ord(up);
+      omax = so > omax ? so : omax;
+    }
+  };
   for (int s = 0; s < nmy; ++s) {
     int later = 0;
 #pragma unroll
@@ -490,9 +523,13 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
     const uint8_t *base = &sh.ring[wave][s % kRingDepth][0];
     RowOperand ops[4];
     load_ops(base, ops);
+    const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + kIdxRowBytes * lane + 64);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f c[4][1], cn[4][1];
     group_dots<4, QF>(q[0], ops, c);
+    if constexpr (kCarry) {
+      if (s > 0) finish();  // the previous chunk
+    }
 #pragma unroll
     for (int g = 1; g < G; ++g) {
       group_dots<4, QF>(q[g], ops, cn);
@@ -500,28 +537,17 @@ __device__ __forceinline__ uint32_t score_tile(const float *__restrict__ qh, con
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[r][0] = cn[r][0];
     }
-    group_acc4(q[G - 1], c, acc);
-    // lane l: row l of the chunk, summed over every head (the sign of a zero
-    // is immaterial to the bracket), and its bracket from the row's four
-    // scale bytes
-    const float v = rows_reduce4(acc);
-    const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + kIdxRowBytes * lane + 64);
-    const int p = kChunkRows * chunk(s) + lane;
-    if (p < rows) {
-      float up, lo;
-      float beta;
-      if (bnd_up) {  // uniform (the bounds mode)
-        beta = row_bracket<true>(v, sb, F, up, lo);
-        bnd_up[p] = up;
-        bnd_lo[p] = lo;
-      } else {
-        beta = row_bracket<false>(v, sb, F, up, lo);
-      }
-      sh.a.score[p] = up;
-      sh.a.beta[p] = bf16_round_up(beta);
-      const uint32_t so = score_ord(up);
-      omax = so > omax ? so : omax;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      cp[r][0] = c[r][0];
+      accp[r] = acc[r];
     }
+    sbp = sb;
+    pp = kChunkRows * chunk(s) + lane;
+    if constexpr (!kCarry) finish();
+  }
+  if constexpr (kCarry) {
+    if (nmy > 0) finish();
   }
   __syncthreads();
   return omax;
